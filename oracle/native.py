@@ -1,0 +1,85 @@
+"""ctypes loader for the C float64 oracle (``kda_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+benchmark's CPU-baseline leg, never by the GPU library.
+
+``build()`` compiles ``kda_oracle.c`` with gcc + OpenMP into
+``oracle/liboracle.so``; ``recurrent()`` calls it on float64 NumPy arrays.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kda_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+GATE_MODES = {"bounded": 0, "logsigmoid": 1}
+
+
+def build(force: bool = True) -> str:
+    """Compile the C oracle (gcc -O2 -fopenmp); returns the library path."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-fno-fast-math", "-fopenmp", "-fPIC", "-shared",
+               "-std=c99", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
+        dp = ctypes.POINTER(ctypes.c_double)
+        lib.kda_oracle_recurrent.argtypes = [dp, dp, dp, dp, dp] + [ctypes.c_long] * 5 + [
+            ctypes.c_double, ctypes.c_int, ctypes.c_int, dp, dp, dp]
+        lib.kda_oracle_recurrent.restype = ctypes.c_int
+        lib.kda_oracle_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def threads() -> int:
+    """OpenMP threads the oracle uses."""
+    return int(_load().kda_oracle_threads())
+
+
+def _f64(x):
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(x):
+    return None if x is None else x.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def recurrent(q, k, v, a, beta, g_min=-5.0, gate="bounded", erase=True, S0=None):
+    """Token-by-token float64 recurrence (see kda_oracle.c for the definition).
+
+    Shapes: q, k, a [B,H,T,dk]; v [B,H,T,dv]; beta [B,H,T]; S0 [B,H,dv,dk] or None.
+    Returns (out [B,H,T,dv], final_state [B,H,dv,dk]) as float64 arrays.
+    """
+    q, k, v, a, beta = (_f64(x) for x in (q, k, v, a, beta))
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    assert k.shape == q.shape and a.shape == q.shape
+    assert v.shape == (B, H, T, dv) and beta.shape == (B, H, T)
+    S0 = None if S0 is None else _f64(S0)
+    if S0 is not None:
+        assert S0.shape == (B, H, dv, dk)
+    out = np.empty((B, H, T, dv), dtype=np.float64)
+    fin = np.empty((B, H, dv, dk), dtype=np.float64)
+    rc = _load().kda_oracle_recurrent(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(beta),
+                                      B, H, T, dk, dv, float(g_min), GATE_MODES[gate],
+                                      1 if erase else 0, _ptr(S0), _ptr(out), _ptr(fin))
+    if rc != 0:
+        raise RuntimeError("kda_oracle_recurrent failed with %d" % rc)
+    return out, fin

@@ -1,0 +1,244 @@
+"""Pins of the oracle against facts fixed by the pages and by mathematics.
+
+None of these compares the oracle with a retyped copy of itself: each check uses
+a value derived by hand, a closed form of a special case, an independent
+formulation (brute-force products of dense transition matrices, the quadratic
+form of decayed linear attention, the chunk-parallel WY/UT form), or an
+invariant of the definition.  A dropped term, a wrong sign, a transposed state
+or a shifted cumulative sum fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import native, overflow, reference
+
+RNG = np.random.default_rng(12345)
+
+
+def _rand_case(B, H, T, dk, dv, rng, a_sigma=1.0, norm=True, beta=None):
+    q = rng.standard_normal((B, H, T, dk))
+    k = rng.standard_normal((B, H, T, dk))
+    if norm:
+        q /= np.linalg.norm(q, axis=-1, keepdims=True)
+        k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((B, H, T, dv))
+    a = rng.standard_normal((B, H, T, dk)) * a_sigma
+    b = 1.0 / (1.0 + np.exp(-rng.standard_normal((B, H, T)))) if beta is None else np.full((B, H, T), beta)
+    return q, k, v, a, b
+
+
+def _golden(golden_dir, name):
+    with open(os.path.join(golden_dir, name)) as f:
+        return json.load(f)
+
+
+def _parse(x):
+    return float(x)  # handles "inf", "-inf", "0"
+
+
+# ---------------------------------------------------------------- hand-derived case
+@pytest.mark.parametrize("case", ["bounded", "logsigmoid"])
+@pytest.mark.parametrize("impl", ["c", "numpy", "chunked1", "chunked2", "brute"])
+def test_hand_derived_delta_rule(golden_dir, case, impl):
+    gd = _golden(golden_dir, "hand_delta_rule.json")
+    tok = gd["tokens"]
+    c = gd["cases"][case]
+    k = np.array(tok["k"])[None, None]
+    v = np.array(tok["v"])[None, None]
+    q = np.array(tok["q"])[None, None]
+    beta = np.array(tok["beta"])[None, None]
+    a = np.array([[_parse(x) for x in row] for row in c["a"]])[None, None]
+    d = math.exp(-2.5) if case == "bounded" else 0.5
+    g_min = c.get("g_min", -5.0)
+    env = {"d": d}
+    want_out = np.array([[eval(x, {}, env) for x in row] for row in gd["out_in_terms_of_d"]])
+    want_fin = np.array([[eval(x, {}, env) for x in row] for row in gd["final_state_in_terms_of_d"]])
+    with np.errstate(over="ignore", invalid="ignore"):
+        if impl == "c":
+            out, fin = native.recurrent(q, k, v, a, beta, g_min, gate=case)
+        elif impl == "numpy":
+            out, fin = reference.recurrent(q, k, v, a, beta, g_min, case)
+        elif impl.startswith("chunked"):
+            out, fin = reference.chunked(q, k, v, a, beta, int(impl[-1]), g_min, case, decay_ref="pairwise")
+        else:
+            out, fin = reference.brute_force(q, k, v, a, beta, g_min, case)
+    np.testing.assert_allclose(out[0, 0], want_out, atol=1e-14, rtol=0)
+    np.testing.assert_allclose(fin[0, 0], want_fin, atol=1e-14, rtol=0)
+
+
+# ---------------------------------------------------------------- the gate
+def test_gate_values():
+    # g_min * sigmoid(0) = g_min / 2 ; sigmoid(+-inf) = 1, 0
+    assert reference.gate(np.array(0.0)) == -2.5
+    assert reference.gate(np.array(np.inf)) == -5.0
+    assert reference.gate(np.array(-np.inf)) == 0.0
+    a = RNG.standard_normal(10000) * 50
+    g = reference.gate(a)
+    assert g.min() >= -5.0 and g.max() <= 0.0
+    # log sigmoid: -ln 2 at 0, exact for large |a| where the naive form fails
+    assert abs(reference.gate(np.array(0.0), mode="logsigmoid") + math.log(2.0)) < 1e-16
+    assert reference.gate(np.array(-1000.0), mode="logsigmoid") == -1000.0
+    assert reference.gate(np.array(1000.0), mode="logsigmoid") == 0.0
+    a = np.linspace(-30, 30, 601)
+    naive = np.log(1.0 / (1.0 + np.exp(-a)))
+    np.testing.assert_allclose(reference.gate(a, mode="logsigmoid"), naive, rtol=1e-12, atol=1e-15)
+
+
+def test_pages_constants(golden_dir):
+    gc = _golden(golden_dir, "pages_constants.json")
+    bmax = float(torch.finfo(torch.bfloat16).max)
+    btiny = float(torch.finfo(torch.bfloat16).tiny)
+    assert abs(math.log(bmax) - gc["ln_bf16_max"]) < 1e-12
+    assert abs(math.log(btiny) - gc["ln_bf16_min_normal"]) < 1e-12
+    span = (gc["safe_tile_tokens"] - 1) * abs(gc["g_min"])
+    assert span == gc["max_diagonal_exponent"]
+    assert span < gc["ln_bf16_max"] and -span > gc["ln_bf16_min_normal"]
+    assert reference.G_MIN == gc["g_min"] and reference.SUBTILE == gc["safe_tile_tokens"]
+
+
+# ---------------------------------------------------------------- brute force
+@pytest.mark.parametrize("gate", ["bounded", "logsigmoid"])
+@pytest.mark.parametrize("with_s0", [False, True])
+def test_brute_force(gate, with_s0):
+    rng = np.random.default_rng(7 + with_s0)
+    q, k, v, a, b = _rand_case(1, 2, 9, 5, 4, rng, a_sigma=2.0)
+    S0 = rng.standard_normal((1, 2, 4, 5)) if with_s0 else None
+    out_c, fin_c = native.recurrent(q, k, v, a, b, -5.0, gate=gate, S0=S0)
+    out_b, fin_b = reference.brute_force(q, k, v, a, b, -5.0, gate, S0=S0)
+    np.testing.assert_allclose(out_c, out_b, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(fin_c, fin_b, rtol=1e-11, atol=1e-12)
+
+
+# ---------------------------------------------------------------- special cases
+def test_scalar_full_erase():
+    # dk = dv = 1, k = +-1, beta = 1: S_{t-1} e^g (1 - k^2) = 0, so S_t = v_t k_t, o_t = v_t k_t q_t
+    rng = np.random.default_rng(3)
+    T = 40
+    k = np.sign(rng.standard_normal((1, 1, T, 1)))
+    q, v, a = (rng.standard_normal((1, 1, T, 1)) for _ in range(3))
+    out, fin = native.recurrent(q, k, v, a, np.ones((1, 1, T)))
+    np.testing.assert_allclose(out, v * k * q, atol=1e-15)
+    np.testing.assert_allclose(fin[0, 0, 0, 0], v[0, 0, -1, 0] * k[0, 0, -1, 0], atol=1e-15)
+
+
+@pytest.mark.parametrize("gate", ["bounded", "logsigmoid"])
+def test_erase_free_is_decayed_linear_attention(gate):
+    # Without the erase term the recurrence is plain decayed linear attention,
+    # whose quadratic form needs no state at all.
+    rng = np.random.default_rng(11)
+    q, k, v, a, b = _rand_case(2, 2, 30, 6, 5, rng, a_sigma=2.0)
+    S0 = rng.standard_normal((2, 2, 5, 6))
+    out, _ = native.recurrent(q, k, v, a, b, -5.0, gate=gate, erase=False, S0=S0)
+    want = reference.decayed_linear_attention(q, k, v, a, b, -5.0, gate, S0=S0)
+    np.testing.assert_allclose(out, want, rtol=1e-11, atol=1e-12)
+
+
+def test_no_decay_no_erase_is_cumulative_sum():
+    # g = 0 (a = -inf under the bounded gate), beta = 1, no erase:
+    # S_t = sum_{s<=t} v_s k_s^T,  o_t = sum_{s<=t} (k_s . q_t) v_s
+    rng = np.random.default_rng(5)
+    q, k, v, _, _ = _rand_case(1, 3, 25, 7, 3, rng, norm=False)
+    a = np.full(q.shape, -np.inf)
+    with np.errstate(over="ignore"):
+        out, fin = native.recurrent(q, k, v, a, np.ones(q.shape[:3]), erase=False)
+    kv = np.cumsum(np.einsum("bhti,bhtj->bhtij", v, k), axis=2)
+    np.testing.assert_allclose(fin, kv[:, :, -1], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(out, np.einsum("bhtij,bhtj->bhti", kv, q), rtol=1e-11, atol=1e-12)
+
+
+def test_beta_zero_gives_zero():
+    rng = np.random.default_rng(6)
+    q, k, v, a, _ = _rand_case(1, 2, 50, 8, 8, rng)
+    out, fin = native.recurrent(q, k, v, a, np.zeros(q.shape[:3]))
+    assert np.all(out == 0.0) and np.all(fin == 0.0)
+
+
+@pytest.mark.parametrize("gate", ["bounded", "logsigmoid"])
+def test_delta_rule_retrieval(gate):
+    # beta = 1 and |k| = 1: the delta rule stores v_t exactly under k_t, S_t k_t = v_t,
+    # whatever the decay; with q = k the output is v.
+    rng = np.random.default_rng(8)
+    _, k, v, a, _ = _rand_case(1, 2, 64, 16, 12, rng, a_sigma=3.0)
+    out, _ = native.recurrent(k, k, v, a, np.ones(k.shape[:3]), -5.0, gate=gate)
+    np.testing.assert_allclose(out, v, atol=1e-12)
+
+
+# ---------------------------------------------------------------- chunk form
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+@pytest.mark.parametrize("decay_ref", ["pairwise", "chunk", "subtile"])
+def test_chunked_equals_recurrent(chunk, decay_ref):
+    rng = np.random.default_rng(chunk)
+    T = 3 * chunk + 19  # several chunks and a ragged tail
+    q, k, v, a, b = _rand_case(1, 2, T, 16, 8, rng, a_sigma=4.0)
+    S0 = rng.standard_normal((1, 2, 8, 16)) * 0.3
+    out_c, fin_c = native.recurrent(q, k, v, a, b, S0=S0)
+    out_k, fin_k = reference.chunked(q, k, v, a, b, chunk, S0=S0, decay_ref=decay_ref)
+    scale = np.sqrt(np.mean(out_c ** 2))
+    assert np.max(np.abs(out_k - out_c)) <= 1e-12 * max(scale, 1.0)
+    assert np.max(np.abs(fin_k - fin_c)) <= 1e-12 * max(np.sqrt(np.mean(fin_c ** 2)), 1.0)
+
+
+def test_c_and_numpy_transcriptions_agree():
+    rng = np.random.default_rng(21)
+    q, k, v, a, b = _rand_case(2, 3, 120, 32, 24, rng, a_sigma=2.0)
+    for gate in ("bounded", "logsigmoid"):
+        o1, f1 = native.recurrent(q, k, v, a, b, -5.0, gate=gate)
+        o2, f2 = reference.recurrent(q, k, v, a, b, -5.0, gate)
+        np.testing.assert_allclose(o1, o2, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(f1, f2, rtol=1e-12, atol=1e-13)
+
+
+# ---------------------------------------------------------------- invariants
+def test_linear_in_v_causal_and_head_independent():
+    rng = np.random.default_rng(31)
+    q, k, v, a, b = _rand_case(1, 2, 80, 8, 6, rng, a_sigma=2.0)
+    v2 = rng.standard_normal(v.shape)
+    o1, _ = native.recurrent(q, k, v, a, b)
+    o2, _ = native.recurrent(q, k, v2, a, b)
+    o3, _ = native.recurrent(q, k, 2.0 * v - 3.0 * v2, a, b)
+    np.testing.assert_allclose(o3, 2.0 * o1 - 3.0 * o2, rtol=1e-11, atol=1e-12)
+    # causality: perturbing token 50 leaves outputs before it bitwise unchanged
+    kp = k.copy()
+    kp[:, :, 50] = -kp[:, :, 50]
+    o4, _ = native.recurrent(q, kp, v, a, b)
+    assert np.array_equal(o4[:, :, :50], o1[:, :, :50])
+    assert not np.allclose(o4[:, :, 50:], o1[:, :, 50:])
+    # heads are independent: head 1 alone gives the same result
+    o5, _ = native.recurrent(q[:, 1:], k[:, 1:], v[:, 1:], a[:, 1:], b[:, 1:])
+    assert np.array_equal(o5[:, 0], o1[:, 1])
+
+
+# ---------------------------------------------------------------- the bound (P8) and the ablation predictor (P9)
+def test_bounded_gate_keeps_subtile_exponent_within_bf16():
+    rng = np.random.default_rng(41)
+    a = rng.standard_normal((1, 2, 1024, 32)) * 40.0   # drive many gates to g_min
+    span = overflow.subtile_spans(a, -5.0, 64, "bounded")
+    assert span <= 15 * 5.0 + 1e-9 and span < math.log(float(torch.finfo(torch.bfloat16).max))
+    k = rng.standard_normal(a.shape)
+    assert overflow.subtile_operand_overflow(a, k, -5.0, 64, "bounded") == (0, 0)
+    # the same gates without the bound exceed the range inside a 16-token tile
+    assert overflow.subtile_spans(a, -5.0, 64, "logsigmoid") > 88.72
+    assert overflow.subtile_operand_overflow(a, k, -5.0, 64, "logsigmoid")[0] > 0
+    # and a whole-64-chunk reference overflows even with the bound
+    assert overflow.whole_chunk_inverse_overflow(a, k, -5.0, 64, "bounded") > 0
+
+
+def test_overflow_predictor_exact_counts():
+    # k = 1, constant gate.  Inside a 16-token tile the operand for offset j is
+    # 2^(j*|g|*log2 e); it is non-finite in bf16 exactly when that exponent
+    # reaches the bf16 overflow threshold (~127.997).
+    T = 256
+    k = np.ones((1, 1, T, 1))
+    # unbounded gate at a = -20: |g| = 20 + 2e-9 -> 28.85 per step -> offsets 5..15 overflow
+    a = np.full((1, 1, T, 1), -20.0)
+    assert overflow.subtile_operand_overflow(a, k, -5.0, 64, "logsigmoid") == (11 * T // 16, 0)
+    # bounded gate pinned at g_min = -5: 7.21 per step, at most 108.2 -> none
+    a = np.full((1, 1, T, 1), np.inf)
+    assert overflow.subtile_operand_overflow(a, k, -5.0, 64, "bounded") == (0, 0)
+    # a bound of -6 is not enough: 8.656 per step -> offset 15 (129.8) overflows
+    assert overflow.subtile_operand_overflow(a, k, -6.0, 64, "bounded") == (T // 16, 0)
