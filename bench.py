@@ -1,0 +1,193 @@
+#!/usr/bin/env python3
+"""Throughput of the bounded-decay KDA chunked forward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload 64k] [--gpus 1]
+
+A step is one whole forward (gate, intra-chunk stage, inter-chunk state and
+output) over the workload's synthetic inputs, which are resident in HBM before
+timing starts.  Prints one JSON line: tokens/s (B*T per step), the path's
+algorithmic TFLOP/s as a fraction of the bf16 MFMA peak, per-kernel HIP-event
+times measured on the launch stream inside the timed region, the roofline of
+the dominant kernel, and the CPU oracle's throughput on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KDA chunked fwd tokens/s at T=64K,H=32,d=128; % of bf16 MFMA peak"
+PEAK_BF16_FLOPS = 2.5e15     # MI355X dense bf16 MFMA
+PEAK_FP32_FLOPS = 157.3e12   # MI355X fp32 matrix
+PEAK_HBM = 8.0e12            # MI355X HBM3E bytes/s
+
+
+def flops_per_token_head(dk, dv, C):
+    """Algorithmic flops of the chunked form per (token, head): the causal 16x16
+    sub-tiles of M and A, the UT solve, W, U~, W S, K^T U, Q S and M U."""
+    return (3 * dk + 2 * dv) * (C + 16) + 6 * dk * dv + C * C / 3.0
+
+
+def path_bytes_per_token_head(dk, dv, es):
+    """q, k, a, v and beta read once, out written once."""
+    return (3 * dk + dv + dv) * es + es
+
+
+def _src_sha():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "chunked_gated_linear_bounded_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(kernel, workload):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel sources (else None)."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        rec = json.load(open(p)).get(kernel + "@" + workload)
+    except Exception:
+        return None
+    if not rec or rec.get("src_sha") != _src_sha():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(inputs, w, seconds):
+    """The float64 oracle on whole heads of the same workload until `seconds`
+    have passed; returns whole-job tokens/s extrapolated from the sampled heads."""
+    import kda_inputs as KI
+    from oracle import native
+    done, t_used = 0, 0.0
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    for (b, h) in heads:
+        hs = KI.head_slice(inputs, b, h)
+        t0 = time.perf_counter()
+        native.recurrent(hs["q"], hs["k"], hs["v"], hs["a"], hs["beta"], w.g_min)
+        t_used += time.perf_counter() - t0
+        done += 1
+        if t_used >= seconds:
+            break
+    per_head = t_used / done
+    job_time = per_head * len(heads)
+    return {"value": w.B * w.T / job_time, "unit": "tokens/s", "cores": native.threads(), "kind": "oracle",
+            "sample": "%d of %d heads (%d tokens each), float64 token recurrence, %.1f s; "
+                      "whole job extrapolated per head" % (done, len(heads), w.T, t_used)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="64k", help="tiny, 8k, 64k, 256k or 1m")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build measures one GPU only (the path shards over heads with no "
+              "communication); --gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import chunked_gated_linear_bounded_amd as kda
+    import kda_inputs as KI
+
+    w = KI.BY_NAME[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print("bench: generating %s inputs on %s" % (w.name, torch.cuda.get_device_name(dev)), file=sys.stderr,
+          flush=True)
+    inp = KI.make_inputs(w, device=dev)
+    es = 4 if w.io == "fp32" else 2
+    ws = torch.empty(kda.workspace_bytes(w.B, w.H, w.T, w.dk, w.dv, w.chunk, w.torch_dtype), dtype=torch.uint8,
+                     device=dev)
+    out = torch.empty((w.B, w.H, w.T, w.dv), dtype=w.torch_dtype, device=dev)
+    fs = torch.empty((w.B, w.H, w.dv, w.dk), dtype=torch.float32, device=dev) if w.final_state else None
+    stream = torch.cuda.current_stream(dev)
+
+    def step(e=None):
+        if e is not None:
+            e[0].record(stream)
+        kda.chunk_intra(inp["q"], inp["k"], inp["v"], inp["a"], inp["beta"], ws, w.g_min, w.chunk, stream=stream)
+        if e is not None:
+            e[1].record(stream)
+        kda.chunk_state(ws, out, fs, w.chunk, dk=w.dk, stream=stream)
+        if e is not None:
+            e[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    print("bench: timing %d steps" % args.steps, file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    intra_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    state_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    assert torch.isfinite(out.float()).all().item(), "non-finite output"
+
+    th = w.B * w.H * w.T
+    flops = flops_per_token_head(w.dk, w.dv, w.chunk) * th
+    peak = PEAK_BF16_FLOPS if w.io == "bf16" else PEAK_FP32_FLOPS
+    tokens_per_s = w.B * w.T / (ms_step * 1e-3)
+    rec_bytes = ws.numel()  # every record written once by the intra stage, read once by the state stage
+    in_bytes = th * ((3 * w.dk + w.dv) * es + es)
+    out_bytes = th * w.dv * es
+    kern = {
+        "kda_intra_kernel": {"ms": intra_ms, "bytes": in_bytes + rec_bytes},
+        "kda_state_kernel": {"ms": state_ms, "bytes": rec_bytes + out_bytes},
+    }
+    dom = max(kern, key=lambda k: kern[k]["ms"])
+    ach = kern[dom]["bytes"] / (kern[dom]["ms"] * 1e-3)
+    traffic = _traffic(dom, w.name)
+    res = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.io,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "dk": w.dk, "dv": w.dv, "chunk": w.chunk,
+                   "io": w.io, "g_min": w.g_min},
+        "mfma_peak_frac": flops / (ms_step * 1e-3) / peak,
+        "path": {"tflops_algorithmic": flops / (ms_step * 1e-3) / 1e12,
+                 "gbps_algorithmic": path_bytes_per_token_head(w.dk, w.dv, es) * th / (ms_step * 1e-3) / 1e9,
+                 "hbm_peak_frac": path_bytes_per_token_head(w.dk, w.dv, es) * th / (ms_step * 1e-3) / PEAK_HBM,
+                 "flop_per_token_head": flops_per_token_head(w.dk, w.dv, w.chunk),
+                 "bytes_per_token_head": path_bytes_per_token_head(w.dk, w.dv, es)},
+        "kernels_ms": {k: v["ms"] for k, v in kern.items()},
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": ach / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                     "frac": ach / PEAK_HBM,
+                     "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        print("bench: timing the CPU oracle", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(inp, w, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,184 @@
+"""MI355X (gfx950) chunked forward of bounded-decay KDA -- Python binding.
+
+A thin ctypes layer over libkda.so (include/kda.h).  It only marshals
+arguments: torch supplies device memory and the current HIP stream, every step
+of the computation runs in the library's HIP kernels.  If the library is not
+built, every entry point raises; there is no fallback.
+
+    import chunked_gated_linear_bounded_amd as kda
+    out, S = kda.chunk_fwd(q, k, v, a, beta, g_min=-5.0, chunk=64, return_final_state=True)
+    G = kda.gate_cumsum(a, g_min=-5.0, chunk=64)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkda.so")
+
+KDA_OK = 0
+KDA_BF16, KDA_FP32 = 0, 1
+GATE_MODES = {"bounded": 0, "logsigmoid": 1}
+_DTYPES = {torch.bfloat16: KDA_BF16, torch.float32: KDA_FP32}
+
+_lib = None
+
+
+class KdaError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__("%s failed: %d (%s)" % (fn, status, status_string(status)))
+
+
+def lib():
+    """The loaded libkda.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libkda.so not built: run python -m chunked_gated_linear_bounded_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        L.kda_abi_version.restype = i
+        L.kda_status_string.argtypes = [i]
+        L.kda_status_string.restype = ctypes.c_char_p
+        L.kda_chunk_fwd_workspace_bytes.argtypes = [i] * 7
+        L.kda_chunk_fwd_workspace_bytes.restype = sz
+        L.kda_gate_cumsum.argtypes = [vp, f, i, i, i, i, i, i, i, vp, vp]
+        L.kda_gate_cumsum.restype = i
+        L.kda_chunk_fwd.argtypes = [vp] * 5 + [f] + [i] * 7 + [vp, vp, vp, sz, vp]
+        L.kda_chunk_fwd.restype = i
+        L.kda_chunk_fwd_ex.argtypes = [vp] * 5 + [f] + [i] * 7 + [vp, vp, vp, sz, vp, i, vp]
+        L.kda_chunk_fwd_ex.restype = i
+        L.kda_chunk_intra.argtypes = [vp] * 5 + [f] + [i] * 7 + [vp, sz, vp, i, vp]
+        L.kda_chunk_intra.restype = i
+        L.kda_chunk_state.argtypes = [vp, sz] + [i] * 7 + [vp, vp, vp, vp]
+        L.kda_chunk_state.restype = i
+        _lib = L
+    return _lib
+
+
+def abi_version() -> int:
+    return int(lib().kda_abi_version())
+
+
+def status_string(status: int) -> str:
+    return lib().kda_status_string(int(status)).decode()
+
+
+def workspace_bytes(B, H, T, dk, dv, chunk, dtype) -> int:
+    io = _DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(lib().kda_chunk_fwd_workspace_bytes(B, H, T, dk, dv, chunk, io))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(t, name, dtype=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a GPU tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+
+
+def gate_cumsum(a, g_min=-5.0, chunk=64, gate="bounded", out=None, stream=None):
+    """G[b,h,t,c] = sum of g over t's chunk up to t (natural log), float32."""
+    _check(a, "a")
+    B, H, T, dk = a.shape
+    if out is None:
+        out = torch.empty((B, H, T, dk), dtype=torch.float32, device=a.device)
+    _check(out, "out", torch.float32, a.device)
+    st = lib().kda_gate_cumsum(_ptr(a), float(g_min), int(chunk), B, H, T, dk, _DTYPES[a.dtype],
+                               GATE_MODES[gate], _ptr(out), _stream(stream))
+    if st != KDA_OK:
+        raise KdaError("kda_gate_cumsum", st)
+    return out
+
+
+def chunk_fwd(q, k, v, a, beta, g_min=-5.0, chunk=64, out=None, final_state=None,
+              return_final_state=False, workspace=None, stream=None, gate="bounded", counts=None):
+    """Chunked KDA forward.  q, k, a: [B,H,T,dk]; v: [B,H,T,dv]; beta: [B,H,T];
+    all bf16 or all float32, contiguous, on one GPU.  Returns out [B,H,T,dv]
+    (and the float32 final state [B,H,dv,dk] when asked for).  `counts`: optional
+    int64 GPU tensor of 2 elements that non-finite counters are added to."""
+    dtype = q.dtype
+    if dtype not in _DTYPES:
+        raise ValueError("unsupported dtype %s" % dtype)
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (a, "a"), (beta, "beta")):
+        _check(t, n, dtype, dev)
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or a.shape != q.shape or v.shape != (B, H, T, dv) or beta.shape != (B, H, T):
+        raise ValueError("shape mismatch")
+    if out is None:
+        out = torch.empty((B, H, T, dv), dtype=dtype, device=dev)
+    _check(out, "out", dtype, dev)
+    if final_state is None and return_final_state:
+        final_state = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+    if final_state is not None:
+        _check(final_state, "final_state", torch.float32, dev)
+    need = workspace_bytes(B, H, T, dk, dv, chunk, dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check(workspace, "workspace", torch.uint8, dev)
+    if counts is not None:
+        _check(counts, "counts", torch.int64, dev)
+    L = lib()
+    args = [_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(beta), float(g_min), int(chunk), B, H, T, dk, dv,
+            _DTYPES[dtype], _ptr(out), _ptr(final_state), _ptr(workspace), workspace.numel(), _stream(stream)]
+    if gate == "bounded" and counts is None:
+        st = L.kda_chunk_fwd(*args)
+        fn = "kda_chunk_fwd"
+    else:
+        st = L.kda_chunk_fwd_ex(*args, GATE_MODES[gate], _ptr(counts))
+        fn = "kda_chunk_fwd_ex"
+    if st != KDA_OK:
+        raise KdaError(fn, st)
+    if return_final_state:
+        return out, final_state
+    return out
+
+
+def chunk_intra(q, k, v, a, beta, workspace, g_min=-5.0, chunk=64, stream=None, gate="bounded", counts=None):
+    """First stage of chunk_fwd: fills `workspace` (uint8 GPU tensor of at least
+    workspace_bytes(...) bytes) with the per-chunk operands."""
+    dtype, dev = q.dtype, q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (a, "a"), (beta, "beta")):
+        _check(t, n, dtype, dev)
+    _check(workspace, "workspace", torch.uint8, dev)
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    st = lib().kda_chunk_intra(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(beta), float(g_min), int(chunk), B, H, T,
+                               dk, dv, _DTYPES[dtype], _ptr(workspace), workspace.numel(), _stream(stream),
+                               GATE_MODES[gate], _ptr(counts))
+    if st != KDA_OK:
+        raise KdaError("kda_chunk_intra", st)
+
+
+def chunk_state(workspace, out, final_state=None, chunk=64, dk=None, stream=None, counts=None):
+    """Second stage of chunk_fwd: reads `workspace`, writes out [B,H,T,dv] (and
+    final_state [B,H,dv,dk] float32 when given).  dk defaults to dv."""
+    _check(out, "out")
+    _check(workspace, "workspace", torch.uint8, out.device)
+    B, H, T, dv = out.shape
+    dk = dv if dk is None else dk
+    st = lib().kda_chunk_state(_ptr(workspace), workspace.numel(), int(chunk), B, H, T, dk, dv, _DTYPES[out.dtype],
+                               _ptr(out), _ptr(final_state), _stream(stream), _ptr(counts))
+    if st != KDA_OK:
+        raise KdaError("kda_chunk_state", st)

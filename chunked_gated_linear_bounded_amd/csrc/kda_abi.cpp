@@ -1,0 +1,191 @@
+// Host side of the C ABI declared in include/kda.h: argument validation (pure
+// host code, no HIP call before every check has passed), workspace sizing and
+// dispatch to the kernel launchers.
+#include <math.h>
+#include <stdint.h>
+
+#include "kda.h"
+#include "kda_launch.h"
+#include "kda_layout.h"
+
+namespace {
+
+bool aligned(const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+int check_shape(int B, int H, int T, int dk, int dv, int chunk, int io) {
+    if (io != KDA_BF16 && io != KDA_FP32) return KDA_ERR_DTYPE;
+    if (chunk != 16 && chunk != 32 && chunk != 64) return KDA_ERR_CHUNK;
+    if (B < 1 || H < 1 || T < 0) return KDA_ERR_SHAPE;
+    if ((dk != 64 && dk != 128) || (dv != 64 && dv != 128)) return KDA_ERR_SHAPE;
+    if (T % chunk != 0) return KDA_ERR_SHAPE;
+    if (H > 65535) return KDA_ERR_SHAPE;
+    const double elems = (double)B * H * (double)T * (dk > dv ? dk : dv);
+    if (elems >= 1099511627776.0) return KDA_ERR_SHAPE;  // 2^40
+    return KDA_OK;
+}
+
+int check_gate(float g_min, int gate_mode) {
+    if (gate_mode != KDA_GATE_BOUNDED && gate_mode != KDA_GATE_LOGSIGMOID) return KDA_ERR_MODE;
+    if (gate_mode == KDA_GATE_BOUNDED) {
+        if (!isfinite(g_min) || !(g_min < 0.0f) || g_min < KDA_G_MIN_LOWEST) return KDA_ERR_GMIN;
+    }
+    return KDA_OK;
+}
+
+size_t workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, int io) {
+    const KdaLayout L = kda_layout(chunk, dk, dv, io == KDA_FP32 ? 4 : 2);
+    return (size_t)B * (size_t)H * (size_t)(T / chunk) * L.stride;
+}
+
+int check_ptrs_ws(int B, int H, int T, int dk, int dv, int chunk, int io, const void *workspace,
+                  size_t workspace_bytes_given) {
+    const size_t need = workspace_bytes(B, H, T, dk, dv, chunk, io);
+    if (need > 0) {
+        if (!workspace || workspace_bytes_given < need) return KDA_ERR_WORKSPACE;
+        if (!aligned(workspace, 16)) return KDA_ERR_ALIGN;
+    }
+    return KDA_OK;
+}
+
+int intra_impl(const void *q, const void *k, const void *v, const void *a, const void *beta, float g_min,
+               int chunk, int B, int H, int T, int dk, int dv, int io, void *workspace,
+               size_t workspace_bytes_given, hipStream_t stream, int gate_mode, unsigned long long *counts,
+               bool launch) {
+    int st = check_shape(B, H, T, dk, dv, chunk, io);
+    if (st != KDA_OK) return st;
+    st = check_gate(g_min, gate_mode);
+    if (st != KDA_OK) return st;
+    if (!q || !k || !v || !a || !beta) return KDA_ERR_NULL;
+    const size_t esz = io == KDA_FP32 ? 4 : 2;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(a, 16) || !aligned(beta, esz) ||
+        (counts && !aligned(counts, 8)))
+        return KDA_ERR_ALIGN;
+    st = check_ptrs_ws(B, H, T, dk, dv, chunk, io, workspace, workspace_bytes_given);
+    if (st != KDA_OK || !launch || T == 0) return st;
+    kda::LaunchArgs p{};
+    p.q = q; p.k = k; p.v = v; p.a = a; p.beta = beta;
+    p.g_min = g_min;
+    p.logsig = gate_mode == KDA_GATE_LOGSIGMOID;
+    p.chunk = chunk; p.B = B; p.H = H; p.T = T; p.dk = dk; p.dv = dv;
+    p.fp32 = io == KDA_FP32;
+    p.workspace = workspace; p.counts = counts; p.stream = stream;
+    return kda::launch_intra(p) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+int state_impl(const void *workspace, size_t workspace_bytes_given, int chunk, int B, int H, int T, int dk,
+               int dv, int io, void *out, float *final_state, hipStream_t stream, unsigned long long *counts,
+               bool launch) {
+    int st = check_shape(B, H, T, dk, dv, chunk, io);
+    if (st != KDA_OK) return st;
+    if (!out) return KDA_ERR_NULL;
+    if (!aligned(out, 16) || (final_state && !aligned(final_state, 16)) || (counts && !aligned(counts, 8)))
+        return KDA_ERR_ALIGN;
+    st = check_ptrs_ws(B, H, T, dk, dv, chunk, io, workspace, workspace_bytes_given);
+    if (st != KDA_OK || !launch) return st;
+    if (T == 0) {  // empty sequence: no output rows, the state stays zero
+        if (final_state &&
+            hipMemsetAsync(final_state, 0, (size_t)B * H * dv * dk * sizeof(float), stream) != hipSuccess)
+            return KDA_ERR_HIP;
+        return KDA_OK;
+    }
+    kda::LaunchArgs p{};
+    p.chunk = chunk; p.B = B; p.H = H; p.T = T; p.dk = dk; p.dv = dv;
+    p.fp32 = io == KDA_FP32;
+    p.out = out; p.final_state = final_state; p.workspace = const_cast<void *>(workspace);
+    p.counts = counts; p.stream = stream;
+    return kda::launch_state(p) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+int fwd_impl(const void *q, const void *k, const void *v, const void *a, const void *beta, float g_min,
+             int chunk, int B, int H, int T, int dk, int dv, int io, void *out, float *final_state,
+             void *workspace, size_t workspace_bytes_given, hipStream_t stream, int gate_mode,
+             unsigned long long *counts) {
+    // validate both stages before launching either
+    int st = intra_impl(q, k, v, a, beta, g_min, chunk, B, H, T, dk, dv, io, workspace, workspace_bytes_given,
+                        stream, gate_mode, counts, false);
+    if (st != KDA_OK) return st;
+    st = state_impl(workspace, workspace_bytes_given, chunk, B, H, T, dk, dv, io, out, final_state, stream,
+                    counts, false);
+    if (st != KDA_OK) return st;
+    st = intra_impl(q, k, v, a, beta, g_min, chunk, B, H, T, dk, dv, io, workspace, workspace_bytes_given,
+                    stream, gate_mode, counts, true);
+    if (st != KDA_OK) return st;
+    return state_impl(workspace, workspace_bytes_given, chunk, B, H, T, dk, dv, io, out, final_state, stream,
+                      counts, true);
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+const char *kda_status_string(int status) {
+    switch (status) {
+    case KDA_OK: return "ok";
+    case KDA_ERR_NULL: return "a required pointer is NULL";
+    case KDA_ERR_SHAPE: return "unsupported shape (dk, dv in {64,128}; B, H >= 1; T >= 0; T % chunk == 0)";
+    case KDA_ERR_DTYPE: return "io_dtype must be KDA_BF16 or KDA_FP32";
+    case KDA_ERR_CHUNK: return "chunk must be 16, 32 or 64";
+    case KDA_ERR_GMIN: return "g_min must be finite with KDA_G_MIN_LOWEST <= g_min < 0";
+    case KDA_ERR_WORKSPACE: return "workspace missing or smaller than kda_chunk_fwd_workspace_bytes()";
+    case KDA_ERR_HIP: return "a HIP call or kernel launch failed";
+    case KDA_ERR_ALIGN: return "a pointer is not aligned as required (16 bytes; beta: element size)";
+    case KDA_ERR_MODE: return "unknown gate_mode";
+    default: return "unknown status";
+    }
+}
+
+size_t kda_chunk_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, int io_dtype) {
+    if (check_shape(B, H, T, dk, dv, chunk, io_dtype) != KDA_OK) return 0;
+    return workspace_bytes(B, H, T, dk, dv, chunk, io_dtype);
+}
+
+int kda_gate_cumsum(const void *a, float g_min, int chunk, int B, int H, int T, int dk, int io_dtype,
+                    int gate_mode, float *G_out, hipStream_t stream) {
+    int st = check_shape(B, H, T, dk, 64, chunk, io_dtype);
+    if (st != KDA_OK) return st;
+    st = check_gate(g_min, gate_mode);
+    if (st != KDA_OK) return st;
+    if (!a || !G_out) return KDA_ERR_NULL;
+    if (!aligned(a, 16) || !aligned(G_out, 16)) return KDA_ERR_ALIGN;
+    if (T == 0) return KDA_OK;
+    kda::LaunchArgs p{};
+    p.a = a; p.g_min = g_min; p.logsig = gate_mode == KDA_GATE_LOGSIGMOID;
+    p.chunk = chunk; p.B = B; p.H = H; p.T = T; p.dk = dk; p.dv = 64;
+    p.fp32 = io_dtype == KDA_FP32;
+    p.G_out = G_out; p.stream = stream;
+    return kda::launch_gate_cumsum(p) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+int kda_chunk_fwd(const void *q, const void *k, const void *v, const void *a, const void *beta, float g_min,
+                  int chunk, int B, int H, int T, int dk, int dv, int io_dtype, void *out, float *final_state,
+                  void *workspace, size_t workspace_bytes_given, hipStream_t stream) {
+    return fwd_impl(q, k, v, a, beta, g_min, chunk, B, H, T, dk, dv, io_dtype, out, final_state, workspace,
+                    workspace_bytes_given, stream, KDA_GATE_BOUNDED, nullptr);
+}
+
+int kda_chunk_fwd_ex(const void *q, const void *k, const void *v, const void *a, const void *beta,
+                     float g_min, int chunk, int B, int H, int T, int dk, int dv, int io_dtype, void *out,
+                     float *final_state, void *workspace, size_t workspace_bytes_given, hipStream_t stream,
+                     int gate_mode, unsigned long long *nonfinite_counts) {
+    return fwd_impl(q, k, v, a, beta, g_min, chunk, B, H, T, dk, dv, io_dtype, out, final_state, workspace,
+                    workspace_bytes_given, stream, gate_mode, nonfinite_counts);
+}
+
+int kda_chunk_intra(const void *q, const void *k, const void *v, const void *a, const void *beta, float g_min,
+                    int chunk, int B, int H, int T, int dk, int dv, int io_dtype, void *workspace,
+                    size_t workspace_bytes_given, hipStream_t stream, int gate_mode,
+                    unsigned long long *nonfinite_counts) {
+    return intra_impl(q, k, v, a, beta, g_min, chunk, B, H, T, dk, dv, io_dtype, workspace, workspace_bytes_given,
+                      stream, gate_mode, nonfinite_counts, true);
+}
+
+int kda_chunk_state(const void *workspace, size_t workspace_bytes_given, int chunk, int B, int H, int T, int dk,
+                    int dv, int io_dtype, void *out, float *final_state, hipStream_t stream,
+                    unsigned long long *nonfinite_counts) {
+    return state_impl(workspace, workspace_bytes_given, chunk, B, H, T, dk, dv, io_dtype, out, final_state, stream,
+                      nonfinite_counts, true);
+}
+
+}  // extern "C"

@@ -1,0 +1,108 @@
+// Kernel instantiations and launchers for the C ABI in include/kda.h.
+#include <hip/hip_runtime.h>
+
+#include "kda_device.h"
+#include "kda_intra.h"
+#include "kda_launch.h"
+#include "kda_state.h"
+
+namespace kda {
+
+// Standalone gate + per-chunk prefix sum: G_out[t][c] = sum over the chunk of
+// g (natural log units).  One work-group per (chunk, head, batch).
+template <int C, int DK, bool F32>
+__global__ __launch_bounds__(256) void kda_gate_kernel(const typename std::conditional<F32, float, __bf16>::type *__restrict__ a,
+                                                      float gmin2, int logsig, int H, int T,
+                                                      float *__restrict__ G_out)
+{
+    constexpr int PG = DK + 4;
+    __shared__ __attribute__((aligned(16))) float sG[C * PG];
+    __shared__ float sScr[256];
+    const size_t tok0 = ((size_t)blockIdx.z * H + blockIdx.y) * (size_t)T + (size_t)blockIdx.x * C;
+    gate_cumsum_tile<C, DK>(a + tok0 * DK, gmin2, logsig, sG, PG, sScr);
+    float *o = G_out + tok0 * DK;
+    constexpr int LPR = DK / 4, RPP = 256 / LPR;
+    for (int r0 = 0; r0 < C; r0 += RPP) {
+        const int r = r0 + threadIdx.x / LPR, c = (threadIdx.x % LPR) * 4;
+        if (r < C) {
+            f32x4 x = *reinterpret_cast<const f32x4 *>(sG + r * PG + c);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[i] *= kLn2;
+            *reinterpret_cast<f32x4 *>(o + (size_t)r * DK + c) = x;
+        }
+    }
+}
+
+template <int C, int DK, bool F32>
+static hipError_t launch_gate_t(const LaunchArgs &p) {
+    using E = typename std::conditional<F32, float, __bf16>::type;
+    dim3 grid(p.T / C, p.H, p.B);
+    hipLaunchKernelGGL((kda_gate_kernel<C, DK, F32>), grid, dim3(256), 0, p.stream,
+                       reinterpret_cast<const E *>(p.a), p.g_min * kLog2e, p.logsig, p.H, p.T, p.G_out);
+    return hipGetLastError();
+}
+
+template <int C, int DK, int DV, bool F32>
+static hipError_t launch_intra_t(const LaunchArgs &p) {
+    using E = typename std::conditional<F32, float, __bf16>::type;
+    dim3 grid(p.T / C, p.H, p.B);
+    hipLaunchKernelGGL((kda_intra_kernel<C, DK, DV, F32>), grid, dim3(256), 0, p.stream,
+                       reinterpret_cast<const E *>(p.q), reinterpret_cast<const E *>(p.k),
+                       reinterpret_cast<const E *>(p.v), reinterpret_cast<const E *>(p.a),
+                       reinterpret_cast<const E *>(p.beta), p.g_min * kLog2e, p.logsig, p.H, p.T,
+                       reinterpret_cast<unsigned char *>(p.workspace), p.counts);
+    return hipGetLastError();
+}
+
+template <int C, int DK, int DV, bool F32>
+static hipError_t launch_state_t(const LaunchArgs &p) {
+    using E = typename std::conditional<F32, float, __bf16>::type;
+    const int BH = p.B * p.H;
+    const int groups = (BH + 7) / 8;
+    dim3 grid(groups * 8 * (DV / 16));
+    hipLaunchKernelGGL((kda_state_kernel<C, DK, DV, F32>), grid, dim3(128), 0, p.stream,
+                       reinterpret_cast<const unsigned char *>(p.workspace), reinterpret_cast<E *>(p.out),
+                       p.final_state, BH, p.T, p.counts);
+    return hipGetLastError();
+}
+
+template <int C, int DK, int DV, bool F32>
+static hipError_t launch_stage_t(const LaunchArgs &p, int stage) {
+    return stage == 0 ? launch_intra_t<C, DK, DV, F32>(p) : launch_state_t<C, DK, DV, F32>(p);
+}
+
+template <int C, bool F32>
+static hipError_t dispatch_c(const LaunchArgs &p, int stage) {
+    if (p.dk == 64 && p.dv == 64) return launch_stage_t<C, 64, 64, F32>(p, stage);
+    if (p.dk == 64 && p.dv == 128) return launch_stage_t<C, 64, 128, F32>(p, stage);
+    if (p.dk == 128 && p.dv == 64) return launch_stage_t<C, 128, 64, F32>(p, stage);
+    return launch_stage_t<C, 128, 128, F32>(p, stage);
+}
+
+template <bool F32>
+static hipError_t dispatch_t(const LaunchArgs &p, int stage) {
+    if (p.chunk == 16) return dispatch_c<16, F32>(p, stage);
+    if (p.chunk == 32) return dispatch_c<32, F32>(p, stage);
+    return dispatch_c<64, F32>(p, stage);
+}
+
+hipError_t launch_intra(const LaunchArgs &p) { return p.fp32 ? dispatch_t<true>(p, 0) : dispatch_t<false>(p, 0); }
+hipError_t launch_state(const LaunchArgs &p) { return p.fp32 ? dispatch_t<true>(p, 1) : dispatch_t<false>(p, 1); }
+
+template <bool F32>
+static hipError_t dispatch_gate_t(const LaunchArgs &p) {
+    if (p.dk == 64) {
+        if (p.chunk == 16) return launch_gate_t<16, 64, F32>(p);
+        if (p.chunk == 32) return launch_gate_t<32, 64, F32>(p);
+        return launch_gate_t<64, 64, F32>(p);
+    }
+    if (p.chunk == 16) return launch_gate_t<16, 128, F32>(p);
+    if (p.chunk == 32) return launch_gate_t<32, 128, F32>(p);
+    return launch_gate_t<64, 128, F32>(p);
+}
+
+hipError_t launch_gate_cumsum(const LaunchArgs &p) {
+    return p.fp32 ? dispatch_gate_t<true>(p) : dispatch_gate_t<false>(p);
+}
+
+}  // namespace kda

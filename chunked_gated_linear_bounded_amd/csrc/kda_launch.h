@@ -1,0 +1,25 @@
+// Internal interface between the host C ABI (kda_abi.cpp) and the kernels.
+#pragma once
+#include <hip/hip_runtime_api.h>
+
+namespace kda {
+
+struct LaunchArgs {
+    const void *q, *k, *v, *a, *beta;
+    float g_min;
+    int logsig;                 // 0: bounded gate, 1: log-sigmoid (ablation)
+    int chunk, B, H, T, dk, dv;
+    bool fp32;                  // I/O element type fp32 (else bf16)
+    void *out;
+    float *final_state;
+    void *workspace;
+    float *G_out;
+    unsigned long long *counts;
+    hipStream_t stream;
+};
+
+hipError_t launch_intra(const LaunchArgs &p);  // chunk-parallel stage -> workspace
+hipError_t launch_state(const LaunchArgs &p);  // sequential stage: workspace -> out, final state
+hipError_t launch_gate_cumsum(const LaunchArgs &p);
+
+}  // namespace kda

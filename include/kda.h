@@ -1,0 +1,154 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) chunked forward of bounded-decay KDA.
+ *
+ * The operator (delta-rule linear attention with a per-channel log-decay):
+ *
+ *   g_t   = g_min * sigmoid(a_t)                 per key channel, g_min < 0
+ *   S_t   = S_{t-1} diag(exp g_t) (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,   S_0 = 0
+ *   o_t   = S_t q_t
+ *
+ * S is dv x dk (row = value channel, column = key channel).
+ *
+ * Sources: the bounded log-decay g = g_min * Sigmoid(.) with g_min = -5, which
+ * keeps the inverse cumulative decay 1/Gamma representable inside any 16-token
+ * tile so that every causal tile (diagonal and off-diagonal) is a dense matrix
+ * product -- "Trillion-Scale MoE Multimodal Models: Practical Techniques for
+ * Ultra-Long Context and Sparse Expert Architectures", sec. 3.1-3.3, and
+ * "Breaking Through Trillion-Parameter Multimodal MoE: Key Innovations from
+ * Ultra-Long Context to Extreme Sparsity", sec. 2.1 (which names the delta rule,
+ * "Delta Net", and the unbounded Log(sigma(x)) form it replaces).  The chunked
+ * recursion with a constant-size state: "Trillion-Parameter MoE Multimodal
+ * Models: Engineering Long-Context and Sparse Expert Architectures", sec. 3.2.
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *    keeps no pointer after the call returns and never allocates device memory.
+ *  - Tensors are contiguous, row-major:
+ *      q, k, a : [B][H][T][dk]      v, out : [B][H][T][dv]      beta : [B][H][T]
+ *      final_state : [B][H][dv][dk] float32, final_state[b][h][i][j] = S_T[i][j]
+ *      G_out : [B][H][T][dk] float32
+ *    Element type of q, k, v, a, beta, out is given by io_dtype (KDA_BF16 or
+ *    KDA_FP32); state, accumulation and G_out are float32.
+ *  - q, k, v, a, out, final_state, G_out and the workspace must be 16-byte
+ *    aligned; beta must be aligned to its element size.
+ *  - Supported: dk, dv in {64, 128}; chunk in {16, 32, 64}; T % chunk == 0;
+ *    B, H >= 1; T >= 0; B*H*T*max(dk,dv) < 2^40.  Bounded mode needs a finite
+ *    g_min with KDA_G_MIN_LOWEST <= g_min < 0 (below that bound a 16-token tile
+ *    can leave the bf16/fp32 exponent range); the ablation mode ignores g_min.
+ *  - Every argument is validated on the host before anything is launched; on a
+ *    bad argument a negative kda_status is returned and nothing is launched.
+ *    Work is enqueued asynchronously on `stream` (0 = the null stream); device
+ *    faults surface at the caller's next synchronisation.  KDA_ERR_HIP reports
+ *    a launch error (hipGetLastError) after enqueueing.
+ *  - Outputs are fully overwritten, never accumulated.  out must not alias any
+ *    input.  Results are bitwise reproducible run to run (no float atomics).
+ *  - No global mutable state: calls from several host threads are safe.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+/* ln(smallest normal float) / 15: the most negative g_min for which 15 steps of
+ * decay inside a 16-token tile stay in the normal exponent range. */
+#define KDA_G_MIN_LOWEST (-5.8224f)
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_NULL = -1,      /* a required pointer is NULL                       */
+    KDA_ERR_SHAPE = -2,     /* B, H, T, dk or dv unsupported, or T % chunk != 0 */
+    KDA_ERR_DTYPE = -3,     /* io_dtype not KDA_BF16 / KDA_FP32                 */
+    KDA_ERR_CHUNK = -4,     /* chunk not in {16, 32, 64}                        */
+    KDA_ERR_GMIN = -5,      /* g_min not finite or outside [KDA_G_MIN_LOWEST,0) */
+    KDA_ERR_WORKSPACE = -6, /* workspace NULL or smaller than required          */
+    KDA_ERR_HIP = -7,       /* a HIP call or kernel launch failed               */
+    KDA_ERR_ALIGN = -8,     /* a pointer is not aligned as required             */
+    KDA_ERR_MODE = -9       /* gate_mode unknown                                */
+} kda_status;
+
+typedef enum { KDA_BF16 = 0, KDA_FP32 = 1 } kda_dtype;
+
+typedef enum {
+    KDA_GATE_BOUNDED = 0,   /* g = g_min * sigmoid(a)   (the method)                     */
+    KDA_GATE_LOGSIGMOID = 1 /* g = log sigmoid(a)       (unbounded form, ablation only)  */
+} kda_gate_mode;
+
+/* Version of this ABI (KDA_ABI_VERSION). */
+int kda_abi_version(void);
+
+/* Static, NUL-terminated description of a kda_status value. */
+const char *kda_status_string(int status);
+
+/* Bytes of device workspace kda_chunk_fwd needs for this problem (0 for an
+ * invalid problem).  The workspace holds the per-chunk operands the chunk-
+ * parallel stage hands to the sequential state stage. */
+size_t kda_chunk_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, int io_dtype);
+
+/* Gate and per-chunk prefix sum (first page sec. 3.2 / third page sec. 2.1 for
+ * the gate; the cumulative decay of the chunked form, first page sec. 3.1):
+ *   g[t][c] = g_min * sigmoid(a[t][c])      (gate_mode = KDA_GATE_BOUNDED)
+ *   g[t][c] = log sigmoid(a[t][c])          (gate_mode = KDA_GATE_LOGSIGMOID)
+ *   G_out[t][c] = sum of g[s][c] over s from the start of t's chunk to t (inclusive),
+ * natural-log units, float32.  Only a and G_out are touched. */
+int kda_gate_cumsum(const void *a, float g_min, int chunk, int B, int H, int T, int dk,
+                    int io_dtype, int gate_mode, float *G_out, hipStream_t stream);
+
+/* Chunked forward: out[b][h][t] = o_t for every token; if final_state is not
+ * NULL it receives S_T.  workspace: device buffer of at least
+ * kda_chunk_fwd_workspace_bytes(...) bytes, contents undefined on entry and on
+ * return; it must not overlap any other argument. */
+int kda_chunk_fwd(const void *q, const void *k, const void *v, const void *a, const void *beta,
+                  float g_min, int chunk, int B, int H, int T, int dk, int dv, int io_dtype,
+                  void *out, float *final_state, void *workspace, size_t workspace_bytes,
+                  hipStream_t stream);
+
+/* As kda_chunk_fwd, plus the gate mode (KDA_GATE_LOGSIGMOID is the unbounded
+ * form the pages replace, kept for the ablation) and optional device counters
+ * (NULL to skip; else a device pointer to 2 unsigned 64-bit integers that are
+ * ADDED to, so zero them first):
+ *   nonfinite_counts[0] += number of Gamma-scaled key operands of the diagonal
+ *                          16-token tiles that are +-inf or NaN after rounding
+ *                          to the operand type (the only scaled operands whose
+ *                          scale factor exceeds 1);
+ *   nonfinite_counts[1] += number of outputs that are +-inf or NaN. */
+int kda_chunk_fwd_ex(const void *q, const void *k, const void *v, const void *a, const void *beta,
+                     float g_min, int chunk, int B, int H, int T, int dk, int dv, int io_dtype,
+                     void *out, float *final_state, void *workspace, size_t workspace_bytes,
+                     hipStream_t stream, int gate_mode, unsigned long long *nonfinite_counts);
+
+/* The two stages kda_chunk_fwd_ex runs, in order, exposed so a caller can
+ * time them separately or schedule other work between them.  Same arguments
+ * and rules as kda_chunk_fwd_ex; the workspace carries everything from the
+ * first call to the second and must not be touched in between.
+ *
+ * kda_chunk_intra -- chunk-parallel stage (one work-group per chunk and head):
+ *   gate and within-chunk prefix sum G; the Gamma-scaled causal 16x16 sub-tiles
+ *   of M = (Q K^T masked) and A = (diag(beta) K K^T strictly masked), all dense
+ *   products with each 16-token row tile referenced to its own first row
+ *   (first page sec. 3.1-3.3, third page sec. 2.1); the delta rule's WY/UT
+ *   transform T = (I + A)^-1, W = T diag(beta) K e^G, U~ = T diag(beta) V; and
+ *   Q e^G, K e^(G_last - G), e^(G_last).  Writes only the workspace and, when
+ *   given, nonfinite_counts[0].
+ * kda_chunk_state -- sequential stage over the chunks of each head (the
+ *   constant-size state carried chunk to chunk, second page sec. 3.2), fused
+ *   with the output combine: U = U~ - W S^T, O = Q e^G S^T + M U,
+ *   S^T <- diag(e^(G_last)) S^T + (K e^(G_last - G))^T U.  Reads the workspace,
+ *   writes out, final_state (if not NULL) and, when given, nonfinite_counts[1]. */
+int kda_chunk_intra(const void *q, const void *k, const void *v, const void *a, const void *beta,
+                    float g_min, int chunk, int B, int H, int T, int dk, int dv, int io_dtype,
+                    void *workspace, size_t workspace_bytes, hipStream_t stream, int gate_mode,
+                    unsigned long long *nonfinite_counts);
+int kda_chunk_state(const void *workspace, size_t workspace_bytes, int chunk, int B, int H, int T,
+                    int dk, int dv, int io_dtype, void *out, float *final_state, hipStream_t stream,
+                    unsigned long long *nonfinite_counts);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KDA_H */

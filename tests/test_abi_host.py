@@ -1,0 +1,108 @@
+"""The C ABI on a machine without a GPU: the library loads, exports every
+function include/kda.h declares, sizes the workspace, and rejects bad
+arguments with the documented status codes before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import chunked_gated_linear_bounded_amd as kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+OK, E_NULL, E_SHAPE, E_DTYPE, E_CHUNK, E_GMIN, E_WS, E_HIP, E_ALIGN, E_MODE = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    L = kda.lib()
+    names = _declared_functions()
+    assert {"kda_abi_version", "kda_status_string", "kda_chunk_fwd_workspace_bytes",
+            "kda_gate_cumsum", "kda_chunk_fwd", "kda_chunk_fwd_ex"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_strings():
+    assert kda.abi_version() == 1
+    for st in (OK, E_NULL, E_SHAPE, E_DTYPE, E_CHUNK, E_GMIN, E_WS, E_HIP, E_ALIGN, E_MODE):
+        s = kda.status_string(st)
+        assert s and s != "unknown status"
+    assert kda.status_string(12345) == "unknown status"
+
+
+def test_workspace_bytes():
+    # per (batch, head, chunk) record at chunk 64, dk = dv = 128, bf16:
+    # W^T, Q~^T, K^, U~ 32 tiles each + 10 causal M^T tiles, 512 B per tile, + 128 float gammas
+    rec = (4 * 32 + 10) * 512 + 128 * 4
+    rec = (rec + 255) // 256 * 256
+    assert kda.workspace_bytes(1, 32, 65536, 128, 128, 64, torch.bfloat16) == 32 * 1024 * rec
+    assert kda.workspace_bytes(1, 2, 256, 64, 64, 16, torch.float32) > 0
+    assert kda.workspace_bytes(1, 2, 0, 64, 64, 16, torch.float32) == 0
+    assert kda.workspace_bytes(1, 2, 100, 64, 64, 16, torch.float32) == 0   # T % chunk != 0
+    assert kda.workspace_bytes(1, 2, 256, 96, 64, 16, torch.float32) == 0   # dk unsupported
+
+
+FAKE = 0x100000  # aligned, never dereferenced: every call below fails validation first
+
+
+def _fwd(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, a=FAKE, beta=FAKE, g_min=-5.0, chunk=64, B=1, H=2, T=128, dk=128, dv=128,
+             io=0, out=FAKE, fs=None, ws=FAKE, wsb=1 << 40, stream=None)
+    a.update(kw)
+    return kda.lib().kda_chunk_fwd(a["q"], a["k"], a["v"], a["a"], a["beta"], a["g_min"], a["chunk"], a["B"],
+                                   a["H"], a["T"], a["dk"], a["dv"], a["io"], a["out"], a["fs"], a["ws"],
+                                   a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=None), E_NULL), (dict(beta=None), E_NULL), (dict(out=None), E_NULL),
+    (dict(io=7), E_DTYPE),
+    (dict(chunk=48), E_CHUNK), (dict(chunk=128), E_CHUNK),
+    (dict(B=0), E_SHAPE), (dict(H=0), E_SHAPE), (dict(T=-64), E_SHAPE), (dict(T=100), E_SHAPE),
+    (dict(dk=96), E_SHAPE), (dict(dv=256), E_SHAPE), (dict(H=70000), E_SHAPE),
+    (dict(g_min=0.0), E_GMIN), (dict(g_min=1.0), E_GMIN), (dict(g_min=-6.0), E_GMIN),
+    (dict(g_min=float("nan")), E_GMIN), (dict(g_min=float("-inf")), E_GMIN),
+    (dict(ws=None), E_WS), (dict(wsb=1000), E_WS),
+    (dict(q=FAKE + 8), E_ALIGN), (dict(out=FAKE + 4), E_ALIGN), (dict(beta=FAKE + 1), E_ALIGN),
+    (dict(ws=FAKE + 8), E_ALIGN), (dict(fs=FAKE + 4), E_ALIGN),
+])
+def test_validation_codes(kw, want):
+    assert _fwd(**kw) == want
+
+
+def test_validation_ex_and_gate():
+    L = kda.lib()
+    args = [FAKE] * 5 + [-5.0, 64, 1, 2, 128, 128, 128, 0, FAKE, None, FAKE, 1 << 40, None]
+    assert L.kda_chunk_fwd_ex(*args, 5, None) == E_MODE
+    # the ablation mode ignores g_min (it must not be rejected for it) -> fails later on the workspace
+    args2 = list(args)
+    args2[5] = 3.0
+    args2[16] = 10
+    assert L.kda_chunk_fwd_ex(*args2, 1, None) == E_WS
+    assert L.kda_chunk_fwd_ex(*args2, 0, None) == E_GMIN
+    assert L.kda_chunk_fwd_ex(*args, 0, FAKE + 4) == E_ALIGN
+    assert L.kda_gate_cumsum(None, -5.0, 64, 1, 2, 128, 128, 0, 0, FAKE, None) == E_NULL
+    assert L.kda_gate_cumsum(FAKE, -5.0, 64, 1, 2, 100, 128, 0, 0, FAKE, None) == E_SHAPE
+    assert L.kda_gate_cumsum(FAKE, 0.5, 64, 1, 2, 128, 128, 0, 0, FAKE, None) == E_GMIN
+    assert L.kda_gate_cumsum(FAKE, -5.0, 64, 1, 2, 128, 128, 0, 3, FAKE, None) == E_MODE
+    assert L.kda_gate_cumsum(FAKE + 2, -5.0, 64, 1, 2, 128, 128, 0, 0, FAKE, None) == E_ALIGN
+    # empty sequence with no final state: nothing to do, no HIP call
+    assert _fwd(T=0, ws=None, wsb=0) == OK
+    assert L.kda_gate_cumsum(FAKE, -5.0, 64, 1, 2, 0, 128, 0, 0, FAKE, None) == OK
+
+
+def test_binding_rejects_host_tensors():
+    x = torch.zeros(1, 1, 64, 64)
+    with pytest.raises(ValueError):
+        kda.chunk_fwd(x, x, x, x, torch.zeros(1, 1, 64), chunk=16)
+    with pytest.raises(ValueError):
+        kda.gate_cumsum(x, chunk=16)

@@ -1,0 +1,239 @@
+"""Parity of the HIP path (through the C ABI) with the float64 oracle.
+
+Bar: bf16 I/O  max|out - oracle| <= 2e-2 * RMS(oracle out);  fp32 I/O  <= 1e-4
+absolute; final state with the same rule against RMS(oracle state).
+Small problems are compared element by element in full; the large workloads
+on whole sampled heads (the oracle runs each sampled head's entire sequence).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import chunked_gated_linear_bounded_amd as kda
+import kda_inputs as KI
+from oracle import native, overflow, reference
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    kda.lib()
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _tol_check(got, ref, io, what="out"):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape
+    assert np.all(np.isfinite(got)), "non-finite %s" % what
+    d = np.abs(got - ref)
+    rms = math.sqrt(float(np.mean(ref ** 2)))
+    mx = float(d.max()) if d.size else 0.0
+    tol = 2e-2 * rms if io == "bf16" else 1e-4
+    _say("  %s: max|d|=%.3e tol=%.3e rms=%.3e rel_rms=%.3e p9999=%.3e" % (
+        what, mx, tol, rms, math.sqrt(float(np.mean(d ** 2))) / max(rms, 1e-30),
+        float(np.quantile(d, 0.9999)) if d.size else 0.0))
+    assert mx <= tol, "%s: max|d| %.4e > tol %.4e" % (what, mx, tol)
+
+
+def _gpu_run(inp, chunk, g_min=-5.0, gate="bounded", counts=None):
+    return kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["a"], inp["beta"], g_min=g_min, chunk=chunk,
+                         return_final_state=True, gate=gate, counts=counts)
+
+
+def _oracle(inp64, g_min=-5.0, gate="bounded"):
+    return native.recurrent(inp64["q"], inp64["k"], inp64["v"], inp64["a"], inp64["beta"], g_min, gate=gate)
+
+
+def _to_dev(inp):
+    return {n: t.cuda() for n, t in inp.items()}
+
+
+# ---------------------------------------------------------------- gate kernel
+@pytest.mark.parametrize("io", ["bf16", "fp32"])
+@pytest.mark.parametrize("chunk,dk", [(16, 64), (32, 128), (64, 128), (64, 64)])
+@pytest.mark.parametrize("gate", ["bounded", "logsigmoid"])
+def test_gate_cumsum(io, chunk, dk, gate):
+    w = KI.Workload("g", 2, 3, 4 * chunk, dk, dk, chunk, io, 4.0, True, 17)
+    _say("gate_cumsum", io, chunk, dk, gate)
+    inp = _to_dev(KI.make_inputs(w))
+    G = kda.gate_cumsum(inp["a"], -5.0, chunk, gate=gate)
+    torch.cuda.synchronize()
+    a64 = inp["a"].double().cpu().numpy()
+    g = reference.gate(a64, -5.0, gate)
+    want = np.concatenate([np.cumsum(g[:, :, n0:n0 + chunk], axis=2) for n0 in range(0, w.T, chunk)], axis=2)
+    got = G.double().cpu().numpy()
+    err = np.abs(got - want)
+    assert np.all(err <= 1e-4 + 2e-6 * np.abs(want)), float(err.max())
+
+
+# ---------------------------------------------------------------- all shapes, small sizes, full compare
+SHAPES = [(dk, dv, c) for dk in (64, 128) for dv in (64, 128) for c in (16, 32, 64)]
+
+
+@pytest.mark.parametrize("io", ["bf16", "fp32"])
+@pytest.mark.parametrize("dk,dv,chunk", SHAPES)
+def test_small_parity_all_shapes(io, dk, dv, chunk):
+    # several chunks, a head count that leaves the last group of 8 heads ragged
+    w = KI.Workload("s", 1, 3, 5 * chunk, dk, dv, chunk, io, 2.0, False, 100 + dk + dv + chunk)
+    _say("small", io, dk, dv, chunk)
+    inp = _to_dev(KI.make_inputs(w))
+    out, fs = _gpu_run(inp, chunk)
+    torch.cuda.synchronize()
+    ro, rf = _oracle(KI.to_f64(inp))
+    _tol_check(out.double().cpu().numpy(), ro, io)
+    _tol_check(fs.double().cpu().numpy(), rf, io, "final_state")
+
+
+def test_tiny_workload_full():
+    w = KI.BY_NAME["tiny"]
+    inp = _to_dev(KI.make_inputs(w))
+    out, fs = _gpu_run(inp, w.chunk)
+    torch.cuda.synchronize()
+    ro, rf = _oracle(KI.to_f64(inp))
+    _tol_check(out.double().cpu().numpy(), ro, "fp32")
+    _tol_check(fs.double().cpu().numpy(), rf, "fp32", "final_state")
+
+
+def test_multi_batch_bf16():
+    w = KI.Workload("mb", 3, 5, 384, 128, 128, 64, "bf16", 4.0, False, 55)
+    inp = _to_dev(KI.make_inputs(w))
+    out, fs = _gpu_run(inp, 64)
+    torch.cuda.synchronize()
+    ro, rf = _oracle(KI.to_f64(inp))
+    _tol_check(out.double().cpu().numpy(), ro, "bf16")
+    _tol_check(fs.double().cpu().numpy(), rf, "bf16", "final_state")
+
+
+# ---------------------------------------------------------------- the large workloads, sampled heads
+def _sampled(w, heads, t_end=None):
+    _say("workload", w.name, "generating on GPU")
+    inp = KI.make_inputs(w, device="cuda")
+    counts = torch.zeros(2, dtype=torch.int64, device="cuda")
+    out, fs = _gpu_run(inp, w.chunk, counts=counts)
+    torch.cuda.synchronize()
+    assert counts.tolist() == [0, 0]
+    for (b, h) in heads:
+        _say(" head", b, h)
+        hs = KI.head_slice(inp, b, h, t_end)
+        ro, rf = _oracle(hs)
+        _tol_check(out[b, h, :t_end].double().cpu().numpy(), ro[0, 0], w.io)
+        if t_end is None:
+            _tol_check(fs[b, h].double().cpu().numpy(), rf[0, 0], w.io, "final_state")
+    return inp, out
+
+
+def test_workload_8k():
+    _sampled(KI.BY_NAME["8k"], [(0, 0), (1, 7), (3, 15)])
+
+
+def test_workload_64k():
+    _sampled(KI.BY_NAME["64k"], [(0, 0), (0, 31)])
+
+
+def test_workload_256k_final_state():
+    _sampled(KI.BY_NAME["256k"], [(0, 5)])
+
+
+def test_workload_1m_bounded():
+    # every output of one head checked over its first 2^17 tokens (the prefix is
+    # exact by causality), all heads run in full, no non-finite values anywhere
+    _sampled(KI.BY_NAME["1m"], [(0, 3)], t_end=131072)
+
+
+# ---------------------------------------------------------------- ablation: unbounded gate
+def test_ablation_overflow_counts():
+    w = KI.BY_NAME["1m"].with_(H=2, T=65536)
+    inp = KI.make_inputs(w, device="cuda")
+    counts = torch.zeros(2, dtype=torch.int64, device="cuda")
+    out = kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["a"], inp["beta"], chunk=64,
+                        gate="logsigmoid", counts=counts)
+    torch.cuda.synchronize()
+    a64 = inp["a"].double().cpu().numpy()
+    k64 = inp["k"].double().cpu().numpy()
+    pred, border = overflow.subtile_operand_overflow(a64, k64, -5.0, 64, "logsigmoid")
+    got = counts.tolist()
+    _say("ablation counts", got, "predicted", pred, "borderline", border)
+    assert pred > 0
+    assert abs(got[0] - pred) <= border
+    assert got[1] > 0
+    # the same data through the bounded gate: nothing overflows
+    counts.zero_()
+    kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["a"], inp["beta"], chunk=64, counts=counts)
+    torch.cuda.synchronize()
+    assert counts.tolist() == [0, 0]
+
+
+# ---------------------------------------------------------------- invariants
+def test_beta_zero_exact_zero():
+    w = KI.Workload("z", 1, 2, 256, 128, 128, 64, "bf16", 4.0, False, 3)
+    inp = _to_dev(KI.make_inputs(w))
+    inp["beta"].zero_()
+    out, fs = _gpu_run(inp, 64)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out).item() == 0 and torch.count_nonzero(fs).item() == 0
+
+
+def test_delta_retrieval_fp32():
+    w = KI.Workload("d", 1, 2, 256, 64, 64, 16, "fp32", 2.0, False, 4)
+    inp = _to_dev(KI.make_inputs(w))
+    inp["q"] = inp["k"].clone()
+    inp["beta"].fill_(1.0)
+    out, _ = _gpu_run(inp, 16)
+    torch.cuda.synchronize()
+    assert float((out - inp["v"]).abs().max()) <= 1e-4
+
+
+def test_deterministic_and_causal():
+    w = KI.Workload("c", 1, 4, 512, 128, 128, 64, "bf16", 4.0, False, 8)
+    inp = _to_dev(KI.make_inputs(w))
+    o1, f1 = _gpu_run(inp, 64)
+    o2, f2 = _gpu_run(inp, 64)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(f1, f2)
+    t = 5 * 64 + 17  # inside chunk 5
+    inp["k"][:, :, t] = -inp["k"][:, :, t]
+    inp["v"][:, :, t] = 3.0
+    o3, _ = _gpu_run(inp, 64)
+    torch.cuda.synchronize()
+    assert torch.equal(o3[:, :, :t], o1[:, :, :t])
+    assert not torch.equal(o3[:, :, t:], o1[:, :, t:])
+
+
+def test_chunk_sizes_agree():
+    w = KI.Workload("cs", 1, 2, 512, 128, 128, 64, "bf16", 4.0, False, 9)
+    inp = _to_dev(KI.make_inputs(w))
+    ro, _ = _oracle(KI.to_f64(inp))
+    for c in (16, 32, 64):
+        o, _ = _gpu_run(inp, c)
+        torch.cuda.synchronize()
+        _tol_check(o.double().cpu().numpy(), ro, "bf16", "out chunk %d" % c)
+
+
+def test_linear_in_v():
+    w = KI.Workload("lv", 1, 2, 256, 64, 64, 32, "fp32", 2.0, False, 10)
+    x = _to_dev(KI.make_inputs(w))
+    y = dict(x)
+    y["v"] = torch.randn_like(x["v"])
+    z = dict(x)
+    z["v"] = 2.0 * x["v"] - 3.0 * y["v"]
+    ox, _ = _gpu_run(x, 32)
+    oy, _ = _gpu_run(y, 32)
+    oz, _ = _gpu_run(z, 32)
+    torch.cuda.synchronize()
+    assert float((oz - (2.0 * ox - 3.0 * oy)).abs().max()) <= 1e-4
+
+
+def test_empty_sequence():
+    inp = {n: torch.empty((1, 2, 0, 64) if n != "beta" else (1, 2, 0), dtype=torch.bfloat16, device="cuda")
+           for n in ("q", "k", "v", "a", "beta")}
+    out, fs = _gpu_run(inp, 16)
+    torch.cuda.synchronize()
+    assert out.shape == (1, 2, 0, 64) and torch.count_nonzero(fs).item() == 0
