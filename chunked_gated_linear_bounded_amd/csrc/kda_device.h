@@ -104,6 +104,47 @@ __device__ __forceinline__ f32x4 mma(const Frag<true> &a, const Frag<true> &b, f
     for (int j = 0; j < 8; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[j], b.v[j], c, 0, 0, 0);
     return c;
 }
+// Split-precision operands: x = hi + lo with hi = bf16(x), lo = bf16(x - hi),
+// good to about 16 significant bits.  A product of two split operands keeps
+// three of the four cross terms (hi*hi + lo*hi + hi*lo); the dropped lo*lo is
+// ~2^-16 relative.  With fp32 operands no split is needed (lo unused).
+template <bool F32> struct Split {
+    Frag<F32> hi, lo;
+    __device__ __forceinline__ static Split make(const float (&x)[8]) {
+        Split s;
+        s.hi = Frag<F32>::make(x);
+        if constexpr (!F32) {
+            float r[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) r[j] = x[j] - s.hi.get(j);
+            s.lo = Frag<F32>::make(r);
+        }
+        return s;
+    }
+};
+template <bool F32>
+__device__ __forceinline__ f32x4 mma3(const Split<F32> &a, const Split<F32> &b, f32x4 c) {
+    c = mma(a.hi, b.hi, c);
+    if constexpr (!F32) {
+        c = mma(a.lo, b.hi, c);
+        c = mma(a.hi, b.lo, c);
+    }
+    return c;
+}
+// one split operand (the other exact in the operand type): hi*b + lo*b
+template <bool F32>
+__device__ __forceinline__ f32x4 mma2a(const Split<F32> &a, const Frag<F32> &b, f32x4 c) {
+    c = mma(a.hi, b, c);
+    if constexpr (!F32) c = mma(a.lo, b, c);
+    return c;
+}
+template <bool F32>
+__device__ __forceinline__ f32x4 mma2b(const Frag<F32> &a, const Split<F32> &b, f32x4 c) {
+    c = mma(a, b.hi, c);
+    if constexpr (!F32) c = mma(a, b.lo, c);
+    return c;
+}
+
 // Plain fp32 16x16x16 step: lane group g supplies k = 4g + s in step s.
 __device__ __forceinline__ f32x4 mma4(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);

@@ -1,13 +1,15 @@
 // Chunk-parallel stage: one work-group (4 waves) per (chunk, head, batch).
 //
 // For one chunk of C tokens (r, s = 0..C-1 local positions, G = inclusive
-// log-cumsum of the gate inside the chunk) it computes, all in fp32 with bf16
-// (or fp32) MFMA operands:
+// log-cumsum of the gate inside the chunk) it computes, fp32 accumulation:
 //   M_rs = sum_c q_rc k_sc e^{G_rc - G_sc}            (s <= r)
 //   A_rs = beta_r sum_c k_rc k_sc e^{G_rc - G_sc}     (s <  r)
-//   T = (I + A)^-1,  W = T diag(beta) (K e^G),  U~ = T diag(beta) V
-//   Q~ = Q e^G,  K^ = K e^{G_last - G},  gamma = e^{G_last}
-// and writes them in fragment order to the chunk's workspace record.
+//   T = (I + A)^-1,  Tb = T diag(beta)
+//   W = Tb (K e^G),  U~ = Tb V                        (WY form of the delta rule)
+//   Oi = M U~        (the chunk's own contribution to its outputs)
+//   Qbar = Q e^G - M W,  K^ = K e^{G_last - G},  gamma = e^{G_last}
+// so that the sequential stage only has to do, per chunk,
+//   U = U~ - W S^T,  O = Oi + Qbar S^T,  S^T <- diag(gamma) S^T + K^^T U.
 //
 // Gamma scaling without a position-pair path ("Trillion-Scale MoE Multimodal
 // Models: Practical Techniques ...", sec. 3.1-3.3; "Breaking Through ...",
@@ -18,9 +20,13 @@
 // range because g >= g_min = -5.  So every causal 16x16 sub-tile, diagonal or
 // not, is one dense MFMA contraction over the key channels.
 //
-// UT solve (delta rule in WY form): the 16x16 diagonal blocks of T are solved
-// by forward substitution (one lane per column), then the off-diagonal blocks
-// level by level, T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ, with fp32 MFMAs.
+// Precision: the scaled operands of M and A, M itself and U~ enter their
+// products as bf16 hi + lo pairs (three MFMAs per K-block), Oi and U~ are kept
+// in fp32; W, T diag(beta), K e^G, Qbar and K^ are single bf16 operands.
+//
+// UT solve: the 16x16 diagonal blocks of T by forward substitution (one lane
+// per column), then the off-diagonal blocks level by level,
+// T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ, with fp32 MFMAs.
 #pragma once
 #include "kda_device.h"
 #include "kda_layout.h"
@@ -38,7 +44,7 @@ struct IntraCfg {
     static constexpr int PG = DK + 4;            // sG pitch (floats)
     static constexpr int PQ = DK + (F32 ? 4 : 8);  // q/k pitch (elements)
     static constexpr int PV = DV + (F32 ? 4 : 8);
-    static constexpr int PA = C + 4;             // A / T pitch (floats)
+    static constexpr int PA = C + 4;             // A / T / M pitch (floats)
     static constexpr int SZ_G = C * PG * 4;
     static constexpr int SZ_TV = C * PA * 4 + C * PV * ES;
     static constexpr int R0 = SZ_G > SZ_TV ? SZ_G : SZ_TV;
@@ -50,6 +56,8 @@ struct IntraCfg {
     static constexpr int OFF_SCR = OFF_B + C * 4;
     static constexpr int SMEM = OFF_SCR + 256 * 4;
     static constexpr int VEC = 16 / ES;          // elements per 16-byte access
+    static constexpr int MAXJ = (NJOB + 3) / 4;  // M/A jobs per wave
+    static constexpr int MAXCT = (NDK + 3) / 4;  // dk tiles per wave
 };
 
 template <int C, int DK, int DV, bool F32>
@@ -65,18 +73,21 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
     using Cfg = IntraCfg<C, DK, DV, F32>;
     using E = typename Cfg::E;
     using F = Frag<F32>;
+    using SP = Split<F32>;
     constexpr int NT = Cfg::NT, NDK = Cfg::NDK, NDV = Cfg::NDV, NKB = Cfg::NKB, NTKB = Cfg::NTKB;
     constexpr int PG = Cfg::PG, PQ = Cfg::PQ, PV = Cfg::PV, PA = Cfg::PA, VEC = Cfg::VEC;
+    constexpr int MAXJ = Cfg::MAXJ, MAXCT = Cfg::MAXCT;
     constexpr KdaLayout L = kda_layout(C, DK, DV, Cfg::ES);
+    constexpr int TE = 256;  // elements per tile
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[Cfg::SMEM];
-    float *sG = reinterpret_cast<float *>(smem);                            // R0: G (log2)
-    float *sT = reinterpret_cast<float *>(smem);                            // R0: T, after G
-    E *sV = reinterpret_cast<E *>(smem + C * PA * 4);                       // R0: V, after G
-    E *sQ = reinterpret_cast<E *>(smem + Cfg::OFF_R1);                      // R1: q
-    float *sA = reinterpret_cast<float *>(smem + Cfg::OFF_R1);              // R1: A, after q
-    E *sK = reinterpret_cast<E *>(smem + Cfg::OFF_R2);                      // R2: k, then beta K~
-    float *sB = reinterpret_cast<float *>(smem + Cfg::OFF_B);               // beta
+    float *sG = reinterpret_cast<float *>(smem);                   // R0: G (log2 units)
+    float *sT = reinterpret_cast<float *>(smem);                   // R0: T, once G is dead
+    E *sV = reinterpret_cast<E *>(smem + C * PA * 4);              // R0: V, once G is dead
+    E *sQ = reinterpret_cast<E *>(smem + Cfg::OFF_R1);             // R1: q
+    float *sA = reinterpret_cast<float *>(smem + Cfg::OFF_R1);     // R1: A, then M
+    E *sK = reinterpret_cast<E *>(smem + Cfg::OFF_R2);             // R2: k, then K e^G
+    float *sB = reinterpret_cast<float *>(smem + Cfg::OFF_B);      // beta
     float *sScr = reinterpret_cast<float *>(smem + Cfg::OFF_SCR);
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
@@ -86,12 +97,9 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
     const size_t tok0 = head * (size_t)T + (size_t)n * C;
     unsigned char *rec = ws + ((size_t)head * NC + n) * L.stride;
     E *wWT = reinterpret_cast<E *>(rec + L.wt);
-    E *wQT = reinterpret_cast<E *>(rec + L.qt);
+    E *wQB = reinterpret_cast<E *>(rec + L.qbt);
     E *wKH = reinterpret_cast<E *>(rec + L.kh);
-    E *wMT = reinterpret_cast<E *>(rec + L.mt);
     float *wGam = reinterpret_cast<float *>(rec + L.gam);
-    E *wUT = reinterpret_cast<E *>(rec + L.ut);
-    constexpr int TE = 256;  // elements per tile
 
     // ------------------------------------------------ phase 0: loads, gate, prefix sum
     if (tid < C) sB[tid] = to_f(beta[tok0 + tid]);
@@ -119,11 +127,10 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
             if (r < C) vreg[it] = *reinterpret_cast<const uint4 *>(vg + (size_t)r * DV + c);
         }
     }
-    gate_cumsum_tile<C, DK, E>(a + tok0 * DK, gmin2, logsig, sG, PG, sScr);  // ends with barrier
+    gate_cumsum_tile<C, DK, E>(a + tok0 * DK, gmin2, logsig, sG, PG, sScr);  // ends with a barrier
 
-    // ------------------------------------------------ phase 1: causal sub-tiles of M and A
-    constexpr int MAXJ = (Cfg::NJOB + 3) / 4;
-    f32x4 accAs[MAXJ];
+    // ------------------------------------------------ phase 1: causal sub-tiles of M and A (split precision)
+    f32x4 accMs[MAXJ], accAs[MAXJ];
     int jobI[MAXJ], jobJ[MAXJ];
     unsigned int nonfinite = 0;
 #pragma unroll
@@ -154,47 +161,47 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
                 ld4(sQ + r * PQ + c, qr);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    cv[4 * hh + i] = ks[i] * ex2(rh[i] - gs[i]);   // key, scaled to rho_I
+                    cv[4 * hh + i] = ks[i] * ex2(rh[i] - gs[i]);   // key s, referenced to rho_I
                     const float e = ex2(gr[i] - rh[i]);            // <= 1
                     qv[4 * hh + i] = qr[i] * e;
                     kv[4 * hh + i] = kr[i] * e;
                 }
             }
-            const F fc = F::make(cv), fq = F::make(qv), fk = F::make(kv);
+            const SP fc = SP::make(cv), fq = SP::make(qv), fk = SP::make(kv);
             if (counts != nullptr && I == J) {
 #pragma unroll
-                for (int j = 0; j < 8; ++j) nonfinite += !__builtin_isfinite(fc.get(j));
+                for (int j = 0; j < 8; ++j) nonfinite += !__builtin_isfinite(fc.hi.get(j));
             }
-            accM = mma(fc, fq, accM);  // rows s, cols r: M^T
-            accA = mma(fk, fc, accA);  // rows r, cols s: A (before beta)
+            accM = mma3(fq, fc, accM);  // rows r, cols s
+            accA = mma3(fk, fc, accA);
         }
-        // M^T tile (st = J, rt = I): keep s <= r
-        f32x4 m = accM;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (I == J && (4 * g + i) > l16) m[i] = 0.f;
-        st_tile(wMT + (I * (I + 1) / 2 + J) * TE, lane, m);
-        // A tile rows r = 16I + 4g + i, cols s = 16J + l16: keep s < r, times beta_r
-        f32x4 aa = accA;
+        // element (row r = 16I + 4g + i, col s = 16J + l16): M keeps s <= r, A keeps s < r (times beta_r)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const bool keep = (I > J) || (l16 < 4 * g + i);
-            aa[i] = keep ? aa[i] * sB[16 * I + 4 * g + i] : 0.f;
+            const int rr = 4 * g + i;
+            if (I == J && l16 > rr) accM[i] = 0.f;
+            accA[i] = (I > J || l16 < rr) ? accA[i] * sB[16 * I + rr] : 0.f;
         }
-        accAs[jj] = aa;
+        accMs[jj] = accM;
+        accAs[jj] = accA;
     }
 
-    // elementwise operands: Q~^T tiles (ct, rt), K^ tiles (st, ct), gamma
-    for (int tix = wave; tix < NDK * NT; tix += 4) {
-        const int ct = tix / NT, rt = tix % NT;
-        const int r = 16 * rt + l16, c = 16 * ct + 4 * g;
-        float qr[4], gr[4];
-        ld4(sQ + r * PQ + c, qr);
-        ld4(sG + r * PG + c, gr);
-        f32x4 o;
+    // Q e^G as Qbar^T tiles (ct, rt) of this wave's dk tiles, kept in registers until phase 3;
+    // K^ tiles (st, ct) and gamma go straight to the workspace.
+    f32x4 qtr[MAXCT][NT];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o[i] = qr[i] * ex2(gr[i]);
-        st_tile(wQT + (ct * NT + rt) * TE, lane, o);
+    for (int ci = 0; ci < MAXCT; ++ci) {
+        const int ct = wave + 4 * ci;
+        if (ct >= NDK) continue;
+#pragma unroll
+        for (int rt = 0; rt < NT; ++rt) {
+            const int r = 16 * rt + l16, c = 16 * ct + 4 * g;
+            float qr[4], gr[4];
+            ld4(sQ + r * PQ + c, qr);
+            ld4(sG + r * PG + c, gr);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) qtr[ci][rt][i] = qr[i] * ex2(gr[i]);
+        }
     }
     for (int tix = wave; tix < NT * NDK; tix += 4) {
         const int st = tix / NDK, ct = tix % NDK;
@@ -211,7 +218,7 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
     if (tid < DK) wGam[tid] = ex2(sG[(C - 1) * PG + tid]);
     __syncthreads();  // q, raw k and the M/A operands are no longer read
 
-    // ------------------------------------------------ phase 1c: A -> LDS, K -> beta K e^G in place
+    // ------------------------------------------------ phase 1c: A -> LDS, K -> K e^G in place
 #pragma unroll
     for (int jj = 0; jj < MAXJ; ++jj) {
         if (jobI[jj] < 0) continue;
@@ -227,32 +234,26 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
                 float kr[4], gs[4];
                 ld4(sK + s * PQ + c, kr);
                 ld4(sG + s * PG + c, gs);
-                const float bs = sB[s];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sK[s * PQ + c + i] = from_f<E>(bs * kr[i] * ex2(gs[i]));
+                for (int i = 0; i < 4; ++i) sK[s * PQ + c + i] = from_f<E>(kr[i] * ex2(gs[i]));
             }
         }
     }
     __syncthreads();  // G is dead from here on
 
     // ------------------------------------------------ phase 2: T = (I + A)^-1
-    {
-        const E *vregE = reinterpret_cast<const E *>(vreg);
-        (void)vregE;
 #pragma unroll
-        for (int it = 0; it < VN; ++it) {
-            const int r = it * VRPP + tid / VLPR, c = (tid % VLPR) * VEC;
-            if (r < C) *reinterpret_cast<uint4 *>(sV + r * PV + c) = vreg[it];
-        }
+    for (int it = 0; it < VN; ++it) {
+        const int r = it * VRPP + tid / VLPR, c = (tid % VLPR) * VEC;
+        if (r < C) *reinterpret_cast<uint4 *>(sV + r * PV + c) = vreg[it];
     }
-    // zero the blocks above the diagonal
-    for (int x = tid; x < NT * NT * 256; x += 256) {
+    for (int x = tid; x < NT * NT * 256; x += 256) {  // zero the blocks above the diagonal
         const int blk = x >> 8, e = x & 255;
         const int I = blk / NT, J = blk % NT;
         if (I < J) sT[(16 * I + (e >> 4)) * PA + 16 * J + (e & 15)] = 0.f;
     }
     if (wave == 0 && g < NT) {
-        // diagonal block I = g, column j = l16, forward substitution
+        // diagonal block I = g, column j = l16: forward substitution
         const int I = g, j = l16;
         const float *Ab = sA + (16 * I) * PA + 16 * I;
         float x[16];
@@ -272,8 +273,7 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
     for (int d = 1; d < NT; ++d) {
         const int J = wave, I = wave + d;
         if (I < NT) {
-            // X = sum_{K=J}^{I-1} A_IK T_KJ
-            f32x4 X = {0.f, 0.f, 0.f, 0.f};
+            f32x4 X = {0.f, 0.f, 0.f, 0.f};  // X = sum_{K=J}^{I-1} A_IK T_KJ
             for (int K = J; K < I; ++K) {
                 float av[4];
                 ld4(sA + (16 * I + l16) * PA + 16 * K + 4 * g, av);
@@ -281,8 +281,7 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
                 for (int st = 0; st < 4; ++st)
                     X = mma4(av[st], sT[(16 * K + 4 * g + st) * PA + 16 * J + l16], X);
             }
-            // T_IJ = -T_II X
-            float tv[4];
+            float tv[4];  // T_IJ = -T_II X
             ld4(sT + (16 * I + l16) * PA + 16 * I + 4 * g, tv);
             f32x4 Y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -292,26 +291,51 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
         }
         __syncthreads();
     }
+    // A is dead: M takes its place
+#pragma unroll
+    for (int jj = 0; jj < MAXJ; ++jj) {
+        if (jobI[jj] < 0) continue;
+        const int I = jobI[jj], J = jobJ[jj];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sA[(16 * I + 4 * g + i) * PA + 16 * J + l16] = accMs[jj][i];
+    }
+    for (int x = tid; x < NT * NT * 256; x += 256) {  // and M's blocks above the diagonal are zero
+        const int blk = x >> 8, e = x & 255;
+        const int I = blk / NT, J = blk % NT;
+        if (I < J) sA[(16 * I + (e >> 4)) * PA + 16 * J + (e & 15)] = 0.f;
+    }
+    __syncthreads();
+    const float *sM = sA;
 
-    // ------------------------------------------------ phase 3: W^T = (beta K~)^T T^T,  U~ = T (beta V)
-    // T fragments: lane l, row r = 16 rt + l16, slots = tokens 32 kb + kslot.
+    // ------------------------------------------------ phase 3
+    // Fragments indexed by (row tile rt, token K-block kb): lane l holds row r = 16 rt + l16,
+    // slots = columns 32 kb + kslot.  tf: T diag(beta); mf: M (hi + lo).
     F tf[NT][NTKB];
+    SP mf[NT][NTKB];
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt)
 #pragma unroll
         for (int kb = 0; kb < NTKB; ++kb) {
-            float x[8];
-            const float *row = sT + (16 * rt + l16) * PA + 32 * kb + 4 * g;
+            float x[8], y[8];
+            const int r = 16 * rt + l16;
             const bool hi = (2 * kb + 1) < NT;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                x[i] = row[i];
-                x[4 + i] = hi ? row[16 + i] : 0.f;
+                const int s0 = 32 * kb + 4 * g + i, s1 = s0 + 16;
+                x[i] = sT[r * PA + s0] * sB[s0];
+                x[4 + i] = hi ? sT[r * PA + s1] * sB[s1] : 0.f;
+                y[i] = sM[r * PA + s0];
+                y[4 + i] = hi ? sM[r * PA + s1] : 0.f;
             }
             tf[rt][kb] = F::make(x);
+            mf[rt][kb] = SP::make(y);
         }
-    for (int ct = wave; ct < NDK; ct += 4) {
-        F kf[NTKB];
+    // dk tiles: W^T (-> workspace), W (registers), Qbar^T = (Q e^G)^T - W^T M^T (-> workspace)
+#pragma unroll
+    for (int ci = 0; ci < MAXCT; ++ci) {
+        const int ct = wave + 4 * ci;
+        if (ct >= NDK) continue;
+        F kf[NTKB];  // (K e^G): lane l holds column c = 16 ct + l16 at token slots
 #pragma unroll
         for (int kb = 0; kb < NTKB; ++kb) {
             float x[8];
@@ -322,32 +346,81 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
             }
             kf[kb] = F::make(x);
         }
+        f32x4 wrow[NT];  // W tiles (st, ct): rows s, cols dk
 #pragma unroll
         for (int rt = 0; rt < NT; ++rt) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            f32x4 accT = {0.f, 0.f, 0.f, 0.f}, accW = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kb = 0; kb <= rt / 2; ++kb) acc = mma(kf[kb], tf[rt][kb], acc);
-            st_tile(wWT + (ct * NT + rt) * TE, lane, acc);
+            for (int kb = 0; kb <= rt / 2; ++kb) {
+                accT = mma(kf[kb], tf[rt][kb], accT);  // W^T (ct, rt)
+                accW = mma(tf[rt][kb], kf[kb], accW);  // W (rt, ct)
+            }
+            st_tile(wWT + (ct * NT + rt) * TE, lane, accT);
+            wrow[rt] = accW;
+        }
+        F wa[NTKB];  // W as the A operand of W^T (m = dk, k = token)
+#pragma unroll
+        for (int kb = 0; kb < NTKB; ++kb) {
+            float x[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int t = 2 * kb + j / 4;
+                x[j] = (t < NT) ? wrow[t < NT ? t : 0][j % 4] : 0.f;
+            }
+            wa[kb] = F::make(x);
+        }
+#pragma unroll
+        for (int rt = 0; rt < NT; ++rt) {
+            f32x4 mw = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb <= rt / 2; ++kb) mw = mma2b(wa[kb], mf[rt][kb], mw);
+            f32x4 o;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = qtr[ci][rt][i] - mw[i];
+            st_tile(wQB + (ct * NT + rt) * TE, lane, o);
         }
     }
+    // dv tiles: U~ (-> workspace, fp32), Oi^T = U~^T M^T (-> workspace, fp32)
     for (int vt = wave; vt < NDV; vt += 4) {
-        F vf[NTKB];
+        float *wU = reinterpret_cast<float *>(rec + L.region1 + vt * L.slice + L.ut);
+        float *wO = reinterpret_cast<float *>(rec + L.region1 + vt * L.slice + L.oit);
+        F vf[NTKB];  // V: lane l holds column 16 vt + l16 at token slots
 #pragma unroll
         for (int kb = 0; kb < NTKB; ++kb) {
             float x[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int s = 32 * kb + (j < 4 ? 4 * g + j : 16 + 4 * g + j - 4);
-                x[j] = (s < C) ? to_f(sV[s * PV + 16 * vt + l16]) * sB[s] : 0.f;
+                x[j] = (s < C) ? to_f(sV[s * PV + 16 * vt + l16]) : 0.f;
             }
             vf[kb] = F::make(x);
         }
+        f32x4 urow[NT];
 #pragma unroll
         for (int rt = 0; rt < NT; ++rt) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb <= rt / 2; ++kb) acc = mma(tf[rt][kb], vf[kb], acc);
-            st_tile(wUT + (vt * NT + rt) * TE, lane, acc);
+            st_tile(wU + rt * TE, lane, acc);
+            urow[rt] = acc;
+        }
+        SP ua[NTKB];  // U~ as the A operand of U~^T (m = dv, k = token), hi + lo
+#pragma unroll
+        for (int kb = 0; kb < NTKB; ++kb) {
+            float x[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int t = 2 * kb + j / 4;
+                x[j] = (t < NT) ? urow[t < NT ? t : 0][j % 4] : 0.f;
+            }
+            ua[kb] = SP::make(x);
+        }
+#pragma unroll
+        for (int rt = 0; rt < NT; ++rt) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb <= rt / 2; ++kb) acc = mma3(ua[kb], mf[rt][kb], acc);
+            st_tile(wO + rt * TE, lane, acc);
         }
     }
     if (counts != nullptr && nonfinite) atomicAdd(&counts[0], (unsigned long long)nonfinite);

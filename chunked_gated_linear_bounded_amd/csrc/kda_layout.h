@@ -4,27 +4,29 @@
 // Every operand is stored as 16x16 tiles in "accumulator fragment order": tile
 // element (row 4*(l/16)+i, column l%16) sits at lane l, slot i (i = 0..3), so
 // lane l's four values are contiguous and a wave stores or loads a whole tile
-// with one coalesced 8-byte (bf16) or 16-byte (fp32) access per lane.
+// with one coalesced access per lane.
 //
 // Per (batch, head, chunk) record, in this order:
-//   WT  : W^T   (dk x C)  tiles [ct][rt]       W = T diag(beta) (K * e^G)
-//   QT  : Q~^T  (dk x C)  tiles [ct][rt]       Q~ = Q * e^G
-//   KH  : K^    (C x dk)  tiles [st][ct]       K^ = K * e^(G_last - G)
-//   MT  : M^T   (C x C)   causal tiles only, index rt*(rt+1)/2 + st (st <= rt)
-//   GAM : e^(G_last)  dk float32
-//   UT  : U~    (C x dv)  tiles [vt][rt]       U~ = T diag(beta) V
-// The first five are contiguous ("region 1"), then the dv/16 column slices of
-// U~ each contiguous, so a consumer that owns one 16-wide slice of the value
-// dimension reads two contiguous byte ranges per chunk.
+//   WT  : W^T    (dk x C)  tiles [ct][rt]  operand type   W = T diag(beta) (K e^G)
+//   QBT : Qbar^T (dk x C)  tiles [ct][rt]  operand type   Qbar = Q e^G - M W
+//   KH  : K^     (C x dk)  tiles [st][ct]  operand type   K^ = K e^(G_last - G)
+//   GAM : e^(G_last)       dk float32
+//   then, for each 16-wide slice vt of the value dimension (contiguous):
+//   UT  : U~     (C x 16)  tiles [rt]      float32        U~ = T diag(beta) V
+//   OIT : Oi^T   (16 x C)  tiles [rt]      float32        Oi = M U~ (intra-chunk output)
+// The first four are "region 1" (read by every slice's consumer); a consumer
+// that owns slice vt reads region 1 plus its own slice: two byte ranges.
 #pragma once
 #include <stddef.h>
 
 struct KdaLayout {
-    int NT, NDK, NDV, NMT;     // C/16, dk/16, dv/16, causal tile count
-    size_t tile;               // bytes per 16x16 tile
-    size_t wt, qt, kh, mt, gam, ut;  // byte offsets inside one record
+    int NT, NDK, NDV;          // C/16, dk/16, dv/16
+    size_t tile;               // bytes per 16x16 operand-type tile
+    size_t tile32;             // bytes per 16x16 float32 tile (1024)
+    size_t wt, qbt, kh, gam;   // byte offsets inside one record
     size_t region1;            // bytes of WT..GAM
-    size_t uslice;             // bytes of one 16-wide U~ slice (NT tiles)
+    size_t slice;              // bytes of one value slice (UT + OIT)
+    size_t ut, oit;            // offsets of UT and OIT inside a slice
     size_t stride;             // bytes per record (256-byte multiple)
 };
 
@@ -34,17 +36,17 @@ static inline constexpr KdaLayout kda_layout(int C, int DK, int DV, int esize)
     L.NT = C / 16;
     L.NDK = DK / 16;
     L.NDV = DV / 16;
-    L.NMT = L.NT * (L.NT + 1) / 2;
     L.tile = (size_t)256 * (size_t)esize;
+    L.tile32 = 1024;
     L.wt = 0;
-    L.qt = L.wt + (size_t)L.NDK * L.NT * L.tile;
-    L.kh = L.qt + (size_t)L.NDK * L.NT * L.tile;
-    L.mt = L.kh + (size_t)L.NT * L.NDK * L.tile;
-    L.gam = L.mt + (size_t)L.NMT * L.tile;
+    L.qbt = L.wt + (size_t)L.NDK * L.NT * L.tile;
+    L.kh = L.qbt + (size_t)L.NDK * L.NT * L.tile;
+    L.gam = L.kh + (size_t)L.NT * L.NDK * L.tile;
     L.region1 = L.gam + (size_t)DK * 4;
-    L.ut = L.region1;
-    L.uslice = (size_t)L.NT * L.tile;
-    size_t end = L.ut + (size_t)L.NDV * L.uslice;
+    L.ut = 0;
+    L.oit = (size_t)L.NT * L.tile32;
+    L.slice = 2 * (size_t)L.NT * L.tile32;
+    size_t end = L.region1 + (size_t)L.NDV * L.slice;
     L.stride = (end + 255) / 256 * 256;
     return L;
 }

@@ -4,21 +4,23 @@
 // column slices (column j of S^T only ever depends on column j of U and of
 // S^T itself).  One work-group per (head, slice) walks the chunks in order:
 //   U   = U~ - W S^T                              (C x 16)
-//   O^T = (S^T)^T Q~^T + U^T M^T                  (16 x C)  -> out, bf16/fp32
+//   O^T = Oi^T + (S^T)^T Qbar^T                   (16 x C)  -> out
 //   S^T = diag(gamma) S^T + K^^T U                (dk x 16)
+// with W, Qbar, K^, gamma, U~ and Oi = M U~ from the chunk-parallel stage
 // ("Trillion-Parameter MoE Multimodal Models: Engineering Long-Context ...",
-// sec. 3.2: a constant-size state updated chunk by chunk.)
+// sec. 3.2: a constant-size state updated chunk by chunk).
 //
 // The slice of S^T stays in the compute wave's registers for the whole
 // sequence in accumulator layout; by the slot convention of kda_device.h the
 // same registers (rounded to the operand type) are the B operand of W S^T and
-// the A operand of (S^T)^T Q~^T, and U's accumulators are the B operand of
-// K^^T U and the A operand of U^T M^T -- no shuffles, no LDS round trips.
+// the A operand of (S^T)^T Qbar^T, and U's accumulators are the B operand of
+// K^^T U -- no shuffles, no LDS round trips.  U enters K^^T U as a bf16
+// hi + lo pair.
 //
 // Work-group = 2 waves: wave 0 computes, wave 1 copies the next chunk's record
-// (from the chunk-parallel stage) into the other half of a double buffer in
-// LDS; one barrier per chunk hands the buffers over.  Work-group ids are mapped
-// so that all slices of a head land on one XCD and share its L2.
+// into the other half of a double buffer in LDS; one barrier per chunk hands
+// the buffers over.  Work-group ids are mapped so that all slices of a head
+// land on one XCD and share its L2.
 #pragma once
 #include "kda_device.h"
 #include "kda_layout.h"
@@ -30,34 +32,41 @@ struct StateCfg {
     using E = typename std::conditional<F32, float, __bf16>::type;
     static constexpr int ES = sizeof(E);
     static constexpr KdaLayout L = kda_layout(C, DK, DV, ES);
-    static constexpr int BUF = (int)(L.region1 + L.uslice);
+    static constexpr int BUF = (int)(L.region1 + L.slice);
     static constexpr int LDS_MAX = 160 * 1024;
     static constexpr int NBUF = (2 * BUF <= LDS_MAX) ? 2 : 1;
     static constexpr int SMEM = NBUF * BUF;
     static constexpr int NS = DV / 16;
 };
 
-// Copy this chunk's record (region 1 + own U~ slice) into an LDS buffer; one wave.
-template <int BUF>
-__device__ __forceinline__ void load_record(unsigned char *dst, const unsigned char *__restrict__ reg1,
-                                            int reg1_bytes, const unsigned char *__restrict__ uslice,
-                                            int uslice_bytes, int lane) {
-    constexpr int B = 16;  // 16-byte loads in flight per batch
-    for (int base = 0; base < reg1_bytes; base += 64 * 16 * B) {
+// Copy BYTES (a multiple of 16) from global memory to LDS with one wave, in
+// batches of 16-byte loads that are all issued before the first store.
+template <int BYTES>
+__device__ __forceinline__ void copy_to_lds(unsigned char *dst, const unsigned char *__restrict__ src, int lane) {
+    static_assert(BYTES % 16 == 0, "16-byte units");
+    constexpr int UNITS = BYTES / 16, PER = (UNITS + 63) / 64, B = 16;
+#pragma unroll
+    for (int b0 = 0; b0 < PER; b0 += B) {
         uint4 x[B];
 #pragma unroll
         for (int i = 0; i < B; ++i) {
-            const int off = base + (i * 64 + lane) * 16;
-            if (off < reg1_bytes) x[i] = *reinterpret_cast<const uint4 *>(reg1 + off);
+            const int u = (b0 + i) * 64 + lane;
+            if (b0 + i < PER && u < UNITS) x[i] = *reinterpret_cast<const uint4 *>(src + (size_t)u * 16);
         }
 #pragma unroll
         for (int i = 0; i < B; ++i) {
-            const int off = base + (i * 64 + lane) * 16;
-            if (off < reg1_bytes) *reinterpret_cast<uint4 *>(dst + off) = x[i];
+            const int u = (b0 + i) * 64 + lane;
+            if (b0 + i < PER && u < UNITS) *reinterpret_cast<uint4 *>(dst + u * 16) = x[i];
         }
     }
-    for (int off = lane * 16; off < uslice_bytes; off += 64 * 16)
-        *reinterpret_cast<uint4 *>(dst + reg1_bytes + off) = *reinterpret_cast<const uint4 *>(uslice + off);
+}
+
+// One chunk's record for one value slice: region 1, then the slice.
+template <int R1, int SL>
+__device__ __forceinline__ void load_record(unsigned char *dst, const unsigned char *__restrict__ rec,
+                                            size_t slice_off, int lane) {
+    copy_to_lds<R1>(dst, rec, lane);
+    copy_to_lds<SL>(dst + R1, rec + slice_off, lane);
 }
 
 template <int C, int DK, int DV, bool F32>
@@ -68,10 +77,12 @@ __global__ __launch_bounds__(128, 1) void kda_state_kernel(
     using Cfg = StateCfg<C, DK, DV, F32>;
     using E = typename Cfg::E;
     using F = Frag<F32>;
+    using SP = Split<F32>;
     constexpr KdaLayout L = Cfg::L;
     constexpr int NT = C / 16, NDK = DK / 16, NKB = DK / 32, NTKB = (NT + 1) / 2;
     constexpr int NS = Cfg::NS, BUF = Cfg::BUF, NBUF = Cfg::NBUF;
     constexpr int TE = 256;
+    constexpr int R1B = (int)L.region1, SLB = (int)L.slice;
 
     // all slices of a head on one XCD: work-group ids are dealt round-robin to the 8 XCDs
     const int id = blockIdx.x;
@@ -83,10 +94,10 @@ __global__ __launch_bounds__(128, 1) void kda_state_kernel(
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
     const int NC = T / C;
     const unsigned char *rec0 = ws + (size_t)hb * NC * L.stride;
+    const size_t soff = L.region1 + (size_t)slice * L.slice;
     const int j0 = 16 * slice;
 
-    if (wave == 1 && NC > 0)
-        load_record<BUF>(smem, rec0, (int)L.region1, rec0 + L.ut + slice * L.uslice, (int)L.uslice, lane);
+    if (wave == 1 && NC > 0) load_record<R1B, SLB>(smem, rec0, soff, lane);
     __syncthreads();
 
     f32x4 S[NDK];
@@ -99,19 +110,18 @@ __global__ __launch_bounds__(128, 1) void kda_state_kernel(
         if (wave == 1) {
             if (NBUF == 2 && n + 1 < NC) {
                 const unsigned char *rec = rec0 + (size_t)(n + 1) * L.stride;
-                load_record<BUF>(smem + ((n + 1) & 1) * BUF, rec, (int)L.region1,
-                                 rec + L.ut + slice * L.uslice, (int)L.uslice, lane);
+                load_record<R1B, SLB>(smem + ((n + 1) & 1) * BUF, rec, soff, lane);
             }
         } else {
             const E *bWT = reinterpret_cast<const E *>(cur + L.wt);
-            const E *bQT = reinterpret_cast<const E *>(cur + L.qt);
+            const E *bQB = reinterpret_cast<const E *>(cur + L.qbt);
             const E *bKH = reinterpret_cast<const E *>(cur + L.kh);
-            const E *bMT = reinterpret_cast<const E *>(cur + L.mt);
             const float *bG = reinterpret_cast<const float *>(cur + L.gam);
-            const E *bU = reinterpret_cast<const E *>(cur + L.region1);
+            const float *bU = reinterpret_cast<const float *>(cur + L.region1 + L.ut);
+            const float *bO = reinterpret_cast<const float *>(cur + L.region1 + L.oit);
             const int lo = lane * 4;
 
-            // state slice as operand (B of W S^T, A of (S^T)^T Q~^T)
+            // state slice as operand (B of W S^T, A of (S^T)^T Qbar^T)
             F Sb[NKB];
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
@@ -120,7 +130,7 @@ __global__ __launch_bounds__(128, 1) void kda_state_kernel(
                 for (int j = 0; j < 8; ++j) x[j] = S[2 * kb + j / 4][j % 4];
                 Sb[kb] = F::make(x);
             }
-            // U = U~ - W S^T
+            // U = U~ - W S^T   (tiles over tokens)
             f32x4 U[NT];
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt) {
@@ -133,7 +143,7 @@ __global__ __launch_bounds__(128, 1) void kda_state_kernel(
 #pragma unroll
                 for (int i = 0; i < 4; ++i) U[tt][i] = ut[i] - acc[i];
             }
-            F Ub[NTKB];
+            SP Ub[NTKB];
 #pragma unroll
             for (int kb = 0; kb < NTKB; ++kb) {
                 float x[8];
@@ -142,38 +152,34 @@ __global__ __launch_bounds__(128, 1) void kda_state_kernel(
                     const int t = 2 * kb + j / 4;
                     x[j] = (t < NT) ? U[t < NT ? t : 0][j % 4] : 0.f;
                 }
-                Ub[kb] = F::make(x);
+                Ub[kb] = SP::make(x);
             }
-            // O^T = (S^T)^T Q~^T + U^T M^T, one 16 x 16 tile per 16 tokens
+            // O^T = Oi^T + (S^T)^T Qbar^T, one 16 x 16 tile per 16 tokens
             const size_t trow = (size_t)hb * T + (size_t)n * C;
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                f32x4 acc = ld_tile(bO + tt * TE, lane);
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb)
-                    acc = mma(Sb[kb], F::load2(bQT + ((2 * kb) * NT + tt) * TE + lo,
-                                               bQT + ((2 * kb + 1) * NT + tt) * TE + lo), acc);
-#pragma unroll
-                for (int kb = 0; kb <= tt / 2; ++kb) {
-                    const int st0 = 2 * kb, st1 = 2 * kb + 1;
-                    const E *p0 = bMT + (tt * (tt + 1) / 2 + st0) * TE + lo;
-                    const F mf = (st1 <= tt) ? F::load2(p0, bMT + (tt * (tt + 1) / 2 + st1) * TE + lo)
-                                             : F::load1(p0);
-                    acc = mma(Ub[kb], mf, acc);
-                }
+                    acc = mma(Sb[kb], F::load2(bQB + ((2 * kb) * NT + tt) * TE + lo,
+                                               bQB + ((2 * kb + 1) * NT + tt) * TE + lo), acc);
                 // lane holds out[token 16 tt + l16][value j0 + 4g + i]
                 E *op = out + (trow + 16 * tt + l16) * DV + j0 + 4 * g;
-                if (counts != nullptr) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) nonfinite += !__builtin_isfinite(to_f(from_f<E>(acc[i])));
-                }
                 if constexpr (F32) {
                     *reinterpret_cast<f32x4 *>(op) = acc;
+                    if (counts != nullptr) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) nonfinite += !__builtin_isfinite(acc[i]);
+                    }
                 } else {
                     bf16x4 bo;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) bo[i] = (__bf16)acc[i];
                     *reinterpret_cast<bf16x4 *>(op) = bo;
+                    if (counts != nullptr) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) nonfinite += !__builtin_isfinite((float)bo[i]);
+                    }
                 }
             }
             // S^T = diag(gamma) S^T + K^^T U
@@ -188,7 +194,7 @@ __global__ __launch_bounds__(128, 1) void kda_state_kernel(
                     const E *p0 = bKH + ((2 * kb) * NDK + mt) * TE + lo;
                     const F kf = (2 * kb + 1 < NT) ? F::load2(p0, bKH + ((2 * kb + 1) * NDK + mt) * TE + lo)
                                                    : F::load1(p0);
-                    acc = mma(kf, Ub[kb], acc);
+                    acc = mma2b(kf, Ub[kb], acc);
                 }
                 S[mt] = acc;
             }
@@ -197,7 +203,7 @@ __global__ __launch_bounds__(128, 1) void kda_state_kernel(
         if (NBUF == 1) {
             if (wave == 1 && n + 1 < NC) {
                 const unsigned char *rec = rec0 + (size_t)(n + 1) * L.stride;
-                load_record<BUF>(smem, rec, (int)L.region1, rec + L.ut + slice * L.uslice, (int)L.uslice, lane);
+                load_record<R1B, SLB>(smem, rec, soff, lane);
             }
             __syncthreads();
         }
