@@ -55,7 +55,7 @@ int intra_impl(const void *q, const void *k, const void *v, const void *a, const
     if (st != KDA_OK) return st;
     st = check_gate(g_min, gate_mode);
     if (st != KDA_OK) return st;
-    if (!q || !k || !v || !a || !beta) return KDA_ERR_NULL;
+    if (T > 0 && (!q || !k || !v || !a || !beta)) return KDA_ERR_NULL;  // empty arrays may be NULL
     const size_t esz = io == KDA_FP32 ? 4 : 2;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(a, 16) || !aligned(beta, esz) ||
         (counts && !aligned(counts, 8)))
@@ -77,7 +77,7 @@ int state_impl(const void *workspace, size_t workspace_bytes_given, int chunk, i
                bool launch) {
     int st = check_shape(B, H, T, dk, dv, chunk, io);
     if (st != KDA_OK) return st;
-    if (!out) return KDA_ERR_NULL;
+    if (T > 0 && !out) return KDA_ERR_NULL;  // an empty out may be NULL
     if (!aligned(out, 16) || (final_state && !aligned(final_state, 16)) || (counts && !aligned(counts, 8)))
         return KDA_ERR_ALIGN;
     st = check_ptrs_ws(B, H, T, dk, dv, chunk, io, workspace, workspace_bytes_given);
@@ -147,7 +147,7 @@ int kda_gate_cumsum(const void *a, float g_min, int chunk, int B, int H, int T, 
     if (st != KDA_OK) return st;
     st = check_gate(g_min, gate_mode);
     if (st != KDA_OK) return st;
-    if (!a || !G_out) return KDA_ERR_NULL;
+    if (T > 0 && (!a || !G_out)) return KDA_ERR_NULL;  // empty arrays may be NULL
     if (!aligned(a, 16) || !aligned(G_out, 16)) return KDA_ERR_ALIGN;
     if (T == 0) return KDA_OK;
     kda::LaunchArgs p{};

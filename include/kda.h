@@ -30,7 +30,8 @@
  *    Element type of q, k, v, a, beta, out is given by io_dtype (KDA_BF16 or
  *    KDA_FP32); state, accumulation and G_out are float32.
  *  - q, k, v, a, out, final_state, G_out and the workspace must be 16-byte
- *    aligned; beta must be aligned to its element size.
+ *    aligned; beta must be aligned to its element size.  A pointer to an
+ *    array with zero elements (T == 0) may be NULL.
  *  - Supported: dk, dv in {64, 128}; chunk in {16, 32, 64}; T % chunk == 0;
  *    B, H >= 1; T >= 0; B*H*T*max(dk,dv) < 2^40.  Bounded mode needs a finite
  *    g_min with KDA_G_MIN_LOWEST <= g_min < 0 (below that bound a 16-token tile

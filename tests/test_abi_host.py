@@ -98,6 +98,8 @@ def test_validation_ex_and_gate():
     assert L.kda_gate_cumsum(FAKE + 2, -5.0, 64, 1, 2, 128, 128, 0, 0, FAKE, None) == E_ALIGN
     # empty sequence with no final state: nothing to do, no HIP call
     assert _fwd(T=0, ws=None, wsb=0) == OK
+    assert _fwd(T=0, q=None, k=None, v=None, a=None, beta=None, out=None, ws=None, wsb=0) == OK
+    assert _fwd(T=64, q=None, ws=None, wsb=0) == E_NULL
     assert L.kda_gate_cumsum(FAKE, -5.0, 64, 1, 2, 0, 128, 0, 0, FAKE, None) == OK
 
 
