@@ -10,17 +10,24 @@
 //    of lane l equal to its accumulator rows in tiles 2kb and 2kb+1.  Hence
 //    an accumulator tile pair of X can be fed back, with no data movement, as
 //    the B operand of X (k = row of X) or the A operand of X^T (m = column of X).
-//  * bf16 operands use v_mfma_f32_16x16x32_bf16 (one instruction per K-block);
-//    fp32 operands use eight v_mfma_f32_16x16x4_f32, step j taking slot j.
+//  * Operand types: bf16 (v_mfma_f32_16x16x32_bf16), fp16 (v_mfma_f32_16x16x32_f16),
+//    one instruction per K-block; fp32 (eight v_mfma_f32_16x16x4_f32, step j
+//    taking slot j).  fp16 operands are always scaled by a power of two chosen
+//    from the block's largest magnitude (see pow2_scale), so they cannot
+//    overflow; the scale is undone exactly on the fp32 result.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 namespace kda {
 
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -28,54 +35,51 @@ constexpr float kLn2 = 0.6931471805599453f;
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float rcpf(float x) { return __builtin_amdgcn_rcpf(x); }
 __device__ __forceinline__ float lg2(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float ldexp2(float x, int e) { return __builtin_amdgcn_ldexpf(x, e); }
 
 __device__ __forceinline__ float to_f(float x) { return x; }
 __device__ __forceinline__ float to_f(__bf16 x) { return (float)x; }
-template <typename E> __device__ __forceinline__ E from_f(float x);
-template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
-template <> __device__ __forceinline__ __bf16 from_f<__bf16>(float x) { return (__bf16)x; }
+__device__ __forceinline__ float to_f(_Float16 x) { return (float)x; }
+template <typename E> __device__ __forceinline__ E from_f(float x) { return (E)x; }
 
 // ---------------------------------------------------------------- operand fragments
-template <bool F32> struct Frag;
+template <typename T> struct VecOf;
+template <> struct VecOf<__bf16> { using v8 = bf16x8; using v4 = bf16x4; };
+template <> struct VecOf<_Float16> { using v8 = f16x8; using v4 = f16x4; };
 
-template <> struct Frag<false> {  // bf16, one 16x16x32 MFMA per K-block
-    bf16x8 v;
+template <typename T> struct Frag {  // 16-bit operand, one 16x16x32 MFMA per K-block
+    using V8 = typename VecOf<T>::v8;
+    using V4 = typename VecOf<T>::v4;
+    V8 v;
     __device__ __forceinline__ static Frag make(const float (&x)[8]) {
         Frag f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) f.v[j] = (__bf16)x[j];
+        for (int j = 0; j < 8; ++j) f.v[j] = (T)x[j];
         return f;
     }
-    __device__ __forceinline__ static Frag zero() { Frag f; f.v = bf16x8{}; return f; }
     // slots 0-3 from p0[0..3], slots 4-7 from p1[0..3] (each 8 contiguous bytes)
-    __device__ __forceinline__ static Frag load2(const __bf16 *p0, const __bf16 *p1) {
-        bf16x4 a = *reinterpret_cast<const bf16x4 *>(p0);
-        bf16x4 b = *reinterpret_cast<const bf16x4 *>(p1);
+    __device__ __forceinline__ static Frag load2(const T *p0, const T *p1) {
+        V4 a = *reinterpret_cast<const V4 *>(p0);
+        V4 b = *reinterpret_cast<const V4 *>(p1);
         Frag f;
         f.v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
         return f;
     }
-    __device__ __forceinline__ static Frag load1(const __bf16 *p0) {  // slots 4-7 zero
-        bf16x4 a = *reinterpret_cast<const bf16x4 *>(p0);
+    __device__ __forceinline__ static Frag load1(const T *p0) {  // slots 4-7 zero
+        V4 a = *reinterpret_cast<const V4 *>(p0);
         Frag f;
-        f.v = __builtin_shufflevector(a, bf16x4{}, 0, 1, 2, 3, 4, 5, 6, 7);
+        f.v = __builtin_shufflevector(a, V4{}, 0, 1, 2, 3, 4, 5, 6, 7);
         return f;
     }
     __device__ __forceinline__ float get(int j) const { return (float)v[j]; }
 };
 
-template <> struct Frag<true> {  // fp32, eight 16x16x4 MFMAs per K-block
+template <> struct Frag<float> {  // fp32, eight 16x16x4 MFMAs per K-block
     float v[8];
     __device__ __forceinline__ static Frag make(const float (&x)[8]) {
         Frag f;
 #pragma unroll
         for (int j = 0; j < 8; ++j) f.v[j] = x[j];
-        return f;
-    }
-    __device__ __forceinline__ static Frag zero() {
-        Frag f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) f.v[j] = 0.f;
         return f;
     }
     __device__ __forceinline__ static Frag load2(const float *p0, const float *p1) {
@@ -96,76 +100,88 @@ template <> struct Frag<true> {  // fp32, eight 16x16x4 MFMAs per K-block
     __device__ __forceinline__ float get(int j) const { return v[j]; }
 };
 
-__device__ __forceinline__ f32x4 mma(const Frag<false> &a, const Frag<false> &b, f32x4 c) {
+__device__ __forceinline__ f32x4 mma(const Frag<__bf16> &a, const Frag<__bf16> &b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, c, 0, 0, 0);
 }
-__device__ __forceinline__ f32x4 mma(const Frag<true> &a, const Frag<true> &b, f32x4 c) {
+__device__ __forceinline__ f32x4 mma(const Frag<_Float16> &a, const Frag<_Float16> &b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a.v, b.v, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma(const Frag<float> &a, const Frag<float> &b, f32x4 c) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[j], b.v[j], c, 0, 0, 0);
     return c;
 }
-// Split-precision operands: x = hi + lo with hi = bf16(x), lo = bf16(x - hi),
-// good to about 16 significant bits.  A product of two split operands keeps
-// three of the four cross terms (hi*hi + lo*hi + hi*lo); the dropped lo*lo is
-// ~2^-16 relative.  With fp32 operands no split is needed (lo unused).
-template <bool F32> struct Split {
-    Frag<F32> hi, lo;
-    __device__ __forceinline__ static Split make(const float (&x)[8]) {
-        Split s;
-        s.hi = Frag<F32>::make(x);
-        if constexpr (!F32) {
-            float r[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) r[j] = x[j] - s.hi.get(j);
-            s.lo = Frag<F32>::make(r);
-        }
-        return s;
-    }
-};
-template <bool F32>
-__device__ __forceinline__ f32x4 mma3(const Split<F32> &a, const Split<F32> &b, f32x4 c) {
-    c = mma(a.hi, b.hi, c);
-    if constexpr (!F32) {
-        c = mma(a.lo, b.hi, c);
-        c = mma(a.hi, b.lo, c);
-    }
-    return c;
-}
-// one split operand (the other exact in the operand type): hi*b + lo*b
-template <bool F32>
-__device__ __forceinline__ f32x4 mma2a(const Split<F32> &a, const Frag<F32> &b, f32x4 c) {
-    c = mma(a.hi, b, c);
-    if constexpr (!F32) c = mma(a.lo, b, c);
-    return c;
-}
-template <bool F32>
-__device__ __forceinline__ f32x4 mma2b(const Frag<F32> &a, const Split<F32> &b, f32x4 c) {
-    c = mma(a, b.hi, c);
-    if constexpr (!F32) c = mma(a, b.lo, c);
-    return c;
-}
-
 // Plain fp32 16x16x16 step: lane group g supplies k = 4g + s in step s.
 __device__ __forceinline__ f32x4 mma4(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// Split-precision bf16 operands: x = hi + lo, hi = bf16(x), lo = bf16(x - hi),
+// good to ~16 significant bits.  A product of two split operands keeps three of
+// the four cross terms (the dropped lo*lo is ~2^-16 relative).  With fp32
+// operands nothing is split (lo unused).
+template <typename T> struct Split {
+    Frag<T> hi, lo;
+    __device__ __forceinline__ static Split make(const float (&x)[8]) {
+        Split s;
+        s.hi = Frag<T>::make(x);
+        if constexpr (!std::is_same<T, float>::value) {
+            float r[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) r[j] = x[j] - s.hi.get(j);
+            s.lo = Frag<T>::make(r);
+        }
+        return s;
+    }
+};
+template <typename T>
+__device__ __forceinline__ f32x4 mma3(const Split<T> &a, const Split<T> &b, f32x4 c) {
+    c = mma(a.hi, b.hi, c);
+    if constexpr (!std::is_same<T, float>::value) {
+        c = mma(a.lo, b.hi, c);
+        c = mma(a.hi, b.lo, c);
+    }
+    return c;
+}
+template <typename T>
+__device__ __forceinline__ f32x4 mma2b(const Frag<T> &a, const Split<T> &b, f32x4 c) {
+    c = mma(a, b.hi, c);
+    if constexpr (!std::is_same<T, float>::value) c = mma(a, b.lo, c);
+    return c;
+}
+
+// ---------------------------------------------------------------- reductions and scaling
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+// Maximum over the 64 lanes of a wave, returned to every lane (wave-uniform).
+__device__ __forceinline__ float wave_max(float x) {
+    x = fmaxf(x, dpp_mov<0xB1>(x));   // quad_perm [1,0,3,2]
+    x = fmaxf(x, dpp_mov<0x4E>(x));   // quad_perm [2,3,0,1]
+    x = fmaxf(x, dpp_mov<0x141>(x));  // row_half_mirror
+    x = fmaxf(x, dpp_mov<0x140>(x));  // row_mirror: every lane has its row's max
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+// Power-of-two exponent s that maps magnitudes <= m into [2^13, 2^14) at the
+// top: x * 2^s is exact and stays below the fp16 maximum (65504).
+__device__ __forceinline__ int pow2_scale(float m) { return 14 - __builtin_amdgcn_frexp_expf(m); }
+
 // Store / load this lane's 4 values of a fragment-ordered 16x16 tile.
-__device__ __forceinline__ void st_tile(__bf16 *tile, int lane, f32x4 x) {
-    bf16x4 b;
+template <typename T>
+__device__ __forceinline__ void st_tile(T *tile, int lane, f32x4 x) {
+    if constexpr (std::is_same<T, float>::value) {
+        *reinterpret_cast<f32x4 *>(tile + lane * 4) = x;
+    } else {
+        typename VecOf<T>::v4 b;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) b[i] = (__bf16)x[i];
-    *reinterpret_cast<bf16x4 *>(tile + lane * 4) = b;
-}
-__device__ __forceinline__ void st_tile(float *tile, int lane, f32x4 x) {
-    *reinterpret_cast<f32x4 *>(tile + lane * 4) = x;
-}
-__device__ __forceinline__ f32x4 ld_tile(const __bf16 *tile, int lane) {
-    bf16x4 b = *reinterpret_cast<const bf16x4 *>(tile + lane * 4);
-    f32x4 x;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = (float)b[i];
-    return x;
+        for (int i = 0; i < 4; ++i) b[i] = (T)x[i];
+        *reinterpret_cast<typename VecOf<T>::v4 *>(tile + lane * 4) = b;
+    }
 }
 __device__ __forceinline__ f32x4 ld_tile(const float *tile, int lane) {
     return *reinterpret_cast<const f32x4 *>(tile + lane * 4);

@@ -21,8 +21,10 @@
 // not, is one dense MFMA contraction over the key channels.
 //
 // Precision: the scaled operands of M and A, M itself and U~ enter their
-// products as bf16 hi + lo pairs (three MFMAs per K-block), Oi and U~ are kept
-// in fp32; W, T diag(beta), K e^G, Qbar and K^ are single bf16 operands.
+// products as bf16 hi + lo pairs (three MFMAs per K-block); Oi and U~ are
+// stored in fp32; W, T diag(beta) and K e^G are bf16 operands; Qbar and K^ are
+// stored as fp16, each chunk's block scaled by a power of two from its largest
+// magnitude (the sequential stage undoes the scale on its fp32 results).
 //
 // UT solve: the 16x16 diagonal blocks of T by forward substitution (one lane
 // per column), then the off-diagonal blocks level by level,
@@ -72,8 +74,10 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
 {
     using Cfg = IntraCfg<C, DK, DV, F32>;
     using E = typename Cfg::E;
-    using F = Frag<F32>;
-    using SP = Split<F32>;
+    using OW = typename std::conditional<F32, float, __bf16>::type;    // MFMA operands here
+    using OH = typename std::conditional<F32, float, _Float16>::type;  // stored Qbar, K^
+    using F = Frag<OW>;
+    using SP = Split<OW>;
     constexpr int NT = Cfg::NT, NDK = Cfg::NDK, NDV = Cfg::NDV, NKB = Cfg::NKB, NTKB = Cfg::NTKB;
     constexpr int PG = Cfg::PG, PQ = Cfg::PQ, PV = Cfg::PV, PA = Cfg::PA, VEC = Cfg::VEC;
     constexpr int MAXJ = Cfg::MAXJ, MAXCT = Cfg::MAXCT;
@@ -96,10 +100,11 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
     const size_t head = (size_t)b * H + h;
     const size_t tok0 = head * (size_t)T + (size_t)n * C;
     unsigned char *rec = ws + ((size_t)head * NC + n) * L.stride;
-    E *wWT = reinterpret_cast<E *>(rec + L.wt);
-    E *wQB = reinterpret_cast<E *>(rec + L.qbt);
-    E *wKH = reinterpret_cast<E *>(rec + L.kh);
+    OW *wWT = reinterpret_cast<OW *>(rec + L.wt);
+    OH *wQB = reinterpret_cast<OH *>(rec + L.qbt);
+    OH *wKH = reinterpret_cast<OH *>(rec + L.kh);
     float *wGam = reinterpret_cast<float *>(rec + L.gam);
+    int *wScl = reinterpret_cast<int *>(rec + L.scl);
 
     // ------------------------------------------------ phase 0: loads, gate, prefix sum
     if (tid < C) sB[tid] = to_f(beta[tok0 + tid]);
@@ -187,7 +192,7 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
     }
 
     // Q e^G as Qbar^T tiles (ct, rt) of this wave's dk tiles, kept in registers until phase 3;
-    // K^ tiles (st, ct) and gamma go straight to the workspace.
+    // K^ tiles (st, ct) wait in registers for the chunk's scale; gamma goes to the workspace.
     f32x4 qtr[MAXCT][NT];
 #pragma unroll
     for (int ci = 0; ci < MAXCT; ++ci) {
@@ -203,20 +208,43 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
             for (int i = 0; i < 4; ++i) qtr[ci][rt][i] = qr[i] * ex2(gr[i]);
         }
     }
-    for (int tix = wave; tix < NT * NDK; tix += 4) {
+    constexpr int MAXKH = (NT * NDK + 3) / 4;
+    f32x4 khr[MAXKH];
+    float khmax = 0.f;
+#pragma unroll
+    for (int xi = 0; xi < MAXKH; ++xi) {
+        const int tix = wave + 4 * xi;
+        if (tix >= NT * NDK) continue;
         const int st = tix / NDK, ct = tix % NDK;
         const int c = 16 * ct + l16;
         const float glast = sG[(C - 1) * PG + c];
-        f32x4 o;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int s = 16 * st + 4 * g + i;
-            o[i] = to_f(sK[s * PQ + c]) * ex2(glast - sG[s * PG + c]);
+            khr[xi][i] = to_f(sK[s * PQ + c]) * ex2(glast - sG[s * PG + c]);
+            khmax = fmaxf(khmax, fabsf(khr[xi][i]));
         }
-        st_tile(wKH + (st * NDK + ct) * TE, lane, o);
     }
+    khmax = wave_max(khmax);
+    if (lane == 0) sScr[wave] = khmax;
     if (tid < DK) wGam[tid] = ex2(sG[(C - 1) * PG + tid]);
     __syncthreads();  // q, raw k and the M/A operands are no longer read
+
+    // ------------------------------------------------ K^ scaled to fp16 range
+    {
+        const int sK_ = F32 ? 0 : pow2_scale(fmaxf(fmaxf(sScr[0], sScr[1]), fmaxf(sScr[2], sScr[3])));
+        if (tid == 0) wScl[1] = sK_;
+#pragma unroll
+        for (int xi = 0; xi < MAXKH; ++xi) {
+            const int tix = wave + 4 * xi;
+            if (tix >= NT * NDK) continue;
+            const int st = tix / NDK, ct = tix % NDK;
+            f32x4 o;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = ldexp2(khr[xi][i], sK_);
+            st_tile(wKH + (st * NDK + ct) * TE, lane, o);
+        }
+    }
 
     // ------------------------------------------------ phase 1c: A -> LDS, K -> K e^G in place
 #pragma unroll
@@ -330,7 +358,8 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
             tf[rt][kb] = F::make(x);
             mf[rt][kb] = SP::make(y);
         }
-    // dk tiles: W^T (-> workspace), W (registers), Qbar^T = (Q e^G)^T - W^T M^T (-> workspace)
+    // dk tiles: W^T (-> workspace), W (registers), Qbar^T = (Q e^G)^T - W^T M^T (registers)
+    float qbmax = 0.f;
 #pragma unroll
     for (int ci = 0; ci < MAXCT; ++ci) {
         const int ct = wave + 4 * ci;
@@ -374,12 +403,15 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
             f32x4 mw = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb <= rt / 2; ++kb) mw = mma2b(wa[kb], mf[rt][kb], mw);
-            f32x4 o;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) o[i] = qtr[ci][rt][i] - mw[i];
-            st_tile(wQB + (ct * NT + rt) * TE, lane, o);
+            for (int i = 0; i < 4; ++i) {
+                qtr[ci][rt][i] -= mw[i];
+                qbmax = fmaxf(qbmax, fabsf(qtr[ci][rt][i]));
+            }
         }
     }
+    qbmax = wave_max(qbmax);
+    if (lane == 0) sScr[4 + wave] = qbmax;
     // dv tiles: U~ (-> workspace, fp32), Oi^T = U~^T M^T (-> workspace, fp32)
     for (int vt = wave; vt < NDV; vt += 4) {
         float *wU = reinterpret_cast<float *>(rec + L.region1 + vt * L.slice + L.ut);
@@ -421,6 +453,24 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
 #pragma unroll
             for (int kb = 0; kb <= rt / 2; ++kb) acc = mma3(ua[kb], mf[rt][kb], acc);
             st_tile(wO + rt * TE, lane, acc);
+        }
+    }
+    __syncthreads();
+    // Qbar scaled to fp16 range
+    {
+        const int sQ_ = F32 ? 0 : pow2_scale(fmaxf(fmaxf(sScr[4], sScr[5]), fmaxf(sScr[6], sScr[7])));
+        if (tid == 0) { wScl[0] = sQ_; wScl[2] = 0; wScl[3] = 0; }
+#pragma unroll
+        for (int ci = 0; ci < MAXCT; ++ci) {
+            const int ct = wave + 4 * ci;
+            if (ct >= NDK) continue;
+#pragma unroll
+            for (int rt = 0; rt < NT; ++rt) {
+                f32x4 o;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[i] = ldexp2(qtr[ci][rt][i], sQ_);
+                st_tile(wQB + (ct * NT + rt) * TE, lane, o);
+            }
         }
     }
     if (counts != nullptr && nonfinite) atomicAdd(&counts[0], (unsigned long long)nonfinite);

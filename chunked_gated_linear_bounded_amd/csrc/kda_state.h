@@ -12,15 +12,18 @@
 //
 // The slice of S^T stays in the compute wave's registers for the whole
 // sequence in accumulator layout; by the slot convention of kda_device.h the
-// same registers (rounded to the operand type) are the B operand of W S^T and
-// the A operand of (S^T)^T Qbar^T, and U's accumulators are the B operand of
-// K^^T U -- no shuffles, no LDS round trips.  U enters K^^T U as a bf16
-// hi + lo pair.
+// same registers are the B operand of W S^T and the A operand of
+// (S^T)^T Qbar^T, and U's accumulators are the B operand of K^^T U -- no
+// shuffles, no LDS round trips.  Operand types: W S^T in bf16; the output and
+// state-update products in fp16, with U and S^T scaled per chunk by a power of
+// two from their wave-wide maximum magnitude (Qbar and K^ arrive scaled the
+// same way), undone exactly on the fp32 results.
 //
-// Work-group = 2 waves: wave 0 computes, wave 1 copies the next chunk's record
-// into the other half of a double buffer in LDS; one barrier per chunk hands
-// the buffers over.  Work-group ids are mapped so that all slices of a head
-// land on one XCD and share its L2.
+// Work-group = 2 waves: wave 0 computes; wave 1 streams the next chunk's record
+// into the other half of a double buffer in LDS with direct global->LDS loads
+// (every load of a record in flight at once, no staging registers); one
+// barrier per chunk hands the buffers over.  Work-group ids are mapped so that
+// all slices of a head land on one XCD and share its L2.
 #pragma once
 #include "kda_device.h"
 #include "kda_layout.h"
@@ -39,34 +42,29 @@ struct StateCfg {
     static constexpr int NS = DV / 16;
 };
 
-// Copy BYTES (a multiple of 16) from global memory to LDS with one wave, in
-// batches of 16-byte loads that are all issued before the first store.
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Issue direct global->LDS copies of BYTES (multiple of 16) with one wave:
+// each instruction moves 64 x 16 bytes to consecutive LDS addresses.  The
+// caller waits for them (vmcnt) before handing the buffer over.
 template <int BYTES>
-__device__ __forceinline__ void copy_to_lds(unsigned char *dst, const unsigned char *__restrict__ src, int lane) {
+__device__ __forceinline__ void dma_to_lds(unsigned char *dst, const unsigned char *__restrict__ src, int lane) {
     static_assert(BYTES % 16 == 0, "16-byte units");
-    constexpr int UNITS = BYTES / 16, PER = (UNITS + 63) / 64, B = 16;
+    constexpr int UNITS = BYTES / 16, NI = (UNITS + 63) / 64;
 #pragma unroll
-    for (int b0 = 0; b0 < PER; b0 += B) {
-        uint4 x[B];
-#pragma unroll
-        for (int i = 0; i < B; ++i) {
-            const int u = (b0 + i) * 64 + lane;
-            if (b0 + i < PER && u < UNITS) x[i] = *reinterpret_cast<const uint4 *>(src + (size_t)u * 16);
-        }
-#pragma unroll
-        for (int i = 0; i < B; ++i) {
-            const int u = (b0 + i) * 64 + lane;
-            if (b0 + i < PER && u < UNITS) *reinterpret_cast<uint4 *>(dst + u * 16) = x[i];
-        }
+    for (int i = 0; i < NI; ++i) {
+        const int u = i * 64 + lane;
+        if (u < UNITS)
+            __builtin_amdgcn_global_load_lds(src + (size_t)u * 16, (lds_void *)(dst + i * 1024), 16, 0, 0);
     }
 }
 
-// One chunk's record for one value slice: region 1, then the slice.
 template <int R1, int SL>
 __device__ __forceinline__ void load_record(unsigned char *dst, const unsigned char *__restrict__ rec,
                                             size_t slice_off, int lane) {
-    copy_to_lds<R1>(dst, rec, lane);
-    copy_to_lds<SL>(dst + R1, rec + slice_off, lane);
+    dma_to_lds<R1>(dst, rec, lane);
+    dma_to_lds<SL>(dst + R1, rec + slice_off, lane);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the copies have landed in LDS
 }
 
 template <int C, int DK, int DV, bool F32>
@@ -76,8 +74,10 @@ __global__ __launch_bounds__(128, 1) void kda_state_kernel(
 {
     using Cfg = StateCfg<C, DK, DV, F32>;
     using E = typename Cfg::E;
-    using F = Frag<F32>;
-    using SP = Split<F32>;
+    using OW = typename std::conditional<F32, float, __bf16>::type;
+    using OH = typename std::conditional<F32, float, _Float16>::type;
+    using FW = Frag<OW>;
+    using FH = Frag<OH>;
     constexpr KdaLayout L = Cfg::L;
     constexpr int NT = C / 16, NDK = DK / 16, NKB = DK / 32, NTKB = (NT + 1) / 2;
     constexpr int NS = Cfg::NS, BUF = Cfg::BUF, NBUF = Cfg::NBUF;
@@ -90,7 +90,7 @@ __global__ __launch_bounds__(128, 1) void kda_state_kernel(
     const int hb = (local / NS) * 8 + xcd, slice = local % NS;
     if (hb >= BH) return;
 
-    __shared__ __attribute__((aligned(16))) unsigned char smem[Cfg::SMEM];
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[Cfg::SMEM];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
     const int NC = T / C;
     const unsigned char *rec0 = ws + (size_t)hb * NC * L.stride;
@@ -108,73 +108,100 @@ __global__ __launch_bounds__(128, 1) void kda_state_kernel(
     for (int n = 0; n < NC; ++n) {
         const unsigned char *cur = smem + (NBUF == 2 ? (n & 1) * BUF : 0);
         if (wave == 1) {
-            if (NBUF == 2 && n + 1 < NC) {
-                const unsigned char *rec = rec0 + (size_t)(n + 1) * L.stride;
-                load_record<R1B, SLB>(smem + ((n + 1) & 1) * BUF, rec, soff, lane);
-            }
+            if (NBUF == 2 && n + 1 < NC)
+                load_record<R1B, SLB>(smem + ((n + 1) & 1) * BUF, rec0 + (size_t)(n + 1) * L.stride, soff, lane);
         } else {
-            const E *bWT = reinterpret_cast<const E *>(cur + L.wt);
-            const E *bQB = reinterpret_cast<const E *>(cur + L.qbt);
-            const E *bKH = reinterpret_cast<const E *>(cur + L.kh);
+            const OW *bWT = reinterpret_cast<const OW *>(cur + L.wt);
+            const OH *bQB = reinterpret_cast<const OH *>(cur + L.qbt);
+            const OH *bKH = reinterpret_cast<const OH *>(cur + L.kh);
             const float *bG = reinterpret_cast<const float *>(cur + L.gam);
+            const int *bScl = reinterpret_cast<const int *>(cur + L.scl);
             const float *bU = reinterpret_cast<const float *>(cur + L.region1 + L.ut);
             const float *bO = reinterpret_cast<const float *>(cur + L.region1 + L.oit);
             const int lo = lane * 4;
 
-            // state slice as operand (B of W S^T, A of (S^T)^T Qbar^T)
-            F Sb[NKB];
+            // state slice as the B operand of W S^T (bf16)
+            FW Sb[NKB];
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
                 float x[8];
 #pragma unroll
                 for (int j = 0; j < 8; ++j) x[j] = S[2 * kb + j / 4][j % 4];
-                Sb[kb] = F::make(x);
+                Sb[kb] = FW::make(x);
+            }
+            // state slice as the A operand of (S^T)^T Qbar^T (fp16, scaled)
+            int sS = 0;
+            if constexpr (!F32) {
+                float m = 0.f;
+#pragma unroll
+                for (int mt = 0; mt < NDK; ++mt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(S[mt][i]));
+                sS = pow2_scale(wave_max(m));
+            }
+            FH Sh[NKB];
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                float x[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) x[j] = ldexp2(S[2 * kb + j / 4][j % 4], sS);
+                Sh[kb] = FH::make(x);
             }
             // U = U~ - W S^T   (tiles over tokens)
             f32x4 U[NT];
+            float um = 0.f;
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb)
-                    acc = mma(F::load2(bWT + ((2 * kb) * NT + tt) * TE + lo,
-                                       bWT + ((2 * kb + 1) * NT + tt) * TE + lo), Sb[kb], acc);
+                    acc = mma(FW::load2(bWT + ((2 * kb) * NT + tt) * TE + lo,
+                                        bWT + ((2 * kb + 1) * NT + tt) * TE + lo), Sb[kb], acc);
                 const f32x4 ut = ld_tile(bU + tt * TE, lane);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) U[tt][i] = ut[i] - acc[i];
+                for (int i = 0; i < 4; ++i) {
+                    U[tt][i] = ut[i] - acc[i];
+                    um = fmaxf(um, fabsf(U[tt][i]));
+                }
             }
-            SP Ub[NTKB];
+            const int sU = F32 ? 0 : pow2_scale(wave_max(um));
+            FH Uh[NTKB];
 #pragma unroll
             for (int kb = 0; kb < NTKB; ++kb) {
                 float x[8];
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const int t = 2 * kb + j / 4;
-                    x[j] = (t < NT) ? U[t < NT ? t : 0][j % 4] : 0.f;
+                    x[j] = (t < NT) ? ldexp2(U[t < NT ? t : 0][j % 4], sU) : 0.f;
                 }
-                Ub[kb] = SP::make(x);
+                Uh[kb] = FH::make(x);
             }
             // O^T = Oi^T + (S^T)^T Qbar^T, one 16 x 16 tile per 16 tokens
+            const int unscaleO = -(sS + bScl[0]);
             const size_t trow = (size_t)hb * T + (size_t)n * C;
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt) {
-                f32x4 acc = ld_tile(bO + tt * TE, lane);
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb)
-                    acc = mma(Sb[kb], F::load2(bQB + ((2 * kb) * NT + tt) * TE + lo,
-                                               bQB + ((2 * kb + 1) * NT + tt) * TE + lo), acc);
+                    acc = mma(Sh[kb], FH::load2(bQB + ((2 * kb) * NT + tt) * TE + lo,
+                                                bQB + ((2 * kb + 1) * NT + tt) * TE + lo), acc);
+                const f32x4 oi = ld_tile(bO + tt * TE, lane);
+                f32x4 o;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[i] = oi[i] + ldexp2(acc[i], unscaleO);
                 // lane holds out[token 16 tt + l16][value j0 + 4g + i]
                 E *op = out + (trow + 16 * tt + l16) * DV + j0 + 4 * g;
                 if constexpr (F32) {
-                    *reinterpret_cast<f32x4 *>(op) = acc;
+                    *reinterpret_cast<f32x4 *>(op) = o;
                     if (counts != nullptr) {
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) nonfinite += !__builtin_isfinite(acc[i]);
+                        for (int i = 0; i < 4; ++i) nonfinite += !__builtin_isfinite(o[i]);
                     }
                 } else {
                     bf16x4 bo;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) bo[i] = (__bf16)acc[i];
+                    for (int i = 0; i < 4; ++i) bo[i] = (__bf16)o[i];
                     *reinterpret_cast<bf16x4 *>(op) = bo;
                     if (counts != nullptr) {
 #pragma unroll
@@ -183,28 +210,26 @@ __global__ __launch_bounds__(128, 1) void kda_state_kernel(
                 }
             }
             // S^T = diag(gamma) S^T + K^^T U
+            const int unscaleS = -(sU + bScl[1]);
 #pragma unroll
             for (int mt = 0; mt < NDK; ++mt) {
                 const f32x4 gm = *reinterpret_cast<const f32x4 *>(bG + 16 * mt + 4 * g);
-                f32x4 acc;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] = S[mt][i] * gm[i];
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kb = 0; kb < NTKB; ++kb) {
-                    const E *p0 = bKH + ((2 * kb) * NDK + mt) * TE + lo;
-                    const F kf = (2 * kb + 1 < NT) ? F::load2(p0, bKH + ((2 * kb + 1) * NDK + mt) * TE + lo)
-                                                   : F::load1(p0);
-                    acc = mma2b(kf, Ub[kb], acc);
+                    const OH *p0 = bKH + ((2 * kb) * NDK + mt) * TE + lo;
+                    const FH kf = (2 * kb + 1 < NT) ? FH::load2(p0, bKH + ((2 * kb + 1) * NDK + mt) * TE + lo)
+                                                    : FH::load1(p0);
+                    acc = mma(kf, Uh[kb], acc);
                 }
-                S[mt] = acc;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) S[mt][i] = S[mt][i] * gm[i] + ldexp2(acc[i], unscaleS);
             }
         }
         __syncthreads();
         if (NBUF == 1) {
-            if (wave == 1 && n + 1 < NC) {
-                const unsigned char *rec = rec0 + (size_t)(n + 1) * L.stride;
-                load_record<R1B, SLB>(smem, rec, soff, lane);
-            }
+            if (wave == 1 && n + 1 < NC)
+                load_record<R1B, SLB>(smem, rec0 + (size_t)(n + 1) * L.stride, soff, lane);
             __syncthreads();
         }
     }
