@@ -71,6 +71,12 @@ template <typename T> struct Frag {  // 16-bit operand, one 16x16x32 MFMA per K-
         f.v = __builtin_shufflevector(a, V4{}, 0, 1, 2, 3, 4, 5, 6, 7);
         return f;
     }
+    // this lane's fragment from a stored tile pair (8 contiguous values)
+    __device__ __forceinline__ static Frag load_pair(const T *pair, int lane) {
+        Frag f;
+        f.v = *reinterpret_cast<const V8 *>(pair + lane * 8);
+        return f;
+    }
     __device__ __forceinline__ float get(int j) const { return (float)v[j]; }
 };
 
@@ -96,6 +102,9 @@ template <> struct Frag<float> {  // fp32, eight 16x16x4 MFMAs per K-block
 #pragma unroll
         for (int j = 0; j < 4; ++j) { f.v[j] = a[j]; f.v[4 + j] = 0.f; }
         return f;
+    }
+    __device__ __forceinline__ static Frag load_pair(const float *pair, int lane) {
+        return load2(pair + lane * 8, pair + lane * 8 + 4);
     }
     __device__ __forceinline__ float get(int j) const { return v[j]; }
 };
@@ -183,8 +192,21 @@ __device__ __forceinline__ void st_tile(T *tile, int lane, f32x4 x) {
         *reinterpret_cast<typename VecOf<T>::v4 *>(tile + lane * 4) = b;
     }
 }
+// Store this lane's 4 values of tile `half` (0: tile 2p, 1: tile 2p+1) of a tile pair.
+template <typename T>
+__device__ __forceinline__ void st_half(T *pair, int lane, int half, f32x4 x) {
+    st_tile(pair + lane * 4 + half * 4, lane, x);  // lands at pair + 8 lane + 4 half
+}
 __device__ __forceinline__ f32x4 ld_tile(const float *tile, int lane) {
     return *reinterpret_cast<const f32x4 *>(tile + lane * 4);
+}
+template <typename T>
+__device__ __forceinline__ f32x4 ld_tile(const T *tile, int lane) {
+    const typename VecOf<T>::v4 b = *reinterpret_cast<const typename VecOf<T>::v4 *>(tile + lane * 4);
+    f32x4 x;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = (float)b[i];
+    return x;
 }
 
 // Four consecutive elements as floats (8 or 16 contiguous bytes).
@@ -197,6 +219,17 @@ __device__ __forceinline__ void ld4(const float *p, float (&x)[4]) {
     f32x4 b = *reinterpret_cast<const f32x4 *>(p);
 #pragma unroll
     for (int i = 0; i < 4; ++i) x[i] = b[i];
+}
+
+// ---------------------------------------------------------------- direct global->LDS loads
+typedef __attribute__((address_space(3))) void lds_void;
+
+// s_waitcnt vmcnt(N) (expcnt, lgkmcnt unconstrained): all but the N most recent
+// vector-memory instructions of this wave have completed.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N <= 63, "vmcnt field is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
 // ---------------------------------------------------------------- the gate

@@ -22,7 +22,7 @@
 //
 // Precision: the scaled operands of M and A, M itself and U~ enter their
 // products as bf16 hi + lo pairs (three MFMAs per K-block); Oi and U~ are
-// stored in fp32; W, T diag(beta) and K e^G are bf16 operands; Qbar and K^ are
+// stored in fp32; T diag(beta) and K e^G are bf16 operands; W, Qbar and K^ are
 // stored as fp16, each chunk's block scaled by a power of two from its largest
 // magnitude (the sequential stage undoes the scale on its fp32 results).
 //
@@ -58,12 +58,11 @@ struct IntraCfg {
     static constexpr int OFF_SCR = OFF_B + C * 4;
     static constexpr int SMEM = OFF_SCR + 256 * 4;
     static constexpr int VEC = 16 / ES;          // elements per 16-byte access
-    static constexpr int MAXJ = (NJOB + 3) / 4;  // M/A jobs per wave
     static constexpr int MAXCT = (NDK + 3) / 4;  // dk tiles per wave
 };
 
 template <int C, int DK, int DV, bool F32>
-__global__ __launch_bounds__(256, 2) void kda_intra_kernel(
+__global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void kda_intra_kernel(
     const typename IntraCfg<C, DK, DV, F32>::E *__restrict__ q,
     const typename IntraCfg<C, DK, DV, F32>::E *__restrict__ k,
     const typename IntraCfg<C, DK, DV, F32>::E *__restrict__ v,
@@ -80,7 +79,7 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
     using SP = Split<OW>;
     constexpr int NT = Cfg::NT, NDK = Cfg::NDK, NDV = Cfg::NDV, NKB = Cfg::NKB, NTKB = Cfg::NTKB;
     constexpr int PG = Cfg::PG, PQ = Cfg::PQ, PV = Cfg::PV, PA = Cfg::PA, VEC = Cfg::VEC;
-    constexpr int MAXJ = Cfg::MAXJ, MAXCT = Cfg::MAXCT;
+    constexpr int MAXCT = Cfg::MAXCT;
     constexpr KdaLayout L = kda_layout(C, DK, DV, Cfg::ES);
     constexpr int TE = 256;  // elements per tile
 
@@ -94,13 +93,14 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
     float *sB = reinterpret_cast<float *>(smem + Cfg::OFF_B);      // beta
     float *sScr = reinterpret_cast<float *>(smem + Cfg::OFF_SCR);
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: branches on it stay scalar
     const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int NC = T / C;
     const size_t head = (size_t)b * H + h;
     const size_t tok0 = head * (size_t)T + (size_t)n * C;
     unsigned char *rec = ws + ((size_t)head * NC + n) * L.stride;
-    OW *wWT = reinterpret_cast<OW *>(rec + L.wt);
+    OH *wWT = reinterpret_cast<OH *>(rec + L.wt);
     OH *wQB = reinterpret_cast<OH *>(rec + L.qbt);
     OH *wKH = reinterpret_cast<OH *>(rec + L.kh);
     float *wGam = reinterpret_cast<float *>(rec + L.gam);
@@ -122,73 +122,84 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
             }
         }
     }
-    constexpr int VLPR = DV / VEC, VRPP = 256 / VLPR, VN = (C + VRPP - 1) / VRPP;
-    uint4 vreg[VN];
-    {
-        const E *vg = v + tok0 * DV;
-#pragma unroll
-        for (int it = 0; it < VN; ++it) {
-            const int r = it * VRPP + tid / VLPR, c = (tid % VLPR) * VEC;
-            if (r < C) vreg[it] = *reinterpret_cast<const uint4 *>(vg + (size_t)r * DV + c);
-        }
-    }
     gate_cumsum_tile<C, DK, E>(a + tok0 * DK, gmin2, logsig, sG, PG, sScr);  // ends with a barrier
 
-    // ------------------------------------------------ phase 1: causal sub-tiles of M and A (split precision)
-    f32x4 accMs[MAXJ], accAs[MAXJ];
-    int jobI[MAXJ], jobJ[MAXJ];
-    unsigned int nonfinite = 0;
+    // ------------------------------------------------ phase 1: causal sub-tiles of M and A
+    // Wave I owns row tile I and computes M_IJ and A_IJ for every J <= I.  The row
+    // operands (q and k of tile I scaled by e^{G_r - rho_I}) are built once per
+    // K-block and reused for all J.  The diagonal tile J = I, whose key operand
+    // carries factors up to e^{15 |g_min|}, takes bf16 hi + lo operands (three
+    // MFMAs); the earlier tiles take single bf16 operands.
+    f32x4 accMs[NT], accAs[NT];  // indexed by J
 #pragma unroll
-    for (int jj = 0; jj < MAXJ; ++jj) {
-        const int jb = wave + 4 * jj;
-        jobI[jj] = -1;
-        if (jb >= Cfg::NJOB) continue;
-        int I = 0, rem = jb;
-        while (rem > I) { rem -= I + 1; ++I; }
-        const int J = rem;
-        jobI[jj] = I;
-        jobJ[jj] = J;
-        const int s = 16 * J + l16, r = 16 * I + l16;
+    for (int J = 0; J < NT; ++J) {
+        accMs[J] = f32x4{0.f, 0.f, 0.f, 0.f};
+        accAs[J] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    unsigned int nonfinite = 0;
+    const int I = wave;
+    if (I < NT) {
+        const int r = 16 * I + l16;
         const float *rho = sG + (16 * I) * PG;
-        f32x4 accM = {0.f, 0.f, 0.f, 0.f}, accA = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
-            float cv[8], qv[8], kv[8];
+            float qv[8], kv[8], rh[8];
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
                 const int c = 32 * kb + 16 * hh + 4 * g;
-                float rh[4], gs[4], gr[4], ks[4], kr[4], qr[4];
-                ld4(rho + c, rh);
-                ld4(sG + s * PG + c, gs);
+                float rr[4], gr[4], kr[4], qr[4];
+                ld4(rho + c, rr);
                 ld4(sG + r * PG + c, gr);
-                ld4(sK + s * PQ + c, ks);
                 ld4(sK + r * PQ + c, kr);
                 ld4(sQ + r * PQ + c, qr);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    cv[4 * hh + i] = ks[i] * ex2(rh[i] - gs[i]);   // key s, referenced to rho_I
-                    const float e = ex2(gr[i] - rh[i]);            // <= 1
+                    const float e = ex2(gr[i] - rr[i]);  // <= 1
                     qv[4 * hh + i] = qr[i] * e;
                     kv[4 * hh + i] = kr[i] * e;
+                    rh[4 * hh + i] = rr[i];
                 }
             }
-            const SP fc = SP::make(cv), fq = SP::make(qv), fk = SP::make(kv);
-            if (counts != nullptr && I == J) {
+            const SP fq = SP::make(qv), fk = SP::make(kv);
 #pragma unroll
-                for (int j = 0; j < 8; ++j) nonfinite += !__builtin_isfinite(fc.hi.get(j));
+            for (int J = 0; J < NT; ++J) {
+                if (J > I) continue;
+                const int s = 16 * J + l16;
+                float cv[8];  // key s referenced to rho_I
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int c = 32 * kb + 16 * hh + 4 * g;
+                    float gs[4], ks[4];
+                    ld4(sG + s * PG + c, gs);
+                    ld4(sK + s * PQ + c, ks);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) cv[4 * hh + i] = ks[i] * ex2(rh[4 * hh + i] - gs[i]);
+                }
+                if (J == I) {
+                    const SP fc = SP::make(cv);
+                    if (counts != nullptr) {
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) nonfinite += !__builtin_isfinite(fc.hi.get(j));
+                    }
+                    accMs[J] = mma3(fq, fc, accMs[J]);  // rows r, cols s
+                    accAs[J] = mma3(fk, fc, accAs[J]);
+                } else {
+                    const F fc = F::make(cv);
+                    accMs[J] = mma(fq.hi, fc, accMs[J]);
+                    accAs[J] = mma(fk.hi, fc, accAs[J]);
+                }
             }
-            accM = mma3(fq, fc, accM);  // rows r, cols s
-            accA = mma3(fk, fc, accA);
         }
         // element (row r = 16I + 4g + i, col s = 16J + l16): M keeps s <= r, A keeps s < r (times beta_r)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int rr = 4 * g + i;
-            if (I == J && l16 > rr) accM[i] = 0.f;
-            accA[i] = (I > J || l16 < rr) ? accA[i] * sB[16 * I + rr] : 0.f;
+        for (int J = 0; J < NT; ++J) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int rr = 4 * g + i;
+                if (I == J && l16 > rr) accMs[J][i] = 0.f;
+                accAs[J][i] = (I > J || l16 < rr) ? accAs[J][i] * sB[16 * I + rr] : 0.f;
+            }
         }
-        accMs[jj] = accM;
-        accAs[jj] = accA;
     }
 
     // Q e^G as Qbar^T tiles (ct, rt) of this wave's dk tiles, kept in registers until phase 3;
@@ -233,7 +244,7 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
     // ------------------------------------------------ K^ scaled to fp16 range
     {
         const int sK_ = F32 ? 0 : pow2_scale(fmaxf(fmaxf(sScr[0], sScr[1]), fmaxf(sScr[2], sScr[3])));
-        if (tid == 0) wScl[1] = sK_;
+        if (tid == 0) wScl[2] = sK_;
 #pragma unroll
         for (int xi = 0; xi < MAXKH; ++xi) {
             const int tix = wave + 4 * xi;
@@ -242,17 +253,20 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
             f32x4 o;
 #pragma unroll
             for (int i = 0; i < 4; ++i) o[i] = ldexp2(khr[xi][i], sK_);
-            st_tile(wKH + (st * NDK + ct) * TE, lane, o);
+            OH *pair = wKH + ((st >> 1) * NDK + ct) * (2 * TE);
+            st_half(pair, lane, st & 1, o);
+            if (NT & 1) st_half(pair, lane, 1, f32x4{0.f, 0.f, 0.f, 0.f});  // odd tile count: empty partner
         }
     }
 
     // ------------------------------------------------ phase 1c: A -> LDS, K -> K e^G in place
+    if (I < NT) {
 #pragma unroll
-    for (int jj = 0; jj < MAXJ; ++jj) {
-        if (jobI[jj] < 0) continue;
-        const int I = jobI[jj], J = jobJ[jj];
+        for (int J = 0; J < NT; ++J) {
+            if (J > I) continue;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sA[(16 * I + 4 * g + i) * PA + 16 * J + l16] = accAs[jj][i];
+            for (int i = 0; i < 4; ++i) sA[(16 * I + 4 * g + i) * PA + 16 * J + l16] = accAs[J][i];
+        }
     }
     {
         constexpr int LPR = DK / 4, RPP = 256 / LPR;
@@ -270,10 +284,17 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
     __syncthreads();  // G is dead from here on
 
     // ------------------------------------------------ phase 2: T = (I + A)^-1
-#pragma unroll
-    for (int it = 0; it < VN; ++it) {
-        const int r = it * VRPP + tid / VLPR, c = (tid % VLPR) * VEC;
-        if (r < C) *reinterpret_cast<uint4 *>(sV + r * PV + c) = vreg[it];
+    {   // V straight into LDS with direct loads (one instruction per 256 bytes of a row);
+        // they land while T is being solved and are waited for before phase 3
+        constexpr int RB = DV * Cfg::ES, NPR = (RB + 255) / 256;
+        const unsigned char *vg = reinterpret_cast<const unsigned char *>(v + tok0 * DV);
+        unsigned char *sVb = reinterpret_cast<unsigned char *>(sV);
+        for (int x = wave; x < C * NPR; x += 4) {
+            const int r = x / NPR, part = x % NPR, off = part * 256 + lane * 4;
+            if (off < RB)
+                __builtin_amdgcn_global_load_lds(vg + (size_t)r * RB + off,
+                                                 (lds_void *)(sVb + r * PV * Cfg::ES + part * 256), 4, 0, 0);
+        }
     }
     for (int x = tid; x < NT * NT * 256; x += 256) {  // zero the blocks above the diagonal
         const int blk = x >> 8, e = x & 255;
@@ -320,18 +341,20 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
         __syncthreads();
     }
     // A is dead: M takes its place
+    if (I < NT) {
 #pragma unroll
-    for (int jj = 0; jj < MAXJ; ++jj) {
-        if (jobI[jj] < 0) continue;
-        const int I = jobI[jj], J = jobJ[jj];
+        for (int J = 0; J < NT; ++J) {
+            if (J > I) continue;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sA[(16 * I + 4 * g + i) * PA + 16 * J + l16] = accMs[jj][i];
+            for (int i = 0; i < 4; ++i) sA[(16 * I + 4 * g + i) * PA + 16 * J + l16] = accMs[J][i];
+        }
     }
     for (int x = tid; x < NT * NT * 256; x += 256) {  // and M's blocks above the diagonal are zero
         const int blk = x >> 8, e = x & 255;
         const int I = blk / NT, J = blk % NT;
         if (I < J) sA[(16 * I + (e >> 4)) * PA + 16 * J + (e & 15)] = 0.f;
     }
+    wait_vmcnt<0>();  // V has landed in LDS
     __syncthreads();
     const float *sM = sA;
 
@@ -358,8 +381,9 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
             tf[rt][kb] = F::make(x);
             mf[rt][kb] = SP::make(y);
         }
-    // dk tiles: W^T (-> workspace), W (registers), Qbar^T = (Q e^G)^T - W^T M^T (registers)
-    float qbmax = 0.f;
+    // dk tiles: W^T, W and Qbar^T = (Q e^G)^T - W^T M^T, kept in registers for the chunk's scale
+    float qbmax = 0.f, wmax = 0.f;
+    f32x4 wtr[MAXCT][NT];
 #pragma unroll
     for (int ci = 0; ci < MAXCT; ++ci) {
         const int ct = wave + 4 * ci;
@@ -384,7 +408,9 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
                 accT = mma(kf[kb], tf[rt][kb], accT);  // W^T (ct, rt)
                 accW = mma(tf[rt][kb], kf[kb], accW);  // W (rt, ct)
             }
-            st_tile(wWT + (ct * NT + rt) * TE, lane, accT);
+            wtr[ci][rt] = accT;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) wmax = fmaxf(wmax, fabsf(accT[i]));
             wrow[rt] = accW;
         }
         F wa[NTKB];  // W as the A operand of W^T (m = dk, k = token)
@@ -411,11 +437,17 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
         }
     }
     qbmax = wave_max(qbmax);
-    if (lane == 0) sScr[4 + wave] = qbmax;
-    // dv tiles: U~ (-> workspace, fp32), Oi^T = U~^T M^T (-> workspace, fp32)
+    wmax = wave_max(wmax);
+    if (lane == 0) {
+        sScr[4 + wave] = qbmax;
+        sScr[8 + wave] = wmax;
+    }
+    // dv slices (one wave each): U~ and Oi^T = U~^T M^T, scaled per slice to fp16 range
     for (int vt = wave; vt < NDV; vt += 4) {
-        float *wU = reinterpret_cast<float *>(rec + L.region1 + vt * L.slice + L.ut);
-        float *wO = reinterpret_cast<float *>(rec + L.region1 + vt * L.slice + L.oit);
+        unsigned char *sl = rec + L.region1 + vt * L.slice;
+        OH *wU = reinterpret_cast<OH *>(sl + L.ut);
+        OH *wO = reinterpret_cast<OH *>(sl + L.oit);
+        int *wS = reinterpret_cast<int *>(sl + L.ssc);
         F vf[NTKB];  // V: lane l holds column 16 vt + l16 at token slots
 #pragma unroll
         for (int kb = 0; kb < NTKB; ++kb) {
@@ -428,13 +460,15 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
             vf[kb] = F::make(x);
         }
         f32x4 urow[NT];
+        float um = 0.f;
 #pragma unroll
         for (int rt = 0; rt < NT; ++rt) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb <= rt / 2; ++kb) acc = mma(tf[rt][kb], vf[kb], acc);
-            st_tile(wU + rt * TE, lane, acc);
             urow[rt] = acc;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) um = fmaxf(um, fabsf(acc[i]));
         }
         SP ua[NTKB];  // U~ as the A operand of U~^T (m = dv, k = token), hi + lo
 #pragma unroll
@@ -447,29 +481,58 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(
             }
             ua[kb] = SP::make(x);
         }
+        f32x4 orow[NT];
+        float om = 0.f;
 #pragma unroll
         for (int rt = 0; rt < NT; ++rt) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb <= rt / 2; ++kb) acc = mma3(ua[kb], mf[rt][kb], acc);
-            st_tile(wO + rt * TE, lane, acc);
+            orow[rt] = acc;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) om = fmaxf(om, fabsf(acc[i]));
+        }
+        const int sU_ = F32 ? 0 : pow2_scale(wave_max(um));
+        const int sO_ = F32 ? 0 : pow2_scale(wave_max(om));
+#pragma unroll
+        for (int rt = 0; rt < NT; ++rt) {
+            f32x4 u, o;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                u[i] = ldexp2(urow[rt][i], sU_);
+                o[i] = ldexp2(orow[rt][i], sO_);
+            }
+            st_tile(wU + rt * TE, lane, u);
+            st_tile(wO + rt * TE, lane, o);
+        }
+        if (lane == 0) {
+            wS[0] = sU_;
+            wS[1] = sO_;
+            wS[2] = 0;
+            wS[3] = 0;
         }
     }
     __syncthreads();
-    // Qbar scaled to fp16 range
+    // W^T and Qbar^T scaled to fp16 range, stored as tile pairs along dk
     {
         const int sQ_ = F32 ? 0 : pow2_scale(fmaxf(fmaxf(sScr[4], sScr[5]), fmaxf(sScr[6], sScr[7])));
-        if (tid == 0) { wScl[0] = sQ_; wScl[2] = 0; wScl[3] = 0; }
+        const int sW_ = F32 ? 0 : pow2_scale(fmaxf(fmaxf(sScr[8], sScr[9]), fmaxf(sScr[10], sScr[11])));
+        if (tid == 0) { wScl[0] = sW_; wScl[1] = sQ_; wScl[3] = 0; }
 #pragma unroll
         for (int ci = 0; ci < MAXCT; ++ci) {
             const int ct = wave + 4 * ci;
             if (ct >= NDK) continue;
 #pragma unroll
             for (int rt = 0; rt < NT; ++rt) {
-                f32x4 o;
+                f32x4 o, w;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) o[i] = ldexp2(qtr[ci][rt][i], sQ_);
-                st_tile(wQB + (ct * NT + rt) * TE, lane, o);
+                for (int i = 0; i < 4; ++i) {
+                    o[i] = ldexp2(qtr[ci][rt][i], sQ_);
+                    w[i] = ldexp2(wtr[ci][rt][i], sW_);
+                }
+                const int pidx = ((ct >> 1) * NT + rt) * (2 * TE);
+                st_half(wQB + pidx, lane, ct & 1, o);
+                st_half(wWT + pidx, lane, ct & 1, w);
             }
         }
     }

@@ -14,15 +14,17 @@
 // sequence in accumulator layout; by the slot convention of kda_device.h the
 // same registers are the B operand of W S^T and the A operand of
 // (S^T)^T Qbar^T, and U's accumulators are the B operand of K^^T U -- no
-// shuffles, no LDS round trips.  Operand types: W S^T in bf16; the output and
-// state-update products in fp16, with U and S^T scaled per chunk by a power of
-// two from their wave-wide maximum magnitude (Qbar and K^ arrive scaled the
-// same way), undone exactly on the fp32 results.
+// shuffles, no LDS round trips.  All three products take fp16 operands: U and
+// S^T are scaled per chunk by a power of two from their wave-wide maximum
+// magnitude (W, Qbar and K^ arrive scaled the same way) and the scales are
+// undone exactly on the fp32 results.  Each operand fragment is one 16-byte
+// LDS read (tile pairs), and independent output tiles keep separate
+// accumulators so consecutive MFMAs do not wait on each other.
 //
-// Work-group = 2 waves: wave 0 computes; wave 1 streams the next chunk's record
-// into the other half of a double buffer in LDS with direct global->LDS loads
-// (every load of a record in flight at once, no staging registers); one
-// barrier per chunk hands the buffers over.  Work-group ids are mapped so that
+// Work-group = 2 waves: wave 0 computes; wave 1 streams chunk records into a
+// ring of three LDS buffers with direct global->LDS loads (every load of a
+// record in flight at once, no staging registers), two chunks ahead of the
+// compute wave; one barrier per chunk hands the buffers over.  Work-group ids are mapped so that
 // all slices of a head land on one XCD and share its L2.
 #pragma once
 #include "kda_device.h"
@@ -37,12 +39,13 @@ struct StateCfg {
     static constexpr KdaLayout L = kda_layout(C, DK, DV, ES);
     static constexpr int BUF = (int)(L.region1 + L.slice);
     static constexpr int LDS_MAX = 160 * 1024;
-    static constexpr int NBUF = (2 * BUF <= LDS_MAX) ? 2 : 1;
+    // direct-load instructions per record (each moves 1 KiB)
+    static constexpr int NDMA = (int)((L.region1 + 1023) / 1024 + (L.slice + 1023) / 1024);
+    // three buffers give two chunks of lookahead; the partial wait needs NDMA <= 63
+    static constexpr int NBUF = (3 * BUF <= LDS_MAX && NDMA <= 63) ? 3 : (2 * BUF <= LDS_MAX) ? 2 : 1;
     static constexpr int SMEM = NBUF * BUF;
     static constexpr int NS = DV / 16;
 };
-
-typedef __attribute__((address_space(3))) void lds_void;
 
 // Issue direct global->LDS copies of BYTES (multiple of 16) with one wave:
 // each instruction moves 64 x 16 bytes to consecutive LDS addresses.  The
@@ -59,24 +62,23 @@ __device__ __forceinline__ void dma_to_lds(unsigned char *dst, const unsigned ch
     }
 }
 
+// Issue the copies of one chunk's record (region 1 + one value slice).
 template <int R1, int SL>
-__device__ __forceinline__ void load_record(unsigned char *dst, const unsigned char *__restrict__ rec,
-                                            size_t slice_off, int lane) {
+__device__ __forceinline__ void issue_record(unsigned char *dst, const unsigned char *__restrict__ rec,
+                                             size_t slice_off, int lane) {
     dma_to_lds<R1>(dst, rec, lane);
     dma_to_lds<SL>(dst + R1, rec + slice_off, lane);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the copies have landed in LDS
 }
 
+
 template <int C, int DK, int DV, bool F32>
-__global__ __launch_bounds__(128, 1) void kda_state_kernel(
+__global__ __launch_bounds__(128, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void kda_state_kernel(
     const unsigned char *__restrict__ ws, typename StateCfg<C, DK, DV, F32>::E *__restrict__ out,
     float *__restrict__ final_state, int BH, int T, unsigned long long *__restrict__ counts)
 {
     using Cfg = StateCfg<C, DK, DV, F32>;
     using E = typename Cfg::E;
-    using OW = typename std::conditional<F32, float, __bf16>::type;
     using OH = typename std::conditional<F32, float, _Float16>::type;
-    using FW = Frag<OW>;
     using FH = Frag<OH>;
     constexpr KdaLayout L = Cfg::L;
     constexpr int NT = C / 16, NDK = DK / 16, NKB = DK / 32, NTKB = (NT + 1) / 2;
@@ -91,13 +93,23 @@ __global__ __launch_bounds__(128, 1) void kda_state_kernel(
     if (hb >= BH) return;
 
     __shared__ __attribute__((aligned(1024))) unsigned char smem[Cfg::SMEM];
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
+    const int wave = tid >> 6;
     const int NC = T / C;
     const unsigned char *rec0 = ws + (size_t)hb * NC * L.stride;
     const size_t soff = L.region1 + (size_t)slice * L.slice;
     const int j0 = 16 * slice;
 
-    if (wave == 1 && NC > 0) load_record<R1B, SLB>(smem, rec0, soff, lane);
+    constexpr int NDMA = Cfg::NDMA;
+    if (wave == 1 && NC > 0) {
+        issue_record<R1B, SLB>(smem, rec0, soff, lane);
+        if (NBUF == 3 && NC > 1) {
+            issue_record<R1B, SLB>(smem + BUF, rec0 + L.stride, soff, lane);
+            wait_vmcnt<NBUF == 3 ? NDMA : 0>();  // chunk 0 has landed
+        } else {
+            wait_vmcnt<0>();
+        }
+    }
     __syncthreads();
 
     f32x4 S[NDK];
@@ -106,30 +118,31 @@ __global__ __launch_bounds__(128, 1) void kda_state_kernel(
     unsigned int nonfinite = 0;
 
     for (int n = 0; n < NC; ++n) {
-        const unsigned char *cur = smem + (NBUF == 2 ? (n & 1) * BUF : 0);
+        const unsigned char *cur = smem + (n % NBUF) * BUF;
         if (wave == 1) {
-            if (NBUF == 2 && n + 1 < NC)
-                load_record<R1B, SLB>(smem + ((n + 1) & 1) * BUF, rec0 + (size_t)(n + 1) * L.stride, soff, lane);
+            if (NBUF == 3) {
+                if (n + 2 < NC) {
+                    issue_record<R1B, SLB>(smem + ((n + 2) % 3) * BUF, rec0 + (size_t)(n + 2) * L.stride, soff, lane);
+                    wait_vmcnt<NBUF == 3 ? NDMA : 0>();  // chunk n + 1 has landed
+                } else {
+                    wait_vmcnt<0>();
+                }
+            } else if (NBUF == 2 && n + 1 < NC) {
+                issue_record<R1B, SLB>(smem + ((n + 1) & 1) * BUF, rec0 + (size_t)(n + 1) * L.stride, soff, lane);
+                wait_vmcnt<0>();
+            }
         } else {
-            const OW *bWT = reinterpret_cast<const OW *>(cur + L.wt);
+            const OH *bWT = reinterpret_cast<const OH *>(cur + L.wt);
             const OH *bQB = reinterpret_cast<const OH *>(cur + L.qbt);
             const OH *bKH = reinterpret_cast<const OH *>(cur + L.kh);
             const float *bG = reinterpret_cast<const float *>(cur + L.gam);
             const int *bScl = reinterpret_cast<const int *>(cur + L.scl);
-            const float *bU = reinterpret_cast<const float *>(cur + L.region1 + L.ut);
-            const float *bO = reinterpret_cast<const float *>(cur + L.region1 + L.oit);
-            const int lo = lane * 4;
+            const OH *bU = reinterpret_cast<const OH *>(cur + L.region1 + L.ut);
+            const OH *bO = reinterpret_cast<const OH *>(cur + L.region1 + L.oit);
+            const int *bSS = reinterpret_cast<const int *>(cur + L.region1 + L.ssc);
+            constexpr int PE = 2 * TE;  // elements per stored tile pair
 
-            // state slice as the B operand of W S^T (bf16)
-            FW Sb[NKB];
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
-                float x[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) x[j] = S[2 * kb + j / 4][j % 4];
-                Sb[kb] = FW::make(x);
-            }
-            // state slice as the A operand of (S^T)^T Qbar^T (fp16, scaled)
+            // state slice, scaled, as the B operand of W S^T and the A operand of (S^T)^T Qbar^T
             int sS = 0;
             if constexpr (!F32) {
                 float m = 0.f;
@@ -147,20 +160,28 @@ __global__ __launch_bounds__(128, 1) void kda_state_kernel(
                 for (int j = 0; j < 8; ++j) x[j] = ldexp2(S[2 * kb + j / 4][j % 4], sS);
                 Sh[kb] = FH::make(x);
             }
-            // U = U~ - W S^T   (tiles over tokens)
+            // W S^T and (S^T)^T Qbar^T: independent accumulators per 16-token tile
+            f32x4 P[NT], O[NT];
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt) {
+                P[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                O[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int tt = 0; tt < NT; ++tt)
+                    P[tt] = mma(FH::load_pair(bWT + (kb * NT + tt) * PE, lane), Sh[kb], P[tt]);
+            // U = U~ - W S^T
+            const int unW = -(sS + bScl[0]), unU = -bSS[0];
             f32x4 U[NT];
             float um = 0.f;
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kb = 0; kb < NKB; ++kb)
-                    acc = mma(FW::load2(bWT + ((2 * kb) * NT + tt) * TE + lo,
-                                        bWT + ((2 * kb + 1) * NT + tt) * TE + lo), Sb[kb], acc);
                 const f32x4 ut = ld_tile(bU + tt * TE, lane);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    U[tt][i] = ut[i] - acc[i];
+                    U[tt][i] = ldexp2(ut[i], unU) - ldexp2(P[tt][i], unW);
                     um = fmaxf(um, fabsf(U[tt][i]));
                 }
             }
@@ -176,60 +197,64 @@ __global__ __launch_bounds__(128, 1) void kda_state_kernel(
                 }
                 Uh[kb] = FH::make(x);
             }
-            // O^T = Oi^T + (S^T)^T Qbar^T, one 16 x 16 tile per 16 tokens
-            const int unscaleO = -(sS + bScl[0]);
+            // S^T <- diag(gamma) S^T + K^^T U: independent accumulators per 16-row dk tile
+            f32x4 A[NDK];
+#pragma unroll
+            for (int mt = 0; mt < NDK; ++mt) A[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < NTKB; ++kb)
+#pragma unroll
+                for (int mt = 0; mt < NDK; ++mt)
+                    A[mt] = mma(FH::load_pair(bKH + (kb * NDK + mt) * PE, lane), Uh[kb], A[mt]);
+            // O^T = Oi^T + (S^T)^T Qbar^T (uses the state before this chunk's update)
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int tt = 0; tt < NT; ++tt)
+                    O[tt] = mma(Sh[kb], FH::load_pair(bQB + (kb * NT + tt) * PE, lane), O[tt]);
+            const float unS = ldexp2(1.f, -(sU + bScl[2]));
+#pragma unroll
+            for (int mt = 0; mt < NDK; ++mt) {
+                const f32x4 gm = *reinterpret_cast<const f32x4 *>(bG + 16 * mt + 4 * g);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) S[mt][i] = fmaf(A[mt][i], unS, S[mt][i] * gm[i]);
+            }
+            const float unO = ldexp2(1.f, -(sS + bScl[1])), unI = ldexp2(1.f, -bSS[1]);
             const size_t trow = (size_t)hb * T + (size_t)n * C;
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kb = 0; kb < NKB; ++kb)
-                    acc = mma(Sh[kb], FH::load2(bQB + ((2 * kb) * NT + tt) * TE + lo,
-                                                bQB + ((2 * kb + 1) * NT + tt) * TE + lo), acc);
                 const f32x4 oi = ld_tile(bO + tt * TE, lane);
                 f32x4 o;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) o[i] = oi[i] + ldexp2(acc[i], unscaleO);
+                for (int i = 0; i < 4; ++i) o[i] = fmaf(O[tt][i], unO, oi[i] * unI);
                 // lane holds out[token 16 tt + l16][value j0 + 4g + i]
                 E *op = out + (trow + 16 * tt + l16) * DV + j0 + 4 * g;
                 if constexpr (F32) {
                     *reinterpret_cast<f32x4 *>(op) = o;
-                    if (counts != nullptr) {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) nonfinite += !__builtin_isfinite(o[i]);
-                    }
                 } else {
                     bf16x4 bo;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) bo[i] = (__bf16)o[i];
                     *reinterpret_cast<bf16x4 *>(op) = bo;
-                    if (counts != nullptr) {
+                    // what was stored, for the optional non-finite count
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) nonfinite += !__builtin_isfinite((float)bo[i]);
-                    }
+                    for (int i = 0; i < 4; ++i) o[i] = (float)bo[i];
                 }
+                O[tt] = o;
             }
-            // S^T = diag(gamma) S^T + K^^T U
-            const int unscaleS = -(sU + bScl[1]);
+            if (counts != nullptr) {
 #pragma unroll
-            for (int mt = 0; mt < NDK; ++mt) {
-                const f32x4 gm = *reinterpret_cast<const f32x4 *>(bG + 16 * mt + 4 * g);
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-                for (int kb = 0; kb < NTKB; ++kb) {
-                    const OH *p0 = bKH + ((2 * kb) * NDK + mt) * TE + lo;
-                    const FH kf = (2 * kb + 1 < NT) ? FH::load2(p0, bKH + ((2 * kb + 1) * NDK + mt) * TE + lo)
-                                                    : FH::load1(p0);
-                    acc = mma(kf, Uh[kb], acc);
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) S[mt][i] = S[mt][i] * gm[i] + ldexp2(acc[i], unscaleS);
+                    for (int i = 0; i < 4; ++i) nonfinite += !__builtin_isfinite(O[tt][i]);
             }
         }
         __syncthreads();
         if (NBUF == 1) {
-            if (wave == 1 && n + 1 < NC)
-                load_record<R1B, SLB>(smem, rec0 + (size_t)(n + 1) * L.stride, soff, lane);
+            if (wave == 1 && n + 1 < NC) {
+                issue_record<R1B, SLB>(smem, rec0 + (size_t)(n + 1) * L.stride, soff, lane);
+                wait_vmcnt<0>();
+            }
             __syncthreads();
         }
     }

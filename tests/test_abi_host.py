@@ -40,10 +40,10 @@ def test_version_and_strings():
 
 
 def test_workspace_bytes():
-    # per (batch, head, chunk) record at chunk 64, dk = dv = 128, bf16 operands:
-    # W^T, Qbar^T, K^ as 32 16-bit tiles each (512 B) + 128 float gammas + 4 int scales, then for each of
-    # the 8 value slices U~ and Oi^T as 4 float32 tiles each (1 KiB)
-    rec = 3 * 32 * 512 + 128 * 4 + 16 + 8 * 2 * 4 * 1024
+    # per (batch, head, chunk) record at chunk 64, dk = dv = 128, bf16 I/O (fp16 operand blocks):
+    # W^T, Qbar^T, K^ as 32 16-bit tiles each (512 B) + 128 float gammas + 4 int exponents, then for
+    # each of the 8 value slices 4 int exponents and U~, Oi^T as 4 fp16 tiles each
+    rec = 3 * 32 * 512 + 128 * 4 + 16 + 8 * (16 + 2 * 4 * 512)
     rec = (rec + 255) // 256 * 256
     assert kda.workspace_bytes(1, 32, 65536, 128, 128, 64, torch.bfloat16) == 32 * 1024 * rec
     assert kda.workspace_bytes(1, 2, 256, 64, 64, 16, torch.float32) > 0
