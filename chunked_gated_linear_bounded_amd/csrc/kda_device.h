@@ -232,6 +232,20 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
+// Work-group barrier that orders LDS traffic only.  __syncthreads() is a fenced
+// barrier: every wave first drains all of its vector-memory operations, which
+// would also retire direct global->LDS loads that are meant to stay in flight
+// across the barrier.  Here each wave waits for its own LDS reads and writes
+// (lgkmcnt(0)) and the compiler keeps memory accesses on their side of the
+// barrier; a wave that filled LDS with direct loads must wait for them itself
+// (wait_vmcnt) before arriving.  Global stores are not made visible by it.
+__device__ __forceinline__ void barrier_lds() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt 63 and expcnt 7 leave the rest alone
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // ---------------------------------------------------------------- the gate
 // g in log2 units (g * log2 e).  Bounded: g_min * sigmoid(a).  Log-sigmoid:
 // log sigmoid(a) = -(max(-a, 0) + log(1 + e^-|a|)), never overflows.

@@ -317,7 +317,7 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 #pragma unroll
         for (int i = 0; i < 16; ++i) Tb[i * PA + j] = x[i];
     }
-    __syncthreads();
+    barrier_lds();  // V loads stay in flight through the solve
 #pragma unroll
     for (int d = 1; d < NT; ++d) {
         const int J = wave, I = wave + d;
@@ -338,7 +338,7 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 #pragma unroll
             for (int i = 0; i < 4; ++i) sT[(16 * I + 4 * g + i) * PA + 16 * J + l16] = -Y[i];
         }
-        __syncthreads();
+        barrier_lds();
     }
     // A is dead: M takes its place
     if (I < NT) {

@@ -110,7 +110,7 @@ __global__ __launch_bounds__(128, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             wait_vmcnt<0>();
         }
     }
-    __syncthreads();
+    barrier_lds();
 
     f32x4 S[NDK];
 #pragma unroll
@@ -142,6 +142,22 @@ __global__ __launch_bounds__(128, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             const int *bSS = reinterpret_cast<const int *>(cur + L.region1 + L.ssc);
             constexpr int PE = 2 * TE;  // elements per stored tile pair
 
+            // Every W and Qbar fragment, U~ tile and exponent of this chunk is read up front, so
+            // the LDS latency overlaps the state's scale reduction instead of stalling each MFMA.
+            FH wt[NKB][NT], qb[NKB][NT];
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int tt = 0; tt < NT; ++tt) {
+                    wt[kb][tt] = FH::load_pair(bWT + (kb * NT + tt) * PE, lane);
+                    qb[kb][tt] = FH::load_pair(bQB + (kb * NT + tt) * PE, lane);
+                }
+            f32x4 ut[NT];
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt) ut[tt] = ld_tile(bU + tt * TE, lane);
+            const int eW = bScl[0], eQ = bScl[1], eK = bScl[2], eU = bSS[0], eO = bSS[1];
+            __builtin_amdgcn_sched_barrier(0);
+
             // state slice, scaled, as the B operand of W S^T and the A operand of (S^T)^T Qbar^T
             int sS = 0;
             if constexpr (!F32) {
@@ -160,7 +176,8 @@ __global__ __launch_bounds__(128, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                 for (int j = 0; j < 8; ++j) x[j] = ldexp2(S[2 * kb + j / 4][j % 4], sS);
                 Sh[kb] = FH::make(x);
             }
-            // W S^T and (S^T)^T Qbar^T: independent accumulators per 16-token tile
+            // W S^T and (S^T)^T Qbar^T (the latter needs no U): independent accumulators per
+            // 16-token tile, interleaved
             f32x4 P[NT], O[NT];
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt) {
@@ -170,18 +187,32 @@ __global__ __launch_bounds__(128, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-                for (int tt = 0; tt < NT; ++tt)
-                    P[tt] = mma(FH::load_pair(bWT + (kb * NT + tt) * PE, lane), Sh[kb], P[tt]);
+                for (int tt = 0; tt < NT; ++tt) {
+                    P[tt] = mma(wt[kb][tt], Sh[kb], P[tt]);
+                    O[tt] = mma(Sh[kb], qb[kb][tt], O[tt]);
+                }
+            __builtin_amdgcn_sched_barrier(0);
+            // K^ fragments, Oi^T tiles and gamma: read while U is formed
+            FH kh[NTKB][NDK];
+#pragma unroll
+            for (int kb = 0; kb < NTKB; ++kb)
+#pragma unroll
+                for (int mt = 0; mt < NDK; ++mt) kh[kb][mt] = FH::load_pair(bKH + (kb * NDK + mt) * PE, lane);
+            f32x4 oi[NT], gm[NDK];
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt) oi[tt] = ld_tile(bO + tt * TE, lane);
+#pragma unroll
+            for (int mt = 0; mt < NDK; ++mt) gm[mt] = *reinterpret_cast<const f32x4 *>(bG + 16 * mt + 4 * g);
+            __builtin_amdgcn_sched_barrier(0);
             // U = U~ - W S^T
-            const int unW = -(sS + bScl[0]), unU = -bSS[0];
+            const int unW = -(sS + eW), unU = -eU;
             f32x4 U[NT];
             float um = 0.f;
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt) {
-                const f32x4 ut = ld_tile(bU + tt * TE, lane);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    U[tt][i] = ldexp2(ut[i], unU) - ldexp2(P[tt][i], unW);
+                    U[tt][i] = ldexp2(ut[tt][i], unU) - ldexp2(P[tt][i], unW);
                     um = fmaxf(um, fabsf(U[tt][i]));
                 }
             }
@@ -204,29 +235,19 @@ __global__ __launch_bounds__(128, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 #pragma unroll
             for (int kb = 0; kb < NTKB; ++kb)
 #pragma unroll
-                for (int mt = 0; mt < NDK; ++mt)
-                    A[mt] = mma(FH::load_pair(bKH + (kb * NDK + mt) * PE, lane), Uh[kb], A[mt]);
-            // O^T = Oi^T + (S^T)^T Qbar^T (uses the state before this chunk's update)
+                for (int mt = 0; mt < NDK; ++mt) A[mt] = mma(kh[kb][mt], Uh[kb], A[mt]);
+            const float unS = ldexp2(1.f, -(sU + eK));
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
+            for (int mt = 0; mt < NDK; ++mt)
 #pragma unroll
-                for (int tt = 0; tt < NT; ++tt)
-                    O[tt] = mma(Sh[kb], FH::load_pair(bQB + (kb * NT + tt) * PE, lane), O[tt]);
-            const float unS = ldexp2(1.f, -(sU + bScl[2]));
-#pragma unroll
-            for (int mt = 0; mt < NDK; ++mt) {
-                const f32x4 gm = *reinterpret_cast<const f32x4 *>(bG + 16 * mt + 4 * g);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) S[mt][i] = fmaf(A[mt][i], unS, S[mt][i] * gm[i]);
-            }
-            const float unO = ldexp2(1.f, -(sS + bScl[1])), unI = ldexp2(1.f, -bSS[1]);
+                for (int i = 0; i < 4; ++i) S[mt][i] = fmaf(A[mt][i], unS, S[mt][i] * gm[mt][i]);
+            const float unO = ldexp2(1.f, -(sS + eQ)), unI = ldexp2(1.f, -eO);
             const size_t trow = (size_t)hb * T + (size_t)n * C;
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt) {
-                const f32x4 oi = ld_tile(bO + tt * TE, lane);
                 f32x4 o;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) o[i] = fmaf(O[tt][i], unO, oi[i] * unI);
+                for (int i = 0; i < 4; ++i) o[i] = fmaf(O[tt][i], unO, oi[tt][i] * unI);
                 // lane holds out[token 16 tt + l16][value j0 + 4g + i]
                 E *op = out + (trow + 16 * tt + l16) * DV + j0 + 4 * g;
                 if constexpr (F32) {
@@ -249,13 +270,13 @@ __global__ __launch_bounds__(128, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                     for (int i = 0; i < 4; ++i) nonfinite += !__builtin_isfinite(O[tt][i]);
             }
         }
-        __syncthreads();
+        barrier_lds();
         if (NBUF == 1) {
             if (wave == 1 && n + 1 < NC) {
                 issue_record<R1B, SLB>(smem, rec0 + (size_t)(n + 1) * L.stride, soff, lane);
                 wait_vmcnt<0>();
             }
-            __syncthreads();
+            barrier_lds();
         }
     }
     if (wave == 0) {
