@@ -64,6 +64,54 @@ def _traffic(kernel, workload):
     return rec.get("bytes_per_launch")
 
 
+def _counter_rows(d):
+    """(kernel name, counter, value) rows of every rocprofv3 counter CSV under `d`."""
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f, newline="") as fh:
+            for r in csv.DictReader(fh):
+                rows.append((r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"])))
+    return rows
+
+
+def record_traffic(fetch_dir, write_dir, workload, copy_bytes):
+    """HBM bytes per launch of the path's kernels from two rocprofv3 --pmc runs of
+    this script (FETCH_SIZE, then WRITE_SIZE, both KiB per dispatch), each scaled
+    by the factor that makes the same counter read the known size of the
+    calibration copy (a float32 negation over `copy_bytes`, which reads and writes
+    `copy_bytes` once).  Writes profiles/traffic.json keyed kernel@workload with
+    the hash of the kernel sources the counters were taken on."""
+    out = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = [r for r in _counter_rows(d) if r[1] == counter]
+        if not rows:
+            raise SystemExit("no %s rows under %s" % (counter, d))
+        cal = [v for (k, _, v) in rows if "neg" in k]
+        if not cal:
+            raise SystemExit("no calibration copy dispatch under %s" % d)
+        factor = copy_bytes / (sum(cal) / len(cal) * 1024.0)
+        for kern in ("kda_intra_kernel", "kda_state_kernel"):
+            vals = [v for (k, _, v) in rows if kern in k]
+            if not vals:
+                raise SystemExit("no %s dispatches under %s" % (kern, d))
+            rec = out.setdefault(kern + "@" + workload, {"src_sha": _src_sha()})
+            rec[counter.lower() + "_kib_raw"] = sum(vals) / len(vals)
+            rec[counter.lower() + "_factor"] = factor
+            rec[counter.lower() + "_bytes"] = sum(vals) / len(vals) * 1024.0 * factor
+            rec["dispatches"] = len(vals)
+    for rec in out.values():
+        rec["bytes_per_launch"] = rec["fetch_size_bytes"] + rec["write_size_bytes"]
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    old = json.load(open(p)) if os.path.exists(p) else {}
+    old.update(out)
+    with open(p, "w") as fh:
+        json.dump(old, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+    print(json.dumps(out, indent=1))
+
+
 def cpu_baseline(inputs, w, seconds):
     """The float64 oracle on whole heads of the same workload until `seconds`
     have passed; returns whole-job tokens/s extrapolated from the sampled heads."""
@@ -94,9 +142,19 @@ def main():
     ap.add_argument("--workload", default="64k", help="tiny, 8k, 64k, 256k or 1m")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="after timing, run one float32 negation over MIB MiB (the counter calibration copy)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU run: turn two rocprofv3 --pmc output folders of this script into "
+                         "profiles/traffic.json (needs --copy-calibration as used in those runs)")
     args = ap.parse_args()
+    if args.traffic_from:
+        if args.copy_calibration <= 0:
+            raise SystemExit("--traffic-from needs --copy-calibration MIB")
+        record_traffic(args.traffic_from[0], args.traffic_from[1], args.workload, args.copy_calibration << 20)
+        return
     if args.gpus != 1:
-        print("bench.py: this build measures one GPU only (the path shards over heads with no "
+        print("bench.py: measures one GPU only (the path shards over heads with no "
               "communication); --gpus %d is not supported" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
@@ -142,6 +200,12 @@ def main():
     intra_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
     state_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
     assert torch.isfinite(out.float()).all().item(), "non-finite output"
+    if args.copy_calibration > 0:
+        cx = torch.ones(args.copy_calibration << 18, dtype=torch.float32, device=dev)
+        cy = torch.empty_like(cx)
+        torch.neg(cx, out=cy)
+        torch.cuda.synchronize()
+        del cx, cy
 
     th = w.B * w.H * w.T
     flops = flops_per_token_head(w.dk, w.dv, w.chunk) * th
