@@ -3,7 +3,11 @@
     python -m chunked_gated_linear_bounded_amd.build
 
 Flags: -O3 for gfx950 only; packed-fp32 instruction selection is disabled
-(-target-feature -packed-fp32-ops) for every device compile.
+(-target-feature -packed-fp32-ops) for every device compile.  MFMA results
+are kept in ordinary VGPRs (-amdgpu-mfma-vgpr-form): a kernel whose LDS use
+already limits it to one work-group per CU otherwise gets the accumulator-
+register form, and every accumulator is copied out with v_accvgpr_read
+before VALU code can use it.
 """
 from __future__ import annotations
 
@@ -23,7 +27,7 @@ ARCH = "gfx950"
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 DEVICE = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          "-munsafe-fp-atomics"]
+          "-munsafe-fp-atomics", "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 # (source, output object, extra defines)
 UNITS = [

@@ -112,9 +112,13 @@ __global__ __launch_bounds__(128, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     }
     barrier_lds();
 
+    // The state slice is kept scaled by 2^sS (wave-uniform), with sS chosen so that its
+    // largest magnitude lies in [2^11, 2^15): the fp16 operand is then a plain conversion,
+    // and the scale is only adjusted when the maximum leaves that range.
     f32x4 S[NDK];
 #pragma unroll
     for (int mt = 0; mt < NDK; ++mt) S[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    int sS = 0;
     unsigned int nonfinite = 0;
 
     for (int n = 0; n < NC; ++n) {
@@ -158,22 +162,13 @@ __global__ __launch_bounds__(128, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             const int eW = bScl[0], eQ = bScl[1], eK = bScl[2], eU = bSS[0], eO = bSS[1];
             __builtin_amdgcn_sched_barrier(0);
 
-            // state slice, scaled, as the B operand of W S^T and the A operand of (S^T)^T Qbar^T
-            int sS = 0;
-            if constexpr (!F32) {
-                float m = 0.f;
-#pragma unroll
-                for (int mt = 0; mt < NDK; ++mt)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(S[mt][i]));
-                sS = pow2_scale(wave_max(m));
-            }
+            // the (scaled) state slice as the B operand of W S^T and the A operand of (S^T)^T Qbar^T
             FH Sh[NKB];
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
                 float x[8];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) x[j] = ldexp2(S[2 * kb + j / 4][j % 4], sS);
+                for (int j = 0; j < 8; ++j) x[j] = S[2 * kb + j / 4][j % 4];
                 Sh[kb] = FH::make(x);
             }
             // W S^T and (S^T)^T Qbar^T (the latter needs no U): independent accumulators per
@@ -204,15 +199,15 @@ __global__ __launch_bounds__(128, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 #pragma unroll
             for (int mt = 0; mt < NDK; ++mt) gm[mt] = *reinterpret_cast<const f32x4 *>(bG + 16 * mt + 4 * g);
             __builtin_amdgcn_sched_barrier(0);
-            // U = U~ - W S^T
-            const int unW = -(sS + eW), unU = -eU;
+            // U = U~ - W S^T (both scalings are exact, the difference rounds once)
+            const float fW = ldexp2(1.f, -(sS + eW)), fU = ldexp2(1.f, -eU);
             f32x4 U[NT];
             float um = 0.f;
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    U[tt][i] = ldexp2(ut[tt][i], unU) - ldexp2(P[tt][i], unW);
+                    U[tt][i] = fmaf(ut[tt][i], fU, -(P[tt][i] * fW));
                     um = fmaxf(um, fabsf(U[tt][i]));
                 }
             }
@@ -236,12 +231,28 @@ __global__ __launch_bounds__(128, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             for (int kb = 0; kb < NTKB; ++kb)
 #pragma unroll
                 for (int mt = 0; mt < NDK; ++mt) A[mt] = mma(kh[kb][mt], Uh[kb], A[mt]);
-            const float unS = ldexp2(1.f, -(sU + eK));
+            const float unO = ldexp2(1.f, -(sS + eQ)), unI = ldexp2(1.f, -eO);  // scale Q S^T was taken at
+            const float unS = ldexp2(1.f, sS - (sU + eK));
 #pragma unroll
             for (int mt = 0; mt < NDK; ++mt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) S[mt][i] = fmaf(A[mt][i], unS, S[mt][i] * gm[mt][i]);
-            const float unO = ldexp2(1.f, -(sS + eQ)), unI = ldexp2(1.f, -eO);
+            if constexpr (!F32) {  // keep the scaled maximum in [2^11, 2^15)
+                float m = 0.f;
+#pragma unroll
+                for (int mt = 0; mt < NDK; ++mt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(S[mt][i]));
+                m = wave_max(m);
+                if (m > 0.f && __builtin_isfinite(m) && (m >= 32768.f || m < 2048.f)) {
+                    const int d = pow2_scale(m);
+#pragma unroll
+                    for (int mt = 0; mt < NDK; ++mt)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) S[mt][i] = ldexp2(S[mt][i], d);
+                    sS += d;
+                }
+            }
             const size_t trow = (size_t)hb * T + (size_t)n * C;
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt) {
@@ -284,7 +295,12 @@ __global__ __launch_bounds__(128, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             // final_state[hb][value j0 + l16][key 16 mt + 4g + i] = S^T[key][value]
             float *fp = final_state + ((size_t)hb * DV + j0 + l16) * DK + 4 * g;
 #pragma unroll
-            for (int mt = 0; mt < NDK; ++mt) *reinterpret_cast<f32x4 *>(fp + 16 * mt) = S[mt];
+            for (int mt = 0; mt < NDK; ++mt) {
+                f32x4 x;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) x[i] = ldexp2(S[mt][i], -sS);
+                *reinterpret_cast<f32x4 *>(fp + 16 * mt) = x;
+            }
         }
         if (counts != nullptr && nonfinite) atomicAdd(&counts[1], (unsigned long long)nonfinite);
     }
