@@ -257,8 +257,10 @@ __device__ __forceinline__ float gate_log2(float a, float gmin2, int logsig) {
 // Gate and inclusive prefix sum over the C rows of one chunk, per channel:
 // sG[r * ldG + c] = sum_{s <= r} g2[s][c] (log2 units).  Threads: 256; thread t
 // takes channel t % DK and the t / DK-th segment of rows; segment totals are
-// combined through sScratch (>= 256 floats).  Ends with a barrier.
-template <int C, int DK, typename E>
+// combined through sScratch (>= 256 floats).  `a` ([C][DK], dense) may be a
+// copy in LDS that sG overwrites (A_ALIASES_G): every thread then reads its
+// values before any G is written.  Ends with a barrier.
+template <int C, int DK, typename E, bool A_ALIASES_G = false>
 __device__ __forceinline__ void gate_cumsum_tile(const E *__restrict__ a, float gmin2, int logsig,
                                                  float *sG, int ldG, float *sScratch) {
     static_assert(256 % DK == 0, "DK must divide 256");
@@ -271,6 +273,7 @@ __device__ __forceinline__ void gate_cumsum_tile(const E *__restrict__ a, float 
     float av[RPS];
 #pragma unroll
     for (int r = 0; r < RPS; ++r) av[r] = to_f(a[(size_t)(r0 + r) * DK + c]);
+    if constexpr (A_ALIASES_G) __syncthreads();
     float run = 0.f;
 #pragma unroll
     for (int r = 0; r < RPS; ++r) {

@@ -26,9 +26,10 @@
 // stored as fp16, each chunk's block scaled by a power of two from its largest
 // magnitude (the sequential stage undoes the scale on its fp32 results).
 //
-// UT solve: the 16x16 diagonal blocks of T by forward substitution (one lane
-// per column), then the off-diagonal blocks level by level,
-// T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ, with fp32 MFMAs.
+// UT solve: each 16x16 diagonal block of T from the finite product series of
+// its strictly lower triangular A block (one wave per block), then the
+// off-diagonal blocks level by level, T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ,
+// all with fp32 MFMAs.
 #pragma once
 #include "kda_device.h"
 #include "kda_layout.h"
@@ -107,22 +108,38 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     int *wScl = reinterpret_cast<int *>(rec + L.scl);
 
     // ------------------------------------------------ phase 0: loads, gate, prefix sum
-    if (tid < C) sB[tid] = to_f(beta[tok0 + tid]);
+    // Every input load of the chunk (q, k and a as 16-byte accesses, beta) is issued before
+    // any of them is consumed, so the chunk pays one memory round trip.  a is staged densely
+    // at the start of region 0, where the prefix sum then overwrites it with G.
     {
-        constexpr int LPR = DK / VEC, RPP = 256 / LPR;
-        const E *qg = q + tok0 * DK, *kg = k + tok0 * DK;
+        constexpr int LPR = DK / VEC, RPP = 256 / LPR, NP = (C + RPP - 1) / RPP;
+        const E *qg = q + tok0 * DK, *kg = k + tok0 * DK, *ag = a + tok0 * DK;
+        E *sAin = reinterpret_cast<E *>(smem);
+        static_assert(C * DK * Cfg::ES <= Cfg::R0, "staged a fits region 0");
+        // loads are unconditional (row indices clamped into the chunk); only the stores are guarded
+        uint4 xq[NP], xk[NP], xa[NP];
+        const E bv = beta[tok0 + (tid < C ? tid : C - 1)];
 #pragma unroll
-        for (int r0 = 0; r0 < C; r0 += RPP) {
-            const int r = r0 + tid / LPR, c = (tid % LPR) * VEC;
-            if (r < C) {
-                uint4 xq = *reinterpret_cast<const uint4 *>(qg + (size_t)r * DK + c);
-                uint4 xk = *reinterpret_cast<const uint4 *>(kg + (size_t)r * DK + c);
-                *reinterpret_cast<uint4 *>(sQ + r * PQ + c) = xq;
-                *reinterpret_cast<uint4 *>(sK + r * PQ + c) = xk;
+        for (int p = 0; p < NP; ++p) {
+            const int r = p * RPP + tid / LPR, c = (tid % LPR) * VEC;
+            const size_t off = (size_t)(r < C ? r : C - 1) * DK + c;
+            xq[p] = *reinterpret_cast<const uint4 *>(qg + off);
+            xk[p] = *reinterpret_cast<const uint4 *>(kg + off);
+            xa[p] = *reinterpret_cast<const uint4 *>(ag + off);
+        }
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const int r = p * RPP + tid / LPR, c = (tid % LPR) * VEC;
+            if (C % RPP == 0 || r < C) {
+                *reinterpret_cast<uint4 *>(sQ + r * PQ + c) = xq[p];
+                *reinterpret_cast<uint4 *>(sK + r * PQ + c) = xk[p];
+                *reinterpret_cast<uint4 *>(sAin + r * DK + c) = xa[p];
             }
         }
+        if (tid < C) sB[tid] = to_f(bv);
+        __syncthreads();
+        gate_cumsum_tile<C, DK, E, true>(sAin, gmin2, logsig, sG, PG, sScr);  // ends with a barrier
     }
-    gate_cumsum_tile<C, DK, E>(a + tok0 * DK, gmin2, logsig, sG, PG, sScr);  // ends with a barrier
 
     // ------------------------------------------------ phase 1: causal sub-tiles of M and A
     // Wave I owns row tile I and computes M_IJ and A_IJ for every J <= I.  The row
@@ -301,21 +318,45 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
         const int I = blk / NT, J = blk % NT;
         if (I < J) sT[(16 * I + (e >> 4)) * PA + 16 * J + (e & 15)] = 0.f;
     }
-    if (wave == 0 && g < NT) {
-        // diagonal block I = g, column j = l16: forward substitution
-        const int I = g, j = l16;
+    if (wave < NT) {
+        // Diagonal block I = wave.  N = A_II is strictly lower triangular, so N^16 = 0 and
+        // (I + N)^-1 = (I - N)(I + N^2)(I + N^4)(I + N^8) exactly: eight chained 16x16x16
+        // fp32 products.  In the 16x16x4 MFMA layout an accumulator holding Z is Z's B operand
+        // and Z^T's A operand as it stands, so Z and Z^T are carried side by side and no
+        // product needs a shuffle.
+        const int I = wave;
         const float *Ab = sA + (16 * I) * PA + 16 * I;
-        float x[16];
+        f32x4 R, Rt;  // R: N[4g + i][l16]; Rt: N[l16][4g + i]
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            float acc = (i == j) ? 1.f : 0.f;
+        for (int i = 0; i < 4; ++i) R[i] = Ab[(4 * g + i) * PA + l16];
+        {
+            float t4[4];
+            ld4(Ab + l16 * PA + 4 * g, t4);
 #pragma unroll
-            for (int kk = 0; kk < i; ++kk) acc -= Ab[i * PA + kk] * x[kk];
-            x[i] = acc;
+            for (int i = 0; i < 4; ++i) Rt[i] = t4[i];
         }
+        // X Y + Z with X given transposed-accumulator style (xt = D(X^T)) and Y as D(Y)
+        auto prod = [](f32x4 xt, f32x4 y, f32x4 z) {
+#pragma unroll
+            for (int st = 0; st < 4; ++st) z = mma4(xt[st], y[st], z);
+            return z;
+        };
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        const f32x4 N2 = prod(Rt, R, zero), N2t = prod(R, Rt, zero);
+        const f32x4 N4 = prod(N2t, N2, zero), N4t = prod(N2, N2t, zero);
+        const f32x4 N8 = prod(N4t, N4, zero);
+        f32x4 Y;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Y[i] = N8[i] + (4 * g + i == l16 ? 1.f : 0.f);
+        Y = prod(N4t, Y, Y);  // (I + N^4)(I + N^8)
+        Y = prod(N2t, Y, Y);  // (I + N^2)(...)
+        f32x4 mRt;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mRt[i] = -Rt[i];
+        Y = prod(mRt, Y, Y);  // (I - N)(...)
         float *Tb = sT + (16 * I) * PA + 16 * I;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) Tb[i * PA + j] = x[i];
+        for (int i = 0; i < 4; ++i) Tb[(4 * g + i) * PA + l16] = Y[i];
     }
     barrier_lds();  // V loads stay in flight through the solve
 #pragma unroll
