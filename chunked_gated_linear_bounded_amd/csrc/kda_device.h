@@ -78,6 +78,10 @@ template <typename T> struct Frag {  // 16-bit operand, one 16x16x32 MFMA per K-
         return f;
     }
     __device__ __forceinline__ float get(int j) const { return (float)v[j]; }
+    // this lane's 8 values to 8 contiguous elements at base + 8 * lane (one 16-byte store)
+    __device__ __forceinline__ void store(T *base, int lane) const {
+        *reinterpret_cast<V8 *>(base + lane * 8) = v;
+    }
 };
 
 template <> struct Frag<float> {  // fp32, eight 16x16x4 MFMAs per K-block
@@ -107,6 +111,10 @@ template <> struct Frag<float> {  // fp32, eight 16x16x4 MFMAs per K-block
         return load2(pair + lane * 8, pair + lane * 8 + 4);
     }
     __device__ __forceinline__ float get(int j) const { return v[j]; }
+    __device__ __forceinline__ void store(float *base, int lane) const {
+        *reinterpret_cast<f32x4 *>(base + lane * 8) = f32x4{v[0], v[1], v[2], v[3]};
+        *reinterpret_cast<f32x4 *>(base + lane * 8 + 4) = f32x4{v[4], v[5], v[6], v[7]};
+    }
 };
 
 __device__ __forceinline__ f32x4 mma(const Frag<__bf16> &a, const Frag<__bf16> &b, f32x4 c) {
@@ -143,6 +151,8 @@ template <typename T> struct Split {
         return s;
     }
 };
+template <typename T>
+__device__ __forceinline__ void st_frag(T *base, int lane, const Frag<T> &f) { f.store(base, lane); }
 template <typename T>
 __device__ __forceinline__ f32x4 mma3(const Split<T> &a, const Split<T> &b, f32x4 c) {
     c = mma(a.hi, b.hi, c);

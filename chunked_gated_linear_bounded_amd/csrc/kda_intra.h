@@ -53,9 +53,14 @@ struct IntraCfg {
     static constexpr int R0 = SZ_G > SZ_TV ? SZ_G : SZ_TV;
     static constexpr int SZ_Q = C * PQ * ES;
     static constexpr int SZ_A = C * PA * 4;
-    static constexpr int R1 = SZ_Q > SZ_A ? SZ_Q : SZ_A;
+    // phase 1 reuses R1 once q is dead: fp32 key operands K'_J of tiles 0..NT-2 (one 8-value
+    // fragment per lane and K-block) and the steps e^{rho_{J+1} - rho_J}
+    static constexpr int SZ_X = (NT - 1) * NKB * 512 * 4;
+    static constexpr int SZ_XD = SZ_X + (NT - 1) * DK * 4;
+    static constexpr int R1 = SZ_Q > SZ_A ? (SZ_Q > SZ_XD ? SZ_Q : SZ_XD) : (SZ_A > SZ_XD ? SZ_A : SZ_XD);
     static constexpr int R2 = C * PQ * ES;
     static constexpr int OFF_R1 = R0, OFF_R2 = R0 + R1, OFF_B = R0 + R1 + R2;
+
     static constexpr int OFF_SCR = OFF_B + C * 4;
     static constexpr int SMEM = OFF_SCR + 256 * 4;
     static constexpr int VEC = 16 / ES;          // elements per 16-byte access
@@ -90,6 +95,8 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     E *sV = reinterpret_cast<E *>(smem + C * PA * 4);              // R0: V, once G is dead
     E *sQ = reinterpret_cast<E *>(smem + Cfg::OFF_R1);             // R1: q
     float *sA = reinterpret_cast<float *>(smem + Cfg::OFF_R1);     // R1: A, then M
+    float *sXk = reinterpret_cast<float *>(smem + Cfg::OFF_R1);    // R1 in phase 1: shared key operands
+    float *sDt = reinterpret_cast<float *>(smem + Cfg::OFF_R1 + Cfg::SZ_X);  // and tile-start steps
     E *sK = reinterpret_cast<E *>(smem + Cfg::OFF_R2);             // R2: k, then K e^G
     float *sB = reinterpret_cast<float *>(smem + Cfg::OFF_B);      // beta
     float *sScr = reinterpret_cast<float *>(smem + Cfg::OFF_SCR);
@@ -142,11 +149,14 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     }
 
     // ------------------------------------------------ phase 1: causal sub-tiles of M and A
-    // Wave I owns row tile I and computes M_IJ and A_IJ for every J <= I.  The row
-    // operands (q and k of tile I scaled by e^{G_r - rho_I}) are built once per
-    // K-block and reused for all J.  The diagonal tile J = I, whose key operand
-    // carries factors up to e^{15 |g_min|}, takes bf16 hi + lo operands (three
-    // MFMAs); the earlier tiles take single bf16 operands.
+    // Wave I owns row tile I and computes M_IJ and A_IJ for every J <= I, every pair referenced
+    // to rho_I, the start of the row tile: row operands q e^{G_r - rho_I} and k e^{G_r - rho_I}
+    // (<= 1), key operands k_s e^{rho_I - G_s}.  The diagonal tile J = I, whose key factors
+    // reach e^{15 |g_min|}, takes bf16 hi + lo operands (three MFMAs); the earlier tiles take
+    // single bf16 operands.  Exponentials are paid once per element: wave J's own key operand
+    // K'_J = k e^{rho_J - G} goes to LDS in fp32, and a later wave I forms its key operand as
+    // K'_J e^{rho_I - rho_J}, the per-channel factor built from the steps between tile starts
+    // e^{rho_{J+1} - rho_J}.  Each pair's key operand is still rounded once, from fp32.
     f32x4 accMs[NT], accAs[NT];  // indexed by J
 #pragma unroll
     for (int J = 0; J < NT; ++J) {
@@ -155,12 +165,14 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     }
     unsigned int nonfinite = 0;
     const int I = wave;
+    F fqh[NKB], fkh[NKB];  // row operands of tile I (single bf16) for the earlier key tiles
+    float kown[NKB][8];    // K'_I in fp32, for the later row tiles
     if (I < NT) {
-        const int r = 16 * I + l16;
+        const int r = 16 * I + l16;  // this lane's row (A operand) and key (B operand)
         const float *rho = sG + (16 * I) * PG;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
-            float qv[8], kv[8], rh[8];
+            float qv[8], kv[8];
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
                 const int c = 32 * kb + 16 * hh + 4 * g;
@@ -174,53 +186,37 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
                     const float e = ex2(gr[i] - rr[i]);  // <= 1
                     qv[4 * hh + i] = qr[i] * e;
                     kv[4 * hh + i] = kr[i] * e;
-                    rh[4 * hh + i] = rr[i];
+                    kown[kb][4 * hh + i] = kr[i] * ex2(rr[i] - gr[i]);  // in [|k|, e^{15 |g_min|} |k|]
                 }
             }
-            const SP fq = SP::make(qv), fk = SP::make(kv);
+            const SP fq = SP::make(qv), fk = SP::make(kv), fc = SP::make(kown[kb]);
+            if (counts != nullptr) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) nonfinite += !__builtin_isfinite(fc.hi.get(j));
+            }
+            fqh[kb] = fq.hi;
+            fkh[kb] = fk.hi;
 #pragma unroll
             for (int J = 0; J < NT; ++J) {
-                if (J > I) continue;
-                const int s = 16 * J + l16;
-                float cv[8];  // key s referenced to rho_I
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const int c = 32 * kb + 16 * hh + 4 * g;
-                    float gs[4], ks[4];
-                    ld4(sG + s * PG + c, gs);
-                    ld4(sK + s * PQ + c, ks);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) cv[4 * hh + i] = ks[i] * ex2(rh[4 * hh + i] - gs[i]);
-                }
-                if (J == I) {
-                    const SP fc = SP::make(cv);
-                    if (counts != nullptr) {
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) nonfinite += !__builtin_isfinite(fc.hi.get(j));
-                    }
-                    accMs[J] = mma3(fq, fc, accMs[J]);  // rows r, cols s
-                    accAs[J] = mma3(fk, fc, accAs[J]);
-                } else {
-                    const F fc = F::make(cv);
-                    accMs[J] = mma(fq.hi, fc, accMs[J]);
-                    accAs[J] = mma(fk.hi, fc, accAs[J]);
-                }
-            }
-        }
-        // element (row r = 16I + 4g + i, col s = 16J + l16): M keeps s <= r, A keeps s < r (times beta_r)
-#pragma unroll
-        for (int J = 0; J < NT; ++J) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int rr = 4 * g + i;
-                if (I == J && l16 > rr) accMs[J][i] = 0.f;
-                accAs[J][i] = (I > J || l16 < rr) ? accAs[J][i] * sB[16 * I + rr] : 0.f;
+                if (J != I) continue;
+                accMs[J] = mma3(fq, fc, accMs[J]);
+                accAs[J] = mma3(fk, fc, accAs[J]);
             }
         }
     }
+    // steps between tile starts, e^{rho_{J+1} - rho_J} (<= 1, J < NT - 1)
+    constexpr int ND = (NT - 1) * DK, NDR = (ND + 255) / 256;
+    float dtab[NDR > 0 ? NDR : 1];
+#pragma unroll
+    for (int x = 0; x < NDR; ++x) {
+        const int e = tid + 256 * x;
+        if (e < ND) {
+            const int J = e / DK, c = e % DK;
+            dtab[x] = ex2(sG[(16 * J + 16) * PG + c] - sG[(16 * J) * PG + c]);
+        }
+    }
 
-    // Q e^G as Qbar^T tiles (ct, rt) of this wave's dk tiles, kept in registers until phase 3;
-    // K^ tiles (st, ct) wait in registers for the chunk's scale; gamma goes to the workspace.
+    // Q e^G as Qbar^T tiles (ct, rt) of this wave's dk tiles, kept in registers until phase 3
     f32x4 qtr[MAXCT][NT];
 #pragma unroll
     for (int ci = 0; ci < MAXCT; ++ci) {
@@ -236,6 +232,64 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
             for (int i = 0; i < 4; ++i) qtr[ci][rt][i] = qr[i] * ex2(gr[i]);
         }
     }
+    if constexpr (NT > 1) {
+        __syncthreads();  // q is no longer read: its region takes the shared key operands and steps
+        if (I < NT - 1) {
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                float *xp = sXk + ((I * NKB + kb) * 64 + lane) * 8;
+                *reinterpret_cast<f32x4 *>(xp) = f32x4{kown[kb][0], kown[kb][1], kown[kb][2], kown[kb][3]};
+                *reinterpret_cast<f32x4 *>(xp + 4) = f32x4{kown[kb][4], kown[kb][5], kown[kb][6], kown[kb][7]};
+            }
+        }
+#pragma unroll
+        for (int x = 0; x < NDR; ++x) {
+            const int e = tid + 256 * x;
+            if (e < ND) sDt[e] = dtab[x];
+        }
+        __syncthreads();
+        if (I < NT) {
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                float f[8];  // e^{rho_I - rho_J} for this lane's channels, J descending
+#pragma unroll
+                for (int j = 0; j < 8; ++j) f[j] = 1.f;
+#pragma unroll
+                for (int J = NT - 2; J >= 0; --J) {
+                    if (J >= I) continue;
+                    float d0[4], d1[4], x0[4], x1[4];
+                    ld4(sDt + J * DK + 32 * kb + 4 * g, d0);
+                    ld4(sDt + J * DK + 32 * kb + 16 + 4 * g, d1);
+                    const float *xp = sXk + ((J * NKB + kb) * 64 + lane) * 8;
+                    ld4(xp, x0);
+                    ld4(xp + 4, x1);
+                    float cv[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        f[j] *= j < 4 ? d0[j] : d1[j - 4];
+                        cv[j] = (j < 4 ? x0[j] : x1[j - 4]) * f[j];  // k_s e^{rho_I - G_s} <= |k_s|
+                    }
+                    const F fc = F::make(cv);
+                    accMs[J] = mma(fqh[kb], fc, accMs[J]);
+                    accAs[J] = mma(fkh[kb], fc, accAs[J]);
+                }
+            }
+        }
+    }
+    if (I < NT) {
+        // element (row r = 16I + 4g + i, col s = 16J + l16): M keeps s <= r, A keeps s < r (times beta_r)
+#pragma unroll
+        for (int J = 0; J < NT; ++J) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int rr = 4 * g + i;
+                if (I == J && l16 > rr) accMs[J][i] = 0.f;
+                accAs[J][i] = (I > J || l16 < rr) ? accAs[J][i] * sB[16 * I + rr] : 0.f;
+            }
+        }
+    }
+
+    // K^ tiles (st, ct) wait in registers for the chunk's scale; gamma goes to the workspace.
     constexpr int MAXKH = (NT * NDK + 3) / 4;
     f32x4 khr[MAXKH];
     float khmax = 0.f;
@@ -256,7 +310,7 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     khmax = wave_max(khmax);
     if (lane == 0) sScr[wave] = khmax;
     if (tid < DK) wGam[tid] = ex2(sG[(C - 1) * PG + tid]);
-    __syncthreads();  // q, raw k and the M/A operands are no longer read
+    __syncthreads();  // raw k and the shared key operands are no longer read
 
     // ------------------------------------------------ K^ scaled to fp16 range
     {
