@@ -174,6 +174,12 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
 }
+// Value of the lane N places lower in the same 16-lane row (0 for the first N lanes of a row).
+template <int N>
+__device__ __forceinline__ float dpp_row_shr(float x) {
+    static_assert(N >= 1 && N <= 15, "row shift");
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x110 + N, 0xF, 0xF, false));
+}
 // Maximum over the 64 lanes of a wave, returned to every lane (wave-uniform).
 __device__ __forceinline__ float wave_max(float x) {
     x = fmaxf(x, dpp_mov<0xB1>(x));   // quad_perm [1,0,3,2]
@@ -264,41 +270,68 @@ __device__ __forceinline__ float gate_log2(float a, float gmin2, int logsig) {
     return -(fmaxf(-a, 0.f) * kLog2e + lg2(1.f + ex2(-fabsf(a) * kLog2e)));
 }
 
-// Gate and inclusive prefix sum over the C rows of one chunk, per channel:
-// sG[r * ldG + c] = sum_{s <= r} g2[s][c] (log2 units).  Threads: 256; thread t
-// takes channel t % DK and the t / DK-th segment of rows; segment totals are
-// combined through sScratch (>= 256 floats).  `a` ([C][DK], dense) may be a
-// copy in LDS that sG overwrites (A_ALIASES_G): every thread then reads its
-// values before any G is written.  Ends with a barrier.
-template <int C, int DK, typename E, bool A_ALIASES_G = false>
-__device__ __forceinline__ void gate_cumsum_tile(const E *__restrict__ a, float gmin2, int logsig,
-                                                 float *sG, int ldG, float *sScratch) {
-    static_assert(256 % DK == 0, "DK must divide 256");
-    constexpr int NSEG = 256 / DK;
-    static_assert(C % NSEG == 0, "chunk too small for the scan split");
-    constexpr int RPS = C / NSEG;
-    const int tid = threadIdx.x;
-    const int c = tid % DK, seg = tid / DK;
-    const int r0 = seg * RPS;
-    float av[RPS];
+// Gate and inclusive prefix sum over the C rows of one chunk, per channel, held in registers:
+// G[r][c] = sum_{s <= r} g2[s][c] (log2 units).  256 threads; the 16 lanes of each row group
+// rg = tid / 16 take one group of VEC channels (rg + 16 p in pass p) and lane m = tid % 16
+// takes the RPL = C / 16 consecutive rows m RPL ...  Each lane loads its values with 16-byte
+// loads, sums its own rows, and the lane totals are prefix-summed across the row group with
+// four DPP row shifts.  load() only issues the loads, so a caller can put other loads in
+// flight before finish() consumes them.
+template <int C, int DK, typename E>
+struct GateScan {
+    static constexpr int VEC = 16 / (int)sizeof(E);  // channels per 16-byte load
+    static constexpr int NG = DK / VEC;              // channel groups
+    static constexpr int NPASS = (NG + 15) / 16;
+    static constexpr int RPL = C / 16;               // rows per lane
+    static_assert(C % 16 == 0 && DK % VEC == 0, "chunk and channel tiling");
+    uint4 raw[NPASS][RPL];
+
+    // a: this chunk's [C][DK] block
+    __device__ __forceinline__ void load(const E *__restrict__ a, int tid) {
+        const int rg = tid >> 4, m = tid & 15;
 #pragma unroll
-    for (int r = 0; r < RPS; ++r) av[r] = to_f(a[(size_t)(r0 + r) * DK + c]);
-    if constexpr (A_ALIASES_G) __syncthreads();
-    float run = 0.f;
+        for (int p = 0; p < NPASS; ++p) {
+            const int gi = rg + 16 * p, gc = gi < NG ? gi : NG - 1;  // clamped: loads stay in bounds
 #pragma unroll
-    for (int r = 0; r < RPS; ++r) {
-        run += gate_log2(av[r], gmin2, logsig);
-        sG[(r0 + r) * ldG + c] = run;
+            for (int j = 0; j < RPL; ++j)
+                raw[p][j] = *reinterpret_cast<const uint4 *>(a + (size_t)(m * RPL + j) * DK + gc * VEC);
+        }
     }
-    sScratch[seg * DK + c] = run;
-    __syncthreads();
-    float off = 0.f;
-    for (int s = 0; s < seg; ++s) off += sScratch[s * DK + c];
-    if (seg > 0) {
+
+    __device__ __forceinline__ void finish(float gmin2, int logsig, float *sG, int ldG, int tid) {
+        const int rg = tid >> 4, m = tid & 15;
 #pragma unroll
-        for (int r = 0; r < RPS; ++r) sG[(r0 + r) * ldG + c] += off;
+        for (int p = 0; p < NPASS; ++p) {
+            const int gi = rg + 16 * p;
+            if (gi >= NG) continue;  // uniform over the 16 lanes of a row group
+            float gv[RPL][VEC];
+#pragma unroll
+            for (int j = 0; j < RPL; ++j) {
+                const E *e = reinterpret_cast<const E *>(&raw[p][j]);
+#pragma unroll
+                for (int c = 0; c < VEC; ++c) gv[j][c] = gate_log2(to_f(e[c]), gmin2, logsig) + (j ? gv[j - 1][c] : 0.f);
+            }
+#pragma unroll
+            for (int c = 0; c < VEC; ++c) {
+                const float own = gv[RPL - 1][c];
+                float t = own;  // inclusive prefix of the lane totals over m
+                t += dpp_row_shr<1>(t);
+                t += dpp_row_shr<2>(t);
+                t += dpp_row_shr<4>(t);
+                t += dpp_row_shr<8>(t);
+                const float before = t - own;
+#pragma unroll
+                for (int j = 0; j < RPL; ++j) gv[j][c] += before;
+            }
+#pragma unroll
+            for (int j = 0; j < RPL; ++j) {
+                float *dst = sG + (m * RPL + j) * ldG + gi * VEC;
+#pragma unroll
+                for (int c = 0; c < VEC; c += 4)
+                    *reinterpret_cast<f32x4 *>(dst + c) = f32x4{gv[j][c], gv[j][c + 1], gv[j][c + 2], gv[j][c + 3]};
+            }
+        }
     }
-    __syncthreads();
-}
+};
 
 }  // namespace kda

@@ -116,15 +116,15 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 
     // ------------------------------------------------ phase 0: loads, gate, prefix sum
     // Every input load of the chunk (q, k and a as 16-byte accesses, beta) is issued before
-    // any of them is consumed, so the chunk pays one memory round trip.  a is staged densely
-    // at the start of region 0, where the prefix sum then overwrites it with G.
+    // any of them is consumed, so the chunk pays one memory round trip.  The gate and its
+    // prefix sum run in registers and write G once.
     {
         constexpr int LPR = DK / VEC, RPP = 256 / LPR, NP = (C + RPP - 1) / RPP;
-        const E *qg = q + tok0 * DK, *kg = k + tok0 * DK, *ag = a + tok0 * DK;
-        E *sAin = reinterpret_cast<E *>(smem);
-        static_assert(C * DK * Cfg::ES <= Cfg::R0, "staged a fits region 0");
+        const E *qg = q + tok0 * DK, *kg = k + tok0 * DK;
+        GateScan<C, DK, E> gate;
+        gate.load(a + tok0 * DK, tid);
         // loads are unconditional (row indices clamped into the chunk); only the stores are guarded
-        uint4 xq[NP], xk[NP], xa[NP];
+        uint4 xq[NP], xk[NP];
         const E bv = beta[tok0 + (tid < C ? tid : C - 1)];
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
@@ -132,7 +132,6 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
             const size_t off = (size_t)(r < C ? r : C - 1) * DK + c;
             xq[p] = *reinterpret_cast<const uint4 *>(qg + off);
             xk[p] = *reinterpret_cast<const uint4 *>(kg + off);
-            xa[p] = *reinterpret_cast<const uint4 *>(ag + off);
         }
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
@@ -140,12 +139,11 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
             if (C % RPP == 0 || r < C) {
                 *reinterpret_cast<uint4 *>(sQ + r * PQ + c) = xq[p];
                 *reinterpret_cast<uint4 *>(sK + r * PQ + c) = xk[p];
-                *reinterpret_cast<uint4 *>(sAin + r * DK + c) = xa[p];
             }
         }
         if (tid < C) sB[tid] = to_f(bv);
+        gate.finish(gmin2, logsig, sG, PG, tid);
         __syncthreads();
-        gate_cumsum_tile<C, DK, E, true>(sAin, gmin2, logsig, sG, PG, sScr);  // ends with a barrier
     }
 
     // ------------------------------------------------ phase 1: causal sub-tiles of M and A
@@ -367,11 +365,6 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
                                                  (lds_void *)(sVb + r * PV * Cfg::ES + part * 256), 4, 0, 0);
         }
     }
-    for (int x = tid; x < NT * NT * 256; x += 256) {  // zero the blocks above the diagonal
-        const int blk = x >> 8, e = x & 255;
-        const int I = blk / NT, J = blk % NT;
-        if (I < J) sT[(16 * I + (e >> 4)) * PA + 16 * J + (e & 15)] = 0.f;
-    }
     if (wave < NT) {
         // Diagonal block I = wave.  N = A_II is strictly lower triangular, so N^16 = 0 and
         // (I + N)^-1 = (I - N)(I + N^2)(I + N^4)(I + N^8) exactly: eight chained 16x16x16
@@ -444,11 +437,6 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
             for (int i = 0; i < 4; ++i) sA[(16 * I + 4 * g + i) * PA + 16 * J + l16] = accMs[J][i];
         }
     }
-    for (int x = tid; x < NT * NT * 256; x += 256) {  // and M's blocks above the diagonal are zero
-        const int blk = x >> 8, e = x & 255;
-        const int I = blk / NT, J = blk % NT;
-        if (I < J) sA[(16 * I + (e >> 4)) * PA + 16 * J + (e & 15)] = 0.f;
-    }
     wait_vmcnt<0>();  // V has landed in LDS
     __syncthreads();
     const float *sM = sA;
@@ -456,15 +444,19 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     // ------------------------------------------------ phase 3
     // Fragments indexed by (row tile rt, token K-block kb): lane l holds row r = 16 rt + l16,
     // slots = columns 32 kb + kslot.  tf: T diag(beta); mf: M (hi + lo).
+    // Only the causal K-blocks kb <= rt / 2 are used.  T and M are stored for blocks on and
+    // below the diagonal only; the one block above the diagonal that such a K-block spans
+    // (column tile 2 kb + 1 = rt + 1) is zero and is never read.
     F tf[NT][NTKB];
     SP mf[NT][NTKB];
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt)
 #pragma unroll
         for (int kb = 0; kb < NTKB; ++kb) {
+            if (kb > rt / 2) continue;
             float x[8], y[8];
             const int r = 16 * rt + l16;
-            const bool hi = (2 * kb + 1) < NT;
+            const bool hi = 2 * kb + 1 <= rt;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int s0 = 32 * kb + 4 * g + i, s1 = s0 + 16;

@@ -17,9 +17,11 @@ __global__ __launch_bounds__(256) void kda_gate_kernel(const typename std::condi
 {
     constexpr int PG = DK + 4;
     __shared__ __attribute__((aligned(16))) float sG[C * PG];
-    __shared__ float sScr[256];
     const size_t tok0 = ((size_t)blockIdx.z * H + blockIdx.y) * (size_t)T + (size_t)blockIdx.x * C;
-    gate_cumsum_tile<C, DK>(a + tok0 * DK, gmin2, logsig, sG, PG, sScr);
+    GateScan<C, DK, typename std::conditional<F32, float, __bf16>::type> gate;
+    gate.load(a + tok0 * DK, threadIdx.x);
+    gate.finish(gmin2, logsig, sG, PG, threadIdx.x);
+    __syncthreads();
     float *o = G_out + tok0 * DK;
     constexpr int LPR = DK / 4, RPP = 256 / LPR;
     for (int r0 = 0; r0 < C; r0 += RPP) {
