@@ -28,6 +28,13 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+// An LDS-typed pointer to a __shared__ object.  Offsets are added to it, never to a generic
+// pointer that is cast afterwards: a generic-to-LDS cast carries a null check, and where that
+// check does not fold this compiler can emit an instruction with an illegal operand.
+template <typename T>
+__device__ __forceinline__ lds_u8 *lds_base(T *shared_object) { return (lds_u8 *)shared_object; }
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -153,6 +160,17 @@ template <typename T> struct Split {
 };
 template <typename T>
 __device__ __forceinline__ void st_frag(T *base, int lane, const Frag<T> &f) { f.store(base, lane); }
+// This lane's 8 values to LDS at base + 8 * lane elements (one 16-byte store per 8 bytes... of
+// 16-bit values, two for float), through an LDS-typed pointer.
+__device__ __forceinline__ void st_frag_lds(lds_u8 *base, int lane, const Frag<_Float16> &f) {
+    *reinterpret_cast<__attribute__((address_space(3))) f16x8 *>(base + 16 * lane) = f.v;
+}
+__device__ __forceinline__ void st_frag_lds(lds_u8 *base, int lane, const Frag<float> &f) {
+    auto *p = reinterpret_cast<__attribute__((address_space(3))) f32x4 *>(base + 32 * lane);
+    p[0] = f32x4{f.v[0], f.v[1], f.v[2], f.v[3]};
+    p[1] = f32x4{f.v[4], f.v[5], f.v[6], f.v[7]};
+}
+
 template <typename T>
 __device__ __forceinline__ f32x4 mma3(const Split<T> &a, const Split<T> &b, f32x4 c) {
     c = mma(a.hi, b.hi, c);
@@ -238,7 +256,6 @@ __device__ __forceinline__ void ld4(const float *p, float (&x)[4]) {
 }
 
 // ---------------------------------------------------------------- direct global->LDS loads
-typedef __attribute__((address_space(3))) void lds_void;
 
 // s_waitcnt vmcnt(N) (expcnt, lgkmcnt unconstrained): all but the N most recent
 // vector-memory instructions of this wave have completed.

@@ -357,7 +357,7 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
         // they land while T is being solved and are waited for before phase 3
         constexpr int RB = DV * Cfg::ES, NPR = (RB + 255) / 256;
         const unsigned char *vg = reinterpret_cast<const unsigned char *>(v + tok0 * DV);
-        unsigned char *sVb = reinterpret_cast<unsigned char *>(sV);
+        lds_u8 *sVb = lds_base(smem) + C * PA * 4;  // sV, LDS-typed
         for (int x = wave; x < C * NPR; x += 4) {
             const int r = x / NPR, part = x % NPR, off = part * 256 + lane * 4;
             if (off < RB)

@@ -62,7 +62,7 @@ static hipError_t launch_state_t(const LaunchArgs &p) {
     const int BH = p.B * p.H;
     const int groups = (BH + 7) / 8;
     dim3 grid(groups * 8 * (DV / 16));
-    hipLaunchKernelGGL((kda_state_kernel<C, DK, DV, F32>), grid, dim3(128), 0, p.stream,
+    hipLaunchKernelGGL((kda_state_kernel<C, DK, DV, F32>), grid, dim3(192), 0, p.stream,
                        reinterpret_cast<const unsigned char *>(p.workspace), reinterpret_cast<E *>(p.out),
                        p.final_state, BH, p.T, p.counts);
     return hipGetLastError();

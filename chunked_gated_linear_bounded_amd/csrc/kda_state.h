@@ -10,22 +10,27 @@
 // ("Trillion-Parameter MoE Multimodal Models: Engineering Long-Context ...",
 // sec. 3.2: a constant-size state updated chunk by chunk).
 //
-// The slice of S^T stays in the compute wave's registers for the whole
-// sequence in accumulator layout; by the slot convention of kda_device.h the
-// same registers are the B operand of W S^T and the A operand of
-// (S^T)^T Qbar^T, and U's accumulators are the B operand of K^^T U -- no
-// shuffles, no LDS round trips.  All three products take fp16 operands: U and
-// S^T are scaled per chunk by a power of two from their wave-wide maximum
-// magnitude (W, Qbar and K^ arrive scaled the same way) and the scales are
-// undone exactly on the fp32 results.  Each operand fragment is one 16-byte
-// LDS read (tile pairs), and independent output tiles keep separate
-// accumulators so consecutive MFMAs do not wait on each other.
+// The slice of S^T stays in the state wave's registers for the whole sequence
+// in accumulator layout; by the slot convention of kda_device.h the same
+// registers are the B operand of W S^T and the A operand of (S^T)^T Qbar^T, and
+// U's accumulators are the B operand of K^^T U -- no shuffles.  All three
+// products take fp16 operands: U and S^T are scaled by a power of two from their
+// wave-wide maximum magnitude (S^T is kept pre-scaled and rescaled only when
+// its maximum leaves [2^11, 2^15); W, Qbar and K^ arrive scaled the same way)
+// and the scales are undone exactly on the fp32 results.  Each operand fragment
+// is one 16-byte LDS read (tile pairs), and independent output tiles keep
+// separate accumulators so consecutive MFMAs do not wait on each other.
 //
-// Work-group = 2 waves: wave 0 computes; wave 1 streams chunk records into a
-// ring of three LDS buffers with direct global->LDS loads (every load of a
-// record in flight at once, no staging registers), two chunks ahead of the
-// compute wave; one barrier per chunk hands the buffers over.  Work-group ids are mapped so that
-// all slices of a head land on one XCD and share its L2.
+// Work-group = 3 waves on three SIMDs: wave 0 carries the state (W S^T, U,
+// K^^T U, S^T); wave 2 forms the output from the fp16 state operand wave 0
+// hands over through LDS (written over W^T of the previous chunk's buffer, so
+// the hand-over costs no extra LDS); wave 1 streams chunk records into a ring
+// of LDS buffers with direct global->LDS loads (every load of a record in
+// flight at once, no staging registers), two chunks ahead.  Two barriers per
+// chunk: the first after the output wave has taken the state operand (the
+// loader only then refills that buffer), the second when the chunk is done.
+// Work-group ids are mapped so that all slices of a head land on one XCD and
+// share its L2.
 #pragma once
 #include "kda_device.h"
 #include "kda_layout.h"
@@ -51,7 +56,7 @@ struct StateCfg {
 // each instruction moves 64 x 16 bytes to consecutive LDS addresses.  The
 // caller waits for them (vmcnt) before handing the buffer over.
 template <int BYTES>
-__device__ __forceinline__ void dma_to_lds(unsigned char *dst, const unsigned char *__restrict__ src, int lane) {
+__device__ __forceinline__ void dma_to_lds(lds_u8 *dst, const unsigned char *__restrict__ src, int lane) {
     static_assert(BYTES % 16 == 0, "16-byte units");
     constexpr int UNITS = BYTES / 16, NI = (UNITS + 63) / 64;
 #pragma unroll
@@ -64,7 +69,7 @@ __device__ __forceinline__ void dma_to_lds(unsigned char *dst, const unsigned ch
 
 // Issue the copies of one chunk's record (region 1 + one value slice).
 template <int R1, int SL>
-__device__ __forceinline__ void issue_record(unsigned char *dst, const unsigned char *__restrict__ rec,
+__device__ __forceinline__ void issue_record(lds_u8 *dst, const unsigned char *__restrict__ rec,
                                              size_t slice_off, int lane) {
     dma_to_lds<R1>(dst, rec, lane);
     dma_to_lds<SL>(dst + R1, rec + slice_off, lane);
@@ -72,7 +77,7 @@ __device__ __forceinline__ void issue_record(unsigned char *dst, const unsigned 
 
 
 template <int C, int DK, int DV, bool F32>
-__global__ __launch_bounds__(128, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void kda_state_kernel(
+__global__ __launch_bounds__(192, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void kda_state_kernel(
     const unsigned char *__restrict__ ws, typename StateCfg<C, DK, DV, F32>::E *__restrict__ out,
     float *__restrict__ final_state, int BH, int T, unsigned long long *__restrict__ counts)
 {
@@ -102,15 +107,14 @@ __global__ __launch_bounds__(128, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 
     constexpr int NDMA = Cfg::NDMA;
     if (wave == 1 && NC > 0) {
-        issue_record<R1B, SLB>(smem, rec0, soff, lane);
+        issue_record<R1B, SLB>(lds_base(smem), rec0, soff, lane);
         if (NBUF == 3 && NC > 1) {
-            issue_record<R1B, SLB>(smem + BUF, rec0 + L.stride, soff, lane);
+            issue_record<R1B, SLB>(lds_base(smem) + BUF, rec0 + L.stride, soff, lane);
             wait_vmcnt<NBUF == 3 ? NDMA : 0>();  // chunk 0 has landed
         } else {
             wait_vmcnt<0>();
         }
     }
-    barrier_lds();
 
     // The state slice is kept scaled by 2^sS (wave-uniform), with sS chosen so that its
     // largest magnitude lies in [2^11, 2^15): the fp16 operand is then a plain conversion,
@@ -121,84 +125,109 @@ __global__ __launch_bounds__(128, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     int sS = 0;
     unsigned int nonfinite = 0;
 
+    // Hand-over of the state operand to the output wave.  With two or more buffers, the state
+    // wave stores chunk n's operand (and its exponent) at the end of chunk n - 1, over W^T in
+    // that chunk's buffer, which only the loader reuses, after the output wave has read the
+    // operand (the first barrier of chunk n).  With one buffer it is stored at the start of
+    // chunk n, over W^T of chunk n once that has been read into registers.
+    constexpr bool EARLY = NBUF >= 2;
+    auto hand_over = [&](int buf, const FH (&sh)[NKB], int e) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+            st_frag_lds(lds_base(smem) + buf * BUF + L.wt + kb * 512 * (int)sizeof(OH), lane, sh[kb]);
+        if (lane == 0) reinterpret_cast<int *>(smem + buf * BUF + L.scl)[3] = e;
+    };
+    auto state_operand = [&](FH (&sh)[NKB]) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            float x[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) x[j] = S[2 * kb + j / 4][j % 4];
+            sh[kb] = FH::make(x);
+        }
+    };
+    if (EARLY && wave == 0 && NC > 0) {  // chunk 0 starts from the zero state
+        FH sh0[NKB];
+        state_operand(sh0);
+        hand_over(NBUF - 1, sh0, 0);
+    }
+    barrier_lds();  // chunk 0 has landed; the first state operand is in place
+
     for (int n = 0; n < NC; ++n) {
-        const unsigned char *cur = smem + (n % NBUF) * BUF;
+        unsigned char *cur = smem + (n % NBUF) * BUF;
+        const OH *bWT = reinterpret_cast<const OH *>(cur + L.wt);
+        const OH *bQB = reinterpret_cast<const OH *>(cur + L.qbt);
+        const OH *bKH = reinterpret_cast<const OH *>(cur + L.kh);
+        const float *bG = reinterpret_cast<const float *>(cur + L.gam);
+        int *bScl = reinterpret_cast<int *>(cur + L.scl);
+        const OH *bU = reinterpret_cast<const OH *>(cur + L.region1 + L.ut);
+        const OH *bO = reinterpret_cast<const OH *>(cur + L.region1 + L.oit);
+        const int *bSS = reinterpret_cast<const int *>(cur + L.region1 + L.ssc);
+        constexpr int PE = 2 * TE;  // elements per stored tile pair
+
+        const int hb_buf = EARLY ? (n + NBUF - 1) % NBUF : 0;  // where chunk n's state operand is
+        const OH *shx = reinterpret_cast<const OH *>(smem + hb_buf * BUF + L.wt);
+        const int *shs = reinterpret_cast<const int *>(smem + hb_buf * BUF + L.scl) + 3;
+
+        // ---- W^T into the state wave's registers; the output wave takes the state operand
+        FH wt[NKB][NT], So[NKB];
+        f32x4 ut[NT];
+        int eW = 0, eK = 0, eU = 0, sSo = 0;
+        if (wave == 0) {
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int tt = 0; tt < NT; ++tt) wt[kb][tt] = FH::load_pair(bWT + (kb * NT + tt) * PE, lane);
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt) ut[tt] = ld_tile(bU + tt * TE, lane);
+            eW = bScl[0];
+            eK = bScl[2];
+            eU = bSS[0];
+            if constexpr (!EARLY) {  // W^T's bytes are only read by this wave, in order before these stores
+                FH sh[NKB];
+                state_operand(sh);
+                hand_over(0, sh, sS);
+            }
+        }
+        if (EARLY && wave == 2) {
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) So[kb] = FH::load_pair(shx + kb * 512, lane);
+            sSo = *shs;
+        }
+        barrier_lds();  // the output wave has the state operand (or, with one buffer, it is in LDS)
+
         if (wave == 1) {
+            // ---- loader: the record two chunks ahead
             if (NBUF == 3) {
                 if (n + 2 < NC) {
-                    issue_record<R1B, SLB>(smem + ((n + 2) % 3) * BUF, rec0 + (size_t)(n + 2) * L.stride, soff, lane);
+                    issue_record<R1B, SLB>(lds_base(smem) + ((n + 2) % 3) * BUF, rec0 + (size_t)(n + 2) * L.stride, soff, lane);
                     wait_vmcnt<NBUF == 3 ? NDMA : 0>();  // chunk n + 1 has landed
                 } else {
                     wait_vmcnt<0>();
                 }
             } else if (NBUF == 2 && n + 1 < NC) {
-                issue_record<R1B, SLB>(smem + ((n + 1) & 1) * BUF, rec0 + (size_t)(n + 1) * L.stride, soff, lane);
+                issue_record<R1B, SLB>(lds_base(smem) + ((n + 1) & 1) * BUF, rec0 + (size_t)(n + 1) * L.stride, soff, lane);
                 wait_vmcnt<0>();
             }
-        } else {
-            const OH *bWT = reinterpret_cast<const OH *>(cur + L.wt);
-            const OH *bQB = reinterpret_cast<const OH *>(cur + L.qbt);
-            const OH *bKH = reinterpret_cast<const OH *>(cur + L.kh);
-            const float *bG = reinterpret_cast<const float *>(cur + L.gam);
-            const int *bScl = reinterpret_cast<const int *>(cur + L.scl);
-            const OH *bU = reinterpret_cast<const OH *>(cur + L.region1 + L.ut);
-            const OH *bO = reinterpret_cast<const OH *>(cur + L.region1 + L.oit);
-            const int *bSS = reinterpret_cast<const int *>(cur + L.region1 + L.ssc);
-            constexpr int PE = 2 * TE;  // elements per stored tile pair
-
-            // Every W and Qbar fragment, U~ tile and exponent of this chunk is read up front, so
-            // the LDS latency overlaps the state's scale reduction instead of stalling each MFMA.
-            FH wt[NKB][NT], qb[NKB][NT];
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                for (int tt = 0; tt < NT; ++tt) {
-                    wt[kb][tt] = FH::load_pair(bWT + (kb * NT + tt) * PE, lane);
-                    qb[kb][tt] = FH::load_pair(bQB + (kb * NT + tt) * PE, lane);
-                }
-            f32x4 ut[NT];
-#pragma unroll
-            for (int tt = 0; tt < NT; ++tt) ut[tt] = ld_tile(bU + tt * TE, lane);
-            const int eW = bScl[0], eQ = bScl[1], eK = bScl[2], eU = bSS[0], eO = bSS[1];
-            __builtin_amdgcn_sched_barrier(0);
-
-            // the (scaled) state slice as the B operand of W S^T and the A operand of (S^T)^T Qbar^T
+        } else if (wave == 0) {
+            // ---- state wave: U = U~ - W S^T;  S^T <- diag(gamma) S^T + K^^T U
             FH Sh[NKB];
+            state_operand(Sh);
+            f32x4 P[NT];
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
-                float x[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) x[j] = S[2 * kb + j / 4][j % 4];
-                Sh[kb] = FH::make(x);
-            }
-            // W S^T and (S^T)^T Qbar^T (the latter needs no U): independent accumulators per
-            // 16-token tile, interleaved
-            f32x4 P[NT], O[NT];
-#pragma unroll
-            for (int tt = 0; tt < NT; ++tt) {
-                P[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-                O[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
+            for (int tt = 0; tt < NT; ++tt) P[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-                for (int tt = 0; tt < NT; ++tt) {
-                    P[tt] = mma(wt[kb][tt], Sh[kb], P[tt]);
-                    O[tt] = mma(Sh[kb], qb[kb][tt], O[tt]);
-                }
-            __builtin_amdgcn_sched_barrier(0);
-            // K^ fragments, Oi^T tiles and gamma: read while U is formed
-            FH kh[NTKB][NDK];
+                for (int tt = 0; tt < NT; ++tt) P[tt] = mma(wt[kb][tt], Sh[kb], P[tt]);
+            FH kh[NTKB][NDK];  // read while W S^T is in flight
 #pragma unroll
             for (int kb = 0; kb < NTKB; ++kb)
 #pragma unroll
                 for (int mt = 0; mt < NDK; ++mt) kh[kb][mt] = FH::load_pair(bKH + (kb * NDK + mt) * PE, lane);
-            f32x4 oi[NT], gm[NDK];
-#pragma unroll
-            for (int tt = 0; tt < NT; ++tt) oi[tt] = ld_tile(bO + tt * TE, lane);
+            f32x4 gm[NDK];
 #pragma unroll
             for (int mt = 0; mt < NDK; ++mt) gm[mt] = *reinterpret_cast<const f32x4 *>(bG + 16 * mt + 4 * g);
-            __builtin_amdgcn_sched_barrier(0);
             // U = U~ - W S^T (both scalings are exact, the difference rounds once)
             const float fW = ldexp2(1.f, -(sS + eW)), fU = ldexp2(1.f, -eU);
             f32x4 U[NT];
@@ -223,7 +252,7 @@ __global__ __launch_bounds__(128, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                 }
                 Uh[kb] = FH::make(x);
             }
-            // S^T <- diag(gamma) S^T + K^^T U: independent accumulators per 16-row dk tile
+            // independent accumulators per 16-row dk tile
             f32x4 A[NDK];
 #pragma unroll
             for (int mt = 0; mt < NDK; ++mt) A[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -231,7 +260,6 @@ __global__ __launch_bounds__(128, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             for (int kb = 0; kb < NTKB; ++kb)
 #pragma unroll
                 for (int mt = 0; mt < NDK; ++mt) A[mt] = mma(kh[kb][mt], Uh[kb], A[mt]);
-            const float unO = ldexp2(1.f, -(sS + eQ)), unI = ldexp2(1.f, -eO);  // scale Q S^T was taken at
             const float unS = ldexp2(1.f, sS - (sU + eK));
 #pragma unroll
             for (int mt = 0; mt < NDK; ++mt)
@@ -253,6 +281,34 @@ __global__ __launch_bounds__(128, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                     sS += d;
                 }
             }
+            if constexpr (EARLY) {  // the next chunk's state operand, over this chunk's (consumed) W^T
+                FH sh[NKB];
+                state_operand(sh);
+                hand_over(n % NBUF, sh, sS);
+            }
+        } else {
+            // ---- output wave: O^T = Oi^T + (S^T)^T Qbar^T with the state the chunk started from
+            if constexpr (!EARLY) {
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) So[kb] = FH::load_pair(shx + kb * 512, lane);
+                sSo = *shs;
+            }
+            FH qb[NKB][NT];
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int tt = 0; tt < NT; ++tt) qb[kb][tt] = FH::load_pair(bQB + (kb * NT + tt) * PE, lane);
+            f32x4 oi[NT];
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt) oi[tt] = ld_tile(bO + tt * TE, lane);
+            const float unO = ldexp2(1.f, -(sSo + bScl[1])), unI = ldexp2(1.f, -bSS[1]);
+            f32x4 O[NT];
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt) O[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int tt = 0; tt < NT; ++tt) O[tt] = mma(So[kb], qb[kb][tt], O[tt]);
             const size_t trow = (size_t)hb * T + (size_t)n * C;
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt) {
@@ -272,38 +328,33 @@ __global__ __launch_bounds__(128, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 #pragma unroll
                     for (int i = 0; i < 4; ++i) o[i] = (float)bo[i];
                 }
-                O[tt] = o;
-            }
-            if (counts != nullptr) {
+                if (counts != nullptr) {
 #pragma unroll
-                for (int tt = 0; tt < NT; ++tt)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) nonfinite += !__builtin_isfinite(O[tt][i]);
+                    for (int i = 0; i < 4; ++i) nonfinite += !__builtin_isfinite(o[i]);
+                }
             }
         }
         barrier_lds();
         if (NBUF == 1) {
             if (wave == 1 && n + 1 < NC) {
-                issue_record<R1B, SLB>(smem, rec0 + (size_t)(n + 1) * L.stride, soff, lane);
+                issue_record<R1B, SLB>(lds_base(smem), rec0 + (size_t)(n + 1) * L.stride, soff, lane);
                 wait_vmcnt<0>();
             }
             barrier_lds();
         }
     }
-    if (wave == 0) {
-        if (final_state != nullptr) {
-            // final_state[hb][value j0 + l16][key 16 mt + 4g + i] = S^T[key][value]
-            float *fp = final_state + ((size_t)hb * DV + j0 + l16) * DK + 4 * g;
+    if (wave == 0 && final_state != nullptr) {
+        // final_state[hb][value j0 + l16][key 16 mt + 4g + i] = S^T[key][value]
+        float *fp = final_state + ((size_t)hb * DV + j0 + l16) * DK + 4 * g;
 #pragma unroll
-            for (int mt = 0; mt < NDK; ++mt) {
-                f32x4 x;
+        for (int mt = 0; mt < NDK; ++mt) {
+            f32x4 x;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) x[i] = ldexp2(S[mt][i], -sS);
-                *reinterpret_cast<f32x4 *>(fp + 16 * mt) = x;
-            }
+            for (int i = 0; i < 4; ++i) x[i] = ldexp2(S[mt][i], -sS);
+            *reinterpret_cast<f32x4 *>(fp + 16 * mt) = x;
         }
-        if (counts != nullptr && nonfinite) atomicAdd(&counts[1], (unsigned long long)nonfinite);
     }
+    if (wave == 2 && counts != nullptr && nonfinite) atomicAdd(&counts[1], (unsigned long long)nonfinite);
 }
 
 }  // namespace kda
