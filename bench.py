@@ -112,6 +112,53 @@ def record_traffic(fetch_dir, write_dir, workload, copy_bytes):
     print(json.dumps(out, indent=1))
 
 
+def decode_bench(args):
+    """Decode throughput: one token per (sequence, head) per step through kda_decode_step, a batch of
+    sequences with the heads of the throughput workload (H=32, dk=dv=128, bf16 I/O), the float32
+    state resident in HBM.  Algorithmic bytes per token-head: the state read and written once
+    (2 dv dk 4) plus q, k, a, v, beta and out."""
+    import torch
+    import chunked_gated_linear_bounded_amd as kda
+    import kda_inputs as KI
+    B, H, d = args.decode_batch, 32, 128
+    w = KI.Workload("decode", B, H, 16, d, d, 16, "bf16", 4.0, False, 9)
+    dev = torch.device("cuda:0")
+    inp = KI.make_inputs(w, device=dev)
+    tok = {n: t[:, :, 0].contiguous() for n, t in inp.items()}
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(9)
+    S = torch.randn((B, H, d, d), generator=gen, device=dev, dtype=torch.float32) * 0.5
+    out = torch.empty((B, H, d), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        kda.decode_step(tok["q"], tok["k"], tok["v"], tok["a"], tok["beta"], S, out=out, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = e0.elapsed_time(e1) / args.steps
+    bph = 2 * d * d * 4 + (3 * d + d + d) * 2 + 2
+    alg = bph * B * H
+    print(json.dumps({
+        "metric": "KDA decode tokens/s (one token per sequence and head, H=32, d=128, bf16 I/O, fp32 state)",
+        "value": B / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "wall_ms_per_step": (t1 - t0) * 1e3 / args.steps, "higher_is_better": True,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "decode", "B": B, "H": H, "dk": d, "dv": d, "state_bytes": B * H * d * d * 4},
+        "roofline": {"kernel": "kda_decode_kernel", "bound": "hbm", "achieved": alg / (ms * 1e-3) / 1e9,
+                     "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": alg / (ms * 1e-3) / PEAK_HBM,
+                     "bytes_per_token_head": bph}}), flush=True)
+
+
 def cpu_baseline(inputs, w, seconds):
     """The float64 oracle on whole heads of the same workload until `seconds`
     have passed; returns whole-job tokens/s extrapolated from the sampled heads."""
@@ -147,7 +194,12 @@ def main():
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU run: turn two rocprofv3 --pmc output folders of this script into "
                          "profiles/traffic.json (needs --copy-calibration as used in those runs)")
+    ap.add_argument("--decode-batch", type=int, default=0, metavar="B",
+                    help="instead of the chunked forward, time kda_decode_step on B sequences x 32 heads")
     args = ap.parse_args()
+    if args.decode_batch > 0:
+        decode_bench(args)
+        return
     if args.traffic_from:
         if args.copy_calibration <= 0:
             raise SystemExit("--traffic-from needs --copy-calibration MIB")

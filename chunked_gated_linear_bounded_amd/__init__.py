@@ -7,6 +7,8 @@ built, every entry point raises; there is no fallback.
 
     import chunked_gated_linear_bounded_amd as kda
     out, S = kda.chunk_fwd(q, k, v, a, beta, g_min=-5.0, chunk=64, return_final_state=True)
+    out2 = kda.chunk_fwd(q2, k2, v2, a2, beta2, initial_state=S)     # continue the sequence
+    o_t = kda.decode_step(q_t, k_t, v_t, a_t, beta_t, S)               # one more token, S in place
     G = kda.gate_cumsum(a, g_min=-5.0, chunk=64)
 """
 from __future__ import annotations
@@ -50,12 +52,14 @@ def lib():
         L.kda_gate_cumsum.restype = i
         L.kda_chunk_fwd.argtypes = [vp] * 5 + [f] + [i] * 7 + [vp, vp, vp, sz, vp]
         L.kda_chunk_fwd.restype = i
-        L.kda_chunk_fwd_ex.argtypes = [vp] * 5 + [f] + [i] * 7 + [vp, vp, vp, sz, vp, i, vp]
+        L.kda_chunk_fwd_ex.argtypes = [vp] * 5 + [f] + [i] * 7 + [vp, vp, vp, sz, vp, i, vp, vp]
         L.kda_chunk_fwd_ex.restype = i
         L.kda_chunk_intra.argtypes = [vp] * 5 + [f] + [i] * 7 + [vp, sz, vp, i, vp]
         L.kda_chunk_intra.restype = i
-        L.kda_chunk_state.argtypes = [vp, sz] + [i] * 7 + [vp, vp, vp, vp]
+        L.kda_chunk_state.argtypes = [vp, sz] + [i] * 7 + [vp, vp, vp, vp, vp]
         L.kda_chunk_state.restype = i
+        L.kda_decode_step.argtypes = [vp] * 5 + [f] + [i] * 6 + [vp, vp, vp]
+        L.kda_decode_step.restype = i
         _lib = L
     return _lib
 
@@ -111,11 +115,14 @@ def gate_cumsum(a, g_min=-5.0, chunk=64, gate="bounded", out=None, stream=None):
 
 
 def chunk_fwd(q, k, v, a, beta, g_min=-5.0, chunk=64, out=None, final_state=None,
-              return_final_state=False, workspace=None, stream=None, gate="bounded", counts=None):
+              return_final_state=False, workspace=None, stream=None, gate="bounded", counts=None,
+              initial_state=None):
     """Chunked KDA forward.  q, k, a: [B,H,T,dk]; v: [B,H,T,dv]; beta: [B,H,T];
     all bf16 or all float32, contiguous, on one GPU.  Returns out [B,H,T,dv]
     (and the float32 final state [B,H,dv,dk] when asked for).  `counts`: optional
-    int64 GPU tensor of 2 elements that non-finite counters are added to."""
+    int64 GPU tensor of 2 elements that non-finite counters are added to.
+    `initial_state`: optional float32 [B,H,dv,dk] state to start from (may be
+    passed as final_state too, to continue in place)."""
     dtype = q.dtype
     if dtype not in _DTYPES:
         raise ValueError("unsupported dtype %s" % dtype)
@@ -139,14 +146,18 @@ def chunk_fwd(q, k, v, a, beta, g_min=-5.0, chunk=64, out=None, final_state=None
     _check(workspace, "workspace", torch.uint8, dev)
     if counts is not None:
         _check(counts, "counts", torch.int64, dev)
+    if initial_state is not None:
+        _check(initial_state, "initial_state", torch.float32, dev)
+        if tuple(initial_state.shape) != (B, H, dv, dk):
+            raise ValueError("initial_state must be [B,H,dv,dk]")
     L = lib()
     args = [_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(beta), float(g_min), int(chunk), B, H, T, dk, dv,
             _DTYPES[dtype], _ptr(out), _ptr(final_state), _ptr(workspace), workspace.numel(), _stream(stream)]
-    if gate == "bounded" and counts is None:
+    if gate == "bounded" and counts is None and initial_state is None:
         st = L.kda_chunk_fwd(*args)
         fn = "kda_chunk_fwd"
     else:
-        st = L.kda_chunk_fwd_ex(*args, GATE_MODES[gate], _ptr(counts))
+        st = L.kda_chunk_fwd_ex(*args, GATE_MODES[gate], _ptr(counts), _ptr(initial_state))
         fn = "kda_chunk_fwd_ex"
     if st != KDA_OK:
         raise KdaError(fn, st)
@@ -171,14 +182,41 @@ def chunk_intra(q, k, v, a, beta, workspace, g_min=-5.0, chunk=64, stream=None, 
         raise KdaError("kda_chunk_intra", st)
 
 
-def chunk_state(workspace, out, final_state=None, chunk=64, dk=None, stream=None, counts=None):
+def chunk_state(workspace, out, final_state=None, chunk=64, dk=None, stream=None, counts=None,
+                initial_state=None):
     """Second stage of chunk_fwd: reads `workspace`, writes out [B,H,T,dv] (and
-    final_state [B,H,dv,dk] float32 when given).  dk defaults to dv."""
+    final_state [B,H,dv,dk] float32 when given), starting from initial_state
+    when given.  dk defaults to dv."""
     _check(out, "out")
     _check(workspace, "workspace", torch.uint8, out.device)
     B, H, T, dv = out.shape
     dk = dv if dk is None else dk
     st = lib().kda_chunk_state(_ptr(workspace), workspace.numel(), int(chunk), B, H, T, dk, dv, _DTYPES[out.dtype],
-                               _ptr(out), _ptr(final_state), _stream(stream), _ptr(counts))
+                               _ptr(out), _ptr(final_state), _stream(stream), _ptr(counts), _ptr(initial_state))
     if st != KDA_OK:
         raise KdaError("kda_chunk_state", st)
+
+
+def decode_step(q, k, v, a, beta, state, g_min=-5.0, gate="bounded", out=None, stream=None):
+    """One token per (batch, head): q, k, a [B,H,dk]; v [B,H,dv]; beta [B,H] (all bf16
+    or all float32); state float32 [B,H,dv,dk], updated in place.  Returns out [B,H,dv]."""
+    dtype = q.dtype
+    if dtype not in _DTYPES:
+        raise ValueError("unsupported dtype %s" % dtype)
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (a, "a"), (beta, "beta")):
+        _check(t, n, dtype, dev)
+    _check(state, "state", torch.float32, dev)
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or a.shape != q.shape or v.shape != (B, H, dv) or beta.shape != (B, H) or \
+            tuple(state.shape) != (B, H, dv, dk):
+        raise ValueError("shape mismatch")
+    if out is None:
+        out = torch.empty((B, H, dv), dtype=dtype, device=dev)
+    _check(out, "out", dtype, dev)
+    st = lib().kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(beta), float(g_min), B, H, dk, dv,
+                               _DTYPES[dtype], GATE_MODES[gate], _ptr(state), _ptr(out), _stream(stream))
+    if st != KDA_OK:
+        raise KdaError("kda_decode_step", st)
+    return out

@@ -74,24 +74,29 @@ int intra_impl(const void *q, const void *k, const void *v, const void *a, const
 
 int state_impl(const void *workspace, size_t workspace_bytes_given, int chunk, int B, int H, int T, int dk,
                int dv, int io, void *out, float *final_state, hipStream_t stream, unsigned long long *counts,
-               bool launch) {
+               const float *init_state, bool launch) {
     int st = check_shape(B, H, T, dk, dv, chunk, io);
     if (st != KDA_OK) return st;
     if (T > 0 && !out) return KDA_ERR_NULL;  // an empty out may be NULL
-    if (!aligned(out, 16) || (final_state && !aligned(final_state, 16)) || (counts && !aligned(counts, 8)))
+    if (!aligned(out, 16) || (final_state && !aligned(final_state, 16)) || (counts && !aligned(counts, 8)) ||
+        (init_state && !aligned(init_state, 16)))
         return KDA_ERR_ALIGN;
     st = check_ptrs_ws(B, H, T, dk, dv, chunk, io, workspace, workspace_bytes_given);
     if (st != KDA_OK || !launch) return st;
-    if (T == 0) {  // empty sequence: no output rows, the state stays zero
-        if (final_state &&
-            hipMemsetAsync(final_state, 0, (size_t)B * H * dv * dk * sizeof(float), stream) != hipSuccess)
+    if (T == 0) {  // empty sequence: no output rows, the state is the initial one
+        const size_t bytes = (size_t)B * H * dv * dk * sizeof(float);
+        if (final_state && !init_state && hipMemsetAsync(final_state, 0, bytes, stream) != hipSuccess)
+            return KDA_ERR_HIP;
+        if (final_state && init_state && final_state != init_state &&
+            hipMemcpyAsync(final_state, init_state, bytes, hipMemcpyDeviceToDevice, stream) != hipSuccess)
             return KDA_ERR_HIP;
         return KDA_OK;
     }
     kda::LaunchArgs p{};
     p.chunk = chunk; p.B = B; p.H = H; p.T = T; p.dk = dk; p.dv = dv;
     p.fp32 = io == KDA_FP32;
-    p.out = out; p.final_state = final_state; p.workspace = const_cast<void *>(workspace);
+    p.out = out; p.final_state = final_state; p.init_state = init_state;
+    p.workspace = const_cast<void *>(workspace);
     p.counts = counts; p.stream = stream;
     return kda::launch_state(p) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
@@ -99,19 +104,19 @@ int state_impl(const void *workspace, size_t workspace_bytes_given, int chunk, i
 int fwd_impl(const void *q, const void *k, const void *v, const void *a, const void *beta, float g_min,
              int chunk, int B, int H, int T, int dk, int dv, int io, void *out, float *final_state,
              void *workspace, size_t workspace_bytes_given, hipStream_t stream, int gate_mode,
-             unsigned long long *counts) {
+             unsigned long long *counts, const float *init_state) {
     // validate both stages before launching either
     int st = intra_impl(q, k, v, a, beta, g_min, chunk, B, H, T, dk, dv, io, workspace, workspace_bytes_given,
                         stream, gate_mode, counts, false);
     if (st != KDA_OK) return st;
     st = state_impl(workspace, workspace_bytes_given, chunk, B, H, T, dk, dv, io, out, final_state, stream,
-                    counts, false);
+                    counts, init_state, false);
     if (st != KDA_OK) return st;
     st = intra_impl(q, k, v, a, beta, g_min, chunk, B, H, T, dk, dv, io, workspace, workspace_bytes_given,
                     stream, gate_mode, counts, true);
     if (st != KDA_OK) return st;
     return state_impl(workspace, workspace_bytes_given, chunk, B, H, T, dk, dv, io, out, final_state, stream,
-                      counts, true);
+                      counts, init_state, true);
 }
 
 }  // namespace
@@ -162,15 +167,15 @@ int kda_chunk_fwd(const void *q, const void *k, const void *v, const void *a, co
                   int chunk, int B, int H, int T, int dk, int dv, int io_dtype, void *out, float *final_state,
                   void *workspace, size_t workspace_bytes_given, hipStream_t stream) {
     return fwd_impl(q, k, v, a, beta, g_min, chunk, B, H, T, dk, dv, io_dtype, out, final_state, workspace,
-                    workspace_bytes_given, stream, KDA_GATE_BOUNDED, nullptr);
+                    workspace_bytes_given, stream, KDA_GATE_BOUNDED, nullptr, nullptr);
 }
 
 int kda_chunk_fwd_ex(const void *q, const void *k, const void *v, const void *a, const void *beta,
                      float g_min, int chunk, int B, int H, int T, int dk, int dv, int io_dtype, void *out,
                      float *final_state, void *workspace, size_t workspace_bytes_given, hipStream_t stream,
-                     int gate_mode, unsigned long long *nonfinite_counts) {
+                     int gate_mode, unsigned long long *nonfinite_counts, const float *initial_state) {
     return fwd_impl(q, k, v, a, beta, g_min, chunk, B, H, T, dk, dv, io_dtype, out, final_state, workspace,
-                    workspace_bytes_given, stream, gate_mode, nonfinite_counts);
+                    workspace_bytes_given, stream, gate_mode, nonfinite_counts, initial_state);
 }
 
 int kda_chunk_intra(const void *q, const void *k, const void *v, const void *a, const void *beta, float g_min,
@@ -183,9 +188,31 @@ int kda_chunk_intra(const void *q, const void *k, const void *v, const void *a, 
 
 int kda_chunk_state(const void *workspace, size_t workspace_bytes_given, int chunk, int B, int H, int T, int dk,
                     int dv, int io_dtype, void *out, float *final_state, hipStream_t stream,
-                    unsigned long long *nonfinite_counts) {
+                    unsigned long long *nonfinite_counts, const float *initial_state) {
     return state_impl(workspace, workspace_bytes_given, chunk, B, H, T, dk, dv, io_dtype, out, final_state, stream,
-                      nonfinite_counts, true);
+                      nonfinite_counts, initial_state, true);
+}
+
+int kda_decode_step(const void *q, const void *k, const void *v, const void *a, const void *beta, float g_min,
+                    int B, int H, int dk, int dv, int io_dtype, int gate_mode, float *state, void *out,
+                    hipStream_t stream) {
+    int st = check_shape(B, H, 16, dk, dv, 16, io_dtype);
+    if (st != KDA_OK) return st;
+    st = check_gate(g_min, gate_mode);
+    if (st != KDA_OK) return st;
+    if (!q || !k || !v || !a || !beta || !state || !out) return KDA_ERR_NULL;
+    const size_t esz = io_dtype == KDA_FP32 ? 4 : 2;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(a, 16) || !aligned(beta, esz) ||
+        !aligned(state, 16) || !aligned(out, 16))
+        return KDA_ERR_ALIGN;
+    kda::LaunchArgs p{};
+    p.q = q; p.k = k; p.v = v; p.a = a; p.beta = beta;
+    p.g_min = g_min;
+    p.logsig = gate_mode == KDA_GATE_LOGSIGMOID;
+    p.B = B; p.H = H; p.T = 1; p.dk = dk; p.dv = dv;
+    p.fp32 = io_dtype == KDA_FP32;
+    p.state = state; p.out = out; p.stream = stream;
+    return kda::launch_decode(p) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
 }  // extern "C"

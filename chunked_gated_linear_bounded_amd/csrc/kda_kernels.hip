@@ -1,6 +1,7 @@
 // Kernel instantiations and launchers for the C ABI in include/kda.h.
 #include <hip/hip_runtime.h>
 
+#include "kda_decode.h"
 #include "kda_device.h"
 #include "kda_intra.h"
 #include "kda_launch.h"
@@ -64,7 +65,7 @@ static hipError_t launch_state_t(const LaunchArgs &p) {
     dim3 grid(groups * 8 * (DV / 16));
     hipLaunchKernelGGL((kda_state_kernel<C, DK, DV, F32>), grid, dim3(192), 0, p.stream,
                        reinterpret_cast<const unsigned char *>(p.workspace), reinterpret_cast<E *>(p.out),
-                       p.final_state, BH, p.T, p.counts);
+                       p.final_state, p.init_state, BH, p.T, p.counts);
     return hipGetLastError();
 }
 
@@ -106,5 +107,27 @@ static hipError_t dispatch_gate_t(const LaunchArgs &p) {
 hipError_t launch_gate_cumsum(const LaunchArgs &p) {
     return p.fp32 ? dispatch_gate_t<true>(p) : dispatch_gate_t<false>(p);
 }
+
+template <int DK, int DV, bool F32>
+static hipError_t launch_decode_t(const LaunchArgs &p) {
+    using E = typename std::conditional<F32, float, __bf16>::type;
+    const int grid = p.B * p.H * (DV / 16);
+    hipLaunchKernelGGL((kda_decode_kernel<DK, DV, F32>), dim3(grid), dim3(256), 0, p.stream,
+                       reinterpret_cast<const E *>(p.q), reinterpret_cast<const E *>(p.k),
+                       reinterpret_cast<const E *>(p.v), reinterpret_cast<const E *>(p.a),
+                       reinterpret_cast<const E *>(p.beta), p.g_min * kLog2e, p.logsig, p.state,
+                       reinterpret_cast<E *>(p.out));
+    return hipGetLastError();
+}
+
+template <bool F32>
+static hipError_t dispatch_decode_t(const LaunchArgs &p) {
+    if (p.dk == 64 && p.dv == 64) return launch_decode_t<64, 64, F32>(p);
+    if (p.dk == 64 && p.dv == 128) return launch_decode_t<64, 128, F32>(p);
+    if (p.dk == 128 && p.dv == 64) return launch_decode_t<128, 64, F32>(p);
+    return launch_decode_t<128, 128, F32>(p);
+}
+
+hipError_t launch_decode(const LaunchArgs &p) { return p.fp32 ? dispatch_decode_t<true>(p) : dispatch_decode_t<false>(p); }
 
 }  // namespace kda

@@ -12,6 +12,8 @@ struct LaunchArgs {
     bool fp32;                  // I/O element type fp32 (else bf16)
     void *out;
     float *final_state;
+    const float *init_state;    // nullable: S_0 of the chunked forward
+    float *state;               // decode: the state, updated in place
     void *workspace;
     float *G_out;
     unsigned long long *counts;
@@ -21,5 +23,6 @@ struct LaunchArgs {
 hipError_t launch_intra(const LaunchArgs &p);  // chunk-parallel stage -> workspace
 hipError_t launch_state(const LaunchArgs &p);  // sequential stage: workspace -> out, final state
 hipError_t launch_gate_cumsum(const LaunchArgs &p);
+hipError_t launch_decode(const LaunchArgs &p);  // one token per head, state in place
 
 }  // namespace kda

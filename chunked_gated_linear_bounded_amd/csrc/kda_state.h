@@ -79,7 +79,7 @@ __device__ __forceinline__ void issue_record(lds_u8 *dst, const unsigned char *_
 template <int C, int DK, int DV, bool F32>
 __global__ __launch_bounds__(192, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void kda_state_kernel(
     const unsigned char *__restrict__ ws, typename StateCfg<C, DK, DV, F32>::E *__restrict__ out,
-    float *__restrict__ final_state, int BH, int T, unsigned long long *__restrict__ counts)
+    float *final_state, const float *init_state, int BH, int T, unsigned long long *__restrict__ counts)
 {
     using Cfg = StateCfg<C, DK, DV, F32>;
     using E = typename Cfg::E;
@@ -124,6 +124,29 @@ __global__ __launch_bounds__(192, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     for (int mt = 0; mt < NDK; ++mt) S[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     int sS = 0;
     unsigned int nonfinite = 0;
+    if (init_state != nullptr && wave == 0) {
+        // S_0: init_state[hb][value j0 + l16][key 16 mt + 4g + i] = S^T[key][value], taken to the
+        // scale the state is kept at (read before this work-group writes final_state, which may
+        // be the same array)
+        const float *ip = init_state + ((size_t)hb * DV + j0 + l16) * DK + 4 * g;
+#pragma unroll
+        for (int mt = 0; mt < NDK; ++mt) S[mt] = *reinterpret_cast<const f32x4 *>(ip + 16 * mt);
+        if constexpr (!F32) {
+            float m = 0.f;
+#pragma unroll
+            for (int mt = 0; mt < NDK; ++mt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(S[mt][i]));
+            m = wave_max(m);
+            if (m > 0.f && __builtin_isfinite(m)) {
+                sS = pow2_scale(m);
+#pragma unroll
+                for (int mt = 0; mt < NDK; ++mt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) S[mt][i] = ldexp2(S[mt][i], sS);
+            }
+        }
+    }
 
     // Hand-over of the state operand to the output wave.  With two or more buffers, the state
     // wave stores chunk n's operand (and its exponent) at the end of chunk n - 1, over W^T in
@@ -146,10 +169,10 @@ __global__ __launch_bounds__(192, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             sh[kb] = FH::make(x);
         }
     };
-    if (EARLY && wave == 0 && NC > 0) {  // chunk 0 starts from the zero state
+    if (EARLY && wave == 0 && NC > 0) {  // chunk 0's state operand
         FH sh0[NKB];
         state_operand(sh0);
-        hand_over(NBUF - 1, sh0, 0);
+        hand_over(NBUF - 1, sh0, sS);
     }
     barrier_lds();  // chunk 0 has landed; the first state operand is in place
 

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 /* ln(smallest normal float) / 15: the most negative g_min for which 15 steps of
  * decay inside a 16-token tile stay in the normal exponent range. */
 #define KDA_G_MIN_LOWEST (-5.8224f)
@@ -110,18 +110,26 @@ int kda_chunk_fwd(const void *q, const void *k, const void *v, const void *a, co
                   hipStream_t stream);
 
 /* As kda_chunk_fwd, plus the gate mode (KDA_GATE_LOGSIGMOID is the unbounded
- * form the pages replace, kept for the ablation) and optional device counters
+ * form the pages replace, kept for the ablation), optional device counters
  * (NULL to skip; else a device pointer to 2 unsigned 64-bit integers that are
  * ADDED to, so zero them first):
  *   nonfinite_counts[0] += number of Gamma-scaled key operands of the diagonal
  *                          16-token tiles that are +-inf or NaN after rounding
  *                          to the operand type (the only scaled operands whose
  *                          scale factor exceeds 1);
- *   nonfinite_counts[1] += number of outputs that are +-inf or NaN. */
+ *   nonfinite_counts[1] += number of outputs that are +-inf or NaN,
+ * and an optional initial state (NULL: S_0 = 0; else a device pointer to
+ * [B][H][dv][dk] float32 in the layout of final_state), so that a sequence can
+ * be processed in pieces, each continuing from the previous piece's final
+ * state (the constant-size state carried across a long context, second page
+ * sec. 3.2; context-parallel prefill, third page sec. 3).  initial_state may
+ * be the same array as final_state (each part of the state is read before it
+ * is overwritten); any other overlap with an argument is not allowed. */
 int kda_chunk_fwd_ex(const void *q, const void *k, const void *v, const void *a, const void *beta,
                      float g_min, int chunk, int B, int H, int T, int dk, int dv, int io_dtype,
                      void *out, float *final_state, void *workspace, size_t workspace_bytes,
-                     hipStream_t stream, int gate_mode, unsigned long long *nonfinite_counts);
+                     hipStream_t stream, int gate_mode, unsigned long long *nonfinite_counts,
+                     const float *initial_state);
 
 /* The two stages kda_chunk_fwd_ex runs, in order, exposed so a caller can
  * time them separately or schedule other work between them.  Same arguments
@@ -147,7 +155,21 @@ int kda_chunk_intra(const void *q, const void *k, const void *v, const void *a, 
                     unsigned long long *nonfinite_counts);
 int kda_chunk_state(const void *workspace, size_t workspace_bytes, int chunk, int B, int H, int T,
                     int dk, int dv, int io_dtype, void *out, float *final_state, hipStream_t stream,
-                    unsigned long long *nonfinite_counts);
+                    unsigned long long *nonfinite_counts, const float *initial_state);
+
+/* One token of the recurrence per (batch, head), the state updated in place
+ * (decoding after a prefill; the constant-size state of the second page,
+ * sec. 3.2; the gate as in kda_gate_cumsum):
+ *   S~ = S diag(exp g),  S <- S~ + beta (v - S~ k) k^T,  out = S q.
+ *   q, k, a : [B][H][dk]     v, out : [B][H][dv]     beta : [B][H]   (io_dtype)
+ *   state   : [B][H][dv][dk] float32, S[i][j] (i = value, j = key), read and
+ *             overwritten; it must not overlap any other argument.
+ * Same rules as above for dtypes, g_min, gate_mode, alignment (16 bytes;
+ * beta: element size), validation and asynchrony.  Supported: dk, dv in
+ * {64, 128}; B, H >= 1. */
+int kda_decode_step(const void *q, const void *k, const void *v, const void *a, const void *beta,
+                    float g_min, int B, int H, int dk, int dv, int io_dtype, int gate_mode,
+                    float *state, void *out, hipStream_t stream);
 
 #ifdef __cplusplus
 }

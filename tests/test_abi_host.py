@@ -26,13 +26,14 @@ def test_header_symbols_exported():
     L = kda.lib()
     names = _declared_functions()
     assert {"kda_abi_version", "kda_status_string", "kda_chunk_fwd_workspace_bytes",
-            "kda_gate_cumsum", "kda_chunk_fwd", "kda_chunk_fwd_ex"} <= set(names)
+            "kda_gate_cumsum", "kda_chunk_fwd", "kda_chunk_fwd_ex", "kda_chunk_intra", "kda_chunk_state",
+            "kda_decode_step"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
 
 def test_version_and_strings():
-    assert kda.abi_version() == 1
+    assert kda.abi_version() == 2
     for st in (OK, E_NULL, E_SHAPE, E_DTYPE, E_CHUNK, E_GMIN, E_WS, E_HIP, E_ALIGN, E_MODE):
         s = kda.status_string(st)
         assert s and s != "unknown status"
@@ -83,14 +84,15 @@ def test_validation_codes(kw, want):
 def test_validation_ex_and_gate():
     L = kda.lib()
     args = [FAKE] * 5 + [-5.0, 64, 1, 2, 128, 128, 128, 0, FAKE, None, FAKE, 1 << 40, None]
-    assert L.kda_chunk_fwd_ex(*args, 5, None) == E_MODE
+    assert L.kda_chunk_fwd_ex(*args, 5, None, None) == E_MODE
     # the ablation mode ignores g_min (it must not be rejected for it) -> fails later on the workspace
     args2 = list(args)
     args2[5] = 3.0
     args2[16] = 10
-    assert L.kda_chunk_fwd_ex(*args2, 1, None) == E_WS
-    assert L.kda_chunk_fwd_ex(*args2, 0, None) == E_GMIN
-    assert L.kda_chunk_fwd_ex(*args, 0, FAKE + 4) == E_ALIGN
+    assert L.kda_chunk_fwd_ex(*args2, 1, None, None) == E_WS
+    assert L.kda_chunk_fwd_ex(*args2, 0, None, None) == E_GMIN
+    assert L.kda_chunk_fwd_ex(*args, 0, FAKE + 4, None) == E_ALIGN
+    assert L.kda_chunk_fwd_ex(*args, 0, None, FAKE + 4) == E_ALIGN  # initial_state: 16-byte aligned
     assert L.kda_gate_cumsum(None, -5.0, 64, 1, 2, 128, 128, 0, 0, FAKE, None) == E_NULL
     assert L.kda_gate_cumsum(FAKE, -5.0, 64, 1, 2, 100, 128, 0, 0, FAKE, None) == E_SHAPE
     assert L.kda_gate_cumsum(FAKE, 0.5, 64, 1, 2, 128, 128, 0, 0, FAKE, None) == E_GMIN
@@ -103,9 +105,26 @@ def test_validation_ex_and_gate():
     assert L.kda_gate_cumsum(FAKE, -5.0, 64, 1, 2, 0, 128, 0, 0, FAKE, None) == OK
 
 
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=None), E_NULL), (dict(state=None), E_NULL), (dict(out=None), E_NULL),
+    (dict(io=3), E_DTYPE), (dict(B=0), E_SHAPE), (dict(dk=32), E_SHAPE), (dict(dv=96), E_SHAPE),
+    (dict(g_min=0.0), E_GMIN), (dict(mode=2), E_MODE),
+    (dict(state=FAKE + 4), E_ALIGN), (dict(k=FAKE + 2), E_ALIGN), (dict(beta=FAKE + 1), E_ALIGN),
+])
+def test_decode_validation(kw, want):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, a=FAKE, beta=FAKE, g_min=-5.0, B=1, H=2, dk=128, dv=128, io=0, mode=0,
+             state=FAKE, out=FAKE)
+    a.update(kw)
+    st = kda.lib().kda_decode_step(a["q"], a["k"], a["v"], a["a"], a["beta"], a["g_min"], a["B"], a["H"], a["dk"],
+                                   a["dv"], a["io"], a["mode"], a["state"], a["out"], None)
+    assert st == want
+
+
 def test_binding_rejects_host_tensors():
     x = torch.zeros(1, 1, 64, 64)
     with pytest.raises(ValueError):
         kda.chunk_fwd(x, x, x, x, torch.zeros(1, 1, 64), chunk=16)
     with pytest.raises(ValueError):
         kda.gate_cumsum(x, chunk=16)
+    with pytest.raises(ValueError):
+        kda.decode_step(x[:, :, 0], x[:, :, 0], x[:, :, 0], x[:, :, 0], torch.zeros(1, 1), torch.zeros(1, 1, 64, 64))

@@ -242,3 +242,35 @@ def test_overflow_predictor_exact_counts():
     assert overflow.subtile_operand_overflow(a, k, -5.0, 64, "bounded") == (0, 0)
     # a bound of -6 is not enough: 8.656 per step -> offset 15 (129.8) overflows
     assert overflow.subtile_operand_overflow(a, k, -6.0, 64, "bounded") == (T // 16, 0)
+
+
+# ---------------------------------------------------------------- the initial state
+@pytest.mark.parametrize("gate", ["bounded", "logsigmoid"])
+def test_beta_zero_state_only_decays(gate):
+    """beta = 0: nothing is written or erased, so S_t = S0 diag(e^{G_t}) with G_t the running sum
+    of the gate from the first token, and o_t = S_t q_t (closed form)."""
+    rng = np.random.default_rng(31)
+    q, k, v, a, _ = _rand_case(1, 2, 24, 6, 5, rng, a_sigma=2.0)
+    b = np.zeros((1, 2, 24))
+    S0 = rng.standard_normal((1, 2, 5, 6))
+    out, fin = native.recurrent(q, k, v, a, b, -5.0, gate=gate, S0=S0)
+    g = -5.0 / (1.0 + np.exp(-a)) if gate == "bounded" else -np.logaddexp(0.0, -a)
+    G = np.cumsum(g, axis=2)
+    want = np.einsum("bhij,bhtj->bhti", S0, np.exp(G) * q)
+    assert np.allclose(out, want, rtol=1e-12, atol=1e-14)
+    assert np.allclose(fin, S0 * np.exp(G[:, :, -1, None, :]), rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("split", [1, 7, 16])
+def test_sequence_split_continues_from_the_final_state(split):
+    """The state summarises the past: running tokens [0, T1) and then [T1, T) from its final state
+    gives the single run's outputs and final state (both the C and the NumPy form)."""
+    rng = np.random.default_rng(32 + split)
+    q, k, v, a, b = _rand_case(2, 2, 32, 6, 5, rng)
+    out, fin = native.recurrent(q, k, v, a, b)
+    s1 = slice(0, split)
+    s2 = slice(split, 32)
+    o1, f1 = native.recurrent(q[:, :, s1], k[:, :, s1], v[:, :, s1], a[:, :, s1], b[:, :, s1])
+    o2, f2 = reference.recurrent(q[:, :, s2], k[:, :, s2], v[:, :, s2], a[:, :, s2], b[:, :, s2], S0=f1)
+    assert np.allclose(np.concatenate([o1, o2], axis=2), out, rtol=1e-12, atol=1e-13)
+    assert np.allclose(f2, fin, rtol=1e-12, atol=1e-13)
