@@ -159,6 +159,62 @@ def decode_bench(args):
                      "bytes_per_token_head": bph}}), flush=True)
 
 
+def packed_bench(args):
+    """Packed documents: the 64k stream of 32 heads holding documents of log-uniform lengths in
+    [32, 4096] tokens (seeded), one kda_chunk_fwd_varlen call per step (plan, chunk stage and state
+    stage), inputs and boundaries resident in HBM.  Algorithmic bytes: inputs read and outputs
+    written once, each chunk record written once and read once."""
+    import torch
+    import chunked_gated_linear_bounded_amd as kda
+    import kda_inputs as KI
+    w = KI.PACKED
+    lengths = KI.packed_lengths(w.T, w.seed)
+    dev = torch.device("cuda:0")
+    print("bench: generating %s inputs (%d documents)" % (w.name, len(lengths)), file=sys.stderr, flush=True)
+    inp = KI.make_packed_inputs(w, device=dev)
+    cu = torch.from_numpy(KI.cu_seqlens(lengths)).to(dev)
+    N = len(lengths)
+    ws = torch.empty(kda.varlen_workspace_bytes(N, w.H, w.T, w.dk, w.dv, w.chunk, w.torch_dtype),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty((w.H, w.T, w.dv), dtype=w.torch_dtype, device=dev)
+    fs = torch.empty((N, w.H, w.dv, w.dk), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        kda.chunk_fwd_varlen(inp["q"], inp["k"], inp["v"], inp["a"], inp["beta"], cu, w.g_min, w.chunk, out=out,
+                             final_state=fs, workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = e0.elapsed_time(e1) / args.steps
+    assert torch.isfinite(out.float()).all().item(), "non-finite output"
+    es = 2
+    chunks = sum((n + w.chunk - 1) // w.chunk for n in lengths)
+    rec = kda.workspace_bytes(1, 1, w.chunk, w.dk, w.dv, w.chunk, w.torch_dtype)
+    th = w.H * w.T
+    alg = th * ((3 * w.dk + 2 * w.dv) * es + es) + 2 * w.H * chunks * rec + N * w.H * w.dv * w.dk * 4
+    print(json.dumps({
+        "metric": "KDA chunked fwd tokens/s over packed documents (T=64K stream, H=32, d=128, bf16 I/O)",
+        "value": w.T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "wall_ms_per_step": (t1 - t0) * 1e3 / args.steps, "higher_is_better": True,
+        "dtype": w.io, "data": "synthetic",
+        "config": {"workload": w.name, "H": w.H, "T": w.T, "dk": w.dk, "dv": w.dv, "chunk": w.chunk,
+                   "documents": N, "doc_len_min": min(lengths), "doc_len_max": max(lengths), "chunks_per_head": chunks},
+        "mfma_peak_frac": flops_per_token_head(w.dk, w.dv, w.chunk) * th / (ms * 1e-3) / PEAK_BF16_FLOPS,
+        "roofline": {"kernel": "kda_chunk_fwd_varlen (plan + chunk stage + state stage)", "bound": "hbm",
+                     "achieved": alg / (ms * 1e-3) / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                     "frac": alg / (ms * 1e-3) / PEAK_HBM, "bytes_per_step": alg}}), flush=True)
+
+
 def cpu_baseline(inputs, w, seconds):
     """The float64 oracle on whole heads of the same workload until `seconds`
     have passed; returns whole-job tokens/s extrapolated from the sampled heads."""
@@ -196,9 +252,14 @@ def main():
                          "profiles/traffic.json (needs --copy-calibration as used in those runs)")
     ap.add_argument("--decode-batch", type=int, default=0, metavar="B",
                     help="instead of the chunked forward, time kda_decode_step on B sequences x 32 heads")
+    ap.add_argument("--packed", action="store_true",
+                    help="instead of the fixed-length workload, time kda_chunk_fwd_varlen on the 64k packed stream")
     args = ap.parse_args()
     if args.decode_batch > 0:
         decode_bench(args)
+        return
+    if args.packed:
+        packed_bench(args)
         return
     if args.traffic_from:
         if args.copy_calibration <= 0:

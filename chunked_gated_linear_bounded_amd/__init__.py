@@ -9,6 +9,7 @@ built, every entry point raises; there is no fallback.
     out, S = kda.chunk_fwd(q, k, v, a, beta, g_min=-5.0, chunk=64, return_final_state=True)
     out2 = kda.chunk_fwd(q2, k2, v2, a2, beta2, initial_state=S)     # continue the sequence
     o_t = kda.decode_step(q_t, k_t, v_t, a_t, beta_t, S)               # one more token, S in place
+    o = kda.chunk_fwd_varlen(q, k, v, a, beta, cu_seqlens)             # packed documents, [H,T,d]
     G = kda.gate_cumsum(a, g_min=-5.0, chunk=64)
 """
 from __future__ import annotations
@@ -58,6 +59,10 @@ def lib():
         L.kda_chunk_intra.restype = i
         L.kda_chunk_state.argtypes = [vp, sz] + [i] * 7 + [vp, vp, vp, vp, vp]
         L.kda_chunk_state.restype = i
+        L.kda_chunk_fwd_varlen_workspace_bytes.argtypes = [i] * 7
+        L.kda_chunk_fwd_varlen_workspace_bytes.restype = sz
+        L.kda_chunk_fwd_varlen.argtypes = [vp] * 5 + [f, i, vp] + [i] * 6 + [vp, vp, vp, sz, vp, i, vp, vp]
+        L.kda_chunk_fwd_varlen.restype = i
         L.kda_decode_step.argtypes = [vp] * 5 + [f] + [i] * 6 + [vp, vp, vp]
         L.kda_decode_step.restype = i
         _lib = L
@@ -195,6 +200,58 @@ def chunk_state(workspace, out, final_state=None, chunk=64, dk=None, stream=None
                                _ptr(out), _ptr(final_state), _stream(stream), _ptr(counts), _ptr(initial_state))
     if st != KDA_OK:
         raise KdaError("kda_chunk_state", st)
+
+
+def varlen_workspace_bytes(N, H, T, dk, dv, chunk, dtype) -> int:
+    io = _DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(lib().kda_chunk_fwd_varlen_workspace_bytes(N, H, T, dk, dv, chunk, io))
+
+
+def chunk_fwd_varlen(q, k, v, a, beta, cu_seqlens, g_min=-5.0, chunk=64, out=None, final_state=None,
+                     return_final_state=False, initial_state=None, workspace=None, stream=None, gate="bounded",
+                     counts=None):
+    """Packed documents: q, k, a [H,T,dk]; v [H,T,dv]; beta [H,T] (all bf16 or all float32);
+    cu_seqlens int32 GPU tensor [N+1] of document boundaries (0 ... T).  Each document
+    runs from its own state: initial_state / final_state are float32 [N,H,dv,dk].
+    Returns out [H,T,dv] (and the final states when asked for)."""
+    dtype = q.dtype
+    if dtype not in _DTYPES:
+        raise ValueError("unsupported dtype %s" % dtype)
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (a, "a"), (beta, "beta")):
+        _check(t, n, dtype, dev)
+    _check(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    H, T, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or a.shape != q.shape or v.shape != (H, T, dv) or beta.shape != (H, T) or \
+            cu_seqlens.dim() != 1:
+        raise ValueError("shape mismatch")
+    N = cu_seqlens.numel() - 1
+    if out is None:
+        out = torch.empty((H, T, dv), dtype=dtype, device=dev)
+    _check(out, "out", dtype, dev)
+    if final_state is None and return_final_state:
+        final_state = torch.empty((N, H, dv, dk), dtype=torch.float32, device=dev)
+    for t, n in ((final_state, "final_state"), (initial_state, "initial_state")):
+        if t is not None:
+            _check(t, n, torch.float32, dev)
+            if tuple(t.shape) != (N, H, dv, dk):
+                raise ValueError("%s must be [N,H,dv,dk]" % n)
+    need = varlen_workspace_bytes(N, H, T, dk, dv, chunk, dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check(workspace, "workspace", torch.uint8, dev)
+    if counts is not None:
+        _check(counts, "counts", torch.int64, dev)
+    st = lib().kda_chunk_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(beta), float(g_min), int(chunk),
+                                    _ptr(cu_seqlens), N, H, T, dk, dv, _DTYPES[dtype], _ptr(out), _ptr(final_state),
+                                    _ptr(workspace), workspace.numel(), _stream(stream), GATE_MODES[gate],
+                                    _ptr(counts), _ptr(initial_state))
+    if st != KDA_OK:
+        raise KdaError("kda_chunk_fwd_varlen", st)
+    if return_final_state:
+        return out, final_state
+    return out
 
 
 def decode_step(q, k, v, a, beta, state, g_min=-5.0, gate="bounded", out=None, stream=None):

@@ -119,6 +119,62 @@ int fwd_impl(const void *q, const void *k, const void *v, const void *a, const v
                       counts, init_state, true);
 }
 
+// Packed documents: chunk records per head (an upper bound on the chunks the documents
+// can need, whatever cu_seqlens holds), and where the plan tables start.
+struct VarlenSizes {
+    long long ncmax;
+    size_t plan_offset, total;
+};
+
+int check_varlen(int N, int H, int T, int dk, int dv, int chunk, int io, VarlenSizes *vs) {
+    if (io != KDA_BF16 && io != KDA_FP32) return KDA_ERR_DTYPE;
+    if (chunk != 16 && chunk != 32 && chunk != 64) return KDA_ERR_CHUNK;
+    if (N < 1 || H < 1 || T < 0) return KDA_ERR_SHAPE;
+    if ((dk != 64 && dk != 128) || (dv != 64 && dv != 128)) return KDA_ERR_SHAPE;
+    if (H > 65535) return KDA_ERR_SHAPE;
+    const long long ncmax = (long long)(T / chunk) + N;
+    if (ncmax > 2147483647LL - 1024) return KDA_ERR_SHAPE;
+    if ((long long)N * H * (dv / 16) + 8LL * (dv / 16) > 2147483647LL) return KDA_ERR_SHAPE;  // state grid
+    const double elems = (double)H * (double)T * (dk > dv ? dk : dv);
+    if (elems >= 1099511627776.0) return KDA_ERR_SHAPE;  // 2^40
+    const KdaLayout L = kda_layout(chunk, dk, dv, io == KDA_FP32 ? 4 : 2);
+    vs->ncmax = ncmax;
+    vs->plan_offset = (size_t)H * (size_t)ncmax * L.stride;
+    vs->total = vs->plan_offset + 8 * ((size_t)N + 1) + 8 * (size_t)ncmax;
+    return KDA_OK;
+}
+
+int varlen_impl(const void *q, const void *k, const void *v, const void *a, const void *beta, float g_min,
+                int chunk, const int *cu_seqlens, int N, int H, int T, int dk, int dv, int io, void *out,
+                float *final_state, void *workspace, size_t workspace_bytes_given, hipStream_t stream,
+                int gate_mode, unsigned long long *counts, const float *init_state) {
+    VarlenSizes vs;
+    int st = check_varlen(N, H, T, dk, dv, chunk, io, &vs);
+    if (st != KDA_OK) return st;
+    st = check_gate(g_min, gate_mode);
+    if (st != KDA_OK) return st;
+    if (!cu_seqlens || !workspace) return KDA_ERR_NULL;
+    if (T > 0 && (!q || !k || !v || !a || !beta || !out)) return KDA_ERR_NULL;  // empty arrays may be NULL
+    const size_t esz = io == KDA_FP32 ? 4 : 2;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(a, 16) || !aligned(beta, esz) ||
+        !aligned(out, 16) || !aligned(cu_seqlens, 4) || !aligned(workspace, 16) ||
+        (final_state && !aligned(final_state, 16)) || (init_state && !aligned(init_state, 16)) ||
+        (counts && !aligned(counts, 8)))
+        return KDA_ERR_ALIGN;
+    if (workspace_bytes_given < vs.total) return KDA_ERR_WORKSPACE;
+    kda::LaunchArgs p{};
+    p.q = q; p.k = k; p.v = v; p.a = a; p.beta = beta;
+    p.g_min = g_min;
+    p.logsig = gate_mode == KDA_GATE_LOGSIGMOID;
+    p.chunk = chunk; p.B = 1; p.H = H; p.T = T; p.dk = dk; p.dv = dv;
+    p.fp32 = io == KDA_FP32;
+    p.out = out; p.final_state = final_state; p.init_state = init_state;
+    p.workspace = workspace; p.counts = counts; p.stream = stream;
+    p.cu = cu_seqlens; p.nseq = N; p.ncmax = (int)vs.ncmax; p.plan_offset = vs.plan_offset;
+    if (kda::launch_intra(p) != hipSuccess) return KDA_ERR_HIP;
+    return kda::launch_state(p) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -129,7 +185,7 @@ const char *kda_status_string(int status) {
     switch (status) {
     case KDA_OK: return "ok";
     case KDA_ERR_NULL: return "a required pointer is NULL";
-    case KDA_ERR_SHAPE: return "unsupported shape (dk, dv in {64,128}; B, H >= 1; T >= 0; T % chunk == 0)";
+    case KDA_ERR_SHAPE: return "unsupported shape (dk, dv in {64,128}; B, H, N >= 1; T >= 0; T % chunk == 0 unless packed)";
     case KDA_ERR_DTYPE: return "io_dtype must be KDA_BF16 or KDA_FP32";
     case KDA_ERR_CHUNK: return "chunk must be 16, 32 or 64";
     case KDA_ERR_GMIN: return "g_min must be finite with KDA_G_MIN_LOWEST <= g_min < 0";
@@ -191,6 +247,21 @@ int kda_chunk_state(const void *workspace, size_t workspace_bytes_given, int chu
                     unsigned long long *nonfinite_counts, const float *initial_state) {
     return state_impl(workspace, workspace_bytes_given, chunk, B, H, T, dk, dv, io_dtype, out, final_state, stream,
                       nonfinite_counts, initial_state, true);
+}
+
+size_t kda_chunk_fwd_varlen_workspace_bytes(int N, int H, int T, int dk, int dv, int chunk, int io_dtype) {
+    VarlenSizes vs;
+    if (check_varlen(N, H, T, dk, dv, chunk, io_dtype, &vs) != KDA_OK) return 0;
+    return vs.total;
+}
+
+int kda_chunk_fwd_varlen(const void *q, const void *k, const void *v, const void *a, const void *beta,
+                         float g_min, int chunk, const int *cu_seqlens, int N, int H, int T, int dk, int dv,
+                         int io_dtype, void *out, float *final_state, void *workspace, size_t workspace_bytes_given,
+                         hipStream_t stream, int gate_mode, unsigned long long *nonfinite_counts,
+                         const float *initial_state) {
+    return varlen_impl(q, k, v, a, beta, g_min, chunk, cu_seqlens, N, H, T, dk, dv, io_dtype, out, final_state,
+                       workspace, workspace_bytes_given, stream, gate_mode, nonfinite_counts, initial_state);
 }
 
 int kda_decode_step(const void *q, const void *k, const void *v, const void *a, const void *beta, float g_min,

@@ -303,19 +303,23 @@ struct GateScan {
     static_assert(C % 16 == 0 && DK % VEC == 0, "chunk and channel tiling");
     uint4 raw[NPASS][RPL];
 
-    // a: this chunk's [C][DK] block
-    __device__ __forceinline__ void load(const E *__restrict__ a, int tid) {
+    // a: this chunk's [C][DK] block, of which the first nrow rows are tokens (the others are
+    // never read: their loads repeat the last token row)
+    __device__ __forceinline__ void load(const E *__restrict__ a, int tid, int nrow) {
         const int rg = tid >> 4, m = tid & 15;
 #pragma unroll
         for (int p = 0; p < NPASS; ++p) {
             const int gi = rg + 16 * p, gc = gi < NG ? gi : NG - 1;  // clamped: loads stay in bounds
 #pragma unroll
-            for (int j = 0; j < RPL; ++j)
-                raw[p][j] = *reinterpret_cast<const uint4 *>(a + (size_t)(m * RPL + j) * DK + gc * VEC);
+            for (int j = 0; j < RPL; ++j) {
+                const int r = m * RPL + j;
+                raw[p][j] = *reinterpret_cast<const uint4 *>(a + (size_t)(r < nrow ? r : nrow - 1) * DK + gc * VEC);
+            }
         }
     }
 
-    __device__ __forceinline__ void finish(float gmin2, int logsig, float *sG, int ldG, int tid) {
+    // G over the chunk; rows from nrow on get g = 0, so G stays flat past the last token
+    __device__ __forceinline__ void finish(float gmin2, int logsig, float *sG, int ldG, int tid, int nrow) {
         const int rg = tid >> 4, m = tid & 15;
 #pragma unroll
         for (int p = 0; p < NPASS; ++p) {
@@ -326,7 +330,8 @@ struct GateScan {
             for (int j = 0; j < RPL; ++j) {
                 const E *e = reinterpret_cast<const E *>(&raw[p][j]);
 #pragma unroll
-                for (int c = 0; c < VEC; ++c) gv[j][c] = gate_log2(to_f(e[c]), gmin2, logsig) + (j ? gv[j - 1][c] : 0.f);
+                for (int c = 0; c < VEC; ++c)
+                    gv[j][c] = (m * RPL + j < nrow ? gate_log2(to_f(e[c]), gmin2, logsig) : 0.f) + (j ? gv[j - 1][c] : 0.f);
             }
 #pragma unroll
             for (int c = 0; c < VEC; ++c) {

@@ -67,7 +67,10 @@ struct IntraCfg {
     static constexpr int MAXCT = (NDK + 3) / 4;  // dk tiles per wave
 };
 
-template <int C, int DK, int DV, bool F32>
+// VL: packed documents (kda_varlen.h).  Work-group x then takes chunk x of the chunk
+// table ctab (records at head * NCmax + x); a chunk with fewer than C rows is padded with
+// zero q, k, beta and a zero gate, and a table entry with no rows ends the work-group.
+template <int C, int DK, int DV, bool F32, bool VL>
 __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void kda_intra_kernel(
     const typename IntraCfg<C, DK, DV, F32>::E *__restrict__ q,
     const typename IntraCfg<C, DK, DV, F32>::E *__restrict__ k,
@@ -75,7 +78,7 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     const typename IntraCfg<C, DK, DV, F32>::E *__restrict__ a,
     const typename IntraCfg<C, DK, DV, F32>::E *__restrict__ beta,
     float gmin2, int logsig, int H, int T, unsigned char *__restrict__ ws,
-    unsigned long long *__restrict__ counts)
+    unsigned long long *__restrict__ counts, const int2 *__restrict__ ctab, int NCmax)
 {
     using Cfg = IntraCfg<C, DK, DV, F32>;
     using E = typename Cfg::E;
@@ -104,10 +107,20 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: branches on it stay scalar
     const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int NC = T / C;
     const size_t head = (size_t)b * H + h;
-    const size_t tok0 = head * (size_t)T + (size_t)n * C;
-    unsigned char *rec = ws + ((size_t)head * NC + n) * L.stride;
+    size_t tok0, recno;
+    int nrow = C;  // rows of the chunk that are tokens (compile-time C unless packed)
+    if constexpr (VL) {
+        const int2 ce = ctab[n];  // same address in every lane: a uniform value
+        if (ce.y <= 0) return;    // past the last chunk of the batch
+        nrow = ce.y < C ? ce.y : C;
+        tok0 = head * (size_t)T + (size_t)ce.x;
+        recno = head * (size_t)NCmax + n;
+    } else {
+        tok0 = head * (size_t)T + (size_t)n * C;
+        recno = head * (size_t)(T / C) + n;
+    }
+    unsigned char *rec = ws + recno * L.stride;
     OH *wWT = reinterpret_cast<OH *>(rec + L.wt);
     OH *wQB = reinterpret_cast<OH *>(rec + L.qbt);
     OH *wKH = reinterpret_cast<OH *>(rec + L.kh);
@@ -122,14 +135,15 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
         constexpr int LPR = DK / VEC, RPP = 256 / LPR, NP = (C + RPP - 1) / RPP;
         const E *qg = q + tok0 * DK, *kg = k + tok0 * DK;
         GateScan<C, DK, E> gate;
-        gate.load(a + tok0 * DK, tid);
-        // loads are unconditional (row indices clamped into the chunk); only the stores are guarded
+        gate.load(a + tok0 * DK, tid, nrow);
+        // loads are unconditional (row indices clamped into the chunk's tokens); only the
+        // stores are guarded, and rows past the tokens of a short chunk are stored as zeros
         uint4 xq[NP], xk[NP];
-        const E bv = beta[tok0 + (tid < C ? tid : C - 1)];
+        const E bv = beta[tok0 + (tid < nrow ? tid : nrow - 1)];
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
             const int r = p * RPP + tid / LPR, c = (tid % LPR) * VEC;
-            const size_t off = (size_t)(r < C ? r : C - 1) * DK + c;
+            const size_t off = (size_t)(r < nrow ? r : nrow - 1) * DK + c;
             xq[p] = *reinterpret_cast<const uint4 *>(qg + off);
             xk[p] = *reinterpret_cast<const uint4 *>(kg + off);
         }
@@ -137,12 +151,18 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
         for (int p = 0; p < NP; ++p) {
             const int r = p * RPP + tid / LPR, c = (tid % LPR) * VEC;
             if (C % RPP == 0 || r < C) {
-                *reinterpret_cast<uint4 *>(sQ + r * PQ + c) = xq[p];
-                *reinterpret_cast<uint4 *>(sK + r * PQ + c) = xk[p];
+                uint4 yq = xq[p], yk = xk[p];
+                if constexpr (VL) {  // bit masks, not a select of the two arrays (which goes to scratch)
+                    const unsigned int mk = r < nrow ? 0xffffffffu : 0u;
+                    yq.x &= mk; yq.y &= mk; yq.z &= mk; yq.w &= mk;
+                    yk.x &= mk; yk.y &= mk; yk.z &= mk; yk.w &= mk;
+                }
+                *reinterpret_cast<uint4 *>(sQ + r * PQ + c) = yq;
+                *reinterpret_cast<uint4 *>(sK + r * PQ + c) = yk;
             }
         }
-        if (tid < C) sB[tid] = to_f(bv);
-        gate.finish(gmin2, logsig, sG, PG, tid);
+        if (tid < C) sB[tid] = (!VL || tid < nrow) ? to_f(bv) : 0.f;
+        gate.finish(gmin2, logsig, sG, PG, tid, nrow);
         __syncthreads();
     }
 
@@ -360,8 +380,10 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
         lds_u8 *sVb = lds_base(smem) + C * PA * 4;  // sV, LDS-typed
         for (int x = wave; x < C * NPR; x += 4) {
             const int r = x / NPR, part = x % NPR, off = part * 256 + lane * 4;
+            // rows past a short chunk's tokens repeat its last row (finite; beta = 0 there)
+            const int rs = (!VL || r < nrow) ? r : nrow - 1;
             if (off < RB)
-                __builtin_amdgcn_global_load_lds(vg + (size_t)r * RB + off,
+                __builtin_amdgcn_global_load_lds(vg + (size_t)rs * RB + off,
                                                  (lds_void *)(sVb + r * PV * Cfg::ES + part * 256), 4, 0, 0);
         }
     }

@@ -6,6 +6,7 @@
 #include "kda_intra.h"
 #include "kda_launch.h"
 #include "kda_state.h"
+#include "kda_varlen.h"
 
 namespace kda {
 
@@ -20,8 +21,8 @@ __global__ __launch_bounds__(256) void kda_gate_kernel(const typename std::condi
     __shared__ __attribute__((aligned(16))) float sG[C * PG];
     const size_t tok0 = ((size_t)blockIdx.z * H + blockIdx.y) * (size_t)T + (size_t)blockIdx.x * C;
     GateScan<C, DK, typename std::conditional<F32, float, __bf16>::type> gate;
-    gate.load(a + tok0 * DK, threadIdx.x);
-    gate.finish(gmin2, logsig, sG, PG, threadIdx.x);
+    gate.load(a + tok0 * DK, threadIdx.x, C);
+    gate.finish(gmin2, logsig, sG, PG, threadIdx.x, C);
     __syncthreads();
     float *o = G_out + tok0 * DK;
     constexpr int LPR = DK / 4, RPP = 256 / LPR;
@@ -45,27 +46,58 @@ static hipError_t launch_gate_t(const LaunchArgs &p) {
     return hipGetLastError();
 }
 
+// Packed documents (p.cu != NULL): the plan tables sit in the workspace after the records
+// (kda_varlen.h); B is 1 and T is the length of the packed stream.
+struct PlanPtrs {
+    int *bnd, *coff;
+    int2 *ctab;
+};
+static PlanPtrs plan_ptrs(const LaunchArgs &p) {
+    int *base = reinterpret_cast<int *>(reinterpret_cast<unsigned char *>(p.workspace) + p.plan_offset);
+    return PlanPtrs{base, base + p.nseq + 1, reinterpret_cast<int2 *>(base + 2 * (p.nseq + 1))};
+}
+
 template <int C, int DK, int DV, bool F32>
 static hipError_t launch_intra_t(const LaunchArgs &p) {
     using E = typename std::conditional<F32, float, __bf16>::type;
+    if (p.cu != nullptr) {
+        const PlanPtrs pl = plan_ptrs(p);
+        hipLaunchKernelGGL((kda_varlen_plan_kernel<C>), dim3(1), dim3(1024), 0, p.stream, p.cu, p.nseq, p.T, p.ncmax,
+                           pl.bnd, pl.coff, pl.ctab);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((kda_intra_kernel<C, DK, DV, F32, true>), dim3(p.ncmax, p.H, 1), dim3(256), 0, p.stream,
+                           reinterpret_cast<const E *>(p.q), reinterpret_cast<const E *>(p.k),
+                           reinterpret_cast<const E *>(p.v), reinterpret_cast<const E *>(p.a),
+                           reinterpret_cast<const E *>(p.beta), p.g_min * kLog2e, p.logsig, p.H, p.T,
+                           reinterpret_cast<unsigned char *>(p.workspace), p.counts, pl.ctab, p.ncmax);
+        return hipGetLastError();
+    }
     dim3 grid(p.T / C, p.H, p.B);
-    hipLaunchKernelGGL((kda_intra_kernel<C, DK, DV, F32>), grid, dim3(256), 0, p.stream,
+    hipLaunchKernelGGL((kda_intra_kernel<C, DK, DV, F32, false>), grid, dim3(256), 0, p.stream,
                        reinterpret_cast<const E *>(p.q), reinterpret_cast<const E *>(p.k),
                        reinterpret_cast<const E *>(p.v), reinterpret_cast<const E *>(p.a),
                        reinterpret_cast<const E *>(p.beta), p.g_min * kLog2e, p.logsig, p.H, p.T,
-                       reinterpret_cast<unsigned char *>(p.workspace), p.counts);
+                       reinterpret_cast<unsigned char *>(p.workspace), p.counts, nullptr, 0);
     return hipGetLastError();
 }
 
 template <int C, int DK, int DV, bool F32>
 static hipError_t launch_state_t(const LaunchArgs &p) {
     using E = typename std::conditional<F32, float, __bf16>::type;
-    const int BH = p.B * p.H;
+    const bool vl = p.cu != nullptr;
+    const int BH = vl ? p.nseq * p.H : p.B * p.H;  // units: (document, head) or (batch, head)
     const int groups = (BH + 7) / 8;
     dim3 grid(groups * 8 * (DV / 16));
-    hipLaunchKernelGGL((kda_state_kernel<C, DK, DV, F32>), grid, dim3(192), 0, p.stream,
-                       reinterpret_cast<const unsigned char *>(p.workspace), reinterpret_cast<E *>(p.out),
-                       p.final_state, p.init_state, BH, p.T, p.counts);
+    const PlanPtrs pl = vl ? plan_ptrs(p) : PlanPtrs{nullptr, nullptr, nullptr};
+    if (vl)
+        hipLaunchKernelGGL((kda_state_kernel<C, DK, DV, F32, true>), grid, dim3(192), 0, p.stream,
+                           reinterpret_cast<const unsigned char *>(p.workspace), reinterpret_cast<E *>(p.out),
+                           p.final_state, p.init_state, BH, p.T, p.counts, pl.bnd, pl.coff, p.H, p.ncmax);
+    else
+        hipLaunchKernelGGL((kda_state_kernel<C, DK, DV, F32, false>), grid, dim3(192), 0, p.stream,
+                           reinterpret_cast<const unsigned char *>(p.workspace), reinterpret_cast<E *>(p.out),
+                           p.final_state, p.init_state, BH, p.T, p.counts, nullptr, nullptr, p.H, 0);
     return hipGetLastError();
 }
 

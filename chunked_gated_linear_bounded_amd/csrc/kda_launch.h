@@ -18,6 +18,11 @@ struct LaunchArgs {
     float *G_out;
     unsigned long long *counts;
     hipStream_t stream;
+    // packed documents (NULL cu: fixed-length batch)
+    const int *cu;              // device cu_seqlens[nseq + 1]
+    int nseq;                   // documents
+    int ncmax;                  // chunk records per head: T / chunk + nseq
+    size_t plan_offset;         // byte offset of the plan tables in the workspace
 };
 
 hipError_t launch_intra(const LaunchArgs &p);  // chunk-parallel stage -> workspace

@@ -76,10 +76,15 @@ __device__ __forceinline__ void issue_record(lds_u8 *dst, const unsigned char *_
 }
 
 
-template <int C, int DK, int DV, bool F32>
+// VL: packed documents (kda_varlen.h).  Unit hb is then (document hb / H, head hb % H):
+// its chunks are records head * NCmax + coff[doc] ..., its tokens bnd[doc] .. bnd[doc + 1]
+// of the head's stream, and only the rows that are tokens are stored.  initial_state and
+// final_state are indexed by unit in both cases.
+template <int C, int DK, int DV, bool F32, bool VL>
 __global__ __launch_bounds__(192, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void kda_state_kernel(
     const unsigned char *__restrict__ ws, typename StateCfg<C, DK, DV, F32>::E *__restrict__ out,
-    float *final_state, const float *init_state, int BH, int T, unsigned long long *__restrict__ counts)
+    float *final_state, const float *init_state, int BH, int T, unsigned long long *__restrict__ counts,
+    const int *__restrict__ bnd, const int *__restrict__ coff, int H, int NCmax)
 {
     using Cfg = StateCfg<C, DK, DV, F32>;
     using E = typename Cfg::E;
@@ -100,8 +105,22 @@ __global__ __launch_bounds__(192, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     __shared__ __attribute__((aligned(1024))) unsigned char smem[Cfg::SMEM];
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
     const int wave = tid >> 6;
-    const int NC = T / C;
-    const unsigned char *rec0 = ws + (size_t)hb * NC * L.stride;
+    int NC, ntok;          // chunks and tokens of this unit
+    size_t row0;           // its first token in out
+    const unsigned char *rec0;
+    if constexpr (VL) {
+        const int doc = hb / H, h = hb % H;
+        const int t0 = bnd[doc], c0 = coff[doc], c1 = coff[doc + 1] < NCmax ? coff[doc + 1] : NCmax;
+        NC = c1 > c0 ? c1 - c0 : 0;
+        ntok = bnd[doc + 1] - t0;
+        row0 = (size_t)h * T + t0;
+        rec0 = ws + ((size_t)h * NCmax + c0) * L.stride;
+    } else {
+        NC = T / C;
+        ntok = T;
+        row0 = (size_t)hb * T;
+        rec0 = ws + (size_t)hb * NC * L.stride;
+    }
     const size_t soff = L.region1 + (size_t)slice * L.slice;
     const int j0 = 16 * slice;
 
@@ -332,12 +351,14 @@ __global__ __launch_bounds__(192, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                 for (int tt = 0; tt < NT; ++tt) O[tt] = mma(So[kb], qb[kb][tt], O[tt]);
-            const size_t trow = (size_t)hb * T + (size_t)n * C;
+            const size_t trow = row0 + (size_t)n * C;
+            const int nval = ntok - n * C;  // rows of this chunk that are tokens (>= C unless packed)
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt) {
                 f32x4 o;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) o[i] = fmaf(O[tt][i], unO, oi[tt][i] * unI);
+                if (VL && 16 * tt + l16 >= nval) continue;
                 // lane holds out[token 16 tt + l16][value j0 + 4g + i]
                 E *op = out + (trow + 16 * tt + l16) * DV + j0 + 4 * g;
                 if constexpr (F32) {

@@ -1,0 +1,86 @@
+// Packed sequences: several documents of different lengths laid end to end in one
+// token stream, each run through the recurrence from its own initial state with
+// nothing carried across a document boundary (packing many short documents into
+// one long training sequence: "Breaking Through Trillion-Parameter Multimodal MoE:
+// Key Innovations from Ultra-Long Context to Extreme Sparsity", sec. 3, the
+// 256K-1M context phase).
+//
+// Document i covers tokens [cu[i], cu[i+1]) of the stream.  It is cut into
+// ceil(len_i / C) chunks; the last one may be short.  A short chunk is padded to
+// C rows with q = k = 0, beta = 0 and g = 0, which leaves every product of the
+// chunk form exactly what the shorter chunk gives (zero rows and columns of A and
+// M, identity rows of T, a flat prefix sum G so e^(G_last) is the decay up to the
+// last real row), and the padded rows' outputs are not stored.
+//
+// The plan kernel below turns cu into the tables both stages index by; it runs as
+// one work-group ahead of them on the same stream:
+//   bnd[i]  (i = 0..N)    document boundaries, made nondecreasing and clipped to [0, T]
+//   coff[i] (i = 0..N)    index of document i's first chunk; coff[N] = chunks in use
+//   ctab[j] (j < NCmax)   {first token, rows} of chunk j; rows = 0 past the last chunk
+// With the boundaries nondecreasing inside [0, T] the chunk count is at most
+// floor(T / C) + N = NCmax, the number of records the workspace holds, so no
+// content of cu can make a stage index outside its buffers.
+#pragma once
+#include "kda_device.h"
+
+namespace kda {
+
+// Inclusive scan over the work-group (sum, or maximum of nonnegative values); `total`
+// receives the reduction over all threads.
+template <bool MAX>
+__device__ __forceinline__ int block_scan(int x, int *red, int &total) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(x, d, 64);
+        if (lane >= d) x = MAX ? (x > y ? x : y) : x + y;
+    }
+    if (lane == 63) red[w] = x;
+    __syncthreads();
+    int before = 0;
+    total = 0;
+    for (int u = 0; u < nw; ++u) {
+        const int r = red[u];
+        if (u < w) before = MAX ? (before > r ? before : r) : before + r;
+        total = MAX ? (total > r ? total : r) : total + r;
+    }
+    __syncthreads();  // red is reused by the next scan
+    return MAX ? (before > x ? before : x) : before + x;
+}
+
+template <int C>
+__global__ __launch_bounds__(1024) void kda_varlen_plan_kernel(const int *__restrict__ cu, int N, int T, int NCmax,
+                                                              int *__restrict__ bnd, int *__restrict__ coff,
+                                                              int2 *__restrict__ ctab)
+{
+    __shared__ int red[16];
+    const int tid = threadIdx.x;
+    auto clip = [T](int x) { return x < 0 ? 0 : (x > T ? T : x); };
+    int cmax = 0, csum = 0;  // running maximum of the clipped boundaries; chunks of earlier tiles
+    for (int base = 0; base < N; base += 1024) {
+        const int i = base + tid;
+        const bool doc = i < N;
+        const int e0 = doc ? clip(cu[i]) : 0, e1 = doc ? clip(cu[i + 1]) : 0;
+        int tmax, tsum;
+        const int s0 = max(cmax, block_scan<true>(e0, red, tmax));  // start of document i
+        const int s1 = max(s0, e1);                                  // its end
+        const int len = doc ? s1 - s0 : 0;
+        const int nch = (len + C - 1) / C;
+        const int c0 = csum + block_scan<false>(nch, red, tsum) - nch;
+        if (doc) {
+            bnd[i] = s0;
+            coff[i] = c0;
+            for (int m = 0; m < nch; ++m)
+                if (c0 + m < NCmax) ctab[c0 + m] = make_int2(s0 + m * C, min(C, len - m * C));
+        }
+        cmax = max(cmax, tmax);
+        csum += tsum;
+    }
+    if (tid == 0) {
+        bnd[N] = max(cmax, clip(cu[N]));
+        coff[N] = min(csum, NCmax);
+    }
+    for (int j = csum + tid; j < NCmax; j += 1024) ctab[j] = make_int2(0, 0);
+}
+
+}  // namespace kda

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 2
+#define KDA_ABI_VERSION 3
 /* ln(smallest normal float) / 15: the most negative g_min for which 15 steps of
  * decay inside a 16-token tile stay in the normal exponent range. */
 #define KDA_G_MIN_LOWEST (-5.8224f)
@@ -156,6 +156,34 @@ int kda_chunk_intra(const void *q, const void *k, const void *v, const void *a, 
 int kda_chunk_state(const void *workspace, size_t workspace_bytes, int chunk, int B, int H, int T,
                     int dk, int dv, int io_dtype, void *out, float *final_state, hipStream_t stream,
                     unsigned long long *nonfinite_counts, const float *initial_state);
+
+/* Packed documents: N documents of any lengths laid end to end in one token
+ * stream per head, each run through the recurrence on its own -- from its own
+ * initial state, nothing carried across a boundary -- as when many short
+ * documents are packed into one long training sequence (third page, sec. 3,
+ * the 256K-1M phase).  Document i is tokens [cu_seqlens[i], cu_seqlens[i+1])
+ * of the stream:
+ *   q, k, a : [H][T][dk]     v, out : [H][T][dv]     beta : [H][T]   (io_dtype)
+ *   cu_seqlens : DEVICE pointer to N + 1 int32, nondecreasing, cu_seqlens[0] = 0,
+ *             cu_seqlens[N] = T (document lengths need not be multiples of chunk)
+ *   initial_state, final_state : [N][H][dv][dk] float32 (NULL: zero / not wanted),
+ *             indexed by document; they may be the same array
+ * T is the stream length and need not be a multiple of chunk; N >= 1.
+ * cu_seqlens is only read on the device (nothing synchronises with the host):
+ * its values are clipped to [0, T] and made nondecreasing there, so contents
+ * outside the contract cannot make a kernel access memory outside the
+ * arguments; they give unspecified results, and out rows of tokens that no
+ * document covers are not written.  workspace: at least
+ * kda_chunk_fwd_varlen_workspace_bytes(N, H, T, dk, dv, chunk, io_dtype) bytes
+ * (0 for an invalid problem).  Everything else (dtypes, g_min, gate_mode,
+ * nonfinite_counts, alignment, validation, asynchrony) as kda_chunk_fwd_ex;
+ * cu_seqlens must be 4-byte aligned. */
+size_t kda_chunk_fwd_varlen_workspace_bytes(int N, int H, int T, int dk, int dv, int chunk, int io_dtype);
+int kda_chunk_fwd_varlen(const void *q, const void *k, const void *v, const void *a, const void *beta,
+                         float g_min, int chunk, const int *cu_seqlens, int N, int H, int T, int dk,
+                         int dv, int io_dtype, void *out, float *final_state, void *workspace,
+                         size_t workspace_bytes, hipStream_t stream, int gate_mode,
+                         unsigned long long *nonfinite_counts, const float *initial_state);
 
 /* One token of the recurrence per (batch, head), the state updated in place
  * (decoding after a prefill; the constant-size state of the second page,

@@ -138,6 +138,38 @@ def make_inputs(w: Workload, device="cpu"):
     return out
 
 
+# Packed documents (short documents laid end to end in one long sequence, "Breaking
+# Through Trillion-Parameter Multimodal MoE ...", sec. 3, 256K-1M phase): document
+# lengths drawn log-uniformly in [lo, hi] from PCG64(SeedSequence([seed, 7])) until
+# they fill T, the last one cut to fit.  The token tensors are those of a B=1
+# workload of the same seed, with the batch axis dropped: [H, T, d].
+PACKED = Workload("packed64k", 1, 32, 65536, 128, 128, 64, "bf16", 4.0, False, 5)
+PACKED_LEN = (32, 4096)
+
+
+def packed_lengths(T, seed, lo=PACKED_LEN[0], hi=PACKED_LEN[1]):
+    """Document lengths (ints >= 1 unless T == 0) that sum to T."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 7])))
+    lens, total = [], 0
+    while total < T:
+        n = int(np.exp(rng.uniform(np.log(lo), np.log(hi + 1))))
+        n = max(1, min(n, T - total))
+        lens.append(n)
+        total += n
+    return lens
+
+
+def cu_seqlens(lengths):
+    """int32 boundaries [0, l0, l0 + l1, ...] of documents of the given lengths."""
+    return np.concatenate([[0], np.cumsum(np.asarray(lengths, dtype=np.int64))]).astype(np.int32)
+
+
+def make_packed_inputs(w: Workload, device="cpu"):
+    """Token tensors of a packed stream: q, k, a [H,T,dk]; v [H,T,dv]; beta [H,T]."""
+    assert w.B == 1
+    return {n: t[0] for n, t in make_inputs(w, device).items()}
+
+
 def head_slice(inputs, b, h, t_end=None):
     """float64 NumPy copies of one (b, h) head's inputs (first t_end tokens), with
     leading singleton B and H axes, for the oracle."""

@@ -83,3 +83,31 @@ def recurrent(q, k, v, a, beta, g_min=-5.0, gate="bounded", erase=True, S0=None)
     if rc != 0:
         raise RuntimeError("kda_oracle_recurrent failed with %d" % rc)
     return out, fin
+
+
+def recurrent_varlen(q, k, v, a, beta, cu_seqlens, g_min=-5.0, gate="bounded", S0=None):
+    """Packed documents: N documents laid end to end in one token stream per head
+    ("Breaking Through Trillion-Parameter Multimodal MoE ...", sec. 3: short
+    documents packed into one long sequence in the 256K-1M phase).  Read as: every
+    document is its own sequence of the recurrence -- it starts from its own state
+    (S0[i], else zero) and nothing crosses a document boundary.
+
+    Shapes: q, k, a [H,T,dk]; v [H,T,dv]; beta [H,T]; cu_seqlens [N+1] ints,
+    nondecreasing, cu_seqlens[0] = 0, cu_seqlens[N] = T; S0 [N,H,dv,dk] or None.
+    Returns (out [H,T,dv], final_state [N,H,dv,dk]) as float64 arrays.
+    """
+    q, k, v, a, beta = (_f64(x) for x in (q, k, v, a, beta))
+    cu = [int(x) for x in np.asarray(cu_seqlens).ravel()]
+    H, T, dk = q.shape
+    dv = v.shape[-1]
+    N = len(cu) - 1
+    assert N >= 1 and cu[0] == 0 and cu[-1] == T and all(x <= y for x, y in zip(cu, cu[1:]))
+    out = np.zeros((H, T, dv), dtype=np.float64)
+    fin = np.empty((N, H, dv, dk), dtype=np.float64)
+    for i in range(N):
+        s, e = cu[i], cu[i + 1]
+        o, f = recurrent(q[None, :, s:e], k[None, :, s:e], v[None, :, s:e], a[None, :, s:e], beta[None, :, s:e],
+                         g_min, gate, S0=None if S0 is None else _f64(S0)[i:i + 1])
+        out[:, s:e] = o[0]
+        fin[i] = f[0]
+    return out, fin

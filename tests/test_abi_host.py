@@ -27,13 +27,13 @@ def test_header_symbols_exported():
     names = _declared_functions()
     assert {"kda_abi_version", "kda_status_string", "kda_chunk_fwd_workspace_bytes",
             "kda_gate_cumsum", "kda_chunk_fwd", "kda_chunk_fwd_ex", "kda_chunk_intra", "kda_chunk_state",
-            "kda_decode_step"} <= set(names)
+            "kda_decode_step", "kda_chunk_fwd_varlen", "kda_chunk_fwd_varlen_workspace_bytes"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
 
 def test_version_and_strings():
-    assert kda.abi_version() == 2
+    assert kda.abi_version() == 3
     for st in (OK, E_NULL, E_SHAPE, E_DTYPE, E_CHUNK, E_GMIN, E_WS, E_HIP, E_ALIGN, E_MODE):
         s = kda.status_string(st)
         assert s and s != "unknown status"
@@ -128,3 +128,35 @@ def test_binding_rejects_host_tensors():
         kda.gate_cumsum(x, chunk=16)
     with pytest.raises(ValueError):
         kda.decode_step(x[:, :, 0], x[:, :, 0], x[:, :, 0], x[:, :, 0], torch.zeros(1, 1), torch.zeros(1, 1, 64, 64))
+    with pytest.raises(ValueError):
+        kda.chunk_fwd_varlen(x[0], x[0], x[0], x[0], torch.zeros(1, 64), torch.zeros(2, dtype=torch.int32))
+
+
+def test_varlen_workspace_bytes():
+    # records for T / chunk + N chunks per head (each document may end in a short chunk), then the
+    # plan tables: N + 1 boundaries, N + 1 chunk offsets, and a {token, rows} pair per chunk
+    rec = kda.workspace_bytes(1, 1, 64, 128, 128, 64, torch.bfloat16)
+    N, H, T = 76, 32, 65536
+    nc = T // 64 + N
+    assert kda.varlen_workspace_bytes(N, H, T, 128, 128, 64, torch.bfloat16) == H * nc * rec + 8 * (N + 1) + 8 * nc
+    assert kda.varlen_workspace_bytes(3, 2, 100, 64, 64, 16, torch.float32) > 0   # T need not divide by chunk
+    assert kda.varlen_workspace_bytes(0, 2, 100, 64, 64, 16, torch.float32) == 0  # no document
+    assert kda.varlen_workspace_bytes(3, 2, 100, 96, 64, 16, torch.float32) == 0
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=None), E_NULL), (dict(cu=None), E_NULL), (dict(ws=None), E_NULL), (dict(out=None), E_NULL),
+    (dict(io=2), E_DTYPE), (dict(chunk=8), E_CHUNK), (dict(N=0), E_SHAPE), (dict(H=0), E_SHAPE),
+    (dict(T=-1), E_SHAPE), (dict(dk=32), E_SHAPE), (dict(N=1 << 30), E_SHAPE),
+    (dict(g_min=-7.0), E_GMIN), (dict(mode=4), E_MODE),
+    (dict(cu=FAKE + 2), E_ALIGN), (dict(q=FAKE + 8), E_ALIGN), (dict(fs=FAKE + 8), E_ALIGN),
+    (dict(s0=FAKE + 4), E_ALIGN), (dict(wsb=100), E_WS),
+])
+def test_varlen_validation(kw, want):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, a=FAKE, beta=FAKE, g_min=-5.0, chunk=64, cu=FAKE, N=3, H=2, T=100, dk=128,
+             dv=128, io=0, out=FAKE, fs=None, ws=FAKE, wsb=1 << 40, mode=0, s0=None)
+    a.update(kw)
+    st = kda.lib().kda_chunk_fwd_varlen(a["q"], a["k"], a["v"], a["a"], a["beta"], a["g_min"], a["chunk"], a["cu"],
+                                        a["N"], a["H"], a["T"], a["dk"], a["dv"], a["io"], a["out"], a["fs"], a["ws"],
+                                        a["wsb"], None, a["mode"], None, a["s0"])
+    assert st == want

@@ -274,3 +274,69 @@ def test_sequence_split_continues_from_the_final_state(split):
     o2, f2 = reference.recurrent(q[:, :, s2], k[:, :, s2], v[:, :, s2], a[:, :, s2], b[:, :, s2], S0=f1)
     assert np.allclose(np.concatenate([o1, o2], axis=2), out, rtol=1e-12, atol=1e-13)
     assert np.allclose(f2, fin, rtol=1e-12, atol=1e-13)
+
+
+# ---------------------------------------------------------------- packed documents
+def _packed(lengths, rng, H=2, dk=6, dv=5):
+    T = int(sum(lengths))
+    q, k, v, a, b = _rand_case(1, H, T, dk, dv, rng, a_sigma=2.0)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    return q[0], k[0], v[0], a[0], b[0], cu
+
+
+def test_packed_first_token_of_every_document():
+    """From a zero state one token leaves S_1 = beta v k^T (the decayed zero state adds nothing), so
+    the first output of every document is beta (k . q) v and a one-token document ends in
+    beta v k^T (closed form): a state carried across a boundary, or a boundary off by one,
+    breaks it."""
+    rng = np.random.default_rng(41)
+    lengths = [5, 1, 7, 3, 1, 9]
+    q, k, v, a, b, cu = _packed(lengths, rng)
+    out, fin = native.recurrent_varlen(q, k, v, a, b, cu)
+    for i, s in enumerate(cu[:-1]):
+        kq = np.sum(k[:, s] * q[:, s], axis=-1)
+        assert np.allclose(out[:, s], (b[:, s] * kq)[:, None] * v[:, s], rtol=1e-13, atol=1e-15)
+        if lengths[i] == 1:
+            assert np.allclose(fin[i], b[:, s, None, None] * v[:, s, :, None] * k[:, s, None, :], rtol=1e-13,
+                               atol=1e-15)
+
+
+def test_packed_documents_do_not_interact():
+    """Changing one document's tokens changes nothing in the others, and reordering the documents
+    moves each one's outputs and final state along with it unchanged."""
+    rng = np.random.default_rng(42)
+    lengths = [6, 11, 4]
+    q, k, v, a, b, cu = _packed(lengths, rng)
+    out, fin = native.recurrent_varlen(q, k, v, a, b, cu)
+    q2, v2, a2 = q.copy(), v.copy(), a.copy()
+    q2[:, cu[1]:cu[2]] += 1.0
+    v2[:, cu[1]:cu[2]] *= -3.0
+    a2[:, cu[1]:cu[2]] += 2.0
+    out2, fin2 = native.recurrent_varlen(q2, k, v2, a2, b, cu)
+    for i in (0, 2):
+        assert np.array_equal(out2[:, cu[i]:cu[i + 1]], out[:, cu[i]:cu[i + 1]])
+        assert np.array_equal(fin2[i], fin[i])
+    assert not np.allclose(out2[:, cu[1]:cu[2]], out[:, cu[1]:cu[2]])
+    order = [2, 0, 1]
+    idx = np.concatenate([np.arange(cu[i], cu[i + 1]) for i in order])
+    cu3 = np.concatenate([[0], np.cumsum([lengths[i] for i in order])])
+    out3, fin3 = native.recurrent_varlen(q[:, idx], k[:, idx], v[:, idx], a[:, idx], b[:, idx], cu3)
+    assert np.allclose(out3, out[:, idx], rtol=1e-13, atol=1e-15)
+    assert np.allclose(fin3, fin[order], rtol=1e-13, atol=1e-15)
+
+
+def test_packed_empty_document_keeps_its_initial_state():
+    """A document with no tokens has no outputs and ends in the state it started from; with
+    beta = 0 everywhere every document's state only decays from its own initial state
+    (closed form S0[i] diag(e^{G}) with G summed over that document alone)."""
+    rng = np.random.default_rng(43)
+    lengths = [4, 0, 6]
+    q, k, v, a, _, cu = _packed(lengths, rng)
+    b = np.zeros(q.shape[:2])
+    S0 = rng.standard_normal((3, 2, 5, 6))
+    out, fin = native.recurrent_varlen(q, k, v, a, b, cu, S0=S0)
+    g = -5.0 / (1.0 + np.exp(-a))
+    assert np.array_equal(fin[1], S0[1])
+    for i in (0, 2):
+        G = np.sum(g[:, cu[i]:cu[i + 1]], axis=1)  # [H, dk]
+        assert np.allclose(fin[i], S0[i] * np.exp(G)[:, None, :], rtol=1e-12, atol=1e-14)
