@@ -215,6 +215,64 @@ def packed_bench(args):
                      "frac": alg / (ms * 1e-3) / PEAK_HBM, "bytes_per_step": alg}}), flush=True)
 
 
+def lowrank_bench(args):
+    """The 64k workload with the gate pre-activation formed in the chunk kernel from a rank-R factor
+    (kda_chunk_fwd_lowrank): one call per step, inputs resident in HBM.  Algorithmic bytes per
+    token-head: q, k, v, beta read and out written once, plus R/H factor values per token-head (h is
+    shared by the heads), with each chunk record written once and read once."""
+    import torch
+    import chunked_gated_linear_bounded_amd as kda
+    import kda_inputs as KI
+    w = KI.BY_NAME["64k"]
+    R = args.lowrank
+    dev = torch.device("cuda:0")
+    print("bench: generating %s inputs with a rank-%d gate factor" % (w.name, R), file=sys.stderr, flush=True)
+    inp = KI.make_inputs(w, device=dev)
+    del inp["a"]
+    lr = KI.make_lowrank_factors(w, R, device=dev)
+    ws = torch.empty(kda.workspace_bytes(w.B, w.H, w.T, w.dk, w.dv, w.chunk, w.torch_dtype), dtype=torch.uint8,
+                     device=dev)
+    out = torch.empty((w.B, w.H, w.T, w.dv), dtype=w.torch_dtype, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        kda.chunk_fwd_lowrank(inp["q"], inp["k"], inp["v"], lr["h"], lr["z"], lr["A_log"], inp["beta"], w.g_min,
+                              w.chunk, out=out, workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = e0.elapsed_time(e1) / args.steps
+    assert torch.isfinite(out.float()).all().item(), "non-finite output"
+    es = 2
+    th = w.B * w.H * w.T
+    bph = (2 * w.dk + 2 * w.dv) * es + es + R * es / w.H
+    alg = th * bph + 2 * ws.numel()
+    print(json.dumps({
+        "metric": "KDA chunked fwd tokens/s, gate pre-activation from a rank-%d factor (T=64K, H=32, d=128, bf16 I/O)"
+                  % R,
+        "value": w.B * w.T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "wall_ms_per_step": (t1 - t0) * 1e3 / args.steps,
+        "higher_is_better": True, "dtype": w.io, "data": "synthetic",
+        "config": {"workload": w.name + "-lowrank", "B": w.B, "H": w.H, "T": w.T, "dk": w.dk, "dv": w.dv,
+                   "chunk": w.chunk, "rank": R},
+        "mfma_peak_frac": (flops_per_token_head(w.dk, w.dv, w.chunk) + 2 * R * w.dk) * th / (ms * 1e-3)
+                          / PEAK_BF16_FLOPS,
+        "path": {"bytes_per_token_head": bph,
+                 "gbps_algorithmic": th * bph / (ms * 1e-3) / 1e9},
+        "roofline": {"kernel": "kda_chunk_fwd_lowrank (chunk stage + state stage)", "bound": "hbm",
+                     "achieved": alg / (ms * 1e-3) / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                     "frac": alg / (ms * 1e-3) / PEAK_HBM, "bytes_per_step": alg}}), flush=True)
+
+
 def cpu_baseline(inputs, w, seconds):
     """The float64 oracle on whole heads of the same workload until `seconds`
     have passed; returns whole-job tokens/s extrapolated from the sampled heads."""
@@ -254,12 +312,17 @@ def main():
                     help="instead of the chunked forward, time kda_decode_step on B sequences x 32 heads")
     ap.add_argument("--packed", action="store_true",
                     help="instead of the fixed-length workload, time kda_chunk_fwd_varlen on the 64k packed stream")
+    ap.add_argument("--lowrank", type=int, default=0, metavar="R",
+                    help="instead of reading a, form the gate pre-activation from a rank-R factor (64k workload)")
     args = ap.parse_args()
     if args.decode_batch > 0:
         decode_bench(args)
         return
     if args.packed:
         packed_bench(args)
+        return
+    if args.lowrank > 0:
+        lowrank_bench(args)
         return
     if args.traffic_from:
         if args.copy_calibration <= 0:

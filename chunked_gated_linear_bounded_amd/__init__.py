@@ -10,6 +10,7 @@ built, every entry point raises; there is no fallback.
     out2 = kda.chunk_fwd(q2, k2, v2, a2, beta2, initial_state=S)     # continue the sequence
     o_t = kda.decode_step(q_t, k_t, v_t, a_t, beta_t, S)               # one more token, S in place
     o = kda.chunk_fwd_varlen(q, k, v, a, beta, cu_seqlens)             # packed documents, [H,T,d]
+    o = kda.chunk_fwd_lowrank(q, k, v, h, z, A_log, beta)              # a = e^A (h z^T) in-kernel
     G = kda.gate_cumsum(a, g_min=-5.0, chunk=64)
 """
 from __future__ import annotations
@@ -59,6 +60,8 @@ def lib():
         L.kda_chunk_intra.restype = i
         L.kda_chunk_state.argtypes = [vp, sz] + [i] * 7 + [vp, vp, vp, vp, vp]
         L.kda_chunk_state.restype = i
+        L.kda_chunk_fwd_lowrank.argtypes = [vp] * 7 + [f] + [i] * 8 + [vp, vp, vp, sz, vp, i, vp, vp]
+        L.kda_chunk_fwd_lowrank.restype = i
         L.kda_chunk_fwd_varlen_workspace_bytes.argtypes = [i] * 7
         L.kda_chunk_fwd_varlen_workspace_bytes.restype = sz
         L.kda_chunk_fwd_varlen.argtypes = [vp] * 5 + [f, i, vp] + [i] * 6 + [vp, vp, vp, sz, vp, i, vp, vp]
@@ -200,6 +203,52 @@ def chunk_state(workspace, out, final_state=None, chunk=64, dk=None, stream=None
                                _ptr(out), _ptr(final_state), _stream(stream), _ptr(counts), _ptr(initial_state))
     if st != KDA_OK:
         raise KdaError("kda_chunk_state", st)
+
+
+def chunk_fwd_lowrank(q, k, v, h, z, A_log, beta, g_min=-5.0, chunk=64, out=None, final_state=None,
+                      return_final_state=False, initial_state=None, workspace=None, stream=None, gate="bounded",
+                      counts=None):
+    """Chunked forward with the gate pre-activation a = exp(A_log) * (h z^T) formed in the chunk
+    kernel: h [B,T,R] (shared by the heads), z [H,dk,R] in the I/O dtype, A_log [H,dk] float32;
+    q, k [B,H,T,dk], v [B,H,T,dv], beta [B,H,T].  Otherwise as chunk_fwd."""
+    dtype = q.dtype
+    if dtype not in _DTYPES:
+        raise ValueError("unsupported dtype %s" % dtype)
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (h, "h"), (z, "z"), (beta, "beta")):
+        _check(t, n, dtype, dev)
+    _check(A_log, "A_log", torch.float32, dev)
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    R = h.shape[-1]
+    if k.shape != q.shape or v.shape != (B, H, T, dv) or beta.shape != (B, H, T) or h.shape != (B, T, R) or \
+            z.shape != (H, dk, R) or A_log.shape != (H, dk):
+        raise ValueError("shape mismatch")
+    if out is None:
+        out = torch.empty((B, H, T, dv), dtype=dtype, device=dev)
+    _check(out, "out", dtype, dev)
+    if final_state is None and return_final_state:
+        final_state = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+    for t, n in ((final_state, "final_state"), (initial_state, "initial_state")):
+        if t is not None:
+            _check(t, n, torch.float32, dev)
+            if tuple(t.shape) != (B, H, dv, dk):
+                raise ValueError("%s must be [B,H,dv,dk]" % n)
+    need = workspace_bytes(B, H, T, dk, dv, chunk, dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check(workspace, "workspace", torch.uint8, dev)
+    if counts is not None:
+        _check(counts, "counts", torch.int64, dev)
+    st = lib().kda_chunk_fwd_lowrank(_ptr(q), _ptr(k), _ptr(v), _ptr(h), _ptr(z), _ptr(A_log), _ptr(beta),
+                                     float(g_min), int(chunk), B, H, T, dk, dv, R, _DTYPES[dtype], _ptr(out),
+                                     _ptr(final_state), _ptr(workspace), workspace.numel(), _stream(stream),
+                                     GATE_MODES[gate], _ptr(counts), _ptr(initial_state))
+    if st != KDA_OK:
+        raise KdaError("kda_chunk_fwd_lowrank", st)
+    if return_final_state:
+        return out, final_state
+    return out
 
 
 def varlen_workspace_bytes(N, H, T, dk, dv, chunk, dtype) -> int:

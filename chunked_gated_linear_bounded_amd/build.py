@@ -32,6 +32,7 @@ DEVICE = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-p
 # (source, output object, extra defines)
 UNITS = [
     ("kda_kernels.hip", "kda_kernels.o", []),
+    ("kda_kernels_lowrank.hip", "kda_kernels_lowrank.o", []),
     ("kda_abi.cpp", "kda_abi.o", []),
 ]
 

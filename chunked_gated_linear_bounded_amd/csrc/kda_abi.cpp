@@ -47,18 +47,29 @@ int check_ptrs_ws(int B, int H, int T, int dk, int dv, int chunk, int io, const 
     return KDA_OK;
 }
 
+// The gate pre-activation from a rank-R factor instead of the a tensor (NULL h: read a).
+struct LowRank {
+    bool on;
+    const void *h, *z;
+    const float *A;
+    int rank;
+};
+
 int intra_impl(const void *q, const void *k, const void *v, const void *a, const void *beta, float g_min,
                int chunk, int B, int H, int T, int dk, int dv, int io, void *workspace,
                size_t workspace_bytes_given, hipStream_t stream, int gate_mode, unsigned long long *counts,
-               bool launch) {
+               bool launch, const LowRank &lr = LowRank{false, nullptr, nullptr, nullptr, 0}) {
     int st = check_shape(B, H, T, dk, dv, chunk, io);
     if (st != KDA_OK) return st;
     st = check_gate(g_min, gate_mode);
     if (st != KDA_OK) return st;
-    if (T > 0 && (!q || !k || !v || !a || !beta)) return KDA_ERR_NULL;  // empty arrays may be NULL
+    const bool low = lr.on;
+    if (low && lr.rank != 16 && lr.rank != 32 && lr.rank != 64 && lr.rank != 128) return KDA_ERR_SHAPE;
+    if (T > 0 && (!q || !k || !v || !beta)) return KDA_ERR_NULL;  // empty arrays may be NULL
+    if (T > 0 && (low ? (!lr.h || !lr.z || !lr.A) : !a)) return KDA_ERR_NULL;
     const size_t esz = io == KDA_FP32 ? 4 : 2;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(a, 16) || !aligned(beta, esz) ||
-        (counts && !aligned(counts, 8)))
+        !aligned(lr.h, 16) || !aligned(lr.z, 16) || !aligned(lr.A, 4) || (counts && !aligned(counts, 8)))
         return KDA_ERR_ALIGN;
     st = check_ptrs_ws(B, H, T, dk, dv, chunk, io, workspace, workspace_bytes_given);
     if (st != KDA_OK || !launch || T == 0) return st;
@@ -69,6 +80,10 @@ int intra_impl(const void *q, const void *k, const void *v, const void *a, const
     p.chunk = chunk; p.B = B; p.H = H; p.T = T; p.dk = dk; p.dv = dv;
     p.fp32 = io == KDA_FP32;
     p.workspace = workspace; p.counts = counts; p.stream = stream;
+    if (low) {
+        p.a = nullptr;
+        p.lr_h = lr.h; p.lr_z = lr.z; p.lr_A = lr.A; p.rank = lr.rank;
+    }
     return kda::launch_intra(p) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
@@ -104,16 +119,17 @@ int state_impl(const void *workspace, size_t workspace_bytes_given, int chunk, i
 int fwd_impl(const void *q, const void *k, const void *v, const void *a, const void *beta, float g_min,
              int chunk, int B, int H, int T, int dk, int dv, int io, void *out, float *final_state,
              void *workspace, size_t workspace_bytes_given, hipStream_t stream, int gate_mode,
-             unsigned long long *counts, const float *init_state) {
+             unsigned long long *counts, const float *init_state,
+             const LowRank &lr = LowRank{false, nullptr, nullptr, nullptr, 0}) {
     // validate both stages before launching either
     int st = intra_impl(q, k, v, a, beta, g_min, chunk, B, H, T, dk, dv, io, workspace, workspace_bytes_given,
-                        stream, gate_mode, counts, false);
+                        stream, gate_mode, counts, false, lr);
     if (st != KDA_OK) return st;
     st = state_impl(workspace, workspace_bytes_given, chunk, B, H, T, dk, dv, io, out, final_state, stream,
                     counts, init_state, false);
     if (st != KDA_OK) return st;
     st = intra_impl(q, k, v, a, beta, g_min, chunk, B, H, T, dk, dv, io, workspace, workspace_bytes_given,
-                    stream, gate_mode, counts, true);
+                    stream, gate_mode, counts, true, lr);
     if (st != KDA_OK) return st;
     return state_impl(workspace, workspace_bytes_given, chunk, B, H, T, dk, dv, io, out, final_state, stream,
                       counts, init_state, true);
@@ -247,6 +263,16 @@ int kda_chunk_state(const void *workspace, size_t workspace_bytes_given, int chu
                     unsigned long long *nonfinite_counts, const float *initial_state) {
     return state_impl(workspace, workspace_bytes_given, chunk, B, H, T, dk, dv, io_dtype, out, final_state, stream,
                       nonfinite_counts, initial_state, true);
+}
+
+int kda_chunk_fwd_lowrank(const void *q, const void *k, const void *v, const void *h, const void *z,
+                          const float *A_log, const void *beta, float g_min, int chunk, int B, int H, int T, int dk,
+                          int dv, int rank, int io_dtype, void *out, float *final_state, void *workspace,
+                          size_t workspace_bytes_given, hipStream_t stream, int gate_mode,
+                          unsigned long long *nonfinite_counts, const float *initial_state) {
+    return fwd_impl(q, k, v, nullptr, beta, g_min, chunk, B, H, T, dk, dv, io_dtype, out, final_state, workspace,
+                    workspace_bytes_given, stream, gate_mode, nonfinite_counts, initial_state,
+                    LowRank{true, h, z, A_log, rank});
 }
 
 size_t kda_chunk_fwd_varlen_workspace_bytes(int N, int H, int T, int dk, int dv, int chunk, int io_dtype) {

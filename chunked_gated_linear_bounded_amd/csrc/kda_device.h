@@ -333,25 +333,54 @@ struct GateScan {
                 for (int c = 0; c < VEC; ++c)
                     gv[j][c] = (m * RPL + j < nrow ? gate_log2(to_f(e[c]), gmin2, logsig) : 0.f) + (j ? gv[j - 1][c] : 0.f);
             }
+            scan_store(gv, sG, ldG, gi, m);
+        }
+    }
+
+    // The same prefix sum when the per-row gate values g2 are already in sG (written there by
+    // the caller, every row of the chunk): G replaces them in place.
+    __device__ __forceinline__ static void scan_lds(float *sG, int ldG, int tid) {
+        const int rg = tid >> 4, m = tid & 15;
 #pragma unroll
-            for (int c = 0; c < VEC; ++c) {
-                const float own = gv[RPL - 1][c];
-                float t = own;  // inclusive prefix of the lane totals over m
-                t += dpp_row_shr<1>(t);
-                t += dpp_row_shr<2>(t);
-                t += dpp_row_shr<4>(t);
-                t += dpp_row_shr<8>(t);
-                const float before = t - own;
-#pragma unroll
-                for (int j = 0; j < RPL; ++j) gv[j][c] += before;
-            }
+        for (int p = 0; p < NPASS; ++p) {
+            const int gi = rg + 16 * p;
+            if (gi >= NG) continue;
+            float gv[RPL][VEC];
 #pragma unroll
             for (int j = 0; j < RPL; ++j) {
-                float *dst = sG + (m * RPL + j) * ldG + gi * VEC;
+                const float *src = sG + (m * RPL + j) * ldG + gi * VEC;
 #pragma unroll
-                for (int c = 0; c < VEC; c += 4)
-                    *reinterpret_cast<f32x4 *>(dst + c) = f32x4{gv[j][c], gv[j][c + 1], gv[j][c + 2], gv[j][c + 3]};
+                for (int c = 0; c < VEC; c += 4) {
+                    const f32x4 x = *reinterpret_cast<const f32x4 *>(src + c);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) gv[j][c + i] = x[i] + (j ? gv[j - 1][c + i] : 0.f);
+                }
             }
+            scan_store(gv, sG, ldG, gi, m);
+        }
+    }
+
+    // gv holds this lane's rows already summed within the lane; add the totals of the lanes
+    // before it in the row group (inclusive DPP scan) and store G.
+    __device__ __forceinline__ static void scan_store(float (&gv)[RPL][VEC], float *sG, int ldG, int gi, int m) {
+#pragma unroll
+        for (int c = 0; c < VEC; ++c) {
+            const float own = gv[RPL - 1][c];
+            float t = own;  // inclusive prefix of the lane totals over m
+            t += dpp_row_shr<1>(t);
+            t += dpp_row_shr<2>(t);
+            t += dpp_row_shr<4>(t);
+            t += dpp_row_shr<8>(t);
+            const float before = t - own;
+#pragma unroll
+            for (int j = 0; j < RPL; ++j) gv[j][c] += before;
+        }
+#pragma unroll
+        for (int j = 0; j < RPL; ++j) {
+            float *dst = sG + (m * RPL + j) * ldG + gi * VEC;
+#pragma unroll
+            for (int c = 0; c < VEC; c += 4)
+                *reinterpret_cast<f32x4 *>(dst + c) = f32x4{gv[j][c], gv[j][c + 1], gv[j][c + 2], gv[j][c + 3]};
         }
     }
 };

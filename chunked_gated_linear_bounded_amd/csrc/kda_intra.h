@@ -67,10 +67,93 @@ struct IntraCfg {
     static constexpr int MAXCT = (NDK + 3) / 4;  // dk tiles per wave
 };
 
+// Gate pre-activation of one 16-row tile from a rank-R factor, on MFMA:
+//   a[r][c] = e^{A[c]} sum_j h[r][j] z[c][j],   g2[r][c] = gate(a[r][c]) in log2 units -> sG
+// (the pre-activation e^A h z of "Trillion-Scale MoE Multimodal Models: Practical Techniques
+// ...", sec. 3.2, with h a rank-R factor per token and z the per-head map from it to the key
+// channels).  This product is private to the tile, so its operands use their own K-slot order:
+// slot j of lane group g is k = 32 kb + 8 g + j, eight contiguous values, one 16-byte load per
+// fragment straight from global memory.  load() only issues the loads (all of them, so the
+// caller can put its own loads behind them); finish() runs the MFMAs, the scale and the gate.
+// R = 16 is half a K-block: lane groups 2 and 3 of the h operand are zero.
+template <int DK, typename E, int R>
+struct LowRankTile {
+    static_assert(R == 16 || R % 32 == 0, "rank 16 or a multiple of 32");
+    static constexpr int NDK = DK / 16, NKB = (R + 31) / 32;
+    // operands held from load() to finish() only while they fit in 128 registers (fp32 at rank
+    // 128 would need 256); otherwise finish() loads them one K-block at a time
+    static constexpr bool PRE = NKB * NDK * (int)sizeof(Frag<E>) <= 128 * 4;
+    static constexpr int NKP = PRE ? NKB : 1;
+    Frag<E> fa[NKP], fb[NKP][NDK];
+    const E *hp = nullptr, *zp = nullptr;
+
+    __device__ __forceinline__ static Frag<E> ld8(const E *p) {
+        if constexpr (std::is_same<E, float>::value) {
+            return Frag<float>::load2(p, p + 4);
+        } else {
+            Frag<E> f;
+            f.v = *reinterpret_cast<const typename VecOf<E>::v8 *>(p);
+            return f;
+        }
+    }
+
+    __device__ __forceinline__ void load_kb(int slot, int kb) {
+        fa[slot] = ld8(hp + 32 * kb);
+#pragma unroll
+        for (int ct = 0; ct < NDK; ++ct) fb[slot][ct] = ld8(zp + (size_t)16 * ct * R + 32 * kb);
+    }
+
+    // h: the tile's first row, pitch R; z: [DK][R]
+    __device__ __forceinline__ void load(const E *__restrict__ h, const E *__restrict__ z, int lane) {
+        const int g = lane >> 4, l16 = lane & 15;
+        const int kg = (R == 16 && g >= 2) ? 8 * (g - 2) : 8 * g;  // R = 16: groups 2, 3 reread (then zeroed)
+        hp = h + (size_t)l16 * R + kg;
+        zp = z + (size_t)l16 * R + kg;
+        if constexpr (PRE) {
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) load_kb(kb, kb);
+        }
+    }
+
+    // MFMAs, scale and gate; g2 of the tile's 16 rows to sG (the caller then runs the prefix sum
+    // over the chunk's rows from LDS)
+    __device__ __forceinline__ void finish(const float *__restrict__ A, float gmin2, int logsig, float *sG, int ldG,
+                                           int row0, int lane) {
+        const int g = lane >> 4, l16 = lane & 15;
+        if constexpr (R == 16) {
+            if (g >= 2) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    if constexpr (std::is_same<E, float>::value) fa[0].v[j] = 0.f;
+                    else fa[0].v[j] = (E)0.f;
+                }
+            }
+        }
+        f32x4 acc[NDK];
+#pragma unroll
+        for (int ct = 0; ct < NDK; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            if constexpr (!PRE) load_kb(0, kb);
+#pragma unroll
+            for (int ct = 0; ct < NDK; ++ct) acc[ct] = mma(fa[PRE ? kb : 0], fb[PRE ? kb : 0][ct], acc[ct]);
+        }
+#pragma unroll
+        for (int ct = 0; ct < NDK; ++ct) {
+            const int c = 16 * ct + l16;
+            const float eA = ex2(A[c] * kLog2e);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sG[(row0 + 4 * g + i) * ldG + c] = gate_log2(acc[ct][i] * eA, gmin2, logsig);
+        }
+    }
+};
+
 // VL: packed documents (kda_varlen.h).  Work-group x then takes chunk x of the chunk
 // table ctab (records at head * NCmax + x); a chunk with fewer than C rows is padded with
 // zero q, k, beta and a zero gate, and a table entry with no rows ends the work-group.
-template <int C, int DK, int DV, bool F32, bool VL>
+// LRK > 0: the gate pre-activation is formed from lrh [B][T][LRK] (shared by the heads), lrz
+// [H][DK][LRK] and lrA [H][DK] (LowRankTile) instead of being read from a.
+template <int C, int DK, int DV, bool F32, bool VL, int LRK>
 __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void kda_intra_kernel(
     const typename IntraCfg<C, DK, DV, F32>::E *__restrict__ q,
     const typename IntraCfg<C, DK, DV, F32>::E *__restrict__ k,
@@ -78,8 +161,12 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     const typename IntraCfg<C, DK, DV, F32>::E *__restrict__ a,
     const typename IntraCfg<C, DK, DV, F32>::E *__restrict__ beta,
     float gmin2, int logsig, int H, int T, unsigned char *__restrict__ ws,
-    unsigned long long *__restrict__ counts, const int2 *__restrict__ ctab, int NCmax)
+    unsigned long long *__restrict__ counts, const int2 *__restrict__ ctab, int NCmax,
+    const typename IntraCfg<C, DK, DV, F32>::E *__restrict__ lrh,
+    const typename IntraCfg<C, DK, DV, F32>::E *__restrict__ lrz, const float *__restrict__ lrA)
 {
+    constexpr bool LR = LRK > 0;
+    static_assert(!(VL && LR), "packed documents take the gate pre-activation as input");
     using Cfg = IntraCfg<C, DK, DV, F32>;
     using E = typename Cfg::E;
     using OW = typename std::conditional<F32, float, __bf16>::type;    // MFMA operands here
@@ -135,7 +222,13 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
         constexpr int LPR = DK / VEC, RPP = 256 / LPR, NP = (C + RPP - 1) / RPP;
         const E *qg = q + tok0 * DK, *kg = k + tok0 * DK;
         GateScan<C, DK, E> gate;
-        gate.load(a + tok0 * DK, tid, nrow);
+        LowRankTile<DK, E, LR ? LRK : 16> lrt;  // its loads go first: its MFMAs need nothing else
+        if constexpr (LR) {
+            if (wave < NT)
+                lrt.load(lrh + ((size_t)b * T + (size_t)n * C + 16 * wave) * LRK, lrz + (size_t)h * DK * LRK, lane);
+        } else {
+            gate.load(a + tok0 * DK, tid, nrow);
+        }
         // loads are unconditional (row indices clamped into the chunk's tokens); only the
         // stores are guarded, and rows past the tokens of a short chunk are stored as zeros
         uint4 xq[NP], xk[NP];
@@ -146,6 +239,10 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
             const size_t off = (size_t)(r < nrow ? r : nrow - 1) * DK + c;
             xq[p] = *reinterpret_cast<const uint4 *>(qg + off);
             xk[p] = *reinterpret_cast<const uint4 *>(kg + off);
+        }
+        // the low-rank gate's MFMAs run while q, k and beta are still in flight
+        if constexpr (LR) {
+            if (wave < NT) lrt.finish(lrA + (size_t)h * DK, gmin2, logsig, sG, PG, 16 * wave, lane);
         }
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
@@ -162,7 +259,12 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
             }
         }
         if (tid < C) sB[tid] = (!VL || tid < nrow) ? to_f(bv) : 0.f;
-        gate.finish(gmin2, logsig, sG, PG, tid, nrow);
+        if constexpr (LR) {
+            __syncthreads();
+            GateScan<C, DK, E>::scan_lds(sG, PG, tid);
+        } else {
+            gate.finish(gmin2, logsig, sG, PG, tid, nrow);
+        }
         __syncthreads();
     }
 

@@ -66,19 +66,22 @@ static hipError_t launch_intra_t(const LaunchArgs &p) {
                            pl.bnd, pl.coff, pl.ctab);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((kda_intra_kernel<C, DK, DV, F32, true>), dim3(p.ncmax, p.H, 1), dim3(256), 0, p.stream,
-                           reinterpret_cast<const E *>(p.q), reinterpret_cast<const E *>(p.k),
+        hipLaunchKernelGGL((kda_intra_kernel<C, DK, DV, F32, true, 0>), dim3(p.ncmax, p.H, 1), dim3(256), 0,
+                           p.stream, reinterpret_cast<const E *>(p.q), reinterpret_cast<const E *>(p.k),
                            reinterpret_cast<const E *>(p.v), reinterpret_cast<const E *>(p.a),
                            reinterpret_cast<const E *>(p.beta), p.g_min * kLog2e, p.logsig, p.H, p.T,
-                           reinterpret_cast<unsigned char *>(p.workspace), p.counts, pl.ctab, p.ncmax);
+                           reinterpret_cast<unsigned char *>(p.workspace), p.counts, pl.ctab, p.ncmax, nullptr,
+                           nullptr, nullptr);
         return hipGetLastError();
     }
+    if (p.lr_h != nullptr) return launch_intra_lowrank(p);
     dim3 grid(p.T / C, p.H, p.B);
-    hipLaunchKernelGGL((kda_intra_kernel<C, DK, DV, F32, false>), grid, dim3(256), 0, p.stream,
+    hipLaunchKernelGGL((kda_intra_kernel<C, DK, DV, F32, false, 0>), grid, dim3(256), 0, p.stream,
                        reinterpret_cast<const E *>(p.q), reinterpret_cast<const E *>(p.k),
                        reinterpret_cast<const E *>(p.v), reinterpret_cast<const E *>(p.a),
                        reinterpret_cast<const E *>(p.beta), p.g_min * kLog2e, p.logsig, p.H, p.T,
-                       reinterpret_cast<unsigned char *>(p.workspace), p.counts, nullptr, 0);
+                       reinterpret_cast<unsigned char *>(p.workspace), p.counts, nullptr, 0, nullptr, nullptr,
+                       nullptr);
     return hipGetLastError();
 }
 

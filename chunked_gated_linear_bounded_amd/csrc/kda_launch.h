@@ -23,9 +23,14 @@ struct LaunchArgs {
     int nseq;                   // documents
     int ncmax;                  // chunk records per head: T / chunk + nseq
     size_t plan_offset;         // byte offset of the plan tables in the workspace
+    // gate pre-activation from a rank-`rank` factor (NULL lr_h: read from a)
+    const void *lr_h, *lr_z;    // [B][T][rank], [H][dk][rank] (I/O element type)
+    const float *lr_A;          // [H][dk]
+    int rank;                   // 16, 32, 64 or 128
 };
 
 hipError_t launch_intra(const LaunchArgs &p);  // chunk-parallel stage -> workspace
+hipError_t launch_intra_lowrank(const LaunchArgs &p);  // the same, gate pre-activation from lr_h, lr_z, lr_A
 hipError_t launch_state(const LaunchArgs &p);  // sequential stage: workspace -> out, final state
 hipError_t launch_gate_cumsum(const LaunchArgs &p);
 hipError_t launch_decode(const LaunchArgs &p);  // one token per head, state in place

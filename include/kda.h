@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 3
+#define KDA_ABI_VERSION 4
 /* ln(smallest normal float) / 15: the most negative g_min for which 15 steps of
  * decay inside a 16-token tile stay in the normal exponent range. */
 #define KDA_G_MIN_LOWEST (-5.8224f)
@@ -156,6 +156,23 @@ int kda_chunk_intra(const void *q, const void *k, const void *v, const void *a, 
 int kda_chunk_state(const void *workspace, size_t workspace_bytes, int chunk, int B, int H, int T,
                     int dk, int dv, int io_dtype, void *out, float *final_state, hipStream_t stream,
                     unsigned long long *nonfinite_counts, const float *initial_state);
+
+/* As kda_chunk_fwd_ex, with the gate pre-activation formed inside the chunk
+ * kernel from a rank-`rank` factor instead of being read from an a tensor:
+ *   a[b][h][t][c] = exp(A_log[h][c]) * sum_j h[b][t][j] * z[h][c][j]
+ * then g = g_min * sigmoid(a) as before (the gate e^A h z of the first page,
+ * sec. 3.2, with h the per-token low-rank gate input shared by all heads and z
+ * each head's map from it to the key channels).  The a tensor (dk values per
+ * token and head) is never materialised; h adds rank values per token.
+ *   h : [B][T][rank] (io_dtype)   z : [H][dk][rank] (io_dtype)   A_log : [H][dk] float32
+ * rank is 16, 32, 64 or 128.  h and z must be 16-byte aligned,
+ * A_log 4-byte aligned.  Workspace as kda_chunk_fwd_workspace_bytes(...).
+ * Everything else as kda_chunk_fwd_ex. */
+int kda_chunk_fwd_lowrank(const void *q, const void *k, const void *v, const void *h, const void *z,
+                          const float *A_log, const void *beta, float g_min, int chunk, int B, int H,
+                          int T, int dk, int dv, int rank, int io_dtype, void *out, float *final_state,
+                          void *workspace, size_t workspace_bytes, hipStream_t stream, int gate_mode,
+                          unsigned long long *nonfinite_counts, const float *initial_state);
 
 /* Packed documents: N documents of any lengths laid end to end in one token
  * stream per head, each run through the recurrence on its own -- from its own

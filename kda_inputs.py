@@ -32,7 +32,8 @@ from dataclasses import dataclass, replace
 import numpy as np
 import torch
 
-TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "a": 3, "beta": 4, "mix_mask": 5, "mix_sign": 6}
+TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "a": 3, "beta": 4, "mix_mask": 5, "mix_sign": 6,
+              "lr_h": 8, "lr_z": 9, "lr_A": 10}
 
 
 @dataclass(frozen=True)
@@ -168,6 +169,26 @@ def make_packed_inputs(w: Workload, device="cpu"):
     """Token tensors of a packed stream: q, k, a [H,T,dk]; v [H,T,dv]; beta [H,T]."""
     assert w.B == 1
     return {n: t[0] for n, t in make_inputs(w, device).items()}
+
+
+# Gate pre-activation from a rank-R factor: h [B,T,R] ~ N(0,1) (one slab per batch, shared by
+# the heads), z [H,dk,R] ~ N(0,1)/sqrt(R) (one slab per head), both rounded to the I/O dtype,
+# and A_log [H,dk] = ln(a_sigma) + 0.25 N(0,1) in float32, so that the pre-activation
+# e^A (h z) has about the workload's a_sigma spread.  Streams as above (ids 8, 9, 10).
+def make_lowrank_factors(w: Workload, rank: int, device="cpu"):
+    device = torch.device(device)
+    dt = w.torch_dtype
+    h = torch.empty((w.B, w.T, rank), dtype=dt, device=device)
+    z = torch.empty((w.H, w.dk, rank), dtype=dt, device=device)
+    A = torch.empty((w.H, w.dk), dtype=torch.float32, device=device)
+    draw = (lambda name, b, hh, n: torch.from_numpy(_draw_cpu(w.seed, name, b, hh, n)).to(device)) \
+        if device.type == "cpu" else (lambda name, b, hh, n: _draw_dev(w.seed, name, b, hh, n, device))
+    for b in range(w.B):
+        h[b] = draw("lr_h", b, 0, w.T * rank).view(w.T, rank).to(dt)
+    for hh in range(w.H):
+        z[hh] = (draw("lr_z", 0, hh, w.dk * rank).view(w.dk, rank) / np.sqrt(rank)).to(dt)
+        A[hh] = (np.log(w.a_sigma) + 0.25 * draw("lr_A", 0, hh, w.dk)).to(torch.float32)
+    return {"h": h, "z": z, "A_log": A}
 
 
 def head_slice(inputs, b, h, t_end=None):

@@ -20,6 +20,7 @@ The state convention is S (dv x dk):
 
 Functions here:
   gate                -- the two gate forms, float64
+  lowrank_preactivation -- the gate pre-activation from a rank-R factor
   recurrent           -- the same token recurrence as kda_oracle.c, vectorised
                          over rows (a second, independent transcription)
   brute_force         -- unrolled products of dense per-token transition matrices
@@ -46,6 +47,18 @@ def gate(a, g_min=G_MIN, mode="bounded"):
         # log sigmoid(a) = -softplus(-a), written so that no exp overflows
         return -(np.maximum(-a, 0.0) + np.log1p(np.exp(-np.abs(a))))
     raise ValueError(mode)
+
+
+def lowrank_preactivation(h, z, A_log):
+    """Gate pre-activation from a rank-R factor (the e^A h z of "Trillion-Scale MoE
+    Multimodal Models: Practical Techniques ...", sec. 3.2), read as
+        a[b, hd, t, c] = exp(A_log[hd, c]) * sum_j h[b, t, j] z[hd, c, j]
+    with h [B,T,R] the per-token low-rank gate input shared by all heads, z [H,dk,R] each
+    head's map from it to the key channels and A_log [H,dk] a per-channel log-scale.
+    Returns a [B,H,T,dk] float64, the input of gate()."""
+    h, z, A_log = _f64(h, z, A_log)
+    lin = np.matmul(h[:, None, :, :], np.swapaxes(z, 1, 2)[None, :, :, :])  # [B,H,T,dk]
+    return np.exp(A_log)[None, :, None, :] * lin
 
 
 def _f64(*xs):

@@ -27,13 +27,14 @@ def test_header_symbols_exported():
     names = _declared_functions()
     assert {"kda_abi_version", "kda_status_string", "kda_chunk_fwd_workspace_bytes",
             "kda_gate_cumsum", "kda_chunk_fwd", "kda_chunk_fwd_ex", "kda_chunk_intra", "kda_chunk_state",
-            "kda_decode_step", "kda_chunk_fwd_varlen", "kda_chunk_fwd_varlen_workspace_bytes"} <= set(names)
+            "kda_decode_step", "kda_chunk_fwd_varlen", "kda_chunk_fwd_varlen_workspace_bytes",
+            "kda_chunk_fwd_lowrank"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
 
 def test_version_and_strings():
-    assert kda.abi_version() == 3
+    assert kda.abi_version() == 4
     for st in (OK, E_NULL, E_SHAPE, E_DTYPE, E_CHUNK, E_GMIN, E_WS, E_HIP, E_ALIGN, E_MODE):
         s = kda.status_string(st)
         assert s and s != "unknown status"
@@ -159,4 +160,21 @@ def test_varlen_validation(kw, want):
     st = kda.lib().kda_chunk_fwd_varlen(a["q"], a["k"], a["v"], a["a"], a["beta"], a["g_min"], a["chunk"], a["cu"],
                                         a["N"], a["H"], a["T"], a["dk"], a["dv"], a["io"], a["out"], a["fs"], a["ws"],
                                         a["wsb"], None, a["mode"], None, a["s0"])
+    assert st == want
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(h=None), E_NULL), (dict(z=None), E_NULL), (dict(A=None), E_NULL), (dict(q=None), E_NULL),
+    (dict(rank=0), E_SHAPE), (dict(rank=8), E_SHAPE), (dict(rank=48), E_SHAPE), (dict(rank=256), E_SHAPE),
+    (dict(T=100), E_SHAPE), (dict(io=5), E_DTYPE), (dict(g_min=-9.0), E_GMIN), (dict(mode=3), E_MODE),
+    (dict(h=FAKE + 8), E_ALIGN), (dict(z=FAKE + 4), E_ALIGN), (dict(A=FAKE + 2), E_ALIGN), (dict(wsb=64), E_WS),
+    (dict(T=0, rank=24), E_SHAPE),
+])
+def test_lowrank_validation(kw, want):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, h=FAKE, z=FAKE, A=FAKE, beta=FAKE, g_min=-5.0, chunk=64, B=1, H=2, T=128,
+             dk=128, dv=128, rank=32, io=0, out=FAKE, fs=None, ws=FAKE, wsb=1 << 40, mode=0)
+    a.update(kw)
+    st = kda.lib().kda_chunk_fwd_lowrank(a["q"], a["k"], a["v"], a["h"], a["z"], a["A"], a["beta"], a["g_min"],
+                                         a["chunk"], a["B"], a["H"], a["T"], a["dk"], a["dv"], a["rank"], a["io"],
+                                         a["out"], a["fs"], a["ws"], a["wsb"], None, a["mode"], None, None)
     assert st == want

@@ -340,3 +340,39 @@ def test_packed_empty_document_keeps_its_initial_state():
     for i in (0, 2):
         G = np.sum(g[:, cu[i]:cu[i + 1]], axis=1)  # [H, dk]
         assert np.allclose(fin[i], S0[i] * np.exp(G)[:, None, :], rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------- low-rank gate pre-activation
+def test_lowrank_preactivation_hand_values():
+    """One token, rank 2, two channels, two heads, worked by hand:
+    head 0: z = [[3, -1], [0.5, 4]], A = [0, ln 2]:  a = [1*3 + 2*(-1), 2 * (1*0.5 + 2*4)] = [1, 17]
+    head 1: z = [[0, 1], [-2, 0]],   A = [ln 3, 0]:   a = [3 * 2, -2]"""
+    h = np.array([[[1.0, 2.0]]])
+    z = np.array([[[3.0, -1.0], [0.5, 4.0]], [[0.0, 1.0], [-2.0, 0.0]]])
+    A = np.array([[0.0, math.log(2.0)], [math.log(3.0), 0.0]])
+    a = reference.lowrank_preactivation(h, z, A)
+    assert a.shape == (1, 2, 1, 2)
+    assert np.allclose(a[0, :, 0], [[1.0, 17.0], [6.0, -2.0]], rtol=1e-15, atol=0)
+
+
+def test_lowrank_preactivation_special_cases():
+    """z = identity (rank = dk) and A = 0 give a = h on every head; scaling z by s and adding
+    -ln s to A leaves a unchanged; the factor is shared, so heads with equal z and A agree."""
+    rng = np.random.default_rng(44)
+    B, T, dk = 2, 5, 8
+    h = rng.standard_normal((B, T, dk))
+    z = np.broadcast_to(np.eye(dk), (3, dk, dk)).copy()
+    a = reference.lowrank_preactivation(h, z, np.zeros((3, dk)))
+    for hd in range(3):
+        assert np.array_equal(a[:, hd], h)
+    R = 4
+    h2 = rng.standard_normal((B, T, R))
+    z2 = rng.standard_normal((3, dk, R))
+    A2 = rng.standard_normal((3, dk))
+    a2 = reference.lowrank_preactivation(h2, z2, A2)
+    a3 = reference.lowrank_preactivation(h2, z2 * 8.0, A2 - math.log(8.0))
+    assert np.allclose(a2, a3, rtol=1e-13, atol=1e-15)
+    z2[2] = z2[0]
+    A2[2] = A2[0]
+    a4 = reference.lowrank_preactivation(h2, z2, A2)
+    assert np.array_equal(a4[:, 2], a4[:, 0])
