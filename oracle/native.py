@@ -4,7 +4,8 @@ TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
 benchmark's CPU-baseline leg, never by the GPU library.
 
 ``build()`` compiles ``kda_oracle.c`` with gcc + OpenMP into
-``oracle/liboracle.so``; ``recurrent()`` calls it on float64 NumPy arrays.
+``oracle/liboracle.so``; ``recurrent()`` and ``backward()`` call it on float64
+NumPy arrays; ``recurrent_varlen()`` runs packed documents through ``recurrent()``.
 """
 from __future__ import annotations
 
@@ -44,6 +45,9 @@ def _load():
             ctypes.c_double, ctypes.c_int, ctypes.c_int, dp, dp, dp]
         lib.kda_oracle_recurrent.restype = ctypes.c_int
         lib.kda_oracle_threads.restype = ctypes.c_int
+        lib.kda_oracle_backward.argtypes = [dp, dp, dp, dp, dp] + [ctypes.c_long] * 5 + [
+            ctypes.c_double, ctypes.c_int, dp, dp, dp, dp, dp, dp, dp, dp, dp]
+        lib.kda_oracle_backward.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -83,6 +87,29 @@ def recurrent(q, k, v, a, beta, g_min=-5.0, gate="bounded", erase=True, S0=None)
     if rc != 0:
         raise RuntimeError("kda_oracle_recurrent failed with %d" % rc)
     return out, fin
+
+
+def backward(q, k, v, a, beta, dout, g_min=-5.0, gate="bounded", S0=None, dfinal=None):
+    """Gradients of L = sum(dout * out) + sum(dfinal * final_state) of the token recurrence
+    with respect to q, k, v, a, beta and the initial state (see kda_oracle.c for the
+    adjoint, written out by hand).  Shapes as recurrent(); dout [B,H,T,dv], dfinal
+    [B,H,dv,dk] or None.  Returns a dict of float64 arrays dq, dk, dv, da, dbeta, dS0."""
+    q, k, v, a, beta, dout = (_f64(x) for x in (q, k, v, a, beta, dout))
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    assert dout.shape == v.shape
+    S0 = None if S0 is None else _f64(S0)
+    dfinal = None if dfinal is None else _f64(dfinal)
+    res = {n: np.empty(s, dtype=np.float64) for n, s in (("dq", q.shape), ("dk", q.shape), ("dv", v.shape),
+                                                          ("da", q.shape), ("dbeta", beta.shape),
+                                                          ("dS0", (B, H, dv, dk)))}
+    rc = _load().kda_oracle_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(beta), B, H, T, dk, dv,
+                                     float(g_min), GATE_MODES[gate], _ptr(S0), _ptr(dout), _ptr(dfinal),
+                                     _ptr(res["dq"]), _ptr(res["dk"]), _ptr(res["dv"]), _ptr(res["da"]),
+                                     _ptr(res["dbeta"]), _ptr(res["dS0"]))
+    if rc != 0:
+        raise RuntimeError("kda_oracle_backward failed with %d" % rc)
+    return res
 
 
 def recurrent_varlen(q, k, v, a, beta, cu_seqlens, g_min=-5.0, gate="bounded", S0=None):

@@ -376,3 +376,67 @@ def test_lowrank_preactivation_special_cases():
     A2[2] = A2[0]
     a4 = reference.lowrank_preactivation(h2, z2, A2)
     assert np.array_equal(a4[:, 2], a4[:, 0])
+
+
+# ---------------------------------------------------------------- gradients (the backward)
+def _loss_fd(args, name, loss, h=1e-6):
+    x = args[name]
+    fd = np.zeros_like(x)
+    for idx in np.ndindex(x.shape):
+        xp, xm = x.copy(), x.copy()
+        xp[idx] += h
+        xm[idx] -= h
+        fd[idx] = (loss(**dict(args, **{name: xp})) - loss(**dict(args, **{name: xm}))) / (2 * h)
+    return fd
+
+
+@pytest.mark.parametrize("gate", ["bounded", "logsigmoid"])
+def test_backward_matches_finite_differences(gate):
+    """Every gradient of L = sum(dout * out) + sum(dfinal * S_T) against central differences of
+    the forward oracle, over 70 tokens (across a 64-token checkpoint block of the adjoint), with
+    an initial state."""
+    rng = np.random.default_rng(51)
+    q, k, v, a, b = _rand_case(1, 2, 70, 3, 2, rng, a_sigma=2.0)
+    S0 = rng.standard_normal((1, 2, 2, 3))
+    do = rng.standard_normal(v.shape)
+    dF = rng.standard_normal(S0.shape)
+    g = native.backward(q, k, v, a, b, do, -5.0, gate, S0=S0, dfinal=dF)
+
+    def loss(q, k, v, a, b, S0):
+        o, f = native.recurrent(q, k, v, a, b, -5.0, gate=gate, S0=S0)
+        return float((o * do).sum() + (f * dF).sum())
+
+    args = dict(q=q, k=k, v=v, a=a, b=b, S0=S0)
+    for name, key in (("q", "dq"), ("k", "dk"), ("v", "dv"), ("a", "da"), ("b", "dbeta"), ("S0", "dS0")):
+        fd = _loss_fd(args, name, loss)
+        assert np.allclose(g[key], fd, rtol=1e-6, atol=1e-8), (name, float(np.abs(g[key] - fd).max()))
+
+
+def test_backward_single_token_closed_form():
+    """One token from S0: S_1 = S0 D (I - beta k k^T) + beta v k^T with D = diag(e^g), so for
+    L = dout . (S_1 q):  dv = beta (k . q) dout,  dbeta = (k . q)(v . dout) - (S0 D k . dout)(k . q),
+    dq = S_1^T dout,  dS0 = ((dout q^T)(I - beta k k^T)) D  (worked by hand)."""
+    rng = np.random.default_rng(52)
+    dk, dv = 4, 3
+    q, k, v, a, b = _rand_case(1, 1, 1, dk, dv, rng)
+    S0 = rng.standard_normal((1, 1, dv, dk))
+    do = rng.standard_normal((1, 1, 1, dv))
+    g = native.backward(q, k, v, a, b, do, -5.0, "bounded", S0=S0)
+    qv, kv, vv, bt, dov = q[0, 0, 0], k[0, 0, 0], v[0, 0, 0], b[0, 0, 0], do[0, 0, 0]
+    D = np.diag(np.exp(-5.0 / (1.0 + np.exp(-a[0, 0, 0]))))
+    S0m = S0[0, 0]
+    E = np.eye(dk) - bt * np.outer(kv, kv)
+    S1 = S0m @ D @ E + bt * np.outer(vv, kv)
+    kq = kv @ qv
+    assert np.allclose(g["dv"][0, 0, 0], bt * kq * dov, rtol=1e-13)
+    assert np.allclose(g["dbeta"][0, 0, 0], kq * (vv @ dov) - (S0m @ D @ kv @ dov) * kq, rtol=1e-12)
+    assert np.allclose(g["dq"][0, 0, 0], S1.T @ dov, rtol=1e-12)
+    assert np.allclose(g["dS0"][0, 0], np.outer(dov, qv) @ E @ D, rtol=1e-12)
+
+
+def test_backward_zero_incoming_gradient_is_zero():
+    rng = np.random.default_rng(53)
+    q, k, v, a, b = _rand_case(1, 2, 20, 4, 3, rng)
+    g = native.backward(q, k, v, a, b, np.zeros(v.shape), -5.0, "bounded", S0=rng.standard_normal((1, 2, 3, 4)))
+    for key in ("dq", "dk", "dv", "da", "dbeta", "dS0"):
+        assert not np.any(g[key]), key
