@@ -190,3 +190,93 @@ def chunked(q, k, v, a, beta, chunk, g_min=G_MIN, gate_mode="bounded", S0=None,
     if return_parts:
         return out, fin, parts
     return out, fin
+
+
+def _gate_derivative(a, g_min, mode):
+    s = 1.0 / (1.0 + np.exp(-a))
+    return g_min * s * (1.0 - s) if mode == "bounded" else 1.0 - s
+
+
+def chunked_backward(q, k, v, a, beta, dout, chunk, g_min=G_MIN, gate_mode="bounded", S0=None, dfinal=None):
+    """Gradients of L = sum(dout * out) + sum(dfinal * final_state) by the chunk form (the
+    algorithm the GPU backward follows), float64.  A forward pass keeps each chunk's start
+    state S_n (S = state^T, dk x dv); a reverse pass over the chunks carries
+    dS' = dL/d(state at the chunk's end), and for each chunk, with the quantities of chunked()
+    and E_rsc = e^{G_rc - G_sc}:
+        dU  = M^T dO + K^ dS'          dQ~ = dO S^T      dK^ = U dS'^T     dW = -dU S^T
+        dM  = tril(dO U^T)             dgamma_c = sum_j S_cj dS'_cj
+        dT  = dW (b K~)^T + dU (b V)^T dX = T^T dW       dY = T^T dU       dA = -strict_tril(T^T dT T^T)
+        dv  = b dY                     dbeta = rowsum(dX K~ + dY V + dA P)   (P = A / b)
+        dq  = sum_s dM_rs k_s E_rs + dQ~ e^G
+        dk  = sum_r dM_rs q_r E_rs + sum_s' (b dA)_ss' k_s' E_ss' + sum_r (b dA)_rs k_r E_rs
+              + b dX e^G + dK^ e^{G_last - G}
+        dG  = q (first dq term) - k (first dk term) + k (second) - k (third) + dQ~ Q~ + b dX K~ - dK^ K^,
+              and dG_last += sum_r dK^ K^ + dgamma e^{G_last}
+        dg  = reverse cumulative sum of dG within the chunk,  da = dg * dg/da
+        dS  = diag(gamma) dS' + Q~^T dO - W^T dU          (carried to the previous chunk)
+    Returns the same dict as the oracle's adjoint: dq, dk, dv, da, dbeta, dS0."""
+    q, k, v, a, beta, dout = _f64(q, k, v, a, beta, dout)
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    g = gate(a, g_min, gate_mode)
+    gp = _gate_derivative(a, g_min, gate_mode)
+    res = {n: np.zeros(s) for n, s in (("dq", q.shape), ("dk", q.shape), ("dv", v.shape), ("da", q.shape),
+                                        ("dbeta", beta.shape), ("dS0", (B, H, dv, dk)))}
+    for b in range(B):
+        for h in range(H):
+            starts = list(range(0, T, chunk))
+            S = np.zeros((dk, dv)) if S0 is None else np.array(S0[b, h], dtype=np.float64).T
+            S_in = []
+            for n0 in starts:                      # forward: chunk start states
+                sl = slice(n0, min(n0 + chunk, T))
+                S_in.append(S.copy())
+                Q, K, V, bt = q[b, h, sl], k[b, h, sl], v[b, h, sl], beta[b, h, sl]
+                G = np.cumsum(g[b, h, sl], axis=0)
+                C = Q.shape[0]
+                E = np.exp(G[:, None, :] - G[None, :, :])
+                A = np.tril(np.einsum("rc,sc,rsc->rs", K, K, E), -1) * bt[:, None]
+                Tm = np.linalg.solve(np.eye(C) + A, np.eye(C))
+                W = Tm @ (bt[:, None] * K * np.exp(G))
+                U = Tm @ (bt[:, None] * V) - W @ S
+                S = np.exp(G[-1])[:, None] * S + (K * np.exp(G[-1] - G)).T @ U
+            dSp = np.zeros((dk, dv)) if dfinal is None else np.array(dfinal[b, h], dtype=np.float64).T
+            for n0, S in zip(starts[::-1], S_in[::-1]):   # reverse over the chunks
+                sl = slice(n0, min(n0 + chunk, T))
+                Q, K, V, bt, dO = q[b, h, sl], k[b, h, sl], v[b, h, sl], beta[b, h, sl], dout[b, h, sl]
+                G = np.cumsum(g[b, h, sl], axis=0)
+                C = Q.shape[0]
+                E = np.exp(G[:, None, :] - G[None, :, :])
+                P = np.tril(np.einsum("rc,sc,rsc->rs", K, K, E), -1)
+                A = P * bt[:, None]
+                M = np.tril(np.einsum("rc,sc,rsc->rs", Q, K, E), 0)
+                Tm = np.linalg.solve(np.eye(C) + A, np.eye(C))
+                Kt, Qt, Kh, gam = K * np.exp(G), Q * np.exp(G), K * np.exp(G[-1] - G), np.exp(G[-1])
+                X, Y = bt[:, None] * Kt, bt[:, None] * V
+                W = Tm @ X
+                U = Tm @ Y - W @ S
+                dU = M.T @ dO + Kh @ dSp
+                dQt = dO @ S.T
+                dKh = U @ dSp.T
+                dW = -dU @ S.T
+                dM = np.tril(dO @ U.T, 0)
+                dgam = np.sum(S * dSp, axis=1)
+                dT = dW @ X.T + dU @ Y.T
+                dX = Tm.T @ dW
+                dY = Tm.T @ dU
+                dA = np.tril(-Tm.T @ dT @ Tm.T, -1)
+                dP = bt[:, None] * dA
+                dqM = np.einsum("rs,sc,rsc->rc", dM, K, E)
+                dkM = np.einsum("rs,rc,rsc->sc", dM, Q, E)
+                dkR = np.einsum("rs,sc,rsc->rc", dP, K, E)
+                dkC = np.einsum("rs,rc,rsc->sc", dP, K, E)
+                res["dv"][b, h, sl] = bt[:, None] * dY
+                res["dbeta"][b, h, sl] = np.sum(dX * Kt, 1) + np.sum(dY * V, 1) + np.sum(dA * P, 1)
+                res["dq"][b, h, sl] = dqM + dQt * np.exp(G)
+                res["dk"][b, h, sl] = dkM + dkR + dkC + dX * bt[:, None] * np.exp(G) + dKh * np.exp(G[-1] - G)
+                dG = Q * dqM - K * dkM + K * dkR - K * dkC + dQt * Qt + bt[:, None] * dX * Kt - dKh * Kh
+                dG[-1] += np.sum(dKh * Kh, 0) + dgam * gam
+                dg = np.cumsum(dG[::-1], axis=0)[::-1]
+                res["da"][b, h, sl] = dg * gp[b, h, sl]
+                dSp = gam[:, None] * dSp + Qt.T @ dO - W.T @ dU
+            res["dS0"][b, h] = dSp.T
+    return res

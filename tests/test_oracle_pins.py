@@ -440,3 +440,19 @@ def test_backward_zero_incoming_gradient_is_zero():
     g = native.backward(q, k, v, a, b, np.zeros(v.shape), -5.0, "bounded", S0=rng.standard_normal((1, 2, 3, 4)))
     for key in ("dq", "dk", "dv", "da", "dbeta", "dS0"):
         assert not np.any(g[key]), key
+
+
+@pytest.mark.parametrize("gate", ["bounded", "logsigmoid"])
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+def test_chunked_backward_equals_the_adjoint(gate, chunk):
+    """The chunk-form backward (the algorithm of the GPU backward) against the hand-written token
+    adjoint, 83 tokens (a ragged last chunk), with an initial state and a final-state gradient."""
+    rng = np.random.default_rng(54)
+    q, k, v, a, b = _rand_case(1, 2, 83, 8, 6, rng, a_sigma=3.0)
+    S0 = rng.standard_normal((1, 2, 6, 8))
+    do = rng.standard_normal(v.shape)
+    dF = rng.standard_normal(S0.shape)
+    ref = native.backward(q, k, v, a, b, do, -5.0, gate, S0=S0, dfinal=dF)
+    got = reference.chunked_backward(q, k, v, a, b, do, chunk, -5.0, gate, S0=S0, dfinal=dF)
+    for key in ref:
+        assert np.allclose(got[key], ref[key], rtol=1e-11, atol=1e-12), key
