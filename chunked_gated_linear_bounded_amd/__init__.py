@@ -11,6 +11,7 @@ built, every entry point raises; there is no fallback.
     o_t = kda.decode_step(q_t, k_t, v_t, a_t, beta_t, S)               # one more token, S in place
     o = kda.chunk_fwd_varlen(q, k, v, a, beta, cu_seqlens)             # packed documents, [H,T,d]
     o = kda.chunk_fwd_lowrank(q, k, v, h, z, A_log, beta)              # a = e^A (h z^T) in-kernel
+    g = kda.chunk_bwd(q, k, v, a, beta, dout)                          # gradients (training)
     G = kda.gate_cumsum(a, g_min=-5.0, chunk=64)
 """
 from __future__ import annotations
@@ -66,6 +67,10 @@ def lib():
         L.kda_chunk_fwd_varlen_workspace_bytes.restype = sz
         L.kda_chunk_fwd_varlen.argtypes = [vp] * 5 + [f, i, vp] + [i] * 6 + [vp, vp, vp, sz, vp, i, vp, vp]
         L.kda_chunk_fwd_varlen.restype = i
+        L.kda_chunk_bwd_workspace_bytes.argtypes = [i] * 6
+        L.kda_chunk_bwd_workspace_bytes.restype = sz
+        L.kda_chunk_bwd.argtypes = [vp] * 5 + [f] + [i] * 7 + [vp] * 10 + [sz, vp]
+        L.kda_chunk_bwd.restype = i
         L.kda_decode_step.argtypes = [vp] * 5 + [f] + [i] * 6 + [vp, vp, vp]
         L.kda_decode_step.restype = i
         _lib = L
@@ -301,6 +306,51 @@ def chunk_fwd_varlen(q, k, v, a, beta, cu_seqlens, g_min=-5.0, chunk=64, out=Non
     if return_final_state:
         return out, final_state
     return out
+
+
+def bwd_workspace_bytes(B, H, T, dk, dv, dtype) -> int:
+    io = _DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(lib().kda_chunk_bwd_workspace_bytes(B, H, T, dk, dv, io))
+
+
+def chunk_bwd(q, k, v, a, beta, dout, g_min=-5.0, initial_state=None, dfinal_state=None, gate="bounded",
+              workspace=None, stream=None, want_dinitial=True):
+    """Gradients of sum(dout * out) + sum(dfinal_state * final_state) of chunk_fwd with respect to
+    q, k, v, a, beta and the initial state.  Inputs as chunk_fwd (T % 16 == 0), dout [B,H,T,dv] in
+    the I/O dtype, dfinal_state float32 [B,H,dv,dk] or None.  Returns a dict of float32 tensors
+    dq, dk, dv, da, dbeta and dinitial_state (None unless want_dinitial)."""
+    dtype = q.dtype
+    if dtype not in _DTYPES:
+        raise ValueError("unsupported dtype %s" % dtype)
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (a, "a"), (beta, "beta"), (dout, "dout")):
+        _check(t, n, dtype, dev)
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or a.shape != q.shape or v.shape != (B, H, T, dv) or beta.shape != (B, H, T) or \
+            dout.shape != v.shape:
+        raise ValueError("shape mismatch")
+    for t, n in ((initial_state, "initial_state"), (dfinal_state, "dfinal_state")):
+        if t is not None:
+            _check(t, n, torch.float32, dev)
+            if tuple(t.shape) != (B, H, dv, dk):
+                raise ValueError("%s must be [B,H,dv,dk]" % n)
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = {"dq": torch.empty((B, H, T, dk), **f32), "dk": torch.empty((B, H, T, dk), **f32),
+         "dv": torch.empty((B, H, T, dv), **f32), "da": torch.empty((B, H, T, dk), **f32),
+         "dbeta": torch.empty((B, H, T), **f32),
+         "dinitial_state": torch.empty((B, H, dv, dk), **f32) if want_dinitial else None}
+    need = bwd_workspace_bytes(B, H, T, dk, dv, dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check(workspace, "workspace", torch.uint8, dev)
+    st = lib().kda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(beta), float(g_min), B, H, T, dk, dv,
+                             _DTYPES[dtype], GATE_MODES[gate], _ptr(initial_state), _ptr(dout), _ptr(dfinal_state),
+                             _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["da"]), _ptr(g["dbeta"]),
+                             _ptr(g["dinitial_state"]), _ptr(workspace), workspace.numel(), _stream(stream))
+    if st != KDA_OK:
+        raise KdaError("kda_chunk_bwd", st)
+    return g
 
 
 def decode_step(q, k, v, a, beta, state, g_min=-5.0, gate="bounded", out=None, stream=None):

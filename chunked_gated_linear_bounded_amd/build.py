@@ -33,6 +33,7 @@ DEVICE = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-p
 UNITS = [
     ("kda_kernels.hip", "kda_kernels.o", []),
     ("kda_kernels_lowrank.hip", "kda_kernels_lowrank.o", []),
+    ("kda_kernels_bwd.hip", "kda_kernels_bwd.o", []),
     ("kda_abi.cpp", "kda_abi.o", []),
 ]
 

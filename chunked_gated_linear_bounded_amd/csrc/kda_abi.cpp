@@ -191,6 +191,23 @@ int varlen_impl(const void *q, const void *k, const void *v, const void *a, cons
     return kda::launch_state(p) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+// Backward: the 16-token chunk records, the chunk start states and the gradients of the chunk
+// end states, in that order.
+struct BwdSizes {
+    size_t rec, states, total;
+};
+
+int check_bwd(int B, int H, int T, int dk, int dv, int io, BwdSizes *bs) {
+    const int st = check_shape(B, H, T, dk, dv, 16, io);
+    if (st != KDA_OK) return st;
+    const KdaLayout L = kda_layout(16, dk, dv, io == KDA_FP32 ? 4 : 2);
+    const size_t nch = (size_t)B * (size_t)H * (size_t)(T / 16);
+    bs->rec = nch * L.stride;
+    bs->states = nch * (size_t)dk * (size_t)dv * sizeof(float);
+    bs->total = bs->rec + 2 * bs->states;
+    return KDA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -288,6 +305,55 @@ int kda_chunk_fwd_varlen(const void *q, const void *k, const void *v, const void
                          const float *initial_state) {
     return varlen_impl(q, k, v, a, beta, g_min, chunk, cu_seqlens, N, H, T, dk, dv, io_dtype, out, final_state,
                        workspace, workspace_bytes_given, stream, gate_mode, nonfinite_counts, initial_state);
+}
+
+size_t kda_chunk_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int io_dtype) {
+    BwdSizes bs;
+    if (check_bwd(B, H, T, dk, dv, io_dtype, &bs) != KDA_OK) return 0;
+    return bs.total;
+}
+
+int kda_chunk_bwd(const void *q, const void *k, const void *v, const void *a, const void *beta, float g_min, int B,
+                  int H, int T, int dk, int dv, int io_dtype, int gate_mode, const float *initial_state,
+                  const void *dout, const float *dfinal_state, float *dq, float *dk_out, float *dv_out, float *da,
+                  float *dbeta, float *dinitial_state, void *workspace, size_t workspace_bytes_given,
+                  hipStream_t stream) {
+    BwdSizes bs;
+    int st = check_bwd(B, H, T, dk, dv, io_dtype, &bs);
+    if (st != KDA_OK) return st;
+    st = check_gate(g_min, gate_mode);
+    if (st != KDA_OK) return st;
+    if (T > 0 && (!q || !k || !v || !a || !beta || !dout || !dq || !dk_out || !dv_out || !da || !dbeta))
+        return KDA_ERR_NULL;
+    const size_t esz = io_dtype == KDA_FP32 ? 4 : 2;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(a, 16) || !aligned(beta, esz) ||
+        !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk_out, 16) || !aligned(dv_out, 16) || !aligned(da, 16) ||
+        !aligned(dbeta, 4) || !aligned(initial_state, 16) || !aligned(dfinal_state, 16) ||
+        !aligned(dinitial_state, 16) || !aligned(workspace, 16))
+        return KDA_ERR_ALIGN;
+    if (bs.total > 0 && (!workspace || workspace_bytes_given < bs.total)) return KDA_ERR_WORKSPACE;
+    if (T == 0) {  // no tokens: the initial state's gradient is the final state's
+        if (!dinitial_state) return KDA_OK;
+        const size_t bytes = (size_t)B * H * dv * dk * sizeof(float);
+        hipError_t e = dfinal_state
+                           ? hipMemcpyAsync(dinitial_state, dfinal_state, bytes, hipMemcpyDeviceToDevice, stream)
+                           : hipMemsetAsync(dinitial_state, 0, bytes, stream);
+        return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    }
+    kda::LaunchArgs p{};
+    p.q = q; p.k = k; p.v = v; p.a = a; p.beta = beta;
+    p.g_min = g_min;
+    p.logsig = gate_mode == KDA_GATE_LOGSIGMOID;
+    p.chunk = 16; p.B = B; p.H = H; p.T = T; p.dk = dk; p.dv = dv;
+    p.fp32 = io_dtype == KDA_FP32;
+    p.init_state = initial_state;
+    p.workspace = workspace;
+    p.states = reinterpret_cast<float *>(static_cast<unsigned char *>(workspace) + bs.rec);
+    p.dstates = reinterpret_cast<float *>(static_cast<unsigned char *>(workspace) + bs.rec + bs.states);
+    p.dout = dout; p.dfinal = dfinal_state;
+    p.dq = dq; p.dk_ = dk_out; p.dv_ = dv_out; p.da = da; p.dbeta = dbeta; p.dinit = dinitial_state;
+    p.stream = stream;
+    return kda::launch_bwd(p) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
 int kda_decode_step(const void *q, const void *k, const void *v, const void *a, const void *beta, float g_min,

@@ -1,0 +1,539 @@
+// Backward pass of the chunked forward: gradients of
+//   L = sum_t dout_t . o_t + <dfinal, S_T>
+// with respect to q, k, v, a, beta and the initial state, for training ("Breaking
+// Through Trillion-Parameter Multimodal MoE ...", sec. 2.1: the operator change must be
+// invisible to the training scripts above it, so it must supply exactly these gradients).
+//
+// The chunk form, with 16-token chunks (the gradients are those of the function, so the
+// backward chooses its own chunk; one 16-row tile per chunk needs a single Gamma reference,
+// the chunk's first row, within the range the bound guarantees).  With S = state^T (dk x
+// dv), per chunk (G the chunk's inclusive log-cumsum, E_rs = e^{G_r - G_s} per channel):
+//   forward, recomputed:  A = strict_tril(diag(b) P),  P_rs = sum_c k_rc k_sc E_rsc,
+//     M = tril(sum_c q_rc k_sc E_rsc),  T = (I + A)^-1,  W = T diag(b) K e^G,
+//     U = T diag(b) V - W S,  K^ = K e^{G_last - G},  gamma = e^{G_last}
+//   reverse over chunks (dS' = dL/d(state at the chunk's end), kda_bwd_dstate_kernel):
+//     dS = diag(gamma) dS' + Qbar^T dO - W^T (K^ dS'),   Qbar = Q e^G - M W
+//   per chunk, in parallel (kda_bwd_chunk_kernel):
+//     dU = M^T dO + K^ dS'   dQ~ = dO S^T   dK^ = U dS'^T   dW = -dU S^T   dM = tril(dO U^T)
+//     dgamma = rowsum(S * dS')   dT = dW (b K e^G)^T + dU (b V)^T   dX = T^T dW   dY = T^T dU
+//     dA = -strict_tril(T^T dT T^T)   dv = b dY   dbeta = rowsum(dX K e^G + dY V + dA P)
+//     and the pairwise terms of M and P into dq, dk and dG, then dg = reverse cumsum of dG.
+// Every product runs on fp32 MFMA (16x16x4), operands read through index functions.
+#pragma once
+#include "kda_device.h"
+#include "kda_layout.h"
+
+namespace kda {
+
+// acc += A (16 x K) B (K x 16) on fp32 MFMA: A(m, k) and B(k, n) return A[m][k] and B[k][n]
+// (m, n in 0..15).  In v_mfma_f32_16x16x4f32 lane l supplies A[l%16][k0 + l/16] and
+// B[k0 + l/16][l%16]; acc[i] is D[4 (l/16) + i][l%16].
+template <int K, typename FA, typename FB>
+__device__ __forceinline__ f32x4 mma_tile(f32x4 acc, const FA &A, const FB &B, int lane) {
+    const int m = lane & 15, kq = lane >> 4;
+#pragma unroll 8
+    for (int k0 = 0; k0 < K; k0 += 4)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A(m, k0 + kq), B(k0 + kq, m), acc, 0, 0, 0);
+    return acc;
+}
+
+// Element (r, c) of a stored tile-pair block (kda_layout.h): tiles of 16 x 16 in
+// accumulator order, the two tiles of a pair interleaved per lane.  `pairs_along_rows`:
+// the pair joins tile rows 2p and 2p+1 (K^), else tile columns (W^T, Qbar^T stored with
+// pairs along dk, their row dimension).  ntc: tiles per row of the block's tile grid in the
+// stored order (NT for W^T/Qbar^T, NDK for K^).
+__device__ __forceinline__ int pair_offset(int r, int c, int ntc) {
+    // a block X stored as pairs [r/32][c/16]: pair (tile rows 2p, 2p+1) for tile column c/16
+    const int tr = r >> 4, tc = c >> 4, rr = r & 15, cc = c & 15;
+    return (((tr >> 1) * ntc + tc) * 64 + 16 * (rr >> 2) + cc) * 8 + 4 * (tr & 1) + (rr & 3);
+}
+
+template <int DK, int DV, bool F32>
+struct BwdCfg {
+    using E = typename std::conditional<F32, float, __bf16>::type;
+    using OH = typename std::conditional<F32, float, _Float16>::type;  // record operand type
+    static constexpr int C = 16;
+    static constexpr KdaLayout L = kda_layout(C, DK, DV, sizeof(E));
+    static constexpr int NS = DV / 16;
+};
+
+// ---------------------------------------------------------------------------------------
+// Reverse pass over the chunks of one head and one 16-wide value slice: carries the slice of
+// dS' (dk x 16, fp32) from the last chunk to the first, storing it for every chunk (the
+// gradient of the state that chunk ends in), and gives dL/dS_0 at the end.  Reads W^T, Qbar^T,
+// K^ and gamma from the chunk records of the forward's chunk stage (16-token chunks) and the
+// chunk's 16 x 16 block of dout.  The next chunk's record bytes and dout block are loaded into
+// registers while the current chunk is computed.
+template <int DK, int DV, bool F32>
+__global__ __launch_bounds__(256) void kda_bwd_dstate_kernel(
+    const unsigned char *__restrict__ ws, const typename BwdCfg<DK, DV, F32>::E *__restrict__ dout,
+    const float *__restrict__ dfinal, int T, float *__restrict__ dstates, float *__restrict__ dinit)
+{
+    using Cfg = BwdCfg<DK, DV, F32>;
+    using E = typename Cfg::E;
+    using OH = typename Cfg::OH;
+    constexpr KdaLayout L = Cfg::L;
+    constexpr int NS = Cfg::NS, NDK = DK / 16, NTW = (NDK + 3) / 4;  // dk tiles per wave
+    constexpr int R1 = (int)L.region1, NU = (R1 + 15) / 16;
+    constexpr int PD = 17;
+
+    constexpr int NBLK = (NU + 63) / 64, RB = NBLK * 1024;  // 1 KiB blocks per record copy
+    __shared__ __attribute__((aligned(1024))) unsigned char sRec[2 * RB];
+    __shared__ float sD[DK * PD];       // dS' slice: [key c][value j]
+    __shared__ float sPp[4][16 * PD];   // split-K partials of P = K^ dS'
+    __shared__ float sdO[16 * PD];
+
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int bh = blockIdx.x / NS, slice = blockIdx.x % NS, j0 = 16 * slice;
+    const int NC = T / 16;
+    const unsigned char *rec0 = ws + (size_t)bh * NC * L.stride;
+
+    // dS' of the last chunk: dfinal (or zero), kept in registers in accumulator order
+    f32x4 D[NTW];
+#pragma unroll
+    for (int x = 0; x < NTW; ++x) {
+        const int mt = wave + 4 * x;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = 16 * mt + 4 * g + i;
+            D[x][i] = (mt < NDK && dfinal != nullptr) ? dfinal[((size_t)bh * DV + j0 + l16) * DK + c] : 0.f;
+        }
+    }
+    // the next chunk's record bytes go straight into the other LDS buffer (direct loads,
+    // issued by all four waves) and its dout block into a register, a chunk ahead
+    E pdo = E(0.f);
+    auto prefetch = [&](int nn) {
+        const unsigned char *src = rec0 + (size_t)nn * L.stride;
+        lds_u8 *dst = lds_base(sRec) + (nn & 1) * RB;
+#pragma unroll
+        for (int i = 0; i < NBLK; i += 4) {
+            const int blk = i + wave, u = blk * 64 + lane;
+            if (blk < NBLK && u < NU)
+                __builtin_amdgcn_global_load_lds(src + (size_t)u * 16, (lds_void *)(dst + blk * 1024), 16, 0, 0);
+        }
+        pdo = dout[((size_t)bh * T + (size_t)nn * 16 + (tid >> 4)) * DV + j0 + (tid & 15)];
+    };
+    if (NC > 0) prefetch(NC - 1);
+    wait_vmcnt<0>();
+    __syncthreads();
+
+    for (int n = NC - 1; n >= 0; --n) {
+        // this chunk's dout block and dS' into LDS (its record is in buffer n & 1)
+        sdO[(tid >> 4) * PD + (tid & 15)] = to_f(pdo);
+#pragma unroll
+        for (int x = 0; x < NTW; ++x) {
+            const int mt = wave + 4 * x;
+            if (mt >= NDK) continue;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sD[(16 * mt + 4 * g + i) * PD + l16] = D[x][i];
+        }
+        __syncthreads();
+        if (n > 0) prefetch(n - 1);
+
+        // dS' of this chunk's end, for the chunk-parallel stage: dstates[bh][n][value][key]
+        for (int e = tid; e < DK * 16; e += 256) {
+            const int j = e / DK, c = e % DK;
+            dstates[(((size_t)bh * NC + n) * DV + j0 + j) * DK + c] = sD[c * PD + j];
+        }
+
+        const unsigned char *cur = sRec + (n & 1) * RB;
+        const OH *rWT = reinterpret_cast<const OH *>(cur + L.wt);
+        const OH *rQB = reinterpret_cast<const OH *>(cur + L.qbt);
+        const OH *rKH = reinterpret_cast<const OH *>(cur + L.kh);
+        const float *rG = reinterpret_cast<const float *>(cur + L.gam);
+        const int *rS = reinterpret_cast<const int *>(cur + L.scl);
+        const float fW = ldexp2(1.f, -rS[0]), fQ = ldexp2(1.f, -rS[1]), fK = ldexp2(1.f, -rS[2]);
+
+        // P = K^ dS' (16 x 16), K split over the four waves
+        {
+            constexpr int KW = DK / 4;
+            const int c0 = KW * wave;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            acc = mma_tile<KW>(acc,
+                               [&](int m, int kk) { return (float)rKH[pair_offset(m, c0 + kk, NDK)] * fK; },
+                               [&](int kk, int nn) { return sD[(c0 + kk) * PD + nn]; }, lane);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sPp[wave][(4 * g + i) * PD + l16] = acc[i];
+        }
+        __syncthreads();
+
+        // dS = diag(gamma) dS' + Qbar^T dO - W^T P  (rows c of this wave's dk tiles)
+#pragma unroll
+        for (int x = 0; x < NTW; ++x) {
+            const int mt = wave + 4 * x;
+            if (mt >= NDK) continue;
+            f32x4 acc;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] = rG[16 * mt + 4 * g + i] * D[x][i];
+            acc = mma_tile<16>(acc, [&](int m, int kk) { return (float)rQB[pair_offset(16 * mt + m, kk, 1)] * fQ; },
+                               [&](int kk, int nn) { return sdO[kk * PD + nn]; }, lane);
+            acc = mma_tile<16>(acc, [&](int m, int kk) { return -(float)rWT[pair_offset(16 * mt + m, kk, 1)] * fW; },
+                               [&](int kk, int nn) {
+                                   const int o = kk * PD + nn;
+                                   return (sPp[0][o] + sPp[1][o]) + (sPp[2][o] + sPp[3][o]);
+                               },
+                               lane);
+            D[x] = acc;
+        }
+        wait_vmcnt<0>();  // the next record has landed
+        __syncthreads();  // sD, sPp, sdO and this record's buffer are rewritten next
+    }
+    if (dinit != nullptr) {
+#pragma unroll
+        for (int x = 0; x < NTW; ++x) {
+            const int mt = wave + 4 * x;
+            if (mt >= NDK) continue;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                dinit[((size_t)bh * DV + j0 + l16) * DK + 16 * mt + 4 * g + i] = D[x][i];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// Gradients of one 16-token chunk of one head, from the state it starts from (states) and
+// the gradient of the state it ends in (dstates).  All intermediates in fp32; the state S
+// is held in LDS, dS' is read from global memory (L2) where a product needs it.  Work-
+// group = 4 waves; products over a dk- or dv-wide dimension are split by 16-column tiles
+// over the waves, and each wave keeps its tiles of dq, dk and dG in registers.
+template <int DK, int DV, bool F32>
+__global__ __launch_bounds__(256, 1) void kda_bwd_chunk_kernel(
+    const typename BwdCfg<DK, DV, F32>::E *__restrict__ q, const typename BwdCfg<DK, DV, F32>::E *__restrict__ k,
+    const typename BwdCfg<DK, DV, F32>::E *__restrict__ v, const typename BwdCfg<DK, DV, F32>::E *__restrict__ a,
+    const typename BwdCfg<DK, DV, F32>::E *__restrict__ beta,
+    const typename BwdCfg<DK, DV, F32>::E *__restrict__ dout, float gmin2, float gmin, int logsig, int T,
+    const float *__restrict__ states, const float *__restrict__ dstates, float *__restrict__ dq,
+    float *__restrict__ dk, float *__restrict__ dv, float *__restrict__ da, float *__restrict__ dbeta)
+{
+    constexpr int C = 16, PK = DK + 1, PV = DV + 1, P16 = 17;
+    constexpr int NDK = DK / 16, NDV = DV / 16, NTK = (NDK + 3) / 4, NTV = (NDV + 3) / 4;
+    __shared__ float sQ[C * PK], sK[C * PK], sG[C * PK], sV[C * PV], sdO[C * PV];
+    __shared__ float sS[DV * PK];  // the chunk's start state as stored: [value j][key c]
+    __shared__ float sW[C * PK];   // W, then dW, then dG
+    __shared__ float sU[C * PV];   // U~, then U
+    __shared__ float sdU[C * PV];  // K^ dS', then dU
+    __shared__ float sP[C * P16], sM[C * P16], sT[C * P16], sdM[C * P16], sdT[C * P16], sdA[C * P16];
+    __shared__ float sB[C], sGl[DK], sDg[DK], sdb[4][C];
+
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = blockIdx.x, bh = blockIdx.y, NC = T / C;
+    const size_t t0 = (size_t)bh * T + (size_t)n * C;  // first token row of the chunk
+    const float *Sg = states + ((size_t)bh * NC + n) * DV * DK;
+    const float *Dg = dstates + ((size_t)bh * NC + n) * DV * DK;  // dS' as [value j][key c]
+
+    // ---------------------------------------------------------------- loads, G
+    for (int e = tid; e < C * DK; e += 256) {
+        const int r = e / DK, c = e % DK;
+        sQ[r * PK + c] = to_f(q[(t0 + r) * DK + c]);
+        sK[r * PK + c] = to_f(k[(t0 + r) * DK + c]);
+    }
+    for (int e = tid; e < C * DV; e += 256) {
+        const int r = e / DV, c = e % DV;
+        sV[r * PV + c] = to_f(v[(t0 + r) * DV + c]);
+        sdO[r * PV + c] = to_f(dout[(t0 + r) * DV + c]);
+    }
+    for (int e = tid; e < DV * DK; e += 256) sS[(e / DK) * PK + e % DK] = Sg[e];
+    if (tid < C) sB[tid] = to_f(beta[t0 + tid]);
+    if (tid < DK) {
+        float acc = 0.f;
+        for (int r = 0; r < C; ++r) {
+            acc += gate_log2(to_f(a[(t0 + r) * DK + tid]), gmin2, logsig);
+            sG[r * PK + tid] = acc;  // log2 units
+        }
+    }
+    __syncthreads();
+
+    // factors (G in log2 units; each at most 1 except Em, at most e^{15 |g_min|})
+    auto G = [&](int r, int c) { return sG[r * PK + c]; };
+    auto Ep = [&](int r, int c) { return ex2(G(r, c) - G(0, c)); };       // e^{G_r - G_0}
+    auto Em = [&](int r, int c) { return ex2(G(0, c) - G(r, c)); };       // e^{G_0 - G_r}
+    auto EG = [&](int r, int c) { return ex2(G(r, c)); };                 // e^{G_r}
+    auto EH = [&](int r, int c) { return ex2(G(C - 1, c) - G(r, c)); };   // e^{G_last - G_r}
+    auto Kv = [&](int r, int c) { return sK[r * PK + c]; };
+    auto Qv = [&](int r, int c) { return sQ[r * PK + c]; };
+
+    // ---------------------------------------------------------------- P, M, T
+    if (wave == 0) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = mma_tile<DK>(acc, [&](int m, int kk) { return Kv(m, kk) * Ep(m, kk); },
+                           [&](int kk, int nn) { return Kv(nn, kk) * Em(nn, kk); }, lane);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sP[(4 * g + i) * P16 + l16] = (l16 < 4 * g + i) ? acc[i] : 0.f;
+    } else if (wave == 1) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = mma_tile<DK>(acc, [&](int m, int kk) { return Qv(m, kk) * Ep(m, kk); },
+                           [&](int kk, int nn) { return Kv(nn, kk) * Em(nn, kk); }, lane);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sM[(4 * g + i) * P16 + l16] = (l16 <= 4 * g + i) ? acc[i] : 0.f;
+    }
+    __syncthreads();
+    if (tid < C) {  // T = (I + A)^-1 by forward substitution, lane = column
+        const int j = tid;
+        for (int r = 0; r < C; ++r) {
+            float x = (r == j) ? 1.f : 0.f;
+            for (int u = j; u < r; ++u) x -= sB[r] * sP[r * P16 + u] * sT[u * P16 + j];
+            sT[r * P16 + j] = (r < j) ? 0.f : x;
+        }
+    }
+    __syncthreads();
+
+    // ---------------------------------------------------------------- W = T X, U~ = T Y
+    auto Xv = [&](int r, int c) { return sB[r] * Kv(r, c) * EG(r, c); };  // b K e^G
+#pragma unroll
+    for (int x = 0; x < NTK; ++x) {
+        const int nt = wave + 4 * x;
+        if (nt >= NDK) continue;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = mma_tile<C>(acc, [&](int m, int kk) { return sT[m * P16 + kk]; },
+                          [&](int kk, int nn) { return Xv(kk, 16 * nt + nn); }, lane);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sW[(4 * g + i) * PK + 16 * nt + l16] = acc[i];
+    }
+#pragma unroll
+    for (int x = 0; x < NTV; ++x) {
+        const int nt = wave + 4 * x;
+        if (nt >= NDV) continue;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = mma_tile<C>(acc, [&](int m, int kk) { return sT[m * P16 + kk]; },
+                          [&](int kk, int nn) { return sB[kk] * sV[kk * PV + 16 * nt + nn]; }, lane);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sU[(4 * g + i) * PV + 16 * nt + l16] = acc[i];
+    }
+    __syncthreads();
+
+    // ---------------------------------------------------------------- U = U~ - W S, dQ~ = dO S^T
+    f32x4 dQa[NTK], dKa[NTK], dGa[NTK];  // this wave's dk tiles of dq, dk and dG
+#pragma unroll
+    for (int x = 0; x < NTV; ++x) {
+        const int nt = wave + 4 * x;
+        if (nt >= NDV) continue;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = mma_tile<DK>(acc, [&](int m, int kk) { return sW[m * PK + kk]; },
+                           [&](int kk, int nn) { return sS[(16 * nt + nn) * PK + kk]; }, lane);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float *p = &sU[(4 * g + i) * PV + 16 * nt + l16];
+            *p = *p - acc[i];
+        }
+    }
+#pragma unroll
+    for (int x = 0; x < NTK; ++x) {
+        const int nt = wave + 4 * x;
+        dQa[x] = dKa[x] = dGa[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (nt >= NDK) continue;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = mma_tile<DV>(acc, [&](int m, int kk) { return sdO[m * PV + kk]; },
+                           [&](int kk, int nn) { return sS[kk * PK + 16 * nt + nn]; }, lane);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * g + i, c = 16 * nt + l16;
+            dQa[x][i] = acc[i] * EG(r, c);        // dQ~ e^G
+            dGa[x][i] = Qv(r, c) * dQa[x][i];     // dQ~ * Q~
+        }
+    }
+    __syncthreads();
+
+    // ---------------------------------------------------------------- with dS': K^ dS', dK^, dgamma
+#pragma unroll
+    for (int x = 0; x < NTV; ++x) {
+        const int nt = wave + 4 * x;
+        if (nt >= NDV) continue;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = mma_tile<DK>(acc, [&](int m, int kk) { return Kv(m, kk) * EH(m, kk); },
+                           [&](int kk, int nn) { return Dg[(16 * nt + nn) * DK + kk]; }, lane);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sdU[(4 * g + i) * PV + 16 * nt + l16] = acc[i];
+    }
+#pragma unroll
+    for (int x = 0; x < NTK; ++x) {
+        const int nt = wave + 4 * x;
+        if (nt >= NDK) continue;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = mma_tile<DV>(acc, [&](int m, int kk) { return sU[m * PV + kk]; },
+                           [&](int kk, int nn) { return Dg[kk * DK + 16 * nt + nn]; }, lane);
+        float col = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * g + i, c = 16 * nt + l16;
+            const float eh = EH(r, c), kh = Kv(r, c) * eh;
+            dKa[x][i] += acc[i] * eh;   // dK^ e^{G_last - G}
+            dGa[x][i] -= acc[i] * kh;   // - dK^ * K^
+            col += acc[i] * kh;
+        }
+        col += __shfl_xor(col, 16, 64);
+        col += __shfl_xor(col, 32, 64);
+        if (g == 0) sGl[16 * nt + l16] = col;  // sum over the chunk's rows of dK^ * K^
+    }
+    for (int c = tid; c < DK; c += 256) {
+        float s = 0.f;
+        for (int j = 0; j < DV; ++j) s += sS[j * PK + c] * Dg[j * DK + c];
+        sDg[c] = s;  // dgamma_c
+    }
+    __syncthreads();
+
+    // ---------------------------------------------------------------- dU = M^T dO + K^ dS', dM
+#pragma unroll
+    for (int x = 0; x < NTV; ++x) {
+        const int nt = wave + 4 * x;
+        if (nt >= NDV) continue;
+        f32x4 acc;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = sdU[(4 * g + i) * PV + 16 * nt + l16];
+        acc = mma_tile<C>(acc, [&](int m, int kk) { return sM[kk * P16 + m]; },
+                          [&](int kk, int nn) { return sdO[kk * PV + 16 * nt + nn]; }, lane);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sdU[(4 * g + i) * PV + 16 * nt + l16] = acc[i];
+    }
+    if (wave == 0) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = mma_tile<DV>(acc, [&](int m, int kk) { return sdO[m * PV + kk]; },
+                           [&](int kk, int nn) { return sU[nn * PV + kk]; }, lane);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sdM[(4 * g + i) * P16 + l16] = (l16 <= 4 * g + i) ? acc[i] : 0.f;
+    }
+    __syncthreads();
+
+    // ---------------------------------------------------------------- dW = -dU S^T
+#pragma unroll
+    for (int x = 0; x < NTK; ++x) {
+        const int nt = wave + 4 * x;
+        if (nt >= NDK) continue;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = mma_tile<DV>(acc, [&](int m, int kk) { return sdU[m * PV + kk]; },
+                           [&](int kk, int nn) { return sS[kk * PK + 16 * nt + nn]; }, lane);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sW[(4 * g + i) * PK + 16 * nt + l16] = -acc[i];
+    }
+    __syncthreads();
+
+    // ---------------------------------------------------------------- dT = dW X^T + dU Y^T
+    if (wave == 0) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = mma_tile<DK>(acc, [&](int m, int kk) { return sW[m * PK + kk]; },
+                           [&](int kk, int nn) { return Xv(nn, kk); }, lane);
+        acc = mma_tile<DV>(acc, [&](int m, int kk) { return sdU[m * PV + kk]; },
+                           [&](int kk, int nn) { return sB[nn] * sV[nn * PV + kk]; }, lane);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sdT[(4 * g + i) * P16 + l16] = acc[i];
+    }
+    __syncthreads();
+
+    // ---------------------------------------------------------------- dX, dY (-> dv, dbeta), dA
+    float db[4] = {0.f, 0.f, 0.f, 0.f};  // this wave's part of dbeta for rows 4g+i
+#pragma unroll
+    for (int x = 0; x < NTK; ++x) {
+        const int nt = wave + 4 * x;
+        if (nt >= NDK) continue;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = mma_tile<C>(acc, [&](int m, int kk) { return sT[kk * P16 + m]; },
+                          [&](int kk, int nn) { return sW[kk * PK + 16 * nt + nn]; }, lane);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * g + i, c = 16 * nt + l16;
+            const float eg = EG(r, c), kt = Kv(r, c) * eg;
+            dKa[x][i] += sB[r] * acc[i] * eg;   // b dX e^G
+            dGa[x][i] += sB[r] * acc[i] * kt;   // b dX * K~
+            db[i] += acc[i] * kt;               // dX * K~
+        }
+    }
+#pragma unroll
+    for (int x = 0; x < NTV; ++x) {
+        const int nt = wave + 4 * x;
+        if (nt >= NDV) continue;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = mma_tile<C>(acc, [&](int m, int kk) { return sT[kk * P16 + m]; },
+                          [&](int kk, int nn) { return sdU[kk * PV + 16 * nt + nn]; }, lane);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * g + i, c = 16 * nt + l16;
+            dv[(t0 + r) * DV + c] = sB[r] * acc[i];
+            db[i] += acc[i] * sV[r * PV + c];
+        }
+    }
+    if (wave == 3) {  // dA = -strict_tril(T^T dT T^T); dbeta += rowsum(dA * P); dP = diag(b) dA
+        f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        z = mma_tile<C>(z, [&](int m, int kk) { return sdT[m * P16 + kk]; },
+                        [&](int kk, int nn) { return sT[nn * P16 + kk]; }, lane);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sdA[(4 * g + i) * P16 + l16] = z[i];  // dT T^T
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = mma_tile<C>(acc, [&](int m, int kk) { return sT[kk * P16 + m]; },
+                          [&](int kk, int nn) { return sdA[kk * P16 + nn]; }, lane);
+        float dpa[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * g + i;
+            dpa[i] = (l16 < r) ? -acc[i] : 0.f;
+            db[i] += dpa[i] * sP[r * P16 + l16];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sdT[(4 * g + i) * P16 + l16] = sB[4 * g + i] * dpa[i];  // dP, over dT
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {  // sum over the 16 columns this lane group holds
+        float s = db[i];
+        s += __shfl_xor(s, 1, 64);
+        s += __shfl_xor(s, 2, 64);
+        s += __shfl_xor(s, 4, 64);
+        s += __shfl_xor(s, 8, 64);
+        if (l16 == 0) sdb[wave][4 * g + i] = s;
+    }
+    __syncthreads();
+
+    // ---------------------------------------------------------------- pairwise terms of M and P
+#pragma unroll
+    for (int x = 0; x < NTK; ++x) {
+        const int nt = wave + 4 * x;
+        if (nt >= NDK) continue;
+        const int cn = 16 * nt;
+        f32x4 x1 = {0.f, 0.f, 0.f, 0.f}, x2 = x1, x3 = x1, x4 = x1;
+        x1 = mma_tile<C>(x1, [&](int m, int kk) { return sdM[m * P16 + kk]; },
+                         [&](int kk, int nn) { return Kv(kk, cn + nn) * Em(kk, cn + nn); }, lane);   // dM Km
+        x2 = mma_tile<C>(x2, [&](int m, int kk) { return sdM[kk * P16 + m]; },
+                         [&](int kk, int nn) { return Qv(kk, cn + nn) * Ep(kk, cn + nn); }, lane);   // dM^T Qp
+        x3 = mma_tile<C>(x3, [&](int m, int kk) { return sdT[m * P16 + kk]; },
+                         [&](int kk, int nn) { return Kv(kk, cn + nn) * Em(kk, cn + nn); }, lane);   // dP Km
+        x4 = mma_tile<C>(x4, [&](int m, int kk) { return sdT[kk * P16 + m]; },
+                         [&](int kk, int nn) { return Kv(kk, cn + nn) * Ep(kk, cn + nn); }, lane);   // dP^T Kp
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * g + i, c = cn + l16;
+            const float ep = Ep(r, c), em = Em(r, c), qr = Qv(r, c), kr = Kv(r, c);
+            const float a1 = x1[i] * ep, a2 = x2[i] * em, a3 = x3[i] * ep, a4 = x4[i] * em;
+            dQa[x][i] += a1;
+            dKa[x][i] += a2 + a3 + a4;
+            dGa[x][i] += qr * a1 - kr * a2 + kr * a3 - kr * a4;
+        }
+    }
+
+    // ---------------------------------------------------------------- outputs; dg = reverse cumsum of dG
+#pragma unroll
+    for (int x = 0; x < NTK; ++x) {
+        const int nt = wave + 4 * x;
+        if (nt >= NDK) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * g + i, c = 16 * nt + l16;
+            float dg = dGa[x][i];
+            if (r == C - 1) dg += sGl[c] + sDg[c] * EG(C - 1, c);  // G_last: K^ and gamma
+            dq[(t0 + r) * DK + c] = dQa[x][i];
+            dk[(t0 + r) * DK + c] = dKa[x][i];
+            sW[r * PK + c] = dg;
+        }
+    }
+    __syncthreads();
+    if (tid < DK) {
+        float acc = 0.f;
+        for (int r = C - 1; r >= 0; --r) {
+            acc += sW[r * PK + tid];
+            const float av = to_f(a[(t0 + r) * DK + tid]);
+            const float s = 1.f / (1.f + __expf(-av));
+            da[(t0 + r) * DK + tid] = acc * (logsig ? (1.f - s) : gmin * s * (1.f - s));
+        }
+    }
+    if (tid < C) dbeta[t0 + tid] = (sdb[0][tid] + sdb[1][tid]) + (sdb[2][tid] + sdb[3][tid]);
+}
+
+}  // namespace kda

@@ -96,11 +96,11 @@ static hipError_t launch_state_t(const LaunchArgs &p) {
     if (vl)
         hipLaunchKernelGGL((kda_state_kernel<C, DK, DV, F32, true>), grid, dim3(192), 0, p.stream,
                            reinterpret_cast<const unsigned char *>(p.workspace), reinterpret_cast<E *>(p.out),
-                           p.final_state, p.init_state, BH, p.T, p.counts, pl.bnd, pl.coff, p.H, p.ncmax);
+                           p.final_state, p.init_state, BH, p.T, p.counts, pl.bnd, pl.coff, p.H, p.ncmax, nullptr);
     else
         hipLaunchKernelGGL((kda_state_kernel<C, DK, DV, F32, false>), grid, dim3(192), 0, p.stream,
                            reinterpret_cast<const unsigned char *>(p.workspace), reinterpret_cast<E *>(p.out),
-                           p.final_state, p.init_state, BH, p.T, p.counts, nullptr, nullptr, p.H, 0);
+                           p.final_state, p.init_state, BH, p.T, p.counts, nullptr, nullptr, p.H, 0, p.states);
     return hipGetLastError();
 }
 

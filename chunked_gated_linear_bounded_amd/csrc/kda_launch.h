@@ -27,6 +27,12 @@ struct LaunchArgs {
     const void *lr_h, *lr_z;    // [B][T][rank], [H][dk][rank] (I/O element type)
     const float *lr_A;          // [H][dk]
     int rank;                   // 16, 32, 64 or 128
+    // backward
+    float *states;              // nullable: chunk start states [B*H][NC][dv][dk] (state stage)
+    float *dstates;             // gradients of the chunk end states, same layout
+    const void *dout;           // [B][H][T][dv] (I/O element type)
+    const float *dfinal;        // nullable: gradient of final_state
+    float *dq, *dk_, *dv_, *da, *dbeta, *dinit;  // float32 gradients (dinit nullable)
 };
 
 hipError_t launch_intra(const LaunchArgs &p);  // chunk-parallel stage -> workspace
@@ -34,5 +40,6 @@ hipError_t launch_intra_lowrank(const LaunchArgs &p);  // the same, gate pre-act
 hipError_t launch_state(const LaunchArgs &p);  // sequential stage: workspace -> out, final state
 hipError_t launch_gate_cumsum(const LaunchArgs &p);
 hipError_t launch_decode(const LaunchArgs &p);  // one token per head, state in place
+hipError_t launch_bwd(const LaunchArgs &p);     // gradients (recompute, reverse state pass, chunk stage)
 
 }  // namespace kda

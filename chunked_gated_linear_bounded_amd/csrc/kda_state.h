@@ -84,8 +84,10 @@ template <int C, int DK, int DV, bool F32, bool VL>
 __global__ __launch_bounds__(192, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void kda_state_kernel(
     const unsigned char *__restrict__ ws, typename StateCfg<C, DK, DV, F32>::E *__restrict__ out,
     float *final_state, const float *init_state, int BH, int T, unsigned long long *__restrict__ counts,
-    const int *__restrict__ bnd, const int *__restrict__ coff, int H, int NCmax)
+    const int *__restrict__ bnd, const int *__restrict__ coff, int H, int NCmax, float *__restrict__ states)
 {
+    // states (nullable, fixed-length only): the state each chunk starts from, [BH][NC][DV][DK] float32 in
+    // final_state's orientation, for the backward pass; out may then be NULL (no outputs stored)
     using Cfg = StateCfg<C, DK, DV, F32>;
     using E = typename Cfg::E;
     using OH = typename std::conditional<F32, float, _Float16>::type;
@@ -253,6 +255,16 @@ __global__ __launch_bounds__(192, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             }
         } else if (wave == 0) {
             // ---- state wave: U = U~ - W S^T;  S^T <- diag(gamma) S^T + K^^T U
+            if (states != nullptr) {  // the state chunk n starts from, unscaled
+                float *sp = states + (((size_t)hb * NC + n) * DV + j0 + l16) * DK + 4 * g;
+#pragma unroll
+                for (int mt = 0; mt < NDK; ++mt) {
+                    f32x4 x;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) x[i] = ldexp2(S[mt][i], -sS);
+                    *reinterpret_cast<f32x4 *>(sp + 16 * mt) = x;
+                }
+            }
             FH Sh[NKB];
             state_operand(Sh);
             f32x4 P[NT];
@@ -358,7 +370,7 @@ __global__ __launch_bounds__(192, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                 f32x4 o;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) o[i] = fmaf(O[tt][i], unO, oi[tt][i] * unI);
-                if (VL && 16 * tt + l16 >= nval) continue;
+                if ((VL && 16 * tt + l16 >= nval) || out == nullptr) continue;
                 // lane holds out[token 16 tt + l16][value j0 + 4g + i]
                 E *op = out + (trow + 16 * tt + l16) * DV + j0 + 4 * g;
                 if constexpr (F32) {

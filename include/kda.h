@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 4
+#define KDA_ABI_VERSION 5
 /* ln(smallest normal float) / 15: the most negative g_min for which 15 steps of
  * decay inside a 16-token tile stay in the normal exponent range. */
 #define KDA_G_MIN_LOWEST (-5.8224f)
@@ -201,6 +201,33 @@ int kda_chunk_fwd_varlen(const void *q, const void *k, const void *v, const void
                          int dv, int io_dtype, void *out, float *final_state, void *workspace,
                          size_t workspace_bytes, hipStream_t stream, int gate_mode,
                          unsigned long long *nonfinite_counts, const float *initial_state);
+
+/* Backward pass: the gradients of L = sum_t dout_t . o_t + <dfinal_state, S_T>
+ * with respect to q, k, v, a, beta and the initial state, for training (the
+ * third page, sec. 2.1: the bounded parameterisation changes the operator, not
+ * the training scripts above it, so the operator supplies exactly these).
+ * Inputs as kda_chunk_fwd_ex (B, H, T, dk, dv, io_dtype, gate_mode, g_min,
+ * initial_state nullable), plus
+ *   dout         : [B][H][T][dv] (io_dtype), the gradient of out
+ *   dfinal_state : [B][H][dv][dk] float32 or NULL (zero)
+ * Outputs, float32 whatever io_dtype, fully overwritten:
+ *   dq_out, dk_out, da_out : [B][H][T][dk]   dv_out : [B][H][T][dv]   dbeta_out : [B][H][T]
+ *   dinitial_state : [B][H][dv][dk] or NULL (not wanted)
+ * da_out is the gradient of the gate pre-activation a (through g = g_min sigmoid(a),
+ * or log sigmoid(a) in the ablation mode).  The backward works on 16-token
+ * chunks whatever chunk the forward used (the gradients do not depend on it):
+ * T % 16 == 0.  workspace: kda_chunk_bwd_workspace_bytes(...) bytes (the
+ * recomputed chunk records and two float32 states per 16-token chunk and head,
+ * B*H*T/16 * (record + 2*dk*dv*4) bytes; 0 for an invalid problem).  No output
+ * may alias an input.  Validation, alignment (16 bytes; beta: element size,
+ * dbeta: 4) and asynchrony as above. */
+size_t kda_chunk_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int io_dtype);
+int kda_chunk_bwd(const void *q, const void *k, const void *v, const void *a, const void *beta,
+                  float g_min, int B, int H, int T, int dk, int dv, int io_dtype, int gate_mode,
+                  const float *initial_state, const void *dout, const float *dfinal_state,
+                  float *dq_out, float *dk_out, float *dv_out, float *da_out, float *dbeta_out,
+                  float *dinitial_state, void *workspace, size_t workspace_bytes,
+                  hipStream_t stream);
 
 /* One token of the recurrence per (batch, head), the state updated in place
  * (decoding after a prefill; the constant-size state of the second page,

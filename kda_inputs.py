@@ -33,7 +33,7 @@ import numpy as np
 import torch
 
 TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "a": 3, "beta": 4, "mix_mask": 5, "mix_sign": 6,
-              "lr_h": 8, "lr_z": 9, "lr_A": 10}
+              "lr_h": 8, "lr_z": 9, "lr_A": 10, "dout": 11, "dfinal": 12}
 
 
 @dataclass(frozen=True)
@@ -189,6 +189,25 @@ def make_lowrank_factors(w: Workload, rank: int, device="cpu"):
         z[hh] = (draw("lr_z", 0, hh, w.dk * rank).view(w.dk, rank) / np.sqrt(rank)).to(dt)
         A[hh] = (np.log(w.a_sigma) + 0.25 * draw("lr_A", 0, hh, w.dk)).to(torch.float32)
     return {"h": h, "z": z, "A_log": A}
+
+
+# Incoming gradients for the backward: dout [B,H,T,dv] ~ N(0,1) in the I/O dtype and dfinal
+# [B,H,dv,dk] ~ 0.1 N(0,1) in float32, per (b, h) slab (ids 11, 12).
+def make_grads(w: Workload, device="cpu"):
+    device = torch.device(device)
+    dout = torch.empty((w.B, w.H, w.T, w.dv), dtype=w.torch_dtype, device=device)
+    dfin = torch.empty((w.B, w.H, w.dv, w.dk), dtype=torch.float32, device=device)
+    for b in range(w.B):
+        for h in range(w.H):
+            if device.type == "cpu":
+                dout[b, h] = torch.from_numpy(_draw_cpu(w.seed, "dout", b, h, w.T * w.dv).reshape(w.T, w.dv)).to(
+                    w.torch_dtype)
+                dfin[b, h] = torch.from_numpy(0.1 * _draw_cpu(w.seed, "dfinal", b, h, w.dv * w.dk).reshape(
+                    w.dv, w.dk)).to(torch.float32)
+            else:
+                dout[b, h] = _draw_dev(w.seed, "dout", b, h, w.T * w.dv, device).view(w.T, w.dv).to(w.torch_dtype)
+                dfin[b, h] = 0.1 * _draw_dev(w.seed, "dfinal", b, h, w.dv * w.dk, device).view(w.dv, w.dk)
+    return dout, dfin
 
 
 def head_slice(inputs, b, h, t_end=None):

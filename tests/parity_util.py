@@ -37,3 +37,21 @@ def _tol_check(got, ref, io, what="out"):
     bad = d > allow
     assert not np.any(bad), "%s: %d elements over the bound, worst excess %.4e" % (
         what, int(bad.sum()), float((d - allow).max()))
+
+
+def _grad_check(got, ref, io, what):
+    """float32 gradients: bf16 inputs |got - ref| <= 2e-2 RMS(ref) + u_bf16 |ref| element-wise (the
+    forward's bar); fp32 inputs |got - ref| <= 1e-4 max(1, RMS(ref)) (the forward's 1e-4, relative
+    once the gradient's own scale passes 1)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, what
+    assert np.all(np.isfinite(got)), "non-finite %s" % what
+    d = np.abs(got - ref)
+    rms = math.sqrt(float(np.mean(ref ** 2))) if ref.size else 0.0
+    allow = (2e-2 * rms + BF16_U * np.abs(ref)) if io == "bf16" else np.full_like(d, 1e-4 * max(1.0, rms))
+    mx = float(d.max()) if d.size else 0.0
+    _say("  %s: max|d|/rms=%.3e rms=%.3e" % (what, mx / max(rms, 1e-30), rms))
+    bad = d > allow
+    assert not np.any(bad), "%s: %d elements over the bound, worst excess %.4e" % (
+        what, int(bad.sum()), float((d - allow).max()))

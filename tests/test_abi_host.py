@@ -28,13 +28,13 @@ def test_header_symbols_exported():
     assert {"kda_abi_version", "kda_status_string", "kda_chunk_fwd_workspace_bytes",
             "kda_gate_cumsum", "kda_chunk_fwd", "kda_chunk_fwd_ex", "kda_chunk_intra", "kda_chunk_state",
             "kda_decode_step", "kda_chunk_fwd_varlen", "kda_chunk_fwd_varlen_workspace_bytes",
-            "kda_chunk_fwd_lowrank"} <= set(names)
+            "kda_chunk_fwd_lowrank", "kda_chunk_bwd", "kda_chunk_bwd_workspace_bytes"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
 
 def test_version_and_strings():
-    assert kda.abi_version() == 4
+    assert kda.abi_version() == 5
     for st in (OK, E_NULL, E_SHAPE, E_DTYPE, E_CHUNK, E_GMIN, E_WS, E_HIP, E_ALIGN, E_MODE):
         s = kda.status_string(st)
         assert s and s != "unknown status"
@@ -177,4 +177,30 @@ def test_lowrank_validation(kw, want):
     st = kda.lib().kda_chunk_fwd_lowrank(a["q"], a["k"], a["v"], a["h"], a["z"], a["A"], a["beta"], a["g_min"],
                                          a["chunk"], a["B"], a["H"], a["T"], a["dk"], a["dv"], a["rank"], a["io"],
                                          a["out"], a["fs"], a["ws"], a["wsb"], None, a["mode"], None, None)
+    assert st == want
+
+
+def test_bwd_workspace_bytes():
+    # the 16-token chunk records plus two float32 states (dk x dv) per 16-token chunk and head
+    rec = kda.workspace_bytes(1, 1, 16, 128, 128, 16, torch.bfloat16)
+    n = 2 * 16 * (4096 // 16)
+    assert kda.bwd_workspace_bytes(2, 16, 4096, 128, 128, torch.bfloat16) == n * (rec + 2 * 128 * 128 * 4)
+    assert kda.bwd_workspace_bytes(1, 2, 40, 64, 64, torch.float32) == 0  # T % 16
+    assert kda.bwd_workspace_bytes(1, 2, 0, 64, 64, torch.float32) == 0
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=None), E_NULL), (dict(dout=None), E_NULL), (dict(dq=None), E_NULL), (dict(dbeta=None), E_NULL),
+    (dict(T=40), E_SHAPE), (dict(dk=96), E_SHAPE), (dict(B=0), E_SHAPE), (dict(io=2), E_DTYPE),
+    (dict(g_min=0.5), E_GMIN), (dict(mode=7), E_MODE), (dict(dout=FAKE + 8), E_ALIGN),
+    (dict(dq=FAKE + 4), E_ALIGN), (dict(s0=FAKE + 4), E_ALIGN), (dict(ws=None), E_WS), (dict(wsb=99), E_WS),
+])
+def test_bwd_validation(kw, want):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, a=FAKE, beta=FAKE, g_min=-5.0, B=1, H=2, T=64, dk=128, dv=128, io=0, mode=0,
+             s0=None, dout=FAKE, dF=None, dq=FAKE, dk_=FAKE, dv_=FAKE, da=FAKE, dbeta=FAKE, dS0=None, ws=FAKE,
+             wsb=1 << 40)
+    a.update(kw)
+    st = kda.lib().kda_chunk_bwd(a["q"], a["k"], a["v"], a["a"], a["beta"], a["g_min"], a["B"], a["H"], a["T"],
+                                 a["dk"], a["dv"], a["io"], a["mode"], a["s0"], a["dout"], a["dF"], a["dq"], a["dk_"],
+                                 a["dv_"], a["da"], a["dbeta"], a["dS0"], a["ws"], a["wsb"], None)
     assert st == want
