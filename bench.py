@@ -273,6 +273,62 @@ def lowrank_bench(args):
                      "frac": alg / (ms * 1e-3) / PEAK_HBM, "bytes_per_step": alg}}), flush=True)
 
 
+def backward_bench(args):
+    """The backward pass (kda_chunk_bwd) over the 64k workload with seeded incoming gradients (dout and
+    a final-state gradient), inputs resident in HBM; one call per step.  Its bytes per step as this
+    design moves them: inputs and dout read, float32 gradients written, the 16-token chunk records
+    written once and read by the state and reverse passes, and the float32 chunk states and their
+    gradients each written once and read once."""
+    import torch
+    import chunked_gated_linear_bounded_amd as kda
+    import kda_inputs as KI
+    w = KI.BY_NAME["64k"]
+    dev = torch.device("cuda:0")
+    print("bench: generating %s inputs and gradients" % w.name, file=sys.stderr, flush=True)
+    inp = KI.make_inputs(w, device=dev)
+    dout, dF = KI.make_grads(w, device=dev)
+    ws = torch.empty(kda.bwd_workspace_bytes(w.B, w.H, w.T, w.dk, w.dv, w.torch_dtype), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        return kda.chunk_bwd(inp["q"], inp["k"], inp["v"], inp["a"], inp["beta"], dout, w.g_min, dfinal_state=dF,
+                             workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        g = step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        g = step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = e0.elapsed_time(e1) / args.steps
+    for key in ("dq", "dk", "dv", "da", "dbeta"):
+        assert torch.isfinite(g[key]).all().item(), "non-finite " + key
+    es = 2
+    th = w.B * w.H * w.T
+    nch = th // 16
+    rec = kda.workspace_bytes(1, 1, 16, w.dk, w.dv, 16, w.torch_dtype)
+    st = w.dk * w.dv * 4
+    io = th * ((3 * w.dk + 2 * w.dv) * es + es)            # q, k, a, v, dout, beta
+    grads = th * ((3 * w.dk + w.dv) * 4 + 4)               # dq, dk, da, dv, dbeta (float32)
+    alg = io + grads + 3 * nch * rec + 4 * nch * st
+    print(json.dumps({
+        "metric": "KDA chunked backward tokens/s (T=64K, H=32, d=128, bf16 inputs, float32 gradients)",
+        "value": w.B * w.T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "wall_ms_per_step": (t1 - t0) * 1e3 / args.steps,
+        "higher_is_better": True, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name + "-backward", "B": w.B, "H": w.H, "T": w.T, "dk": w.dk, "dv": w.dv,
+                   "bwd_chunk": 16, "io": w.io},
+        "roofline": {"kernel": "kda_chunk_bwd (all stages)", "bound": "hbm", "achieved": alg / (ms * 1e-3) / 1e9,
+                     "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": alg / (ms * 1e-3) / PEAK_HBM,
+                     "bytes_per_step": alg}}), flush=True)
+
+
 def cpu_baseline(inputs, w, seconds):
     """The float64 oracle on whole heads of the same workload until `seconds`
     have passed; returns whole-job tokens/s extrapolated from the sampled heads."""
@@ -314,6 +370,8 @@ def main():
                     help="instead of the fixed-length workload, time kda_chunk_fwd_varlen on the 64k packed stream")
     ap.add_argument("--lowrank", type=int, default=0, metavar="R",
                     help="instead of reading a, form the gate pre-activation from a rank-R factor (64k workload)")
+    ap.add_argument("--backward", action="store_true",
+                    help="instead of the forward, time the backward pass (kda_chunk_bwd) on the 64k workload")
     args = ap.parse_args()
     if args.decode_batch > 0:
         decode_bench(args)
@@ -323,6 +381,9 @@ def main():
         return
     if args.lowrank > 0:
         lowrank_bench(args)
+        return
+    if args.backward:
+        backward_bench(args)
         return
     if args.traffic_from:
         if args.copy_calibration <= 0:

@@ -62,10 +62,13 @@ struct BwdCfg {
 // dS' (dk x 16, fp32) from the last chunk to the first, storing it for every chunk (the
 // gradient of the state that chunk ends in), and gives dL/dS_0 at the end.  Reads W^T, Qbar^T,
 // K^ and gamma from the chunk records of the forward's chunk stage (16-token chunks) and the
-// chunk's 16 x 16 block of dout.  The next chunk's record bytes and dout block are loaded into
-// registers while the current chunk is computed.
+// chunk's 16 x 16 block of dout.
+// Work-group = 5 waves: waves 0-3 compute (P = K^ dS' split over the key dimension, then each
+// wave's dk tiles of the update), wave 4 streams each chunk's record and dout block into a ring
+// of three LDS slots with direct global->LDS loads, two chunks ahead; it alone waits on its
+// memory counter, so the barriers only order LDS traffic.
 template <int DK, int DV, bool F32>
-__global__ __launch_bounds__(256) void kda_bwd_dstate_kernel(
+__global__ __launch_bounds__(320) void kda_bwd_dstate_kernel(
     const unsigned char *__restrict__ ws, const typename BwdCfg<DK, DV, F32>::E *__restrict__ dout,
     const float *__restrict__ dfinal, int T, float *__restrict__ dstates, float *__restrict__ dinit)
 {
@@ -73,21 +76,41 @@ __global__ __launch_bounds__(256) void kda_bwd_dstate_kernel(
     using E = typename Cfg::E;
     using OH = typename Cfg::OH;
     constexpr KdaLayout L = Cfg::L;
-    constexpr int NS = Cfg::NS, NDK = DK / 16, NTW = (NDK + 3) / 4;  // dk tiles per wave
-    constexpr int R1 = (int)L.region1, NU = (R1 + 15) / 16;
+    constexpr int NS = Cfg::NS, NDK = DK / 16, NTW = (NDK + 3) / 4;  // dk tiles per compute wave
+    constexpr int R1 = (int)L.region1, NU = (R1 + 15) / 16;          // 16-byte units of region 1
+    constexpr int NBLK = (NU + 63) / 64;                              // 1 KiB direct-load blocks
+    constexpr int RB = NBLK * 1024, SLOT = RB + 1024;                 // record + dout block
+    constexpr int NDMA = NBLK + 1;                                    // loader instructions per chunk
+    static_assert(NDMA <= 63, "partial wait needs the count in the vmcnt field");
     constexpr int PD = 17;
 
-    constexpr int NBLK = (NU + 63) / 64, RB = NBLK * 1024;  // 1 KiB blocks per record copy
-    __shared__ __attribute__((aligned(1024))) unsigned char sRec[2 * RB];
+    __shared__ __attribute__((aligned(1024))) unsigned char sRing[3 * SLOT];
     __shared__ float sD[DK * PD];       // dS' slice: [key c][value j]
     __shared__ float sPp[4][16 * PD];   // split-K partials of P = K^ dS'
-    __shared__ float sdO[16 * PD];
 
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int bh = blockIdx.x / NS, slice = blockIdx.x % NS, j0 = 16 * slice;
     const int NC = T / 16;
     const unsigned char *rec0 = ws + (size_t)bh * NC * L.stride;
+
+    // loader: chunk n into slot s (every lane of every instruction loads; the last block's spare
+    // lanes re-read the last unit into the slot's padding)
+    auto issue = [&](int n, int s) {
+        const unsigned char *src = rec0 + (size_t)n * L.stride;
+        lds_u8 *dst = lds_base(sRing) + s * SLOT;
+#pragma unroll
+        for (int blk = 0; blk < NBLK; ++blk) {
+            const int u = min(blk * 64 + lane, NU - 1);
+            __builtin_amdgcn_global_load_lds(src + (size_t)u * 16, (lds_void *)(dst + blk * 1024), 16, 0, 0);
+        }
+        // dout block: 16 rows x 16 values of this slice, 16 bytes per lane
+        constexpr int LPR = 16 * (int)sizeof(E) / 16;  // lanes per row (2 or 4)
+        const int row = min(lane / LPR, 15), part = lane % LPR;
+        const unsigned char *srow = reinterpret_cast<const unsigned char *>(
+            dout + ((size_t)bh * T + (size_t)n * 16 + row) * DV + j0);
+        __builtin_amdgcn_global_load_lds(srow + 16 * part, (lds_void *)(dst + RB), 16, 0, 0);
+    };
 
     // dS' of the last chunk: dfinal (or zero), kept in registers in accumulator order
     f32x4 D[NTW];
@@ -97,58 +120,47 @@ __global__ __launch_bounds__(256) void kda_bwd_dstate_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int c = 16 * mt + 4 * g + i;
-            D[x][i] = (mt < NDK && dfinal != nullptr) ? dfinal[((size_t)bh * DV + j0 + l16) * DK + c] : 0.f;
+            D[x][i] = (wave < 4 && mt < NDK && dfinal != nullptr) ? dfinal[((size_t)bh * DV + j0 + l16) * DK + c] : 0.f;
         }
     }
-    // the next chunk's record bytes go straight into the other LDS buffer (direct loads,
-    // issued by all four waves) and its dout block into a register, a chunk ahead
-    E pdo = E(0.f);
-    auto prefetch = [&](int nn) {
-        const unsigned char *src = rec0 + (size_t)nn * L.stride;
-        lds_u8 *dst = lds_base(sRec) + (nn & 1) * RB;
-#pragma unroll
-        for (int i = 0; i < NBLK; i += 4) {
-            const int blk = i + wave, u = blk * 64 + lane;
-            if (blk < NBLK && u < NU)
-                __builtin_amdgcn_global_load_lds(src + (size_t)u * 16, (lds_void *)(dst + blk * 1024), 16, 0, 0);
+    if (wave == 4 && NC > 0) {
+        issue(NC - 1, 0);
+        if (NC > 1) {
+            issue(NC - 2, 1);
+            wait_vmcnt<NDMA>();
+        } else {
+            wait_vmcnt<0>();
         }
-        pdo = dout[((size_t)bh * T + (size_t)nn * 16 + (tid >> 4)) * DV + j0 + (tid & 15)];
-    };
-    if (NC > 0) prefetch(NC - 1);
-    wait_vmcnt<0>();
-    __syncthreads();
+    }
 
-    for (int n = NC - 1; n >= 0; --n) {
-        // this chunk's dout block and dS' into LDS (its record is in buffer n & 1)
-        sdO[(tid >> 4) * PD + (tid & 15)] = to_f(pdo);
+    for (int it = 0; it < NC; ++it) {
+        const int n = NC - 1 - it;
+        const unsigned char *cur = sRing + (it % 3) * SLOT;
+        barrier_lds();  // (A) chunk n's slot has landed; the previous chunk is done with sD and sPp
+        if (wave < 4) {
 #pragma unroll
-        for (int x = 0; x < NTW; ++x) {
-            const int mt = wave + 4 * x;
-            if (mt >= NDK) continue;
+            for (int x = 0; x < NTW; ++x) {
+                const int mt = wave + 4 * x;
+                if (mt >= NDK) continue;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sD[(16 * mt + 4 * g + i) * PD + l16] = D[x][i];
+                for (int i = 0; i < 4; ++i) sD[(16 * mt + 4 * g + i) * PD + l16] = D[x][i];
+                // dS' of this chunk's end, for the chunk-parallel stage: dstates[bh][n][value][key]
+                *reinterpret_cast<f32x4 *>(dstates + (((size_t)bh * NC + n) * DV + j0 + l16) * DK + 16 * mt + 4 * g) = D[x];
+            }
         }
-        __syncthreads();
-        if (n > 0) prefetch(n - 1);
-
-        // dS' of this chunk's end, for the chunk-parallel stage: dstates[bh][n][value][key]
-        for (int e = tid; e < DK * 16; e += 256) {
-            const int j = e / DK, c = e % DK;
-            dstates[(((size_t)bh * NC + n) * DV + j0 + j) * DK + c] = sD[c * PD + j];
-        }
-
-        const unsigned char *cur = sRec + (n & 1) * RB;
+        barrier_lds();  // (B) sD holds dS'
         const OH *rWT = reinterpret_cast<const OH *>(cur + L.wt);
         const OH *rQB = reinterpret_cast<const OH *>(cur + L.qbt);
         const OH *rKH = reinterpret_cast<const OH *>(cur + L.kh);
         const float *rG = reinterpret_cast<const float *>(cur + L.gam);
         const int *rS = reinterpret_cast<const int *>(cur + L.scl);
-        const float fW = ldexp2(1.f, -rS[0]), fQ = ldexp2(1.f, -rS[1]), fK = ldexp2(1.f, -rS[2]);
-
-        // P = K^ dS' (16 x 16), K split over the four waves
-        {
+        const E *rdO = reinterpret_cast<const E *>(cur + RB);  // [row][16]
+        if (wave == 4) {
+            if (it + 2 < NC) issue(n - 2, (it + 2) % 3);
+        } else {  // P = K^ dS' (16 x 16), the key dimension split over the four waves
             constexpr int KW = DK / 4;
             const int c0 = KW * wave;
+            const float fK = ldexp2(1.f, -rS[2]);
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             acc = mma_tile<KW>(acc,
                                [&](int m, int kk) { return (float)rKH[pair_offset(m, c0 + kk, NDK)] * fK; },
@@ -156,37 +168,38 @@ __global__ __launch_bounds__(256) void kda_bwd_dstate_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i) sPp[wave][(4 * g + i) * PD + l16] = acc[i];
         }
-        __syncthreads();
-
-        // dS = diag(gamma) dS' + Qbar^T dO - W^T P  (rows c of this wave's dk tiles)
+        barrier_lds();  // (C) the partials of P are in
+        if (wave == 4) {
+            if (it + 2 < NC) wait_vmcnt<NDMA>();  // chunk n - 1 has landed (n - 2 may be in flight)
+            else wait_vmcnt<0>();
+        } else {
+            // dS = diag(gamma) dS' + Qbar^T dO - W^T P  (rows c of this wave's dk tiles)
+            const float fW = ldexp2(1.f, -rS[0]), fQ = ldexp2(1.f, -rS[1]);
 #pragma unroll
-        for (int x = 0; x < NTW; ++x) {
-            const int mt = wave + 4 * x;
-            if (mt >= NDK) continue;
-            f32x4 acc;
+            for (int x = 0; x < NTW; ++x) {
+                const int mt = wave + 4 * x;
+                if (mt >= NDK) continue;
+                f32x4 acc;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] = rG[16 * mt + 4 * g + i] * D[x][i];
-            acc = mma_tile<16>(acc, [&](int m, int kk) { return (float)rQB[pair_offset(16 * mt + m, kk, 1)] * fQ; },
-                               [&](int kk, int nn) { return sdO[kk * PD + nn]; }, lane);
-            acc = mma_tile<16>(acc, [&](int m, int kk) { return -(float)rWT[pair_offset(16 * mt + m, kk, 1)] * fW; },
-                               [&](int kk, int nn) {
-                                   const int o = kk * PD + nn;
-                                   return (sPp[0][o] + sPp[1][o]) + (sPp[2][o] + sPp[3][o]);
-                               },
-                               lane);
-            D[x] = acc;
+                for (int i = 0; i < 4; ++i) acc[i] = rG[16 * mt + 4 * g + i] * D[x][i];
+                acc = mma_tile<16>(acc, [&](int m, int kk) { return (float)rQB[pair_offset(16 * mt + m, kk, 1)] * fQ; },
+                                   [&](int kk, int nn) { return to_f(rdO[kk * 16 + nn]); }, lane);
+                acc = mma_tile<16>(acc, [&](int m, int kk) { return -(float)rWT[pair_offset(16 * mt + m, kk, 1)] * fW; },
+                                   [&](int kk, int nn) {
+                                       const int o = kk * PD + nn;
+                                       return (sPp[0][o] + sPp[1][o]) + (sPp[2][o] + sPp[3][o]);
+                                   },
+                                   lane);
+                D[x] = acc;
+            }
         }
-        wait_vmcnt<0>();  // the next record has landed
-        __syncthreads();  // sD, sPp, sdO and this record's buffer are rewritten next
     }
-    if (dinit != nullptr) {
+    if (dinit != nullptr && wave < 4) {
 #pragma unroll
         for (int x = 0; x < NTW; ++x) {
             const int mt = wave + 4 * x;
             if (mt >= NDK) continue;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                dinit[((size_t)bh * DV + j0 + l16) * DK + 16 * mt + 4 * g + i] = D[x][i];
+            *reinterpret_cast<f32x4 *>(dinit + ((size_t)bh * DV + j0 + l16) * DK + 16 * mt + 4 * g) = D[x];
         }
     }
 }
@@ -194,7 +207,7 @@ __global__ __launch_bounds__(256) void kda_bwd_dstate_kernel(
 // ---------------------------------------------------------------------------------------
 // Gradients of one 16-token chunk of one head, from the state it starts from (states) and
 // the gradient of the state it ends in (dstates).  All intermediates in fp32; the state S
-// is held in LDS, dS' is read from global memory (L2) where a product needs it.  Work-
+// is held in LDS, dS' is staged through LDS a quarter at a time.  Work-
 // group = 4 waves; products over a dk- or dv-wide dimension are split by 16-column tiles
 // over the waves, and each wave keeps its tiles of dq, dk and dG in registers.
 template <int DK, int DV, bool F32>
@@ -215,6 +228,7 @@ __global__ __launch_bounds__(256, 1) void kda_bwd_chunk_kernel(
     __shared__ float sdU[C * PV];  // K^ dS', then dU
     __shared__ float sP[C * P16], sM[C * P16], sT[C * P16], sdM[C * P16], sdT[C * P16], sdA[C * P16];
     __shared__ float sB[C], sGl[DK], sDg[DK], sdb[4][C];
+    __shared__ float sDq[DV / 4 * PK];  // a quarter of dS' (value rows) at a time
 
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -224,23 +238,82 @@ __global__ __launch_bounds__(256, 1) void kda_bwd_chunk_kernel(
     const float *Dg = dstates + ((size_t)bh * NC + n) * DV * DK;  // dS' as [value j][key c]
 
     // ---------------------------------------------------------------- loads, G
-    for (int e = tid; e < C * DK; e += 256) {
-        const int r = e / DK, c = e % DK;
-        sQ[r * PK + c] = to_f(q[(t0 + r) * DK + c]);
-        sK[r * PK + c] = to_f(k[(t0 + r) * DK + c]);
+    // Every load of the chunk is issued before any is consumed (16-byte accesses; a chunk's
+    // rows of q, k, v, dout and a are contiguous, as is its state), so the work-group pays one
+    // memory round trip; a goes to LDS (its gate and prefix sum are taken from there).
+    {
+        using E = typename BwdCfg<DK, DV, F32>::E;
+        constexpr int VE = 16 / (int)sizeof(E);                       // elements per 16 bytes
+        constexpr int UK = C * DK / VE, UV = C * DV / VE;             // 16-byte units per block
+        constexpr int NK = (UK + 255) / 256, NV = (UV + 255) / 256, NSS = DV * DK / 4 / 256;
+        uint4 xq[NK], xk[NK], xa[NK], xv[NV], xo[NV];
+        f32x4 xs[NSS];
+        const uint4 *gq = reinterpret_cast<const uint4 *>(q + t0 * DK);
+        const uint4 *gk = reinterpret_cast<const uint4 *>(k + t0 * DK);
+        const uint4 *ga = reinterpret_cast<const uint4 *>(a + t0 * DK);
+        const uint4 *gv = reinterpret_cast<const uint4 *>(v + t0 * DV);
+        const uint4 *go = reinterpret_cast<const uint4 *>(dout + t0 * DV);
+#pragma unroll
+        for (int x = 0; x < NSS; ++x) xs[x] = reinterpret_cast<const f32x4 *>(Sg)[tid + 256 * x];
+#pragma unroll
+        for (int x = 0; x < NK; ++x) {
+            const int u = min(tid + 256 * x, UK - 1);
+            xq[x] = gq[u];
+            xk[x] = gk[u];
+            xa[x] = ga[u];
+        }
+#pragma unroll
+        for (int x = 0; x < NV; ++x) {
+            const int u = min(tid + 256 * x, UV - 1);
+            xv[x] = gv[u];
+            xo[x] = go[u];
+        }
+        const float bv = to_f(beta[t0 + (tid & (C - 1))]);
+#pragma unroll
+        for (int x = 0; x < NSS; ++x) {
+            const int e = 4 * (tid + 256 * x), j = e / DK, c = e % DK;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sS[j * PK + c + i] = xs[x][i];
+        }
+#pragma unroll
+        for (int x = 0; x < NK; ++x) {
+            const int u = tid + 256 * x;
+            if (u >= UK) continue;
+            const int e = u * VE, r = e / DK, c = e % DK;
+            const E *pq = reinterpret_cast<const E *>(&xq[x]), *pk = reinterpret_cast<const E *>(&xk[x]);
+            const E *pa = reinterpret_cast<const E *>(&xa[x]);
+#pragma unroll
+            for (int i = 0; i < VE; ++i) {
+                sQ[r * PK + c + i] = to_f(pq[i]);
+                sK[r * PK + c + i] = to_f(pk[i]);
+                sG[r * PK + c + i] = to_f(pa[i]);  // a for now; G below
+            }
+        }
+#pragma unroll
+        for (int x = 0; x < NV; ++x) {
+            const int u = tid + 256 * x;
+            if (u >= UV) continue;
+            const int e = u * VE, r = e / DV, c = e % DV;
+            const E *pv = reinterpret_cast<const E *>(&xv[x]), *po = reinterpret_cast<const E *>(&xo[x]);
+#pragma unroll
+            for (int i = 0; i < VE; ++i) {
+                sV[r * PV + c + i] = to_f(pv[i]);
+                sdO[r * PV + c + i] = to_f(po[i]);
+            }
+        }
+        if (tid < C) sB[tid] = bv;
     }
-    for (int e = tid; e < C * DV; e += 256) {
-        const int r = e / DV, c = e % DV;
-        sV[r * PV + c] = to_f(v[(t0 + r) * DV + c]);
-        sdO[r * PV + c] = to_f(dout[(t0 + r) * DV + c]);
-    }
-    for (int e = tid; e < DV * DK; e += 256) sS[(e / DK) * PK + e % DK] = Sg[e];
-    if (tid < C) sB[tid] = to_f(beta[t0 + tid]);
-    if (tid < DK) {
+    __syncthreads();
+    float gpr[C];  // dg/da of column tid (threads tid < DK), used at the end
+    if (tid < DK) {  // gate and prefix sum down the chunk, in place (log2 units); g'(a) kept for da
         float acc = 0.f;
+#pragma unroll
         for (int r = 0; r < C; ++r) {
-            acc += gate_log2(to_f(a[(t0 + r) * DK + tid]), gmin2, logsig);
-            sG[r * PK + tid] = acc;  // log2 units
+            const float av = sG[r * PK + tid];
+            acc += gate_log2(av, gmin2, logsig);
+            const float sg = 1.f / (1.f + __expf(-av));
+            gpr[r] = logsig ? (1.f - sg) : gmin * sg * (1.f - sg);  // dg/da, kept by this thread
+            sG[r * PK + tid] = acc;
         }
     }
     __syncthreads();
@@ -336,40 +409,66 @@ __global__ __launch_bounds__(256, 1) void kda_bwd_chunk_kernel(
     __syncthreads();
 
     // ---------------------------------------------------------------- with dS': K^ dS', dK^, dgamma
+    // dS' is staged through LDS a quarter of its value rows at a time (QJ rows of [value][key]);
+    // the next quarter is loaded into registers while the current one is used.
+    {
+        constexpr int QJ = DV / 4, QN = QJ * DK / 256;  // rows and values per thread of a quarter
+        float pf[QN];
 #pragma unroll
-    for (int x = 0; x < NTV; ++x) {
-        const int nt = wave + 4 * x;
-        if (nt >= NDV) continue;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = mma_tile<DK>(acc, [&](int m, int kk) { return Kv(m, kk) * EH(m, kk); },
-                           [&](int kk, int nn) { return Dg[(16 * nt + nn) * DK + kk]; }, lane);
+        for (int x = 0; x < QN; ++x) pf[x] = Dg[tid + 256 * x];
+        f32x4 dKh[NTK];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sdU[(4 * g + i) * PV + 16 * nt + l16] = acc[i];
-    }
+        for (int x = 0; x < NTK; ++x) dKh[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float dgam = 0.f;
+        for (int qd = 0; qd < 4; ++qd) {
 #pragma unroll
-    for (int x = 0; x < NTK; ++x) {
-        const int nt = wave + 4 * x;
-        if (nt >= NDK) continue;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = mma_tile<DV>(acc, [&](int m, int kk) { return sU[m * PV + kk]; },
-                           [&](int kk, int nn) { return Dg[kk * DK + 16 * nt + nn]; }, lane);
-        float col = 0.f;
+            for (int x = 0; x < QN; ++x) {
+                const int e = tid + 256 * x;
+                sDq[(e / DK) * PK + e % DK] = pf[x];
+            }
+            __syncthreads();
+            if (qd < 3) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 4 * g + i, c = 16 * nt + l16;
-            const float eh = EH(r, c), kh = Kv(r, c) * eh;
-            dKa[x][i] += acc[i] * eh;   // dK^ e^{G_last - G}
-            dGa[x][i] -= acc[i] * kh;   // - dK^ * K^
-            col += acc[i] * kh;
+                for (int x = 0; x < QN; ++x) pf[x] = Dg[(size_t)(qd + 1) * QJ * DK + tid + 256 * x];
+            }
+            if (wave < QJ / 16) {  // dUs = K^ dS' for the quarter's value tiles
+                const int nt = qd * (QJ / 16) + wave;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                acc = mma_tile<DK>(acc, [&](int m, int kk) { return Kv(m, kk) * EH(m, kk); },
+                                   [&](int kk, int nn) { return sDq[(16 * wave + nn) * PK + kk]; }, lane);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sdU[(4 * g + i) * PV + 16 * nt + l16] = acc[i];
+            }
+#pragma unroll
+            for (int x = 0; x < NTK; ++x) {  // dK^ += U[:, quarter] dS'[quarter rows]
+                const int nt = wave + 4 * x;
+                if (nt >= NDK) continue;
+                dKh[x] = mma_tile<QJ>(dKh[x], [&](int m, int kk) { return sU[m * PV + qd * QJ + kk]; },
+                                      [&](int kk, int nn) { return sDq[kk * PK + 16 * nt + nn]; }, lane);
+            }
+            if (tid < DK) {
+                for (int jj = 0; jj < QJ; ++jj) dgam += sS[(qd * QJ + jj) * PK + tid] * sDq[jj * PK + tid];
+            }
+            __syncthreads();
         }
-        col += __shfl_xor(col, 16, 64);
-        col += __shfl_xor(col, 32, 64);
-        if (g == 0) sGl[16 * nt + l16] = col;  // sum over the chunk's rows of dK^ * K^
-    }
-    for (int c = tid; c < DK; c += 256) {
-        float s = 0.f;
-        for (int j = 0; j < DV; ++j) s += sS[j * PK + c] * Dg[j * DK + c];
-        sDg[c] = s;  // dgamma_c
+        if (tid < DK) sDg[tid] = dgam;  // dgamma_c
+#pragma unroll
+        for (int x = 0; x < NTK; ++x) {
+            const int nt = wave + 4 * x;
+            if (nt >= NDK) continue;
+            float col = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * g + i, c = 16 * nt + l16;
+                const float eh = EH(r, c), kh = Kv(r, c) * eh;
+                dKa[x][i] += dKh[x][i] * eh;   // dK^ e^{G_last - G}
+                dGa[x][i] -= dKh[x][i] * kh;   // - dK^ * K^
+                col += dKh[x][i] * kh;
+            }
+            col += __shfl_xor(col, 16, 64);
+            col += __shfl_xor(col, 32, 64);
+            if (g == 0) sGl[16 * nt + l16] = col;  // sum over the chunk's rows of dK^ * K^
+        }
     }
     __syncthreads();
 
@@ -526,11 +625,10 @@ __global__ __launch_bounds__(256, 1) void kda_bwd_chunk_kernel(
     __syncthreads();
     if (tid < DK) {
         float acc = 0.f;
+#pragma unroll
         for (int r = C - 1; r >= 0; --r) {
             acc += sW[r * PK + tid];
-            const float av = to_f(a[(t0 + r) * DK + tid]);
-            const float s = 1.f / (1.f + __expf(-av));
-            da[(t0 + r) * DK + tid] = acc * (logsig ? (1.f - s) : gmin * s * (1.f - s));
+            da[(t0 + r) * DK + tid] = acc * gpr[r];
         }
     }
     if (tid < C) dbeta[t0 + tid] = (sdb[0][tid] + sdb[1][tid]) + (sdb[2][tid] + sdb[3][tid]);

@@ -12,7 +12,7 @@ template <int DK, int DV, bool F32>
 static hipError_t launch_bwd_t(const LaunchArgs &p) {
     using E = typename std::conditional<F32, float, __bf16>::type;
     const int BH = p.B * p.H, NC = p.T / 16;
-    hipLaunchKernelGGL((kda_bwd_dstate_kernel<DK, DV, F32>), dim3(BH * (DV / 16)), dim3(256), 0, p.stream,
+    hipLaunchKernelGGL((kda_bwd_dstate_kernel<DK, DV, F32>), dim3(BH * (DV / 16)), dim3(320), 0, p.stream,
                        reinterpret_cast<const unsigned char *>(p.workspace), reinterpret_cast<const E *>(p.dout),
                        p.dfinal, p.T, p.dstates, p.dinit);
     hipError_t e = hipGetLastError();
