@@ -207,11 +207,12 @@ __global__ __launch_bounds__(320) void kda_bwd_dstate_kernel(
 // ---------------------------------------------------------------------------------------
 // Gradients of one 16-token chunk of one head, from the state it starts from (states) and
 // the gradient of the state it ends in (dstates).  All intermediates in fp32; the state S
-// is held in LDS, dS' is staged through LDS a quarter at a time.  Work-
-// group = 4 waves; products over a dk- or dv-wide dimension are split by 16-column tiles
-// over the waves, and each wave keeps its tiles of dq, dk and dG in registers.
+// is held in LDS, dS' is staged through LDS a quarter at a time.  Work-group = 8 waves
+// (two per SIMD, the LDS allows one work-group per CU); products over a dk- or dv-wide
+// dimension are split by 16-column tiles over the waves, and each wave keeps its tiles of
+// dq, dk and dG in registers.
 template <int DK, int DV, bool F32>
-__global__ __launch_bounds__(256, 1) void kda_bwd_chunk_kernel(
+__global__ __launch_bounds__(512, 1) void kda_bwd_chunk_kernel(
     const typename BwdCfg<DK, DV, F32>::E *__restrict__ q, const typename BwdCfg<DK, DV, F32>::E *__restrict__ k,
     const typename BwdCfg<DK, DV, F32>::E *__restrict__ v, const typename BwdCfg<DK, DV, F32>::E *__restrict__ a,
     const typename BwdCfg<DK, DV, F32>::E *__restrict__ beta,
@@ -219,15 +220,15 @@ __global__ __launch_bounds__(256, 1) void kda_bwd_chunk_kernel(
     const float *__restrict__ states, const float *__restrict__ dstates, float *__restrict__ dq,
     float *__restrict__ dk, float *__restrict__ dv, float *__restrict__ da, float *__restrict__ dbeta)
 {
-    constexpr int C = 16, PK = DK + 1, PV = DV + 1, P16 = 17;
-    constexpr int NDK = DK / 16, NDV = DV / 16, NTK = (NDK + 3) / 4, NTV = (NDV + 3) / 4;
+    constexpr int C = 16, PK = DK + 1, PV = DV + 1, P16 = 17, NW = 8, NTH = 64 * NW;
+    constexpr int NDK = DK / 16, NDV = DV / 16, NTK = (NDK + NW - 1) / NW, NTV = (NDV + NW - 1) / NW;
     __shared__ float sQ[C * PK], sK[C * PK], sG[C * PK], sV[C * PV], sdO[C * PV];
     __shared__ float sS[DV * PK];  // the chunk's start state as stored: [value j][key c]
     __shared__ float sW[C * PK];   // W, then dW, then dG
     __shared__ float sU[C * PV];   // U~, then U
     __shared__ float sdU[C * PV];  // K^ dS', then dU
     __shared__ float sP[C * P16], sM[C * P16], sT[C * P16], sdM[C * P16], sdT[C * P16], sdA[C * P16];
-    __shared__ float sB[C], sGl[DK], sDg[DK], sdb[4][C];
+    __shared__ float sB[C], sGl[DK], sDg[DK], sdb[NW][C];
     __shared__ float sDq[DV / 4 * PK];  // a quarter of dS' (value rows) at a time
 
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
@@ -245,7 +246,7 @@ __global__ __launch_bounds__(256, 1) void kda_bwd_chunk_kernel(
         using E = typename BwdCfg<DK, DV, F32>::E;
         constexpr int VE = 16 / (int)sizeof(E);                       // elements per 16 bytes
         constexpr int UK = C * DK / VE, UV = C * DV / VE;             // 16-byte units per block
-        constexpr int NK = (UK + 255) / 256, NV = (UV + 255) / 256, NSS = DV * DK / 4 / 256;
+        constexpr int NK = (UK + NTH - 1) / NTH, NV = (UV + NTH - 1) / NTH, NSS = DV * DK / 4 / NTH;
         uint4 xq[NK], xk[NK], xa[NK], xv[NV], xo[NV];
         f32x4 xs[NSS];
         const uint4 *gq = reinterpret_cast<const uint4 *>(q + t0 * DK);
@@ -254,30 +255,30 @@ __global__ __launch_bounds__(256, 1) void kda_bwd_chunk_kernel(
         const uint4 *gv = reinterpret_cast<const uint4 *>(v + t0 * DV);
         const uint4 *go = reinterpret_cast<const uint4 *>(dout + t0 * DV);
 #pragma unroll
-        for (int x = 0; x < NSS; ++x) xs[x] = reinterpret_cast<const f32x4 *>(Sg)[tid + 256 * x];
+        for (int x = 0; x < NSS; ++x) xs[x] = reinterpret_cast<const f32x4 *>(Sg)[tid + NTH * x];
 #pragma unroll
         for (int x = 0; x < NK; ++x) {
-            const int u = min(tid + 256 * x, UK - 1);
+            const int u = min(tid + NTH * x, UK - 1);
             xq[x] = gq[u];
             xk[x] = gk[u];
             xa[x] = ga[u];
         }
 #pragma unroll
         for (int x = 0; x < NV; ++x) {
-            const int u = min(tid + 256 * x, UV - 1);
+            const int u = min(tid + NTH * x, UV - 1);
             xv[x] = gv[u];
             xo[x] = go[u];
         }
         const float bv = to_f(beta[t0 + (tid & (C - 1))]);
 #pragma unroll
         for (int x = 0; x < NSS; ++x) {
-            const int e = 4 * (tid + 256 * x), j = e / DK, c = e % DK;
+            const int e = 4 * (tid + NTH * x), j = e / DK, c = e % DK;
 #pragma unroll
             for (int i = 0; i < 4; ++i) sS[j * PK + c + i] = xs[x][i];
         }
 #pragma unroll
         for (int x = 0; x < NK; ++x) {
-            const int u = tid + 256 * x;
+            const int u = tid + NTH * x;
             if (u >= UK) continue;
             const int e = u * VE, r = e / DK, c = e % DK;
             const E *pq = reinterpret_cast<const E *>(&xq[x]), *pk = reinterpret_cast<const E *>(&xk[x]);
@@ -291,7 +292,7 @@ __global__ __launch_bounds__(256, 1) void kda_bwd_chunk_kernel(
         }
 #pragma unroll
         for (int x = 0; x < NV; ++x) {
-            const int u = tid + 256 * x;
+            const int u = tid + NTH * x;
             if (u >= UV) continue;
             const int e = u * VE, r = e / DV, c = e % DV;
             const E *pv = reinterpret_cast<const E *>(&xv[x]), *po = reinterpret_cast<const E *>(&xo[x]);
@@ -356,7 +357,7 @@ __global__ __launch_bounds__(256, 1) void kda_bwd_chunk_kernel(
     auto Xv = [&](int r, int c) { return sB[r] * Kv(r, c) * EG(r, c); };  // b K e^G
 #pragma unroll
     for (int x = 0; x < NTK; ++x) {
-        const int nt = wave + 4 * x;
+        const int nt = wave + NW * x;
         if (nt >= NDK) continue;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         acc = mma_tile<C>(acc, [&](int m, int kk) { return sT[m * P16 + kk]; },
@@ -366,7 +367,7 @@ __global__ __launch_bounds__(256, 1) void kda_bwd_chunk_kernel(
     }
 #pragma unroll
     for (int x = 0; x < NTV; ++x) {
-        const int nt = wave + 4 * x;
+        const int nt = wave + NW * x;
         if (nt >= NDV) continue;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         acc = mma_tile<C>(acc, [&](int m, int kk) { return sT[m * P16 + kk]; },
@@ -380,7 +381,7 @@ __global__ __launch_bounds__(256, 1) void kda_bwd_chunk_kernel(
     f32x4 dQa[NTK], dKa[NTK], dGa[NTK];  // this wave's dk tiles of dq, dk and dG
 #pragma unroll
     for (int x = 0; x < NTV; ++x) {
-        const int nt = wave + 4 * x;
+        const int nt = wave + NW * x;
         if (nt >= NDV) continue;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         acc = mma_tile<DK>(acc, [&](int m, int kk) { return sW[m * PK + kk]; },
@@ -393,7 +394,7 @@ __global__ __launch_bounds__(256, 1) void kda_bwd_chunk_kernel(
     }
 #pragma unroll
     for (int x = 0; x < NTK; ++x) {
-        const int nt = wave + 4 * x;
+        const int nt = wave + NW * x;
         dQa[x] = dKa[x] = dGa[x] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (nt >= NDK) continue;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -412,10 +413,10 @@ __global__ __launch_bounds__(256, 1) void kda_bwd_chunk_kernel(
     // dS' is staged through LDS a quarter of its value rows at a time (QJ rows of [value][key]);
     // the next quarter is loaded into registers while the current one is used.
     {
-        constexpr int QJ = DV / 4, QN = QJ * DK / 256;  // rows and values per thread of a quarter
+        constexpr int QJ = DV / 4, QN = QJ * DK / NTH;  // rows and values per thread of a quarter
         float pf[QN];
 #pragma unroll
-        for (int x = 0; x < QN; ++x) pf[x] = Dg[tid + 256 * x];
+        for (int x = 0; x < QN; ++x) pf[x] = Dg[tid + NTH * x];
         f32x4 dKh[NTK];
 #pragma unroll
         for (int x = 0; x < NTK; ++x) dKh[x] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -423,13 +424,13 @@ __global__ __launch_bounds__(256, 1) void kda_bwd_chunk_kernel(
         for (int qd = 0; qd < 4; ++qd) {
 #pragma unroll
             for (int x = 0; x < QN; ++x) {
-                const int e = tid + 256 * x;
+                const int e = tid + NTH * x;
                 sDq[(e / DK) * PK + e % DK] = pf[x];
             }
             __syncthreads();
             if (qd < 3) {
 #pragma unroll
-                for (int x = 0; x < QN; ++x) pf[x] = Dg[(size_t)(qd + 1) * QJ * DK + tid + 256 * x];
+                for (int x = 0; x < QN; ++x) pf[x] = Dg[(size_t)(qd + 1) * QJ * DK + tid + NTH * x];
             }
             if (wave < QJ / 16) {  // dUs = K^ dS' for the quarter's value tiles
                 const int nt = qd * (QJ / 16) + wave;
@@ -441,7 +442,7 @@ __global__ __launch_bounds__(256, 1) void kda_bwd_chunk_kernel(
             }
 #pragma unroll
             for (int x = 0; x < NTK; ++x) {  // dK^ += U[:, quarter] dS'[quarter rows]
-                const int nt = wave + 4 * x;
+                const int nt = wave + NW * x;
                 if (nt >= NDK) continue;
                 dKh[x] = mma_tile<QJ>(dKh[x], [&](int m, int kk) { return sU[m * PV + qd * QJ + kk]; },
                                       [&](int kk, int nn) { return sDq[kk * PK + 16 * nt + nn]; }, lane);
@@ -454,7 +455,7 @@ __global__ __launch_bounds__(256, 1) void kda_bwd_chunk_kernel(
         if (tid < DK) sDg[tid] = dgam;  // dgamma_c
 #pragma unroll
         for (int x = 0; x < NTK; ++x) {
-            const int nt = wave + 4 * x;
+            const int nt = wave + NW * x;
             if (nt >= NDK) continue;
             float col = 0.f;
 #pragma unroll
@@ -475,7 +476,7 @@ __global__ __launch_bounds__(256, 1) void kda_bwd_chunk_kernel(
     // ---------------------------------------------------------------- dU = M^T dO + K^ dS', dM
 #pragma unroll
     for (int x = 0; x < NTV; ++x) {
-        const int nt = wave + 4 * x;
+        const int nt = wave + NW * x;
         if (nt >= NDV) continue;
         f32x4 acc;
 #pragma unroll
@@ -497,7 +498,7 @@ __global__ __launch_bounds__(256, 1) void kda_bwd_chunk_kernel(
     // ---------------------------------------------------------------- dW = -dU S^T
 #pragma unroll
     for (int x = 0; x < NTK; ++x) {
-        const int nt = wave + 4 * x;
+        const int nt = wave + NW * x;
         if (nt >= NDK) continue;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         acc = mma_tile<DV>(acc, [&](int m, int kk) { return sdU[m * PV + kk]; },
@@ -523,7 +524,7 @@ __global__ __launch_bounds__(256, 1) void kda_bwd_chunk_kernel(
     float db[4] = {0.f, 0.f, 0.f, 0.f};  // this wave's part of dbeta for rows 4g+i
 #pragma unroll
     for (int x = 0; x < NTK; ++x) {
-        const int nt = wave + 4 * x;
+        const int nt = wave + NW * x;
         if (nt >= NDK) continue;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         acc = mma_tile<C>(acc, [&](int m, int kk) { return sT[kk * P16 + m]; },
@@ -539,7 +540,7 @@ __global__ __launch_bounds__(256, 1) void kda_bwd_chunk_kernel(
     }
 #pragma unroll
     for (int x = 0; x < NTV; ++x) {
-        const int nt = wave + 4 * x;
+        const int nt = wave + NW * x;
         if (nt >= NDV) continue;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         acc = mma_tile<C>(acc, [&](int m, int kk) { return sT[kk * P16 + m]; },
@@ -584,7 +585,7 @@ __global__ __launch_bounds__(256, 1) void kda_bwd_chunk_kernel(
     // ---------------------------------------------------------------- pairwise terms of M and P
 #pragma unroll
     for (int x = 0; x < NTK; ++x) {
-        const int nt = wave + 4 * x;
+        const int nt = wave + NW * x;
         if (nt >= NDK) continue;
         const int cn = 16 * nt;
         f32x4 x1 = {0.f, 0.f, 0.f, 0.f}, x2 = x1, x3 = x1, x4 = x1;
@@ -610,7 +611,7 @@ __global__ __launch_bounds__(256, 1) void kda_bwd_chunk_kernel(
     // ---------------------------------------------------------------- outputs; dg = reverse cumsum of dG
 #pragma unroll
     for (int x = 0; x < NTK; ++x) {
-        const int nt = wave + 4 * x;
+        const int nt = wave + NW * x;
         if (nt >= NDK) continue;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -631,7 +632,12 @@ __global__ __launch_bounds__(256, 1) void kda_bwd_chunk_kernel(
             da[(t0 + r) * DK + tid] = acc * gpr[r];
         }
     }
-    if (tid < C) dbeta[t0 + tid] = (sdb[0][tid] + sdb[1][tid]) + (sdb[2][tid] + sdb[3][tid]);
+    if (tid < C) {
+        float sb = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) sb += sdb[w][tid];
+        dbeta[t0 + tid] = sb;
+    }
 }
 
 }  // namespace kda

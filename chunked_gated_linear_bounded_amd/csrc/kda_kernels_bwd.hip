@@ -17,7 +17,7 @@ static hipError_t launch_bwd_t(const LaunchArgs &p) {
                        p.dfinal, p.T, p.dstates, p.dinit);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((kda_bwd_chunk_kernel<DK, DV, F32>), dim3(NC, BH), dim3(256), 0, p.stream,
+    hipLaunchKernelGGL((kda_bwd_chunk_kernel<DK, DV, F32>), dim3(NC, BH), dim3(512), 0, p.stream,
                        reinterpret_cast<const E *>(p.q), reinterpret_cast<const E *>(p.k),
                        reinterpret_cast<const E *>(p.v), reinterpret_cast<const E *>(p.a),
                        reinterpret_cast<const E *>(p.beta), reinterpret_cast<const E *>(p.dout), p.g_min * kLog2e,
