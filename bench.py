@@ -40,12 +40,20 @@ def path_bytes_per_token_head(dk, dv, es):
     return (3 * dk + dv + dv) * es + es
 
 
+# the sources the forward's chunk and state kernels are compiled from (the translation unit and
+# every header it includes): counters taken on other sources are not reported
+FWD_SOURCES = ("kda_kernels.hip", "kda_device.h", "kda_intra.h", "kda_state.h", "kda_layout.h", "kda_launch.h",
+               "kda_varlen.h", "kda_decode.h")
+
+
 def _src_sha():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "chunked_gated_linear_bounded_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in FWD_SOURCES:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
+    with open(os.path.join(ROOT, "chunked_gated_linear_bounded_amd", "build.py"), "rb") as fh:  # the flags
+        h.update(fh.read())
     return h.hexdigest()[:16]
 
 
