@@ -12,6 +12,7 @@ built, every entry point raises; there is no fallback.
     o = kda.chunk_fwd_varlen(q, k, v, a, beta, cu_seqlens)             # packed documents, [H,T,d]
     o = kda.chunk_fwd_lowrank(q, k, v, h, z, A_log, beta)              # a = e^A (h z^T) in-kernel
     g = kda.chunk_bwd(q, k, v, a, beta, dout)                          # gradients (training)
+    out, S = kda.KdaChunkFunction.apply(q, k, v, a, beta)              # the same, under autograd
     G = kda.gate_cumsum(a, g_min=-5.0, chunk=64)
 """
 from __future__ import annotations
@@ -351,6 +352,30 @@ def chunk_bwd(q, k, v, a, beta, dout, g_min=-5.0, initial_state=None, dfinal_sta
     if st != KDA_OK:
         raise KdaError("kda_chunk_bwd", st)
     return g
+
+
+class KdaChunkFunction(torch.autograd.Function):
+    """out, final_state = KdaChunkFunction.apply(q, k, v, a, beta, g_min, chunk, gate): the chunked
+    forward with its backward, for training.  Forward through kda_chunk_fwd_ex, backward through
+    kda_chunk_bwd (T % 16 == 0); the float32 gradients are returned in the inputs' dtype.  No
+    initial state (S_0 = 0)."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, a, beta, g_min=-5.0, chunk=64, gate="bounded"):
+        out, fs = chunk_fwd(q, k, v, a, beta, g_min=g_min, chunk=chunk, return_final_state=True, gate=gate)
+        ctx.save_for_backward(q, k, v, a, beta)
+        ctx.g_min, ctx.gate = g_min, gate
+        return out, fs
+
+    @staticmethod
+    def backward(ctx, dout, dfinal):
+        q, k, v, a, beta = ctx.saved_tensors
+        dout = torch.zeros_like(q[..., :1].expand(*q.shape[:-1], v.shape[-1])) if dout is None else dout
+        g = chunk_bwd(q, k, v, a, beta, dout.contiguous().to(q.dtype), ctx.g_min,
+                      dfinal_state=None if dfinal is None else dfinal.contiguous().float(), gate=ctx.gate,
+                      want_dinitial=False)
+        return (g["dq"].to(q.dtype), g["dk"].to(k.dtype), g["dv"].to(v.dtype), g["da"].to(a.dtype),
+                g["dbeta"].to(beta.dtype), None, None, None)
 
 
 def decode_step(q, k, v, a, beta, state, g_min=-5.0, gate="bounded", out=None, stream=None):

@@ -18,7 +18,7 @@ int check_shape(int B, int H, int T, int dk, int dv, int chunk, int io) {
     if (B < 1 || H < 1 || T < 0) return KDA_ERR_SHAPE;
     if ((dk != 64 && dk != 128) || (dv != 64 && dv != 128)) return KDA_ERR_SHAPE;
     if (T % chunk != 0) return KDA_ERR_SHAPE;
-    if (H > 65535) return KDA_ERR_SHAPE;
+    if (H > 65535 || B > 65535) return KDA_ERR_SHAPE;  // grid y and z of the chunk stage
     const double elems = (double)B * H * (double)T * (dk > dv ? dk : dv);
     if (elems >= 1099511627776.0) return KDA_ERR_SHAPE;  // 2^40
     return KDA_OK;
@@ -200,6 +200,7 @@ struct BwdSizes {
 int check_bwd(int B, int H, int T, int dk, int dv, int io, BwdSizes *bs) {
     const int st = check_shape(B, H, T, dk, dv, 16, io);
     if (st != KDA_OK) return st;
+    if ((long long)B * H > 65535) return KDA_ERR_SHAPE;  // grid y of the chunk-parallel gradient stage
     const KdaLayout L = kda_layout(16, dk, dv, io == KDA_FP32 ? 4 : 2);
     const size_t nch = (size_t)B * (size_t)H * (size_t)(T / 16);
     bs->rec = nch * L.stride;

@@ -33,7 +33,7 @@
  *    aligned; beta must be aligned to its element size.  A pointer to an
  *    array with zero elements (T == 0) may be NULL.
  *  - Supported: dk, dv in {64, 128}; chunk in {16, 32, 64}; T % chunk == 0;
- *    B, H >= 1; T >= 0; B*H*T*max(dk,dv) < 2^40.  Bounded mode needs a finite
+ *    1 <= B, H <= 65535; T >= 0; B*H*T*max(dk,dv) < 2^40.  Bounded mode needs a finite
  *    g_min with KDA_G_MIN_LOWEST <= g_min < 0 (below that bound a 16-token tile
  *    can leave the bf16/fp32 exponent range); the ablation mode ignores g_min.
  *  - Every argument is validated on the host before anything is launched; on a
@@ -216,7 +216,7 @@ int kda_chunk_fwd_varlen(const void *q, const void *k, const void *v, const void
  * da_out is the gradient of the gate pre-activation a (through g = g_min sigmoid(a),
  * or log sigmoid(a) in the ablation mode).  The backward works on 16-token
  * chunks whatever chunk the forward used (the gradients do not depend on it):
- * T % 16 == 0.  workspace: kda_chunk_bwd_workspace_bytes(...) bytes (the
+ * T % 16 == 0, and B*H <= 65535.  workspace: kda_chunk_bwd_workspace_bytes(...) bytes (the
  * recomputed chunk records and two float32 states per 16-token chunk and head,
  * B*H*T/16 * (record + 2*dk*dv*4) bytes; 0 for an invalid problem).  No output
  * may alias an input.  Validation, alignment (16 bytes; beta: element size,

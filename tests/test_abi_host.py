@@ -71,7 +71,7 @@ def _fwd(**kw):
     (dict(io=7), E_DTYPE),
     (dict(chunk=48), E_CHUNK), (dict(chunk=128), E_CHUNK),
     (dict(B=0), E_SHAPE), (dict(H=0), E_SHAPE), (dict(T=-64), E_SHAPE), (dict(T=100), E_SHAPE),
-    (dict(dk=96), E_SHAPE), (dict(dv=256), E_SHAPE), (dict(H=70000), E_SHAPE),
+    (dict(dk=96), E_SHAPE), (dict(dv=256), E_SHAPE), (dict(H=70000), E_SHAPE), (dict(B=70000, T=64), E_SHAPE),
     (dict(g_min=0.0), E_GMIN), (dict(g_min=1.0), E_GMIN), (dict(g_min=-6.0), E_GMIN),
     (dict(g_min=float("nan")), E_GMIN), (dict(g_min=float("-inf")), E_GMIN),
     (dict(ws=None), E_WS), (dict(wsb=1000), E_WS),
@@ -192,6 +192,7 @@ def test_bwd_workspace_bytes():
 @pytest.mark.parametrize("kw,want", [
     (dict(q=None), E_NULL), (dict(dout=None), E_NULL), (dict(dq=None), E_NULL), (dict(dbeta=None), E_NULL),
     (dict(T=40), E_SHAPE), (dict(dk=96), E_SHAPE), (dict(B=0), E_SHAPE), (dict(io=2), E_DTYPE),
+    (dict(B=300, H=300), E_SHAPE),
     (dict(g_min=0.5), E_GMIN), (dict(mode=7), E_MODE), (dict(dout=FAKE + 8), E_ALIGN),
     (dict(dq=FAKE + 4), E_ALIGN), (dict(s0=FAKE + 4), E_ALIGN), (dict(ws=None), E_WS), (dict(wsb=99), E_WS),
 ])

@@ -79,3 +79,19 @@ def test_bwd_64k_workload_two_heads():
     inp = KI.make_inputs(w, device="cuda")
     dout, dF = KI.make_grads(w, device="cuda")
     _run_and_check(w, inp, dout, None, dF, heads=(0, 31))
+
+
+def test_autograd_function_matches_the_backward():
+    """KdaChunkFunction under torch autograd: loss = sum(dout * out) + sum(dfinal * final_state);
+    the gradients autograd hands back are kda_chunk_bwd's, and match the oracle's adjoint."""
+    w = KI.Workload("ag", 1, 2, 128, 64, 64, 32, "fp32", 2.0, False, 121)
+    inp = {n: t.cuda().requires_grad_(True) for n, t in KI.make_inputs(w).items()}
+    dout, dF = (t.cuda() for t in KI.make_grads(w))
+    out, fs = kda.KdaChunkFunction.apply(inp["q"], inp["k"], inp["v"], inp["a"], inp["beta"], -5.0, 32)
+    ((out * dout).sum() + (fs * dF).sum()).backward()
+    torch.cuda.synchronize()
+    x = {n: t.detach().double().cpu().numpy() for n, t in inp.items()}
+    ref = native.backward(x["q"], x["k"], x["v"], x["a"], x["beta"], dout.double().cpu().numpy(), -5.0,
+                          dfinal=dF.double().cpu().numpy())
+    for n, rkey in (("q", "dq"), ("k", "dk"), ("v", "dv"), ("a", "da"), ("beta", "dbeta")):
+        _grad_check(inp[n].grad.double().cpu().numpy(), ref[rkey], "fp32", "autograd d" + n)
