@@ -20,11 +20,12 @@
 // range because g >= g_min = -5.  So every causal 16x16 sub-tile, diagonal or
 // not, is one dense MFMA contraction over the key channels.
 //
-// Precision: the scaled operands of M and A, M itself and U~ enter their
-// products as bf16 hi + lo pairs (three MFMAs per K-block); Oi and U~ are
-// stored in fp32; T diag(beta) and K e^G are bf16 operands; W, Qbar and K^ are
-// stored as fp16, each chunk's block scaled by a power of two from its largest
-// magnitude (the sequential stage undoes the scale on its fp32 results).
+// Precision: the Gamma-scaled operands of the diagonal sub-tiles of M and A
+// (factors up to e^75, outside the fp16 range) enter their products as bf16
+// hi + lo pairs (three MFMAs per K-block); M, W and U~ enter M W and M U~ as
+// fp16 (|M| <= 1); T diag(beta), K e^G and V are bf16 operands; W, Qbar, K^,
+// U~ and Oi are stored as fp16, each block scaled by a power of two from its
+// largest magnitude (the sequential stage undoes the scale on its fp32 results).
 //
 // UT solve: each 16x16 diagonal block of T from the finite product series of
 // its strictly lower triangular A block (one wave per block), then the
@@ -567,12 +568,16 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 
     // ------------------------------------------------ phase 3
     // Fragments indexed by (row tile rt, token K-block kb): lane l holds row r = 16 rt + l16,
-    // slots = columns 32 kb + kslot.  tf: T diag(beta); mf: M (hi + lo).
+    // slots = columns 32 kb + kslot.  tf: T diag(beta); mf: M.  The products with M (M W and
+    // M U~) take fp16 operands: |M| <= 1 (unit q, k and factors e^{G_r - G_s} <= 1), and W and
+    // U~ are far inside the fp16 range, so one fp16 MFMA (11 significand bits) replaces the
+    // two or three bf16 hi + lo products.
     // Only the causal K-blocks kb <= rt / 2 are used.  T and M are stored for blocks on and
     // below the diagonal only; the one block above the diagonal that such a K-block spans
     // (column tile 2 kb + 1 = rt + 1) is zero and is never read.
+    using FM = Frag<OH>;  // fp16 (fp32 with fp32 I/O)
     F tf[NT][NTKB];
-    SP mf[NT][NTKB];
+    FM mf[NT][NTKB];
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt)
 #pragma unroll
@@ -590,7 +595,7 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
                 y[4 + i] = hi ? sM[r * PA + s1] : 0.f;
             }
             tf[rt][kb] = F::make(x);
-            mf[rt][kb] = SP::make(y);
+            mf[rt][kb] = FM::make(y);
         }
     // dk tiles: W^T, W and Qbar^T = (Q e^G)^T - W^T M^T, kept in registers for the chunk's scale
     float qbmax = 0.f, wmax = 0.f;
@@ -624,7 +629,7 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
             for (int i = 0; i < 4; ++i) wmax = fmaxf(wmax, fabsf(accT[i]));
             wrow[rt] = accW;
         }
-        F wa[NTKB];  // W as the A operand of W^T (m = dk, k = token)
+        FM wa[NTKB];  // W as the A operand of W^T (m = dk, k = token)
 #pragma unroll
         for (int kb = 0; kb < NTKB; ++kb) {
             float x[8];
@@ -633,13 +638,13 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
                 const int t = 2 * kb + j / 4;
                 x[j] = (t < NT) ? wrow[t < NT ? t : 0][j % 4] : 0.f;
             }
-            wa[kb] = F::make(x);
+            wa[kb] = FM::make(x);
         }
 #pragma unroll
         for (int rt = 0; rt < NT; ++rt) {
             f32x4 mw = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kb = 0; kb <= rt / 2; ++kb) mw = mma2b(wa[kb], mf[rt][kb], mw);
+            for (int kb = 0; kb <= rt / 2; ++kb) mw = mma(wa[kb], mf[rt][kb], mw);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 qtr[ci][rt][i] -= mw[i];
@@ -681,7 +686,7 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 #pragma unroll
             for (int i = 0; i < 4; ++i) um = fmaxf(um, fabsf(acc[i]));
         }
-        SP ua[NTKB];  // U~ as the A operand of U~^T (m = dv, k = token), hi + lo
+        FM ua[NTKB];  // U~ as the A operand of U~^T (m = dv, k = token)
 #pragma unroll
         for (int kb = 0; kb < NTKB; ++kb) {
             float x[8];
@@ -690,7 +695,7 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
                 const int t = 2 * kb + j / 4;
                 x[j] = (t < NT) ? urow[t < NT ? t : 0][j % 4] : 0.f;
             }
-            ua[kb] = SP::make(x);
+            ua[kb] = FM::make(x);
         }
         f32x4 orow[NT];
         float om = 0.f;
@@ -698,7 +703,7 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
         for (int rt = 0; rt < NT; ++rt) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kb = 0; kb <= rt / 2; ++kb) acc = mma3(ua[kb], mf[rt][kb], acc);
+            for (int kb = 0; kb <= rt / 2; ++kb) acc = mma(ua[kb], mf[rt][kb], acc);
             orow[rt] = acc;
 #pragma unroll
             for (int i = 0; i < 4; ++i) om = fmaxf(om, fabsf(acc[i]));
