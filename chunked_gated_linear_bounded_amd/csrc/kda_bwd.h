@@ -37,6 +37,43 @@ __device__ __forceinline__ f32x4 mma_tile(f32x4 acc, const FA &A, const FB &B, i
     return acc;
 }
 
+// The same product with bf16 hi + lo operands: x = hi + lo with hi = bf16(x), lo = bf16(x - hi)
+// (about 16 significand bits, the full fp32 range), three 16x16x32 MFMAs per 32-deep block
+// (hi hi, lo hi, hi lo).  This product is private to the tile, so its K slots are its own:
+// slot j of lane group g is k = k0 + 8 g + j.  K a multiple of 16 (a half block is padded
+// with zeros).
+template <int K, typename FA, typename FB>
+__device__ __forceinline__ f32x4 mma_tile_split(f32x4 acc, const FA &A, const FB &B, int lane) {
+    const int m = lane & 15, g8 = 8 * (lane >> 4);
+    static_assert(K % 16 == 0, "K in 16-deep steps");
+#pragma unroll 2
+    for (int k0 = 0; k0 < K; k0 += 32) {
+        bf16x8 ah, al, bh, bl;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int kk = k0 + g8 + j;
+            const bool in = (K % 32 == 0) || kk < K;
+            const float x = in ? A(m, kk) : 0.f, y = in ? B(kk, m) : 0.f;
+            ah[j] = (__bf16)x;
+            al[j] = (__bf16)(x - (float)ah[j]);
+            bh[j] = (__bf16)y;
+            bl[j] = (__bf16)(y - (float)bh[j]);
+        }
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
+    }
+    return acc;
+}
+
+// The products of the chunk-parallel stage over a dk- or dv-deep dimension: fp32 for fp32
+// inputs (their 1e-4 bar), bf16 hi + lo otherwise.
+template <bool F32, int K, typename FA, typename FB>
+__device__ __forceinline__ f32x4 mma_big(f32x4 acc, const FA &A, const FB &B, int lane) {
+    if constexpr (F32) return mma_tile<K>(acc, A, B, lane);
+    else return mma_tile_split<K>(acc, A, B, lane);
+}
+
 // Element (r, c) of a stored tile-pair block (kda_layout.h): tiles of 16 x 16 in
 // accumulator order, the two tiles of a pair interleaved per lane.  `pairs_along_rows`:
 // the pair joins tile rows 2p and 2p+1 (K^), else tile columns (W^T, Qbar^T stored with
@@ -331,13 +368,13 @@ __global__ __launch_bounds__(512, 1) void kda_bwd_chunk_kernel(
     // ---------------------------------------------------------------- P, M, T
     if (wave == 0) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = mma_tile<DK>(acc, [&](int m, int kk) { return Kv(m, kk) * Ep(m, kk); },
+        acc = mma_big<F32, DK>(acc, [&](int m, int kk) { return Kv(m, kk) * Ep(m, kk); },
                            [&](int kk, int nn) { return Kv(nn, kk) * Em(nn, kk); }, lane);
 #pragma unroll
         for (int i = 0; i < 4; ++i) sP[(4 * g + i) * P16 + l16] = (l16 < 4 * g + i) ? acc[i] : 0.f;
     } else if (wave == 1) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = mma_tile<DK>(acc, [&](int m, int kk) { return Qv(m, kk) * Ep(m, kk); },
+        acc = mma_big<F32, DK>(acc, [&](int m, int kk) { return Qv(m, kk) * Ep(m, kk); },
                            [&](int kk, int nn) { return Kv(nn, kk) * Em(nn, kk); }, lane);
 #pragma unroll
         for (int i = 0; i < 4; ++i) sM[(4 * g + i) * P16 + l16] = (l16 <= 4 * g + i) ? acc[i] : 0.f;
@@ -384,7 +421,7 @@ __global__ __launch_bounds__(512, 1) void kda_bwd_chunk_kernel(
         const int nt = wave + NW * x;
         if (nt >= NDV) continue;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = mma_tile<DK>(acc, [&](int m, int kk) { return sW[m * PK + kk]; },
+        acc = mma_big<F32, DK>(acc, [&](int m, int kk) { return sW[m * PK + kk]; },
                            [&](int kk, int nn) { return sS[(16 * nt + nn) * PK + kk]; }, lane);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -398,7 +435,7 @@ __global__ __launch_bounds__(512, 1) void kda_bwd_chunk_kernel(
         dQa[x] = dKa[x] = dGa[x] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (nt >= NDK) continue;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = mma_tile<DV>(acc, [&](int m, int kk) { return sdO[m * PV + kk]; },
+        acc = mma_big<F32, DV>(acc, [&](int m, int kk) { return sdO[m * PV + kk]; },
                            [&](int kk, int nn) { return sS[kk * PK + 16 * nt + nn]; }, lane);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -435,7 +472,7 @@ __global__ __launch_bounds__(512, 1) void kda_bwd_chunk_kernel(
             if (wave < QJ / 16) {  // dUs = K^ dS' for the quarter's value tiles
                 const int nt = qd * (QJ / 16) + wave;
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                acc = mma_tile<DK>(acc, [&](int m, int kk) { return Kv(m, kk) * EH(m, kk); },
+                acc = mma_big<F32, DK>(acc, [&](int m, int kk) { return Kv(m, kk) * EH(m, kk); },
                                    [&](int kk, int nn) { return sDq[(16 * wave + nn) * PK + kk]; }, lane);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sdU[(4 * g + i) * PV + 16 * nt + l16] = acc[i];
@@ -444,7 +481,7 @@ __global__ __launch_bounds__(512, 1) void kda_bwd_chunk_kernel(
             for (int x = 0; x < NTK; ++x) {  // dK^ += U[:, quarter] dS'[quarter rows]
                 const int nt = wave + NW * x;
                 if (nt >= NDK) continue;
-                dKh[x] = mma_tile<QJ>(dKh[x], [&](int m, int kk) { return sU[m * PV + qd * QJ + kk]; },
+                dKh[x] = mma_big<F32, QJ>(dKh[x], [&](int m, int kk) { return sU[m * PV + qd * QJ + kk]; },
                                       [&](int kk, int nn) { return sDq[kk * PK + 16 * nt + nn]; }, lane);
             }
             if (tid < DK) {
@@ -488,7 +525,7 @@ __global__ __launch_bounds__(512, 1) void kda_bwd_chunk_kernel(
     }
     if (wave == 0) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = mma_tile<DV>(acc, [&](int m, int kk) { return sdO[m * PV + kk]; },
+        acc = mma_big<F32, DV>(acc, [&](int m, int kk) { return sdO[m * PV + kk]; },
                            [&](int kk, int nn) { return sU[nn * PV + kk]; }, lane);
 #pragma unroll
         for (int i = 0; i < 4; ++i) sdM[(4 * g + i) * P16 + l16] = (l16 <= 4 * g + i) ? acc[i] : 0.f;
@@ -501,7 +538,7 @@ __global__ __launch_bounds__(512, 1) void kda_bwd_chunk_kernel(
         const int nt = wave + NW * x;
         if (nt >= NDK) continue;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = mma_tile<DV>(acc, [&](int m, int kk) { return sdU[m * PV + kk]; },
+        acc = mma_big<F32, DV>(acc, [&](int m, int kk) { return sdU[m * PV + kk]; },
                            [&](int kk, int nn) { return sS[kk * PK + 16 * nt + nn]; }, lane);
 #pragma unroll
         for (int i = 0; i < 4; ++i) sW[(4 * g + i) * PK + 16 * nt + l16] = -acc[i];
@@ -511,9 +548,9 @@ __global__ __launch_bounds__(512, 1) void kda_bwd_chunk_kernel(
     // ---------------------------------------------------------------- dT = dW X^T + dU Y^T
     if (wave == 0) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = mma_tile<DK>(acc, [&](int m, int kk) { return sW[m * PK + kk]; },
+        acc = mma_big<F32, DK>(acc, [&](int m, int kk) { return sW[m * PK + kk]; },
                            [&](int kk, int nn) { return Xv(nn, kk); }, lane);
-        acc = mma_tile<DV>(acc, [&](int m, int kk) { return sdU[m * PV + kk]; },
+        acc = mma_big<F32, DV>(acc, [&](int m, int kk) { return sdU[m * PV + kk]; },
                            [&](int kk, int nn) { return sB[nn] * sV[nn * PV + kk]; }, lane);
 #pragma unroll
         for (int i = 0; i < 4; ++i) sdT[(4 * g + i) * P16 + l16] = acc[i];
