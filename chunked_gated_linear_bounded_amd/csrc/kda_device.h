@@ -337,29 +337,6 @@ struct GateScan {
         }
     }
 
-    // The same prefix sum when the per-row gate values g2 are already in sG (written there by
-    // the caller, every row of the chunk): G replaces them in place.
-    __device__ __forceinline__ static void scan_lds(float *sG, int ldG, int tid) {
-        const int rg = tid >> 4, m = tid & 15;
-#pragma unroll
-        for (int p = 0; p < NPASS; ++p) {
-            const int gi = rg + 16 * p;
-            if (gi >= NG) continue;
-            float gv[RPL][VEC];
-#pragma unroll
-            for (int j = 0; j < RPL; ++j) {
-                const float *src = sG + (m * RPL + j) * ldG + gi * VEC;
-#pragma unroll
-                for (int c = 0; c < VEC; c += 4) {
-                    const f32x4 x = *reinterpret_cast<const f32x4 *>(src + c);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) gv[j][c + i] = x[i] + (j ? gv[j - 1][c + i] : 0.f);
-                }
-            }
-            scan_store(gv, sG, ldG, gi, m);
-        }
-    }
-
     // gv holds this lane's rows already summed within the lane; add the totals of the lanes
     // before it in the row group (inclusive DPP scan) and store G.
     __device__ __forceinline__ static void scan_store(float (&gv)[RPL][VEC], float *sG, int ldG, int gi, int m) {

@@ -68,25 +68,28 @@ struct IntraCfg {
     static constexpr int MAXCT = (NDK + 3) / 4;  // dk tiles per wave
 };
 
-// Gate pre-activation of one 16-row tile from a rank-R factor, on MFMA:
-//   a[r][c] = e^{A[c]} sum_j h[r][j] z[c][j],   g2[r][c] = gate(a[r][c]) in log2 units -> sG
+// Gate pre-activation and its prefix sum from a rank-R factor, on MFMA:
+//   a[r][c] = e^{A[c]} sum_j h[r][j] z[c][j],   G[r][c] = sum_{s <= r} gate(a[s][c])  (log2 units)
 // (the pre-activation e^A h z of "Trillion-Scale MoE Multimodal Models: Practical Techniques
 // ...", sec. 3.2, with h a rank-R factor per token and z the per-head map from it to the key
-// channels).  This product is private to the tile, so its operands use their own K-slot order:
-// slot j of lane group g is k = 32 kb + 8 g + j, eight contiguous values, one 16-byte load per
-// fragment straight from global memory.  load() only issues the loads (all of them, so the
-// caller can put its own loads behind them); finish() runs the MFMAs, the scale and the gate.
-// R = 16 is half a K-block: lane groups 2 and 3 of the h operand are zero.
-template <int DK, typename E, int R>
-struct LowRankTile {
+// channels).  Wave w takes the key-channel tiles w, w + 4, ... for all C rows of the chunk, so it
+// reads only its own rows of z, and each channel's whole column is in one wave: the prefix sum
+// down the chunk runs in registers (in each lane over its 4 rows, over the 4 lane groups with
+// two shuffles, and from tile to tile with the carried total) and G is stored once.  This
+// product is private, so its operands use their own K-slot order: slot j of lane group g is
+// k = 32 kb + 8 g + j, eight contiguous values, one 16-byte load per fragment straight from
+// global memory.  load() only issues the loads (all of them while they fit in 128 registers,
+// so the caller can put its own loads behind them); finish() runs the MFMAs, the gate and the
+// prefix sum.  R = 16 is half a K-block: lane groups 2 and 3 of the h operand are zero.
+template <int C, int DK, typename E, int R>
+struct LowRankGate {
     static_assert(R == 16 || R % 32 == 0, "rank 16 or a multiple of 32");
-    static constexpr int NDK = DK / 16, NKB = (R + 31) / 32;
-    // operands held from load() to finish() only while they fit in 128 registers (fp32 at rank
-    // 128 would need 256); otherwise finish() loads them one K-block at a time
-    static constexpr bool PRE = NKB * NDK * (int)sizeof(Frag<E>) <= 128 * 4;
+    static constexpr int NT = C / 16, NDK = DK / 16, NCW = (NDK + 3) / 4, NKB = (R + 31) / 32;
+    static constexpr bool PRE = NKB * (NT + NCW) * (int)sizeof(Frag<E>) <= 128 * 4;
     static constexpr int NKP = PRE ? NKB : 1;
-    Frag<E> fa[NKP], fb[NKP][NDK];
+    Frag<E> fa[NKP][NT], fb[NKP][NCW];
     const E *hp = nullptr, *zp = nullptr;
+    int wave = 0;
 
     __device__ __forceinline__ static Frag<E> ld8(const E *p) {
         if constexpr (std::is_same<E, float>::value) {
@@ -99,15 +102,20 @@ struct LowRankTile {
     }
 
     __device__ __forceinline__ void load_kb(int slot, int kb) {
-        fa[slot] = ld8(hp + 32 * kb);
 #pragma unroll
-        for (int ct = 0; ct < NDK; ++ct) fb[slot][ct] = ld8(zp + (size_t)16 * ct * R + 32 * kb);
+        for (int rt = 0; rt < NT; ++rt) fa[slot][rt] = ld8(hp + (size_t)16 * rt * R + 32 * kb);
+#pragma unroll
+        for (int ci = 0; ci < NCW; ++ci) {
+            const int ct = wave + 4 * ci;
+            fb[slot][ci] = ld8(zp + (size_t)16 * (ct < NDK ? ct : 0) * R + 32 * kb);
+        }
     }
 
-    // h: the tile's first row, pitch R; z: [DK][R]
-    __device__ __forceinline__ void load(const E *__restrict__ h, const E *__restrict__ z, int lane) {
+    // h: the chunk's first row, pitch R; z: [DK][R]
+    __device__ __forceinline__ void load(const E *__restrict__ h, const E *__restrict__ z, int w, int lane) {
         const int g = lane >> 4, l16 = lane & 15;
         const int kg = (R == 16 && g >= 2) ? 8 * (g - 2) : 8 * g;  // R = 16: groups 2, 3 reread (then zeroed)
+        wave = w;
         hp = h + (size_t)l16 * R + kg;
         zp = z + (size_t)l16 * R + kg;
         if constexpr (PRE) {
@@ -116,35 +124,57 @@ struct LowRankTile {
         }
     }
 
-    // MFMAs, scale and gate; g2 of the tile's 16 rows to sG (the caller then runs the prefix sum
-    // over the chunk's rows from LDS)
     __device__ __forceinline__ void finish(const float *__restrict__ A, float gmin2, int logsig, float *sG, int ldG,
-                                           int row0, int lane) {
+                                           int lane) {
         const int g = lane >> 4, l16 = lane & 15;
-        if constexpr (R == 16) {
-            if (g >= 2) {
+        f32x4 acc[NT][NCW];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    if constexpr (std::is_same<E, float>::value) fa[0].v[j] = 0.f;
-                    else fa[0].v[j] = (E)0.f;
-                }
-            }
-        }
-        f32x4 acc[NDK];
+        for (int rt = 0; rt < NT; ++rt)
 #pragma unroll
-        for (int ct = 0; ct < NDK; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int ci = 0; ci < NCW; ++ci) acc[rt][ci] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
             if constexpr (!PRE) load_kb(0, kb);
+            const int sl = PRE ? kb : 0;
+            if constexpr (R == 16) {
+                if (g >= 2) {
 #pragma unroll
-            for (int ct = 0; ct < NDK; ++ct) acc[ct] = mma(fa[PRE ? kb : 0], fb[PRE ? kb : 0][ct], acc[ct]);
+                    for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) {
+                            if constexpr (std::is_same<E, float>::value) fa[sl][rt].v[j] = 0.f;
+                            else fa[sl][rt].v[j] = (E)0.f;
+                        }
+                }
+            }
+#pragma unroll
+            for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+                for (int ci = 0; ci < NCW; ++ci) acc[rt][ci] = mma(fa[sl][rt], fb[sl][ci], acc[rt][ci]);
         }
 #pragma unroll
-        for (int ct = 0; ct < NDK; ++ct) {
+        for (int ci = 0; ci < NCW; ++ci) {
+            const int ct = wave + 4 * ci;
+            if (ct >= NDK) continue;
             const int c = 16 * ct + l16;
             const float eA = ex2(A[c] * kLog2e);
+            float carry = 0.f;  // G of the last row of the tiles above
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sG[(row0 + 4 * g + i) * ldG + c] = gate_log2(acc[ct][i] * eA, gmin2, logsig);
+            for (int rt = 0; rt < NT; ++rt) {
+                float x[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) x[i] = gate_log2(acc[rt][ci][i] * eA, gmin2, logsig) + (i ? x[i - 1] : 0.f);
+                const float own = x[3];  // inclusive scan of the lane totals over the lane groups
+                float t = own;
+                const float u1 = __shfl_up(t, 16, 64);
+                t += g >= 1 ? u1 : 0.f;
+                const float u2 = __shfl_up(t, 32, 64);
+                t += g >= 2 ? u2 : 0.f;
+                const float add = carry + (t - own);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sG[(16 * rt + 4 * g + i) * ldG + c] = x[i] + add;
+                carry += __shfl(t, 48 + l16, 64);  // the tile's total, from lane group 3
+            }
         }
     }
 };
@@ -153,7 +183,7 @@ struct LowRankTile {
 // table ctab (records at head * NCmax + x); a chunk with fewer than C rows is padded with
 // zero q, k, beta and a zero gate, and a table entry with no rows ends the work-group.
 // LRK > 0: the gate pre-activation is formed from lrh [B][T][LRK] (shared by the heads), lrz
-// [H][DK][LRK] and lrA [H][DK] (LowRankTile) instead of being read from a.
+// [H][DK][LRK] and lrA [H][DK] (LowRankGate) instead of being read from a.
 template <int C, int DK, int DV, bool F32, bool VL, int LRK>
 __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void kda_intra_kernel(
     const typename IntraCfg<C, DK, DV, F32>::E *__restrict__ q,
@@ -223,10 +253,9 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
         constexpr int LPR = DK / VEC, RPP = 256 / LPR, NP = (C + RPP - 1) / RPP;
         const E *qg = q + tok0 * DK, *kg = k + tok0 * DK;
         GateScan<C, DK, E> gate;
-        LowRankTile<DK, E, LR ? LRK : 16> lrt;  // its loads go first: its MFMAs need nothing else
+        LowRankGate<C, DK, E, LR ? LRK : 16> lrt;  // its loads go first: its MFMAs need nothing else
         if constexpr (LR) {
-            if (wave < NT)
-                lrt.load(lrh + ((size_t)b * T + (size_t)n * C + 16 * wave) * LRK, lrz + (size_t)h * DK * LRK, lane);
+            lrt.load(lrh + ((size_t)b * T + (size_t)n * C) * LRK, lrz + (size_t)h * DK * LRK, wave, lane);
         } else {
             gate.load(a + tok0 * DK, tid, nrow);
         }
@@ -241,10 +270,8 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
             xq[p] = *reinterpret_cast<const uint4 *>(qg + off);
             xk[p] = *reinterpret_cast<const uint4 *>(kg + off);
         }
-        // the low-rank gate's MFMAs run while q, k and beta are still in flight
-        if constexpr (LR) {
-            if (wave < NT) lrt.finish(lrA + (size_t)h * DK, gmin2, logsig, sG, PG, 16 * wave, lane);
-        }
+        // the low-rank gate's MFMAs and prefix sum run while q, k and beta are still in flight
+        if constexpr (LR) lrt.finish(lrA + (size_t)h * DK, gmin2, logsig, sG, PG, lane);
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
             const int r = p * RPP + tid / LPR, c = (tid % LPR) * VEC;
@@ -260,12 +287,7 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
             }
         }
         if (tid < C) sB[tid] = (!VL || tid < nrow) ? to_f(bv) : 0.f;
-        if constexpr (LR) {
-            __syncthreads();
-            GateScan<C, DK, E>::scan_lds(sG, PG, tid);
-        } else {
-            gate.finish(gmin2, logsig, sG, PG, tid, nrow);
-        }
+        if constexpr (!LR) gate.finish(gmin2, logsig, sG, PG, tid, nrow);
         __syncthreads();
     }
 
