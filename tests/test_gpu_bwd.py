@@ -95,3 +95,29 @@ def test_autograd_function_matches_the_backward():
                           dfinal=dF.double().cpu().numpy())
     for n, rkey in (("q", "dq"), ("k", "dk"), ("v", "dv"), ("a", "da"), ("beta", "dbeta")):
         _grad_check(inp[n].grad.double().cpu().numpy(), ref[rkey], "fp32", "autograd d" + n)
+
+
+@pytest.mark.parametrize("io", ["fp32", "bf16"])
+def test_bwd_single_chunk_odd_batch_and_heads(io):
+    """One 16-token chunk per sequence, B=2 and H=3, dk=128 with dv=64, initial state and final-state
+    gradient: the reverse pass runs a single step."""
+    w = KI.Workload("bw1", 2, 3, 16, 128, 64, 16, io, 3.0, False, 131)
+    inp = {n: t.cuda() for n, t in KI.make_inputs(w).items()}
+    dout, dF = (t.cuda() for t in KI.make_grads(w))
+    S0 = torch.randn(2, 3, 64, 128, device="cuda") * 0.5
+    _run_and_check(w, inp, dout, S0, dF)
+
+
+def test_bwd_empty_sequence():
+    """No tokens: the only gradient is the initial state's, and it is the final state's."""
+    w = KI.Workload("bw0", 1, 2, 0, 64, 64, 16, "bf16", 1.0, False, 132)
+    inp = {n: t.cuda() for n, t in KI.make_inputs(w).items()}
+    dout = torch.empty((1, 2, 0, 64), dtype=torch.bfloat16, device="cuda")
+    dF = torch.randn(1, 2, 64, 64, device="cuda")
+    g = kda.chunk_bwd(inp["q"], inp["k"], inp["v"], inp["a"], inp["beta"], dout, dfinal_state=dF)
+    torch.cuda.synchronize()
+    assert g["dq"].numel() == 0 and g["dbeta"].numel() == 0
+    assert torch.equal(g["dinitial_state"], dF)
+    g0 = kda.chunk_bwd(inp["q"], inp["k"], inp["v"], inp["a"], inp["beta"], dout)
+    torch.cuda.synchronize()
+    assert not torch.any(g0["dinitial_state"])
