@@ -139,6 +139,7 @@ int fwd_impl(const void *q, const void *k, const void *v, const void *a, const v
 // can need, whatever cu_seqlens holds), and where the plan tables start.
 struct VarlenSizes {
     long long ncmax;
+    int nrun;  // runs of documents: enough (document, head, slice) walks to give every CU one, at most N
     size_t plan_offset, total;
 };
 
@@ -154,9 +155,13 @@ int check_varlen(int N, int H, int T, int dk, int dv, int chunk, int io, VarlenS
     const double elems = (double)H * (double)T * (dk > dv ? dk : dv);
     if (elems >= 1099511627776.0) return KDA_ERR_SHAPE;  // 2^40
     const KdaLayout L = kda_layout(chunk, dk, dv, io == KDA_FP32 ? 4 : 2);
+    const long long units = (long long)H * (dv / 16);
+    long long nrun = (256 + units - 1) / units;
+    if (nrun > N) nrun = N;
     vs->ncmax = ncmax;
+    vs->nrun = (int)nrun;
     vs->plan_offset = (size_t)H * (size_t)ncmax * L.stride;
-    vs->total = vs->plan_offset + 8 * ((size_t)N + 1) + 8 * (size_t)ncmax;
+    vs->total = vs->plan_offset + 16 * (size_t)ncmax + 8 * ((size_t)N + 1) + 4 * ((size_t)nrun + 1);
     return KDA_OK;
 }
 
@@ -186,7 +191,7 @@ int varlen_impl(const void *q, const void *k, const void *v, const void *a, cons
     p.fp32 = io == KDA_FP32;
     p.out = out; p.final_state = final_state; p.init_state = init_state;
     p.workspace = workspace; p.counts = counts; p.stream = stream;
-    p.cu = cu_seqlens; p.nseq = N; p.ncmax = (int)vs.ncmax; p.plan_offset = vs.plan_offset;
+    p.cu = cu_seqlens; p.nseq = N; p.ncmax = (int)vs.ncmax; p.nrun = vs.nrun; p.plan_offset = vs.plan_offset;
     if (kda::launch_intra(p) != hipSuccess) return KDA_ERR_HIP;
     return kda::launch_state(p) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }

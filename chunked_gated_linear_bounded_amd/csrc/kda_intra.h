@@ -192,7 +192,7 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     const typename IntraCfg<C, DK, DV, F32>::E *__restrict__ a,
     const typename IntraCfg<C, DK, DV, F32>::E *__restrict__ beta,
     float gmin2, int logsig, int H, int T, unsigned char *__restrict__ ws,
-    unsigned long long *__restrict__ counts, const int2 *__restrict__ ctab, int NCmax,
+    unsigned long long *__restrict__ counts, const int4 *__restrict__ ctab, int NCmax,
     const typename IntraCfg<C, DK, DV, F32>::E *__restrict__ lrh,
     const typename IntraCfg<C, DK, DV, F32>::E *__restrict__ lrz, const float *__restrict__ lrA)
 {
@@ -229,7 +229,7 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     size_t tok0, recno;
     int nrow = C;  // rows of the chunk that are tokens (compile-time C unless packed)
     if constexpr (VL) {
-        const int2 ce = ctab[n];  // same address in every lane: a uniform value
+        const int4 ce = ctab[n];  // same address in every lane: a uniform value
         if (ce.y <= 0) return;    // past the last chunk of the batch
         nrow = ce.y < C ? ce.y : C;
         tok0 = head * (size_t)T + (size_t)ce.x;

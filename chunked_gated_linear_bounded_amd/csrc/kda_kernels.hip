@@ -47,14 +47,17 @@ static hipError_t launch_gate_t(const LaunchArgs &p) {
 }
 
 // Packed documents (p.cu != NULL): the plan tables sit in the workspace after the records
-// (kda_varlen.h); B is 1 and T is the length of the packed stream.
+// (kda_varlen.h): ctab [NCmax] int4, then bnd and coff [N + 1] and seg [P + 1] int; B is 1 and
+// T is the length of the packed stream.
 struct PlanPtrs {
-    int *bnd, *coff;
-    int2 *ctab;
+    int4 *ctab;
+    int *bnd, *coff, *seg;
 };
 static PlanPtrs plan_ptrs(const LaunchArgs &p) {
-    int *base = reinterpret_cast<int *>(reinterpret_cast<unsigned char *>(p.workspace) + p.plan_offset);
-    return PlanPtrs{base, base + p.nseq + 1, reinterpret_cast<int2 *>(base + 2 * (p.nseq + 1))};
+    unsigned char *base = reinterpret_cast<unsigned char *>(p.workspace) + p.plan_offset;
+    int4 *ctab = reinterpret_cast<int4 *>(base);
+    int *bnd = reinterpret_cast<int *>(ctab + p.ncmax);
+    return PlanPtrs{ctab, bnd, bnd + p.nseq + 1, bnd + 2 * (p.nseq + 1)};
 }
 
 template <int C, int DK, int DV, bool F32>
@@ -65,6 +68,11 @@ static hipError_t launch_intra_t(const LaunchArgs &p) {
         hipLaunchKernelGGL((kda_varlen_plan_kernel<C>), dim3(1), dim3(1024), 0, p.stream, p.cu, p.nseq, p.T, p.ncmax,
                            pl.bnd, pl.coff, pl.ctab);
         hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const int nb = (p.ncmax + 255) / 256;
+        hipLaunchKernelGGL(kda_varlen_seg_kernel, dim3(1 + nb + p.nseq), dim3(256), 0, p.stream, pl.bnd, pl.coff,
+                           p.nseq, p.nrun, pl.seg, pl.ctab, nb, p.init_state, p.final_state, p.H * p.dv * p.dk);
+        e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL((kda_intra_kernel<C, DK, DV, F32, true, 0>), dim3(p.ncmax, p.H, 1), dim3(256), 0,
                            p.stream, reinterpret_cast<const E *>(p.q), reinterpret_cast<const E *>(p.k),
@@ -89,18 +97,20 @@ template <int C, int DK, int DV, bool F32>
 static hipError_t launch_state_t(const LaunchArgs &p) {
     using E = typename std::conditional<F32, float, __bf16>::type;
     const bool vl = p.cu != nullptr;
-    const int BH = vl ? p.nseq * p.H : p.B * p.H;  // units: (document, head) or (batch, head)
+    const int BH = vl ? p.nrun * p.H : p.B * p.H;  // units: (run of documents, head) or (batch, head)
     const int groups = (BH + 7) / 8;
     dim3 grid(groups * 8 * (DV / 16));
-    const PlanPtrs pl = vl ? plan_ptrs(p) : PlanPtrs{nullptr, nullptr, nullptr};
+    const PlanPtrs pl = vl ? plan_ptrs(p) : PlanPtrs{nullptr, nullptr, nullptr, nullptr};
     if (vl)
         hipLaunchKernelGGL((kda_state_kernel<C, DK, DV, F32, true>), grid, dim3(192), 0, p.stream,
                            reinterpret_cast<const unsigned char *>(p.workspace), reinterpret_cast<E *>(p.out),
-                           p.final_state, p.init_state, BH, p.T, p.counts, pl.bnd, pl.coff, p.H, p.ncmax, nullptr);
+                           p.final_state, p.init_state, BH, p.T, p.counts, pl.ctab, pl.seg, pl.coff, p.H, p.ncmax,
+                           nullptr);
     else
         hipLaunchKernelGGL((kda_state_kernel<C, DK, DV, F32, false>), grid, dim3(192), 0, p.stream,
                            reinterpret_cast<const unsigned char *>(p.workspace), reinterpret_cast<E *>(p.out),
-                           p.final_state, p.init_state, BH, p.T, p.counts, nullptr, nullptr, p.H, 0, p.states);
+                           p.final_state, p.init_state, BH, p.T, p.counts, nullptr, nullptr, nullptr, p.H, 0,
+                           p.states);
     return hipGetLastError();
 }
 

@@ -22,6 +22,7 @@ struct LaunchArgs {
     const int *cu;              // device cu_seqlens[nseq + 1]
     int nseq;                   // documents
     int ncmax;                  // chunk records per head: T / chunk + nseq
+    int nrun;                   // runs of documents the state stage walks (one work-group each per head and slice)
     size_t plan_offset;         // byte offset of the plan tables in the workspace
     // gate pre-activation from a rank-`rank` factor (NULL lr_h: read from a)
     const void *lr_h, *lr_z;    // [B][T][rank], [H][dk][rank] (I/O element type)

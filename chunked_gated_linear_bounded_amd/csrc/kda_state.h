@@ -37,15 +37,17 @@
 
 namespace kda {
 
-template <int C, int DK, int DV, bool F32>
+// VL: each buffer also holds the chunk's 16-byte chunk-table entry after the record.
+template <int C, int DK, int DV, bool F32, bool VL = false>
 struct StateCfg {
     using E = typename std::conditional<F32, float, __bf16>::type;
     static constexpr int ES = sizeof(E);
     static constexpr KdaLayout L = kda_layout(C, DK, DV, ES);
-    static constexpr int BUF = (int)(L.region1 + L.slice);
+    static constexpr int ENT = (int)(L.region1 + L.slice);  // VL: the chunk-table entry
+    static constexpr int BUF = ENT + (VL ? 16 : 0);
     static constexpr int LDS_MAX = 160 * 1024;
-    // direct-load instructions per record (each moves 1 KiB)
-    static constexpr int NDMA = (int)((L.region1 + 1023) / 1024 + (L.slice + 1023) / 1024);
+    // direct-load instructions per record (each moves 1 KiB; VL adds the entry's)
+    static constexpr int NDMA = (int)((L.region1 + 1023) / 1024 + (L.slice + 1023) / 1024) + (VL ? 1 : 0);
     // three buffers give two chunks of lookahead; the partial wait needs NDMA <= 63
     static constexpr int NBUF = (3 * BUF <= LDS_MAX && NDMA <= 63) ? 3 : (2 * BUF <= LDS_MAX) ? 2 : 1;
     static constexpr int SMEM = NBUF * BUF;
@@ -67,28 +69,35 @@ __device__ __forceinline__ void dma_to_lds(lds_u8 *dst, const unsigned char *__r
     }
 }
 
-// Issue the copies of one chunk's record (region 1 + one value slice).
+// Issue the copies of one chunk's record (region 1 + one value slice) and, when `ent` is not
+// NULL, of its 16-byte chunk-table entry (one lane) right after them.
 template <int R1, int SL>
 __device__ __forceinline__ void issue_record(lds_u8 *dst, const unsigned char *__restrict__ rec,
-                                             size_t slice_off, int lane) {
+                                             size_t slice_off, int lane, const int4 *ent = nullptr) {
     dma_to_lds<R1>(dst, rec, lane);
     dma_to_lds<SL>(dst + R1, rec + slice_off, lane);
+    if (ent != nullptr && lane == 0)
+        __builtin_amdgcn_global_load_lds(ent, (lds_void *)(dst + R1 + SL), 16, 0, 0);
 }
 
 
-// VL: packed documents (kda_varlen.h).  Unit hb is then (document hb / H, head hb % H):
-// its chunks are records head * NCmax + coff[doc] ..., its tokens bnd[doc] .. bnd[doc + 1]
-// of the head's stream, and only the rows that are tokens are stored.  initial_state and
-// final_state are indexed by unit in both cases.
+// VL: packed documents (kda_varlen.h).  Unit hb is then (run p = hb / H of documents, head
+// hb % H): it walks the run's chunk records back to back (records head * NCmax + coff[seg[p]]
+// ...), each chunk's first token, rows, document and first/last flags taken from the chunk table
+// a chunk ahead; at a document's last chunk the state wave stores that document's final state
+// and starts the next document from its initial state (loaded a chunk ahead), and only the rows
+// that are tokens are stored.  initial_state and final_state are then indexed by (document,
+// head), else by unit.
 template <int C, int DK, int DV, bool F32, bool VL>
 __global__ __launch_bounds__(192, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void kda_state_kernel(
-    const unsigned char *__restrict__ ws, typename StateCfg<C, DK, DV, F32>::E *__restrict__ out,
+    const unsigned char *__restrict__ ws, typename StateCfg<C, DK, DV, F32, VL>::E *__restrict__ out,
     float *final_state, const float *init_state, int BH, int T, unsigned long long *__restrict__ counts,
-    const int *__restrict__ bnd, const int *__restrict__ coff, int H, int NCmax, float *__restrict__ states)
+    const int4 *__restrict__ ctab, const int *__restrict__ seg, const int *__restrict__ coff, int H, int NCmax,
+    float *__restrict__ states)
 {
     // states (nullable, fixed-length only): the state each chunk starts from, [BH][NC][DV][DK] float32 in
     // final_state's orientation, for the backward pass; out may then be NULL (no outputs stored)
-    using Cfg = StateCfg<C, DK, DV, F32>;
+    using Cfg = StateCfg<C, DK, DV, F32, VL>;
     using E = typename Cfg::E;
     using OH = typename std::conditional<F32, float, _Float16>::type;
     using FH = Frag<OH>;
@@ -107,30 +116,37 @@ __global__ __launch_bounds__(192, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     __shared__ __attribute__((aligned(1024))) unsigned char smem[Cfg::SMEM];
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
     const int wave = tid >> 6;
-    int NC, ntok;          // chunks and tokens of this unit
-    size_t row0;           // its first token in out
+    const int j0 = 16 * slice;
+    int NC;                // chunks of this unit
+    size_t row0;           // the first token of its head's stream in out (VL) or of its sequence
     const unsigned char *rec0;
+    int head = hb, cbase = 0;  // VL: the head, and the run's first chunk in the chunk table
     if constexpr (VL) {
-        const int doc = hb / H, h = hb % H;
-        const int t0 = bnd[doc], c0 = coff[doc], c1 = coff[doc + 1] < NCmax ? coff[doc + 1] : NCmax;
+        const int p = hb / H;
+        head = hb % H;
+        const int d0 = seg[p], d1 = seg[p + 1];
+        const int c0 = coff[d0], c1 = coff[d1] < NCmax ? coff[d1] : NCmax;
         NC = c1 > c0 ? c1 - c0 : 0;
-        ntok = bnd[doc + 1] - t0;
-        row0 = (size_t)h * T + t0;
-        rec0 = ws + ((size_t)h * NCmax + c0) * L.stride;
+        cbase = c0;
+        row0 = (size_t)head * T;
+        rec0 = ws + ((size_t)head * NCmax + c0) * L.stride;
     } else {
         NC = T / C;
-        ntok = T;
         row0 = (size_t)hb * T;
         rec0 = ws + (size_t)hb * NC * L.stride;
     }
+    const int4 *ent0 = VL ? ctab + cbase : nullptr;  // VL: the run's chunk-table entries, in chunk order
+    // where this lane's part of a state slice is: [document][head][value][key] (VL), [unit][value][key]
+    auto state_off = [&](int doc) {
+        return ((size_t)(VL ? (size_t)doc * H + head : (size_t)hb) * DV + j0 + l16) * DK + 4 * g;
+    };
     const size_t soff = L.region1 + (size_t)slice * L.slice;
-    const int j0 = 16 * slice;
 
     constexpr int NDMA = Cfg::NDMA;
     if (wave == 1 && NC > 0) {
-        issue_record<R1B, SLB>(lds_base(smem), rec0, soff, lane);
+        issue_record<R1B, SLB>(lds_base(smem), rec0, soff, lane, ent0);
         if (NBUF == 3 && NC > 1) {
-            issue_record<R1B, SLB>(lds_base(smem) + BUF, rec0 + L.stride, soff, lane);
+            issue_record<R1B, SLB>(lds_base(smem) + BUF, rec0 + L.stride, soff, lane, VL ? ent0 + 1 : nullptr);
             wait_vmcnt<NBUF == 3 ? NDMA : 0>();  // chunk 0 has landed
         } else {
             wait_vmcnt<0>();
@@ -145,13 +161,9 @@ __global__ __launch_bounds__(192, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     for (int mt = 0; mt < NDK; ++mt) S[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     int sS = 0;
     unsigned int nonfinite = 0;
-    if (init_state != nullptr && wave == 0) {
-        // S_0: init_state[hb][value j0 + l16][key 16 mt + 4g + i] = S^T[key][value], taken to the
-        // scale the state is kept at (read before this work-group writes final_state, which may
-        // be the same array)
-        const float *ip = init_state + ((size_t)hb * DV + j0 + l16) * DK + 4 * g;
-#pragma unroll
-        for (int mt = 0; mt < NDK; ++mt) S[mt] = *reinterpret_cast<const f32x4 *>(ip + 16 * mt);
+    // a fresh state taken to the scale the state is kept at (bf16 I/O)
+    auto take_scale = [&]() {
+        sS = 0;
         if constexpr (!F32) {
             float m = 0.f;
 #pragma unroll
@@ -167,7 +179,18 @@ __global__ __launch_bounds__(192, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                     for (int i = 0; i < 4; ++i) S[mt][i] = ldexp2(S[mt][i], sS);
             }
         }
+    };
+    if (init_state != nullptr && wave == 0 && (!VL || NC > 0)) {
+        // S_0: init_state[..][value j0 + l16][key 16 mt + 4g + i] = S^T[key][value] (read before this
+        // work-group writes final_state, which may be the same array)
+        const float *ip = init_state + state_off(VL ? ctab[cbase].z : 0);  // the run's first document
+#pragma unroll
+        for (int mt = 0; mt < NDK; ++mt) S[mt] = *reinterpret_cast<const f32x4 *>(ip + 16 * mt);
+        take_scale();
     }
+    f32x4 Si[VL ? NDK : 1];  // VL: the next document's initial state, loaded as its predecessor's last chunk starts
+#pragma unroll
+    for (int mt = 0; mt < (VL ? NDK : 1); ++mt) Si[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // Hand-over of the state operand to the output wave.  With two or more buffers, the state
     // wave stores chunk n's operand (and its exponent) at the end of chunk n - 1, over W^T in
@@ -244,17 +267,29 @@ __global__ __launch_bounds__(192, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             // ---- loader: the record two chunks ahead
             if (NBUF == 3) {
                 if (n + 2 < NC) {
-                    issue_record<R1B, SLB>(lds_base(smem) + ((n + 2) % 3) * BUF, rec0 + (size_t)(n + 2) * L.stride, soff, lane);
+                    issue_record<R1B, SLB>(lds_base(smem) + ((n + 2) % 3) * BUF, rec0 + (size_t)(n + 2) * L.stride, soff,
+                                           lane, VL ? ent0 + n + 2 : nullptr);
                     wait_vmcnt<NBUF == 3 ? NDMA : 0>();  // chunk n + 1 has landed
                 } else {
                     wait_vmcnt<0>();
                 }
             } else if (NBUF == 2 && n + 1 < NC) {
-                issue_record<R1B, SLB>(lds_base(smem) + ((n + 1) & 1) * BUF, rec0 + (size_t)(n + 1) * L.stride, soff, lane);
+                issue_record<R1B, SLB>(lds_base(smem) + ((n + 1) & 1) * BUF, rec0 + (size_t)(n + 1) * L.stride, soff,
+                                       lane, VL ? ent0 + n + 1 : nullptr);
                 wait_vmcnt<0>();
             }
         } else if (wave == 0) {
             // ---- state wave: U = U~ - W S^T;  S^T <- diag(gamma) S^T + K^^T U
+            int4 e_cur = make_int4(0, 0, 0, 0);
+            if constexpr (VL) {  // this chunk's entry; at a document's last chunk, the next one's initial state
+                e_cur = *reinterpret_cast<const int4 *>(cur + Cfg::ENT);
+                const int next_doc = (e_cur.w >> 2) - 1;
+                if (init_state != nullptr && (e_cur.w & 2) && next_doc >= 0) {
+                    const float *ip = init_state + state_off(next_doc);
+#pragma unroll
+                    for (int mt = 0; mt < NDK; ++mt) Si[mt] = *reinterpret_cast<const f32x4 *>(ip + 16 * mt);
+                }
+            }
             if (states != nullptr) {  // the state chunk n starts from, unscaled
                 float *sp = states + (((size_t)hb * NC + n) * DV + j0 + l16) * DK + 4 * g;
 #pragma unroll
@@ -335,6 +370,25 @@ __global__ __launch_bounds__(192, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                     sS += d;
                 }
             }
+            if constexpr (VL) {
+                if (e_cur.w & 2) {  // the last chunk of its document
+                    if (final_state != nullptr) {
+                        float *fp = final_state + state_off(e_cur.z);
+#pragma unroll
+                        for (int mt = 0; mt < NDK; ++mt) {
+                            f32x4 x;
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) x[i] = ldexp2(S[mt][i], -sS);
+                            *reinterpret_cast<f32x4 *>(fp + 16 * mt) = x;
+                        }
+                    }
+                    if (n + 1 < NC) {  // the next document starts from its own state
+#pragma unroll
+                        for (int mt = 0; mt < NDK; ++mt) S[mt] = init_state != nullptr ? Si[mt] : f32x4{0.f, 0.f, 0.f, 0.f};
+                        take_scale();
+                    }
+                }
+            }
             if constexpr (EARLY) {  // the next chunk's state operand, over this chunk's (consumed) W^T
                 FH sh[NKB];
                 state_operand(sh);
@@ -342,6 +396,7 @@ __global__ __launch_bounds__(192, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             }
         } else {
             // ---- output wave: O^T = Oi^T + (S^T)^T Qbar^T with the state the chunk started from
+            const int4 e_cur = VL ? *reinterpret_cast<const int4 *>(cur + Cfg::ENT) : make_int4(0, 0, 0, 0);
             if constexpr (!EARLY) {
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb) So[kb] = FH::load_pair(shx + kb * 512, lane);
@@ -363,8 +418,8 @@ __global__ __launch_bounds__(192, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                 for (int tt = 0; tt < NT; ++tt) O[tt] = mma(So[kb], qb[kb][tt], O[tt]);
-            const size_t trow = row0 + (size_t)n * C;
-            const int nval = ntok - n * C;  // rows of this chunk that are tokens (>= C unless packed)
+            const size_t trow = VL ? row0 + (size_t)e_cur.x : row0 + (size_t)n * C;
+            const int nval = VL ? e_cur.y : C;  // rows of this chunk that are tokens
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt) {
                 f32x4 o;
@@ -393,13 +448,14 @@ __global__ __launch_bounds__(192, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         barrier_lds();
         if (NBUF == 1) {
             if (wave == 1 && n + 1 < NC) {
-                issue_record<R1B, SLB>(lds_base(smem), rec0 + (size_t)(n + 1) * L.stride, soff, lane);
+                issue_record<R1B, SLB>(lds_base(smem), rec0 + (size_t)(n + 1) * L.stride, soff, lane,
+                                       VL ? ent0 + n + 1 : nullptr);
                 wait_vmcnt<0>();
             }
             barrier_lds();
         }
     }
-    if (wave == 0 && final_state != nullptr) {
+    if (!VL && wave == 0 && final_state != nullptr) {
         // final_state[hb][value j0 + l16][key 16 mt + 4g + i] = S^T[key][value]
         float *fp = final_state + ((size_t)hb * DV + j0 + l16) * DK + 4 * g;
 #pragma unroll

@@ -12,11 +12,16 @@
 // M, identity rows of T, a flat prefix sum G so e^(G_last) is the decay up to the
 // last real row), and the padded rows' outputs are not stored.
 //
-// The plan kernel below turns cu into the tables both stages index by; it runs as
-// one work-group ahead of them on the same stream:
+// The plan kernels below turn cu into the tables both stages index by; they run ahead of
+// them on the same stream:
 //   bnd[i]  (i = 0..N)    document boundaries, made nondecreasing and clipped to [0, T]
 //   coff[i] (i = 0..N)    index of document i's first chunk; coff[N] = chunks in use
-//   ctab[j] (j < NCmax)   {first token, rows} of chunk j; rows = 0 past the last chunk
+//   ctab[j] (j < NCmax)   {first token, rows, document, flags} of chunk j (flags: bit 0 = the
+//                         document's first chunk, bit 1 = its last; on a last chunk, bits 2.. =
+//                         1 + the document of the next chunk, 0 if there is none); rows = 0
+//                         past the last chunk
+//   seg[p]  (p = 0..P)    the documents split into P runs of about equal chunk counts: run p
+//                         is documents seg[p] .. seg[p+1]-1, chunks coff[seg[p]] .. coff[seg[p+1]]-1
 // With the boundaries nondecreasing inside [0, T] the chunk count is at most
 // floor(T / C) + N = NCmax, the number of records the workspace holds, so no
 // content of cu can make a stage index outside its buffers.
@@ -51,7 +56,7 @@ __device__ __forceinline__ int block_scan(int x, int *red, int &total) {
 template <int C>
 __global__ __launch_bounds__(1024) void kda_varlen_plan_kernel(const int *__restrict__ cu, int N, int T, int NCmax,
                                                               int *__restrict__ bnd, int *__restrict__ coff,
-                                                              int2 *__restrict__ ctab)
+                                                              int4 *__restrict__ ctab)
 {
     __shared__ int red[16];
     const int tid = threadIdx.x;
@@ -71,7 +76,8 @@ __global__ __launch_bounds__(1024) void kda_varlen_plan_kernel(const int *__rest
             bnd[i] = s0;
             coff[i] = c0;
             for (int m = 0; m < nch; ++m)
-                if (c0 + m < NCmax) ctab[c0 + m] = make_int2(s0 + m * C, min(C, len - m * C));
+                if (c0 + m < NCmax)
+                    ctab[c0 + m] = make_int4(s0 + m * C, min(C, len - m * C), i, (m == 0 ? 1 : 0) | (m == nch - 1 ? 2 : 0));
         }
         cmax = max(cmax, tmax);
         csum += tsum;
@@ -80,7 +86,41 @@ __global__ __launch_bounds__(1024) void kda_varlen_plan_kernel(const int *__rest
         bnd[N] = max(cmax, clip(cu[N]));
         coff[N] = min(csum, NCmax);
     }
-    for (int j = csum + tid; j < NCmax; j += 1024) ctab[j] = make_int2(0, 0);
+    for (int j = csum + tid; j < NCmax; j += 1024) ctab[j] = make_int4(0, 0, 0, 0);
+}
+
+// Second plan kernel (after the first): block 0 splits the documents into P runs of about equal
+// chunk counts (seg); blocks 1 .. NB mark each document's last chunk with the document of the
+// chunk after it; block 1 + NB + i gives document i, if it has no tokens, its final state (its
+// initial state, else zero) for every head, since no chunk of the state stage will.
+__global__ __launch_bounds__(256) void kda_varlen_seg_kernel(const int *__restrict__ bnd, const int *__restrict__ coff,
+                                                             int N, int P, int *__restrict__ seg, int4 *__restrict__ ctab,
+                                                             int NB, const float *init, float *final_state, int per_doc) {
+    const int tid = threadIdx.x;
+    if (blockIdx.x >= 1 && blockIdx.x <= NB) {
+        const int j = (blockIdx.x - 1) * 256 + tid, ntot = coff[N];
+        if (j < ntot && (ctab[j].w & 2)) ctab[j].w |= (j + 1 < ntot ? ctab[j + 1].z + 1 : 0) << 2;
+        return;
+    }
+    if (blockIdx.x == 0) {
+        const long long ntot = coff[N];
+        for (int p = tid; p <= P; p += 256) {
+            const long long target = (ntot * p + P - 1) / P;
+            int lo = 0, hi = N;  // lowest i with coff[i] >= target (coff is nondecreasing, coff[N] = ntot)
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (coff[mid] >= target) hi = mid;
+                else lo = mid + 1;
+            }
+            seg[p] = p == 0 ? 0 : (p == P ? N : lo);
+        }
+        return;
+    }
+    const int i = blockIdx.x - 1 - NB;
+    if (final_state == nullptr || bnd[i + 1] != bnd[i]) return;
+    float *dst = final_state + (size_t)i * per_doc;
+    const float *src = init == nullptr ? nullptr : init + (size_t)i * per_doc;
+    for (int e = tid; e < per_doc; e += 256) dst[e] = src == nullptr ? 0.f : src[e];
 }
 
 }  // namespace kda

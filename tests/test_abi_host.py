@@ -135,11 +135,17 @@ def test_binding_rejects_host_tensors():
 
 def test_varlen_workspace_bytes():
     # records for T / chunk + N chunks per head (each document may end in a short chunk), then the
-    # plan tables: N + 1 boundaries, N + 1 chunk offsets, and a {token, rows} pair per chunk
+    # plan tables: a {token, rows, document, flags} entry per chunk, N + 1 boundaries, N + 1 chunk
+    # offsets and R + 1 run boundaries (R = enough runs to give 256 walks over heads and slices, at
+    # most N)
     rec = kda.workspace_bytes(1, 1, 64, 128, 128, 64, torch.bfloat16)
     N, H, T = 76, 32, 65536
     nc = T // 64 + N
-    assert kda.varlen_workspace_bytes(N, H, T, 128, 128, 64, torch.bfloat16) == H * nc * rec + 8 * (N + 1) + 8 * nc
+    assert kda.varlen_workspace_bytes(N, H, T, 128, 128, 64, torch.bfloat16) == \
+        H * nc * rec + 16 * nc + 8 * (N + 1) + 4 * (1 + 1)
+    rec2 = kda.workspace_bytes(1, 1, 16, 64, 64, 16, torch.float32)
+    assert kda.varlen_workspace_bytes(5, 2, 100, 64, 64, 16, torch.float32) == \
+        2 * (100 // 16 + 5) * rec2 + 16 * (100 // 16 + 5) + 8 * 6 + 4 * (5 + 1)  # R = min(5, 256 / 8)
     assert kda.varlen_workspace_bytes(3, 2, 100, 64, 64, 16, torch.float32) > 0   # T need not divide by chunk
     assert kda.varlen_workspace_bytes(0, 2, 100, 64, 64, 16, torch.float32) == 0  # no document
     assert kda.varlen_workspace_bytes(3, 2, 100, 96, 64, 16, torch.float32) == 0
