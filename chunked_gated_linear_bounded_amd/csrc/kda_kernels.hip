@@ -66,12 +66,13 @@ static hipError_t launch_intra_t(const LaunchArgs &p) {
     if (p.cu != nullptr) {
         const PlanPtrs pl = plan_ptrs(p);
         hipLaunchKernelGGL((kda_varlen_plan_kernel<C>), dim3(1), dim3(1024), 0, p.stream, p.cu, p.nseq, p.T, p.ncmax,
-                           pl.bnd, pl.coff, pl.ctab);
+                           pl.bnd, pl.coff);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         const int nb = (p.ncmax + 255) / 256;
-        hipLaunchKernelGGL(kda_varlen_seg_kernel, dim3(1 + nb + p.nseq), dim3(256), 0, p.stream, pl.bnd, pl.coff,
-                           p.nseq, p.nrun, pl.seg, pl.ctab, nb, p.init_state, p.final_state, p.H * p.dv * p.dk);
+        hipLaunchKernelGGL((kda_varlen_seg_kernel<C>), dim3(1 + nb + p.nseq), dim3(256), 0, p.stream, pl.bnd, pl.coff,
+                           p.nseq, p.nrun, p.ncmax, pl.seg, pl.ctab, nb, p.init_state, p.final_state,
+                           p.H * p.dv * p.dk);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL((kda_intra_kernel<C, DK, DV, F32, true, 0>), dim3(p.ncmax, p.H, 1), dim3(256), 0,

@@ -69,6 +69,12 @@ __device__ __forceinline__ void dma_to_lds(lds_u8 *dst, const unsigned char *__r
     }
 }
 
+// A value every lane holds alike (read from one LDS address), moved to scalar registers.
+__device__ __forceinline__ int4 uniform(int4 e) {
+    return make_int4(__builtin_amdgcn_readfirstlane(e.x), __builtin_amdgcn_readfirstlane(e.y),
+                     __builtin_amdgcn_readfirstlane(e.z), __builtin_amdgcn_readfirstlane(e.w));
+}
+
 // Issue the copies of one chunk's record (region 1 + one value slice) and, when `ent` is not
 // NULL, of its 16-byte chunk-table entry (one lane) right after them.
 template <int R1, int SL>
@@ -282,7 +288,7 @@ __global__ __launch_bounds__(192, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             // ---- state wave: U = U~ - W S^T;  S^T <- diag(gamma) S^T + K^^T U
             int4 e_cur = make_int4(0, 0, 0, 0);
             if constexpr (VL) {  // this chunk's entry; at a document's last chunk, the next one's initial state
-                e_cur = *reinterpret_cast<const int4 *>(cur + Cfg::ENT);
+                e_cur = uniform(*reinterpret_cast<const int4 *>(cur + Cfg::ENT));
                 const int next_doc = (e_cur.w >> 2) - 1;
                 if (init_state != nullptr && (e_cur.w & 2) && next_doc >= 0) {
                     const float *ip = init_state + state_off(next_doc);
@@ -396,7 +402,7 @@ __global__ __launch_bounds__(192, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             }
         } else {
             // ---- output wave: O^T = Oi^T + (S^T)^T Qbar^T with the state the chunk started from
-            const int4 e_cur = VL ? *reinterpret_cast<const int4 *>(cur + Cfg::ENT) : make_int4(0, 0, 0, 0);
+            const int4 e_cur = VL ? uniform(*reinterpret_cast<const int4 *>(cur + Cfg::ENT)) : make_int4(0, 0, 0, 0);
             if constexpr (!EARLY) {
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb) So[kb] = FH::load_pair(shx + kb * 512, lane);

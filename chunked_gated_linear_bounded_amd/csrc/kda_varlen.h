@@ -12,8 +12,8 @@
 // M, identity rows of T, a flat prefix sum G so e^(G_last) is the decay up to the
 // last real row), and the padded rows' outputs are not stored.
 //
-// The plan kernels below turn cu into the tables both stages index by; they run ahead of
-// them on the same stream:
+// The two plan kernels below turn cu into the tables both stages index by; they run ahead
+// of them on the same stream (the first writes bnd and coff, the second the rest):
 //   bnd[i]  (i = 0..N)    document boundaries, made nondecreasing and clipped to [0, T]
 //   coff[i] (i = 0..N)    index of document i's first chunk; coff[N] = chunks in use
 //   ctab[j] (j < NCmax)   {first token, rows, document, flags} of chunk j (flags: bit 0 = the
@@ -55,8 +55,7 @@ __device__ __forceinline__ int block_scan(int x, int *red, int &total) {
 
 template <int C>
 __global__ __launch_bounds__(1024) void kda_varlen_plan_kernel(const int *__restrict__ cu, int N, int T, int NCmax,
-                                                              int *__restrict__ bnd, int *__restrict__ coff,
-                                                              int4 *__restrict__ ctab)
+                                                              int *__restrict__ bnd, int *__restrict__ coff)
 {
     __shared__ int red[16];
     const int tid = threadIdx.x;
@@ -75,9 +74,6 @@ __global__ __launch_bounds__(1024) void kda_varlen_plan_kernel(const int *__rest
         if (doc) {
             bnd[i] = s0;
             coff[i] = c0;
-            for (int m = 0; m < nch; ++m)
-                if (c0 + m < NCmax)
-                    ctab[c0 + m] = make_int4(s0 + m * C, min(C, len - m * C), i, (m == 0 ? 1 : 0) | (m == nch - 1 ? 2 : 0));
         }
         cmax = max(cmax, tmax);
         csum += tsum;
@@ -86,20 +82,44 @@ __global__ __launch_bounds__(1024) void kda_varlen_plan_kernel(const int *__rest
         bnd[N] = max(cmax, clip(cu[N]));
         coff[N] = min(csum, NCmax);
     }
-    for (int j = csum + tid; j < NCmax; j += 1024) ctab[j] = make_int4(0, 0, 0, 0);
+}
+
+// The document that chunk j (< coff[N]) belongs to: the last i with coff[i] <= j.  Documents
+// without chunks share their offset with the next one, so the search lands on a document
+// that has tokens.
+__device__ __forceinline__ int doc_of_chunk(const int *__restrict__ coff, int N, int j) {
+    int lo = 0, hi = N + 1;  // first index with coff[index] > j lies in (0, N]
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (coff[mid] > j) hi = mid;
+        else lo = mid + 1;
+    }
+    return lo - 1;
 }
 
 // Second plan kernel (after the first): block 0 splits the documents into P runs of about equal
-// chunk counts (seg); blocks 1 .. NB mark each document's last chunk with the document of the
-// chunk after it; block 1 + NB + i gives document i, if it has no tokens, its final state (its
-// initial state, else zero) for every head, since no chunk of the state stage will.
+// chunk counts (seg); blocks 1 .. NB write the chunk table, one entry per thread, so a long
+// document costs no more than many short ones; block 1 + NB + i gives document i, if it has no
+// tokens, its final state (its initial state, else zero) for every head, since no chunk of the
+// state stage will.
+template <int C>
 __global__ __launch_bounds__(256) void kda_varlen_seg_kernel(const int *__restrict__ bnd, const int *__restrict__ coff,
-                                                             int N, int P, int *__restrict__ seg, int4 *__restrict__ ctab,
-                                                             int NB, const float *init, float *final_state, int per_doc) {
+                                                             int N, int P, int NCmax, int *__restrict__ seg,
+                                                             int4 *__restrict__ ctab, int NB, const float *init,
+                                                             float *final_state, int per_doc) {
     const int tid = threadIdx.x;
     if (blockIdx.x >= 1 && blockIdx.x <= NB) {
         const int j = (blockIdx.x - 1) * 256 + tid, ntot = coff[N];
-        if (j < ntot && (ctab[j].w & 2)) ctab[j].w |= (j + 1 < ntot ? ctab[j + 1].z + 1 : 0) << 2;
+        if (j >= NCmax) return;
+        int4 e = make_int4(0, 0, 0, 0);
+        if (j < ntot) {
+            const int i = doc_of_chunk(coff, N, j), m = j - coff[i], nch = coff[i + 1] - coff[i];
+            const int len = bnd[i + 1] - bnd[i];
+            int flags = (m == 0 ? 1 : 0) | (m == nch - 1 ? 2 : 0);
+            if (m == nch - 1 && j + 1 < ntot) flags |= (doc_of_chunk(coff, N, j + 1) + 1) << 2;
+            e = make_int4(bnd[i] + m * C, min(C, len - m * C), i, flags);
+        }
+        ctab[j] = e;
         return;
     }
     if (blockIdx.x == 0) {
