@@ -8,25 +8,50 @@
 // Practical Techniques ...", sec. 3.2).
 //
 // The step reads and writes the whole state once, so it is bound by HBM.  One work-group
-// per (head, block of 16 value rows); each wave takes 4 rows, its lanes the key channels
-// (coalesced 256-byte row segments).  Per row the two dot products y_i = S~_i . k and
-// S~_i . q are reduced over the wave together; k . q is reduced once.
+// per (head, block of 16 value rows), 4 rows per wave.  A row of S is read as 16-byte
+// pieces, 4 key channels per lane: DK/4 lanes per row, so one wave-wide access covers
+// 256/DK rows.  Every load of the wave (its rows of S, and q, k, a, v) is issued before any
+// is used, so a wave keeps all its bytes in flight at once; the two dot products of a row,
+// y = S~ k and S~ q, are then reduced over the row's lanes, and k . q once.
 #pragma once
 #include "kda_device.h"
 
 namespace kda {
 
-// Sum over the 64 lanes of a wave, returned to every lane (wave-uniform).
-__device__ __forceinline__ float wave_sum(float x) {
+// Sum over each group of LPR consecutive lanes (16 or 32), returned to every lane of the group.
+template <int LPR>
+__device__ __forceinline__ float group_sum(float x) {
     x += dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]
     x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]
     x += dpp_mov<0x141>(x);  // row_half_mirror
-    x += dpp_mov<0x140>(x);  // row_mirror: every lane holds its row's sum
-    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 0));
-    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 16));
-    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 32));
-    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 48));
-    return (r0 + r1) + (r2 + r3);
+    x += dpp_mov<0x140>(x);  // row_mirror: every lane holds its 16-lane row's sum
+    if constexpr (LPR == 16) {
+        return x;
+    } else {
+        static_assert(LPR == 32, "groups of 16 or 32 lanes");
+        const int xi = __builtin_bit_cast(int, x);
+        const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 0));
+        const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 16));
+        const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 32));
+        const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 48));
+        return (threadIdx.x & 32) ? r2 + r3 : r0 + r1;
+    }
+}
+
+// Four consecutive elements as floats (one 8-byte load for bf16, one 16-byte load for fp32).
+template <typename E>
+__device__ __forceinline__ void load4(const E *__restrict__ p, float (&x)[4]) {
+    if constexpr (sizeof(E) == 4) {
+        const f32x4 v = *reinterpret_cast<const f32x4 *>(p);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = v[i];
+    } else {
+        const uint2 u = *reinterpret_cast<const uint2 *>(p);
+        x[0] = __builtin_bit_cast(float, u.x << 16);
+        x[1] = __builtin_bit_cast(float, u.x & 0xffff0000u);
+        x[2] = __builtin_bit_cast(float, u.y << 16);
+        x[3] = __builtin_bit_cast(float, u.y & 0xffff0000u);
+    }
 }
 
 template <int DK, int DV, bool F32>
@@ -40,44 +65,61 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(
     typename std::conditional<F32, float, __bf16>::type *__restrict__ out)
 {
     using E = typename std::conditional<F32, float, __bf16>::type;
-    constexpr int CPL = DK / 64;        // key channels per lane
-    constexpr int RB = 16;              // value rows per work-group
-    constexpr int NB = DV / RB;         // row blocks per head
+    constexpr int LPR = DK / 4;    // lanes per state row
+    constexpr int RPI = 64 / LPR;  // rows per wave-wide access
+    constexpr int RPW = 4;         // rows per wave
+    constexpr int NI = RPW / RPI;  // accesses per wave
+    static_assert(RPW % RPI == 0, "whole accesses per wave");
+    constexpr int RB = 4 * RPW;    // value rows per work-group
+    constexpr int NB = DV / RB;    // row blocks per head
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const size_t head = blockIdx.x / NB;
-    const int r0 = (blockIdx.x % NB) * RB + 4 * wave;  // this wave's 4 rows
+    const int c0 = 4 * (lane % LPR);                               // this lane's 4 key channels
+    const int rw = (blockIdx.x % NB) * RB + RPW * wave + lane / LPR;  // its row in access 0
 
-    float kc[CPL], qc[CPL], ec[CPL];
+    // every load first
+    f32x4 st[NI];
+    float vr[NI];
+#pragma unroll
+    for (int x = 0; x < NI; ++x) {
+        const int i = rw + RPI * x;
+        st[x] = *reinterpret_cast<const f32x4 *>(state + (head * DV + i) * DK + c0);
+        vr[x] = to_f(v[head * DV + i]);
+    }
+    float kc[4], qc[4], ac[4];
+    load4(k + head * DK + c0, kc);
+    load4(q + head * DK + c0, qc);
+    load4(a + head * DK + c0, ac);
+    const float b = to_f(beta[head]);
+
+    float ec[4];
     float kq = 0.f;
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-        const int c = lane + 64 * j;
-        kc[j] = to_f(k[head * DK + c]);
-        qc[j] = to_f(q[head * DK + c]);
-        ec[j] = ex2(gate_log2(to_f(a[head * DK + c]), gmin2, logsig));  // e^g, in (0, 1]
+    for (int j = 0; j < 4; ++j) {
+        ec[j] = ex2(gate_log2(ac[j], gmin2, logsig));  // e^g, in (0, 1]
         kq += kc[j] * qc[j];
     }
-    kq = wave_sum(kq);
-    const float b = to_f(beta[head]);
+    kq = group_sum<LPR>(kq);
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-        const int i = r0 + rr;
-        float *row = state + (head * DV + i) * DK;
-        float s[CPL];
+    for (int x = 0; x < NI; ++x) {
+        const int i = rw + RPI * x;
+        float s[4];
         float yk = 0.f, yq = 0.f;
 #pragma unroll
-        for (int j = 0; j < CPL; ++j) {
-            s[j] = row[lane + 64 * j] * ec[j];
+        for (int j = 0; j < 4; ++j) {
+            s[j] = st[x][j] * ec[j];
             yk += s[j] * kc[j];
             yq += s[j] * qc[j];
         }
-        yk = wave_sum(yk);
-        yq = wave_sum(yq);
-        const float d = b * (to_f(v[head * DV + i]) - yk);
+        yk = group_sum<LPR>(yk);
+        yq = group_sum<LPR>(yq);
+        const float d = b * (vr[x] - yk);
+        f32x4 o;
 #pragma unroll
-        for (int j = 0; j < CPL; ++j) row[lane + 64 * j] = fmaf(d, kc[j], s[j]);
-        if (lane == 0) out[head * DV + i] = from_f<E>(fmaf(d, kq, yq));
+        for (int j = 0; j < 4; ++j) o[j] = fmaf(d, kc[j], s[j]);
+        *reinterpret_cast<f32x4 *>(state + (head * DV + i) * DK + c0) = o;
+        if (lane % LPR == 0) out[head * DV + i] = from_f<E>(fmaf(d, kq, yq));
     }
 }
 
