@@ -18,6 +18,9 @@
 
 namespace kda {
 
+constexpr int kDecodeRowsPerWave = 4;                       // value rows per wave
+constexpr int kDecodeRowsPerBlock = 4 * kDecodeRowsPerWave;  // per 256-thread work-group
+
 // Sum over each group of LPR consecutive lanes (16 or 32), returned to every lane of the group.
 template <int LPR>
 __device__ __forceinline__ float group_sum(float x) {
@@ -67,10 +70,10 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(
     using E = typename std::conditional<F32, float, __bf16>::type;
     constexpr int LPR = DK / 4;    // lanes per state row
     constexpr int RPI = 64 / LPR;  // rows per wave-wide access
-    constexpr int RPW = 4;         // rows per wave
+    constexpr int RPW = kDecodeRowsPerWave;
     constexpr int NI = RPW / RPI;  // accesses per wave
     static_assert(RPW % RPI == 0, "whole accesses per wave");
-    constexpr int RB = 4 * RPW;    // value rows per work-group
+    constexpr int RB = kDecodeRowsPerBlock;
     constexpr int NB = DV / RB;    // row blocks per head
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);

@@ -157,7 +157,8 @@ hipError_t launch_gate_cumsum(const LaunchArgs &p) {
 template <int DK, int DV, bool F32>
 static hipError_t launch_decode_t(const LaunchArgs &p) {
     using E = typename std::conditional<F32, float, __bf16>::type;
-    const int grid = p.B * p.H * (DV / 16);
+    static_assert(DV % kDecodeRowsPerBlock == 0, "whole row blocks");
+    const int grid = p.B * p.H * (DV / kDecodeRowsPerBlock);
     hipLaunchKernelGGL((kda_decode_kernel<DK, DV, F32>), dim3(grid), dim3(256), 0, p.stream,
                        reinterpret_cast<const E *>(p.q), reinterpret_cast<const E *>(p.k),
                        reinterpret_cast<const E *>(p.v), reinterpret_cast<const E *>(p.a),
