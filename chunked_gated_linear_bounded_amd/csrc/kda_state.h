@@ -30,7 +30,12 @@
 // chunk: the first after the output wave has taken the state operand (the
 // loader only then refills that buffer), the second when the chunk is done.
 // Work-group ids are mapped so that all slices of a head land on one XCD and
-// share its L2.
+// share its L2.  The slices of a head read each record in the same order at
+// nearly the same time, so one of them takes the HBM miss and the others hit
+// in L2; the ring alone then keeps only two records per head in flight, which
+// bounds the stage by HBM latency.  The loader therefore also touches its
+// slice's share of the record four chunks ahead, so that the ring's loads
+// find it in L2.
 #pragma once
 #include "kda_device.h"
 #include "kda_layout.h"
@@ -50,8 +55,15 @@ struct StateCfg {
     static constexpr int NDMA = (int)((L.region1 + 1023) / 1024 + (L.slice + 1023) / 1024) + (VL ? 1 : 0);
     // three buffers give two chunks of lookahead; the partial wait needs NDMA <= 63
     static constexpr int NBUF = (3 * BUF <= LDS_MAX && NDMA <= 63) ? 3 : (2 * BUF <= LDS_MAX) ? 2 : 1;
-    static constexpr int SMEM = NBUF * BUF;
     static constexpr int NS = DV / 16;
+    // L2 prefetch (three buffers only): each of a head's NS slice work-groups touches its 1/NS
+    // share of the record PF chunks ahead, one 4-byte direct load per 128-byte line into a
+    // 256-byte sink after the ring, so the ring's own loads find the record in L2
+    static constexpr int PF = 4;
+    static constexpr int PF_SHARE = (int)(L.stride / NS);
+    static constexpr int PF_LINES = (PF_SHARE + 127) / 128, PF_INST = (PF_LINES + 63) / 64;
+    static constexpr bool PREFETCH = NBUF == 3 && NDMA + PF_INST <= 63 && NBUF * BUF + 256 <= LDS_MAX;
+    static constexpr int SMEM = NBUF * BUF + (PREFETCH ? 256 : 0);
 };
 
 // Issue direct global->LDS copies of BYTES (multiple of 16) with one wave:
@@ -148,8 +160,21 @@ __global__ __launch_bounds__(192, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     };
     const size_t soff = L.region1 + (size_t)slice * L.slice;
 
-    constexpr int NDMA = Cfg::NDMA;
+    constexpr int NDMA = Cfg::NDMA, PF = Cfg::PF, PF_INST = Cfg::PF_INST;
+    // this slice's share of chunk m's record into L2 (m < NC)
+    auto prefetch = [&](int m) {
+        const unsigned char *src = rec0 + (size_t)m * L.stride + (size_t)slice * Cfg::PF_SHARE;
+#pragma unroll
+        for (int i = 0; i < PF_INST; ++i) {
+            const int line = i * 64 + lane;
+            if (line < Cfg::PF_LINES)
+                __builtin_amdgcn_global_load_lds(src + (size_t)line * 128, (lds_void *)(lds_base(smem) + NBUF * BUF), 4, 0, 0);
+        }
+    };
     if (wave == 1 && NC > 0) {
+        if constexpr (Cfg::PREFETCH) {  // chunks 2 .. PF - 1 (the loop prefetches chunk n + PF)
+            for (int m = 2; m < PF && m < NC; ++m) prefetch(m);
+        }
         issue_record<R1B, SLB>(lds_base(smem), rec0, soff, lane, ent0);
         if (NBUF == 3 && NC > 1) {
             issue_record<R1B, SLB>(lds_base(smem) + BUF, rec0 + L.stride, soff, lane, VL ? ent0 + 1 : nullptr);
@@ -275,7 +300,12 @@ __global__ __launch_bounds__(192, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                 if (n + 2 < NC) {
                     issue_record<R1B, SLB>(lds_base(smem) + ((n + 2) % 3) * BUF, rec0 + (size_t)(n + 2) * L.stride, soff,
                                            lane, VL ? ent0 + n + 2 : nullptr);
-                    wait_vmcnt<NBUF == 3 ? NDMA : 0>();  // chunk n + 1 has landed
+                    if (Cfg::PREFETCH && n + PF < NC) {
+                        prefetch(n + PF);
+                        wait_vmcnt<Cfg::PREFETCH ? NDMA + PF_INST : 0>();  // chunk n + 1 has landed
+                    } else {
+                        wait_vmcnt<NBUF == 3 ? NDMA : 0>();  // chunk n + 1 has landed
+                    }
                 } else {
                     wait_vmcnt<0>();
                 }
