@@ -96,6 +96,21 @@ def test_multi_batch_bf16():
     _tol_check(fs.double().cpu().numpy(), rf, "bf16", "final_state")
 
 
+@pytest.mark.parametrize("nchunks", [1, 2, 3, 4, 5, 9])
+def test_sequences_around_the_prefetch_distance(nchunks):
+    # bf16, d = 128, chunk 64: the state stage touches each record four chunks ahead of its LDS
+    # ring; sequences shorter than, equal to and longer than that distance, 12 heads (a ragged
+    # group of 8 heads on the last XCD)
+    w = KI.Workload("pf", 1, 12, 64 * nchunks, 128, 128, 64, "bf16", 4.0, False, 300 + nchunks)
+    _say("prefetch distance", nchunks)
+    inp = _to_dev(KI.make_inputs(w))
+    out, fs = _gpu_run(inp, 64)
+    torch.cuda.synchronize()
+    ro, rf = _oracle(KI.to_f64(inp))
+    _tol_check(out.double().cpu().numpy(), ro, "bf16")
+    _tol_check(fs.double().cpu().numpy(), rf, "bf16", "final_state")
+
+
 # ---------------------------------------------------------------- the large workloads, sampled heads
 def _sampled(w, heads, t_end=None):
     _say("workload", w.name, "generating on GPU")
