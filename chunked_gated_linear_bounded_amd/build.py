@@ -7,7 +7,10 @@ Flags: -O3 for gfx950 only; packed-fp32 instruction selection is disabled
 are kept in ordinary VGPRs (-amdgpu-mfma-vgpr-form): a kernel whose LDS use
 already limits it to one work-group per CU otherwise gets the accumulator-
 register form, and every accumulator is copied out with v_accvgpr_read
-before VALU code can use it.
+before VALU code can use it.  The machine scheduler favours instruction-level
+parallelism over occupancy (-amdgpu-sched-strategy=max-ilp): the chunk kernel's
+occupancy is set by its LDS and the state kernel runs one work-group per CU, so
+latency hiding inside a wave is what pays (about 1 % and 3 % faster, same results).
 """
 from __future__ import annotations
 
@@ -27,7 +30,8 @@ ARCH = "gfx950"
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 DEVICE = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          "-munsafe-fp-atomics", "-mllvm", "-amdgpu-mfma-vgpr-form"]
+          "-munsafe-fp-atomics", "-mllvm", "-amdgpu-mfma-vgpr-form",
+          "-mllvm", "-amdgpu-sched-strategy=max-ilp"]
 
 # (source, output object, extra defines)
 UNITS = [
