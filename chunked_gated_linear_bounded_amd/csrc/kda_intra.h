@@ -591,9 +591,10 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     // ------------------------------------------------ phase 3
     // Fragments indexed by (row tile rt, token K-block kb): lane l holds row r = 16 rt + l16,
     // slots = columns 32 kb + kslot.  tf: T diag(beta); mf: M.  The products with M (M W and
-    // M U~) take fp16 operands: |M| <= 1 (unit q, k and factors e^{G_r - G_s} <= 1), and W and
-    // U~ are far inside the fp16 range, so one fp16 MFMA (11 significand bits) replaces the
-    // two or three bf16 hi + lo products.
+    // M U~) take fp16 operands, so one fp16 MFMA (11 significand bits) replaces the two or three
+    // bf16 hi + lo products: |M| <= 1 (unit q, k and factors e^{G_r - G_s} <= 1) and W is far
+    // inside the fp16 range (unit keys); U~ follows the scale of v, so it enters scaled by the
+    // power of two of its block's maximum.
     // Only the causal K-blocks kb <= rt / 2 are used.  T and M are stored for blocks on and
     // below the diagonal only; the one block above the diagonal that such a K-block spans
     // (column tile 2 kb + 1 = rt + 1) is zero and is never read.
@@ -708,18 +709,21 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 #pragma unroll
             for (int i = 0; i < 4; ++i) um = fmaxf(um, fabsf(acc[i]));
         }
-        FM ua[NTKB];  // U~ as the A operand of U~^T (m = dv, k = token)
+        // U~ 2^sU as the A operand of U~^T (m = dv, k = token): the block scale keeps the fp16
+        // operand in range whatever the magnitude of v; Oi comes out scaled by 2^sU as well
+        const int sU_ = F32 ? 0 : pow2_scale(wave_max(um));
+        FM ua[NTKB];
 #pragma unroll
         for (int kb = 0; kb < NTKB; ++kb) {
             float x[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int t = 2 * kb + j / 4;
-                x[j] = (t < NT) ? urow[t < NT ? t : 0][j % 4] : 0.f;
+                x[j] = (t < NT) ? ldexp2(urow[t < NT ? t : 0][j % 4], sU_) : 0.f;
             }
             ua[kb] = FM::make(x);
         }
-        f32x4 orow[NT];
+        f32x4 orow[NT];  // Oi 2^sU
         float om = 0.f;
 #pragma unroll
         for (int rt = 0; rt < NT; ++rt) {
@@ -730,8 +734,7 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 #pragma unroll
             for (int i = 0; i < 4; ++i) om = fmaxf(om, fabsf(acc[i]));
         }
-        const int sU_ = F32 ? 0 : pow2_scale(wave_max(um));
-        const int sO_ = F32 ? 0 : pow2_scale(wave_max(om));
+        const int sO_ = F32 ? 0 : pow2_scale(wave_max(om));  // Oi is stored scaled by 2^(sU + sO)
 #pragma unroll
         for (int rt = 0; rt < NT; ++rt) {
             f32x4 u, o;
@@ -745,7 +748,7 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
         }
         if (lane == 0) {
             wS[0] = sU_;
-            wS[1] = sO_;
+            wS[1] = sU_ + sO_;
             wS[2] = 0;
             wS[3] = 0;
         }

@@ -101,7 +101,12 @@ int kda_gate_cumsum(const void *a, float g_min, int chunk, int B, int H, int T, 
                     int io_dtype, int gate_mode, float *G_out, hipStream_t stream);
 
 /* Chunked forward: out[b][h][t] = o_t for every token; if final_state is not
- * NULL it receives S_T.  workspace: device buffer of at least
+ * NULL it receives S_T.  q and k are expected L2-normalised per token and head
+ * (the delta rule's convention, under which I - beta k k^T is a contraction):
+ * the fp16 operands formed from them inside the chunk stage (M, W) rely on it.
+ * v may have any magnitude in the range of the I/O type: every operand that
+ * follows its scale is block-scaled by a power of two, so scaling v by 2^e
+ * scales out and the final state by exactly 2^e.  workspace: device buffer of at least
  * kda_chunk_fwd_workspace_bytes(...) bytes, contents undefined on entry and on
  * return; it must not overlap any other argument. */
 int kda_chunk_fwd(const void *q, const void *k, const void *v, const void *a, const void *beta,

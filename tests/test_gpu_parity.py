@@ -230,6 +230,25 @@ def test_linear_in_v():
     assert float((oz - (2.0 * ox - 3.0 * oy)).abs().max()) <= 1e-4
 
 
+@pytest.mark.parametrize("io", ["bf16", "fp32"])
+@pytest.mark.parametrize("chunk", [16, 64])
+def test_power_of_two_scaling_of_v_is_exact(io, chunk):
+    # Every 16-bit operand that follows the scale of v is scaled by a power of two taken from its
+    # own block, so scaling v by 2^e changes no rounding: out and the final state scale by exactly
+    # 2^e, far beyond the fp16 range in both directions.
+    w = KI.Workload("p2", 1, 3, 4 * chunk, 128, 128, chunk, io, 4.0, False, 77 + chunk)
+    _say("power-of-two scaling", io, chunk)
+    inp = _to_dev(KI.make_inputs(w))
+    out, fs = _gpu_run(inp, chunk)
+    for e in (-20, 20):
+        x = dict(inp)
+        x["v"] = inp["v"] * 2.0 ** e
+        o2, f2 = _gpu_run(x, chunk)
+        torch.cuda.synchronize()
+        assert torch.equal(o2.float(), out.float() * 2.0 ** e), (e, float((o2.float() - out.float() * 2.0 ** e).abs().max()))
+        assert torch.equal(f2, fs * 2.0 ** e), e
+
+
 def test_empty_sequence():
     inp = {n: torch.empty((1, 2, 0, 64) if n != "beta" else (1, 2, 0), dtype=torch.bfloat16, device="cuda")
            for n in ("q", "k", "v", "a", "beta")}
