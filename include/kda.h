@@ -34,8 +34,9 @@
  *    array with zero elements (T == 0) may be NULL.
  *  - Supported: dk, dv in {64, 128}; chunk in {16, 32, 64}; T % chunk == 0;
  *    1 <= B, H <= 65535; T >= 0; B*H*T*max(dk,dv) < 2^40.  Bounded mode needs a finite
- *    g_min with KDA_G_MIN_LOWEST <= g_min < 0 (below that bound a 16-token tile
- *    can leave the bf16/fp32 exponent range); the ablation mode ignores g_min.
+ *    g_min with KDA_G_MIN_LOWEST <= g_min < 0 (below that bound the decay factors
+ *    of a 16-token tile leave the range in which 16-bit operands keep their
+ *    precision); the ablation mode ignores g_min.
  *  - Every argument is validated on the host before anything is launched; on a
  *    bad argument a negative kda_status is returned and nothing is launched.
  *    Work is enqueued asynchronously on `stream` (0 = the null stream); device
@@ -55,10 +56,16 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 5
-/* ln(smallest normal float) / 15: the most negative g_min for which 15 steps of
- * decay inside a 16-token tile stay in the normal exponent range. */
-#define KDA_G_MIN_LOWEST (-5.8224f)
+#define KDA_ABI_VERSION 6
+/* The most negative g_min accepted: the constant the method fixes.  Inside a
+ * 16-token tile the key operands of the diagonal sub-tile grow by up to
+ * e^(15 |g_min|) and the row operands shrink by as much; at g_min = -5 both stay
+ * e^12 inside the bf16/fp32 normal range (largest e^88.7, smallest normal
+ * e^-87.3), so a row-operand component flushes only below 4.4e-6.  Closer to
+ * the edge the shrunk row operands of a tile's last rows turn subnormal while
+ * their products with the grown key operands are O(1) entries of M and A: with
+ * every gate saturated, g_min = -5.6 already misses the bf16 tolerance. */
+#define KDA_G_MIN_LOWEST (-5.0f)
 
 typedef enum {
     KDA_OK = 0,

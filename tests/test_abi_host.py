@@ -34,7 +34,7 @@ def test_header_symbols_exported():
 
 
 def test_version_and_strings():
-    assert kda.abi_version() == 5
+    assert kda.abi_version() == 6
     for st in (OK, E_NULL, E_SHAPE, E_DTYPE, E_CHUNK, E_GMIN, E_WS, E_HIP, E_ALIGN, E_MODE):
         s = kda.status_string(st)
         assert s and s != "unknown status"
@@ -73,6 +73,7 @@ def _fwd(**kw):
     (dict(B=0), E_SHAPE), (dict(H=0), E_SHAPE), (dict(T=-64), E_SHAPE), (dict(T=100), E_SHAPE),
     (dict(dk=96), E_SHAPE), (dict(dv=256), E_SHAPE), (dict(H=70000), E_SHAPE), (dict(B=70000, T=64), E_SHAPE),
     (dict(g_min=0.0), E_GMIN), (dict(g_min=1.0), E_GMIN), (dict(g_min=-6.0), E_GMIN),
+    (dict(g_min=-5.001), E_GMIN), (dict(g_min=-5.6), E_GMIN),
     (dict(g_min=float("nan")), E_GMIN), (dict(g_min=float("-inf")), E_GMIN),
     (dict(ws=None), E_WS), (dict(wsb=1000), E_WS),
     (dict(q=FAKE + 8), E_ALIGN), (dict(out=FAKE + 4), E_ALIGN), (dict(beta=FAKE + 1), E_ALIGN),
@@ -211,3 +212,21 @@ def test_bwd_validation(kw, want):
                                  a["dk"], a["dv"], a["io"], a["mode"], a["s0"], a["dout"], a["dF"], a["dq"], a["dk_"],
                                  a["dv_"], a["da"], a["dbeta"], a["dS0"], a["ws"], a["wsb"], None)
     assert st == want
+
+
+def test_lowest_g_min_is_the_pages_constant(golden_dir):
+    # the header's most negative accepted g_min is the constant the pages fix (below it the
+    # shrunk row operands of a 16-token tile reach the subnormal range), and the ABI accepts it
+    import json
+    import re
+    hdr = open(os.path.join(os.path.dirname(golden_dir), "..", "include", "kda.h")).read()
+    lowest = float(re.search(r"#define KDA_G_MIN_LOWEST \((-?[0-9.]+)f\)", hdr).group(1))
+    pages = json.load(open(os.path.join(golden_dir, "pages_constants.json")))
+    assert lowest == pages["g_min"] == -5.0
+    span = 15 * abs(lowest)
+    assert span == pages["max_diagonal_exponent"]
+    assert span + 12 < pages["ln_bf16_max"] and -span - 12 > pages["ln_bf16_min_normal"]
+    # accepted: validation gets past g_min and stops at the (too small) workspace, before any launch
+    assert _fwd(g_min=lowest, wsb=1000) == E_WS
+    assert _fwd(g_min=lowest - 0.001, wsb=1000) == E_GMIN
+

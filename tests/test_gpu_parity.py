@@ -249,6 +249,24 @@ def test_power_of_two_scaling_of_v_is_exact(io, chunk):
         assert torch.equal(f2, fs * 2.0 ** e), e
 
 
+@pytest.mark.parametrize("io,chunk", [("bf16", 64), ("bf16", 16), ("fp32", 64)])
+def test_every_gate_saturated_at_the_bound(io, chunk):
+    # a = +12 everywhere: every g sits at g_min = -5, the most negative value accepted, so the
+    # diagonal sub-tiles' key factors reach e^75 and their row factors e^-75 -- the extreme
+    # the bound allows, checked element by element against the oracle
+    w = KI.Workload("sat", 1, 3, 4 * 64, 128, 128, chunk, io, 1.0, False, 41)
+    _say("saturated gates", io, chunk)
+    inp = _to_dev(KI.make_inputs(w))
+    inp["a"] = torch.full_like(inp["a"], 12.0)
+    counts = torch.zeros(2, dtype=torch.int64, device="cuda")
+    out, fs = _gpu_run(inp, chunk, counts=counts)
+    torch.cuda.synchronize()
+    assert counts.tolist() == [0, 0]
+    ro, rf = _oracle(KI.to_f64(inp))
+    _tol_check(out.double().cpu().numpy(), ro, io)
+    _tol_check(fs.double().cpu().numpy(), rf, io, "final_state")
+
+
 def test_empty_sequence():
     inp = {n: torch.empty((1, 2, 0, 64) if n != "beta" else (1, 2, 0), dtype=torch.bfloat16, device="cuda")
            for n in ("q", "k", "v", "a", "beta")}
