@@ -121,3 +121,25 @@ def test_bwd_empty_sequence():
     g0 = kda.chunk_bwd(inp["q"], inp["k"], inp["v"], inp["a"], inp["beta"], dout)
     torch.cuda.synchronize()
     assert not torch.any(g0["dinitial_state"])
+
+
+@pytest.mark.parametrize("io", ["bf16", "fp32"])
+def test_bwd_power_of_two_scaling_of_v_is_exact(io):
+    # out is linear in v; with dout fixed (and no final-state term) the gradients of q, k, a and
+    # beta scale with v and those of v and of the initial state do not depend on it.  Every
+    # operand scale inside the backward is a power of two taken from its own block, so scaling v
+    # by 2^e changes no rounding: the first group scales by exactly 2^e, the second is unchanged.
+    w = KI.Workload("bws", 1, 3, 128, 128, 128, 16, io, 2.0, False, 131)
+    _say("backward power-of-two scaling", io)
+    inp = {n: t.cuda() for n, t in KI.make_inputs(w).items()}
+    dout, _ = (t.cuda() for t in KI.make_grads(w))
+    g0 = kda.chunk_bwd(inp["q"], inp["k"], inp["v"], inp["a"], inp["beta"], dout)
+    for e in (-20, 20):
+        x = dict(inp)
+        x["v"] = inp["v"] * 2.0 ** e
+        g1 = kda.chunk_bwd(x["q"], x["k"], x["v"], x["a"], x["beta"], dout)
+        torch.cuda.synchronize()
+        for key in ("dq", "dk", "da", "dbeta"):
+            assert torch.equal(g1[key], g0[key] * 2.0 ** e), (key, e)
+        for key in ("dv", "dinitial_state"):
+            assert torch.equal(g1[key], g0[key]), (key, e)
