@@ -112,6 +112,29 @@ def test_runs_of_empty_documents_and_one_covering_document():
         assert torch.equal(fs[i], S0[i])
 
 
+def test_thousands_of_short_documents():
+    """2,600 documents of 0 to 40 tokens (about one in ten empty): the plan kernel's scans run
+    over three 1024-document tiles and the chunk table holds thousands of short chunks; every
+    output and every document's final state against the oracle."""
+    rng = np.random.default_rng(74)
+    lengths = [int(x) if rng.random() > 0.1 else 0 for x in rng.integers(1, 41, size=2600)]
+    w, inp, cu = _packed_case(lengths, "bf16", 74, dk=64, dv=64, chunk=16, H=3)
+    N = len(lengths)
+    S0 = _states(N, w, 74)
+    _say("documents", N, "tokens", w.T)
+    out, fs = kda.chunk_fwd_varlen(inp["q"], inp["k"], inp["v"], inp["a"], inp["beta"],
+                                   torch.from_numpy(cu).cuda(), chunk=16, return_final_state=True, initial_state=S0)
+    torch.cuda.synchronize()
+    i64 = _f64(inp)
+    ro, rf = native.recurrent_varlen(i64["q"], i64["k"], i64["v"], i64["a"], i64["beta"], cu,
+                                     S0=S0.double().cpu().numpy())
+    _tol_check(out.double().cpu().numpy(), ro, "bf16")
+    _tol_check(fs.double().cpu().numpy(), rf, "bf16", "final_state")
+    for i in range(N):
+        if lengths[i] == 0:  # an empty document keeps its initial state exactly
+            assert torch.equal(fs[i], S0[i])
+
+
 def test_in_place_states():
     """initial_state and final_state may be one array (each document's state is read before it is
     written)."""
