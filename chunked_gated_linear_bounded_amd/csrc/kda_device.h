@@ -198,17 +198,24 @@ __device__ __forceinline__ float dpp_row_shr(float x) {
     static_assert(N >= 1 && N <= 15, "row shift");
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x110 + N, 0xF, 0xF, false));
 }
-// Maximum over the 64 lanes of a wave, returned to every lane (wave-uniform).
+// x combined with the DPP-moved copy of itself; lanes whose rows ROWMASK leaves out keep x.
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ float dpp_max_with(float x) {
+    const int xi = __builtin_bit_cast(int, x);
+    return fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(xi, xi, CTRL, ROWMASK, 0xF, false)));
+}
+// Maximum over the 64 lanes of a wave, returned to every lane (wave-uniform): four steps inside
+// each 16-lane row, then the gfx9 row broadcasts carry row 0 into row 1 and row 2 into row 3
+// (lane 15, resp. 47) and row 1 into rows 2 and 3 (lane 31), so lane 63 holds the maximum; one
+// readlane instead of four.
 __device__ __forceinline__ float wave_max(float x) {
-    x = fmaxf(x, dpp_mov<0xB1>(x));   // quad_perm [1,0,3,2]
-    x = fmaxf(x, dpp_mov<0x4E>(x));   // quad_perm [2,3,0,1]
-    x = fmaxf(x, dpp_mov<0x141>(x));  // row_half_mirror
-    x = fmaxf(x, dpp_mov<0x140>(x));  // row_mirror: every lane has its row's max
-    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 0));
-    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 16));
-    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 32));
-    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 48));
-    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+    x = dpp_max_with<0xB1, 0xF>(x);   // quad_perm [1,0,3,2]
+    x = dpp_max_with<0x4E, 0xF>(x);   // quad_perm [2,3,0,1]
+    x = dpp_max_with<0x141, 0xF>(x);  // row_half_mirror
+    x = dpp_max_with<0x140, 0xF>(x);  // row_mirror: every lane has its row's max
+    x = dpp_max_with<0x142, 0xA>(x);  // row_bcast:15 into rows 1 and 3
+    x = dpp_max_with<0x143, 0xC>(x);  // row_bcast:31 into rows 2 and 3
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
 }
 // Power-of-two exponent s that maps magnitudes <= m into [2^13, 2^14) at the
 // top: x * 2^s is exact and stays below the fp16 maximum (65504).
