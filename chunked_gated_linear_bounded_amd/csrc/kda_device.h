@@ -221,6 +221,12 @@ __device__ __forceinline__ float wave_max(float x) {
 // top: x * 2^s is exact and stays below the fp16 maximum (65504).
 __device__ __forceinline__ int pow2_scale(float m) { return 14 - __builtin_amdgcn_frexp_expf(m); }
 
+// Whether the wave-wide maximum of x (x >= 0, not NaN) lies in [lo, hi): no lane at or above hi,
+// some lane at or above lo.  Two compares and two lane masks; no data crosses lanes.
+__device__ __forceinline__ bool wave_max_in(float x, float lo, float hi) {
+    return __builtin_amdgcn_ballot_w64(x >= hi) == 0 && __builtin_amdgcn_ballot_w64(x >= lo) != 0;
+}
+
 // Store / load this lane's 4 values of a fragment-ordered 16x16 tile.
 template <typename T>
 __device__ __forceinline__ void st_tile(T *tile, int lane, f32x4 x) {

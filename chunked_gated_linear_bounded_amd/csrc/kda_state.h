@@ -396,14 +396,16 @@ __global__ __launch_bounds__(192, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                 for (int mt = 0; mt < NDK; ++mt)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(S[mt][i]));
-                m = wave_max(m);
-                if (m > 0.f && __builtin_isfinite(m) && (m >= 32768.f || m < 2048.f)) {
-                    const int d = pow2_scale(m);
+                if (!wave_max_in(m, 2048.f, 32768.f)) {  // the wave-wide maximum only when it is needed
+                    m = wave_max(m);
+                    if (m > 0.f && __builtin_isfinite(m) && (m >= 32768.f || m < 2048.f)) {
+                        const int d = pow2_scale(m);
 #pragma unroll
-                    for (int mt = 0; mt < NDK; ++mt)
+                        for (int mt = 0; mt < NDK; ++mt)
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) S[mt][i] = ldexp2(S[mt][i], d);
-                    sS += d;
+                            for (int i = 0; i < 4; ++i) S[mt][i] = ldexp2(S[mt][i], d);
+                        sS += d;
+                    }
                 }
             }
             if constexpr (VL) {
