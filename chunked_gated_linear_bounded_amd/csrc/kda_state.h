@@ -23,12 +23,13 @@
 //
 // Work-group = 3 waves on three SIMDs: wave 0 carries the state (W S^T, U,
 // K^^T U, S^T); wave 2 forms the output from the fp16 state operand wave 0
-// hands over through LDS (written over W^T of the previous chunk's buffer, so
-// the hand-over costs no extra LDS); wave 1 streams chunk records into a ring
-// of LDS buffers with direct global->LDS loads (every load of a record in
-// flight at once, no staging registers), two chunks ahead.  Two barriers per
-// chunk: the first after the output wave has taken the state operand (the
-// loader only then refills that buffer), the second when the chunk is done.
+// hands over through LDS (written over W^T in the chunk's own buffer once wave 0
+// has read W^T, so the hand-over costs no extra LDS); wave 1 streams chunk
+// records into a ring of LDS buffers with direct global->LDS loads (every load
+// of a record in flight at once, no staging registers), two chunks ahead.  Two
+// barriers per chunk: the first once the state operand is in LDS (the loader
+// then refills the buffer of the chunk before), the second when the chunk is
+// done.
 // Work-group ids are mapped so that all slices of a head land on one XCD and
 // share its L2.  The slices of a head read each record in the same order at
 // nearly the same time, so one of them takes the HBM miss and the others hit
@@ -223,12 +224,13 @@ __global__ __launch_bounds__(192, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 #pragma unroll
     for (int mt = 0; mt < (VL ? NDK : 1); ++mt) Si[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // Hand-over of the state operand to the output wave.  With two or more buffers, the state
-    // wave stores chunk n's operand (and its exponent) at the end of chunk n - 1, over W^T in
-    // that chunk's buffer, which only the loader reuses, after the output wave has read the
-    // operand (the first barrier of chunk n).  With one buffer it is stored at the start of
-    // chunk n, over W^T of chunk n once that has been read into registers.
-    constexpr bool EARLY = NBUF >= 2;
+    // Hand-over of the state operand to the output wave: at the start of chunk n the state wave
+    // converts S to the fp16 operand once (its own W S^T uses it too) and stores it, with its
+    // exponent, over W^T in chunk n's buffer once W^T has been read into registers (LDS
+    // accesses of one wave stay in order).  The output wave reads it after the first barrier;
+    // the loader refills that buffer only after the chunk's last barrier.  Storing it at the end
+    // of chunk n - 1 instead puts the stores in front of that chunk's last barrier and converts
+    // S twice.
     auto hand_over = [&](int buf, const FH (&sh)[NKB], int e) {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
@@ -244,12 +246,7 @@ __global__ __launch_bounds__(192, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             sh[kb] = FH::make(x);
         }
     };
-    if (EARLY && wave == 0 && NC > 0) {  // chunk 0's state operand
-        FH sh0[NKB];
-        state_operand(sh0);
-        hand_over(NBUF - 1, sh0, sS);
-    }
-    barrier_lds();  // chunk 0 has landed; the first state operand is in place
+    barrier_lds();  // chunk 0 has landed
 
     for (int n = 0; n < NC; ++n) {
         unsigned char *cur = smem + (n % NBUF) * BUF;
@@ -263,12 +260,11 @@ __global__ __launch_bounds__(192, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         const int *bSS = reinterpret_cast<const int *>(cur + L.region1 + L.ssc);
         constexpr int PE = 2 * TE;  // elements per stored tile pair
 
-        const int hb_buf = EARLY ? (n + NBUF - 1) % NBUF : 0;  // where chunk n's state operand is
-        const OH *shx = reinterpret_cast<const OH *>(smem + hb_buf * BUF + L.wt);
-        const int *shs = reinterpret_cast<const int *>(smem + hb_buf * BUF + L.scl) + 3;
+        const OH *shx = reinterpret_cast<const OH *>(cur + L.wt);  // chunk n's state operand
+        const int *shs = reinterpret_cast<const int *>(cur + L.scl) + 3;
 
-        // ---- W^T into the state wave's registers; the output wave takes the state operand
-        FH wt[NKB][NT], So[NKB];
+        // ---- W^T into the state wave's registers, then the state operand over it
+        FH wt[NKB][NT], So[NKB], Sh[NKB];
         f32x4 ut[NT];
         int eW = 0, eK = 0, eU = 0, sSo = 0;
         if (wave == 0) {
@@ -281,18 +277,10 @@ __global__ __launch_bounds__(192, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             eW = bScl[0];
             eK = bScl[2];
             eU = bSS[0];
-            if constexpr (!EARLY) {  // W^T's bytes are only read by this wave, in order before these stores
-                FH sh[NKB];
-                state_operand(sh);
-                hand_over(0, sh, sS);
-            }
+            state_operand(Sh);
+            hand_over(n % NBUF, Sh, sS);
         }
-        if (EARLY && wave == 2) {
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) So[kb] = FH::load_pair(shx + kb * 512, lane);
-            sSo = *shs;
-        }
-        barrier_lds();  // the output wave has the state operand (or, with one buffer, it is in LDS)
+        barrier_lds();  // the state operand is in LDS
 
         if (wave == 1) {
             // ---- loader: the record two chunks ahead
@@ -336,8 +324,6 @@ __global__ __launch_bounds__(192, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                     *reinterpret_cast<f32x4 *>(sp + 16 * mt) = x;
                 }
             }
-            FH Sh[NKB];
-            state_operand(Sh);
             f32x4 P[NT];
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt) P[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -427,19 +413,12 @@ __global__ __launch_bounds__(192, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                     }
                 }
             }
-            if constexpr (EARLY) {  // the next chunk's state operand, over this chunk's (consumed) W^T
-                FH sh[NKB];
-                state_operand(sh);
-                hand_over(n % NBUF, sh, sS);
-            }
         } else {
             // ---- output wave: O^T = Oi^T + (S^T)^T Qbar^T with the state the chunk started from
             const int4 e_cur = VL ? uniform(*reinterpret_cast<const int4 *>(cur + Cfg::ENT)) : make_int4(0, 0, 0, 0);
-            if constexpr (!EARLY) {
 #pragma unroll
-                for (int kb = 0; kb < NKB; ++kb) So[kb] = FH::load_pair(shx + kb * 512, lane);
-                sSo = *shs;
-            }
+            for (int kb = 0; kb < NKB; ++kb) So[kb] = FH::load_pair(shx + kb * 512, lane);
+            sSo = *shs;
             FH qb[NKB][NT];
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)
