@@ -199,23 +199,28 @@ __device__ __forceinline__ float dpp_row_shr(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x110 + N, 0xF, 0xF, false));
 }
 // x combined with the DPP-moved copy of itself; lanes whose rows ROWMASK leaves out keep x.
+// Unsigned max on the bit patterns: for non-negative floats that are not NaN it orders exactly as
+// the float max and needs no NaN quieting.  Lanes the row mask leaves out see 0, the identity of
+// the unsigned max, so the move folds into one v_max_u32_dpp.
 template <int CTRL, int ROWMASK>
-__device__ __forceinline__ float dpp_max_with(float x) {
-    const int xi = __builtin_bit_cast(int, x);
-    return fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(xi, xi, CTRL, ROWMASK, 0xF, false)));
+__device__ __forceinline__ unsigned dpp_max_with(unsigned x) {
+    const unsigned y = (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROWMASK, 0xF, false);
+    return x > y ? x : y;
 }
-// Maximum over the 64 lanes of a wave, returned to every lane (wave-uniform): four steps inside
-// each 16-lane row, then the gfx9 row broadcasts carry row 0 into row 1 and row 2 into row 3
-// (lane 15, resp. 47) and row 1 into rows 2 and 3 (lane 31), so lane 63 holds the maximum; one
-// readlane instead of four.
-__device__ __forceinline__ float wave_max(float x) {
+// Maximum over the 64 lanes of a wave of x >= 0 (not NaN; +inf allowed), returned to every lane
+// (wave-uniform): four steps inside each 16-lane row, then the gfx9 row broadcasts carry row 0
+// into row 1 and row 2 into row 3 (lane 15, resp. 47) and row 1 into rows 2 and 3 (lane 31), so
+// lane 63 holds the maximum; one readlane instead of four.  Every caller passes a maximum of
+// magnitudes taken with fmaxf, which never returns NaN unless all its inputs are NaN.
+__device__ __forceinline__ float wave_max(float xf) {
+    unsigned x = __builtin_bit_cast(unsigned, xf);
     x = dpp_max_with<0xB1, 0xF>(x);   // quad_perm [1,0,3,2]
     x = dpp_max_with<0x4E, 0xF>(x);   // quad_perm [2,3,0,1]
     x = dpp_max_with<0x141, 0xF>(x);  // row_half_mirror
     x = dpp_max_with<0x140, 0xF>(x);  // row_mirror: every lane has its row's max
     x = dpp_max_with<0x142, 0xA>(x);  // row_bcast:15 into rows 1 and 3
     x = dpp_max_with<0x143, 0xC>(x);  // row_bcast:31 into rows 2 and 3
-    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane((int)x, 63));
 }
 // Power-of-two exponent s that maps magnitudes <= m into [2^13, 2^14) at the
 // top: x * 2^s is exact and stays below the fp16 maximum (65504).
