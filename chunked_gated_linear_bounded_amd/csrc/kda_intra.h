@@ -682,7 +682,10 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
         sScr[8 + wave] = wmax;
     }
     // dv slices (one wave each): U~ and Oi^T = U~^T M^T, scaled per slice to fp16 range
-    for (int vt = wave; vt < NDV; vt += 4) {
+#pragma unroll
+    for (int vi = 0; vi < (NDV + 3) / 4; ++vi) {  // unrolled: the slices' chains interleave
+        const int vt = wave + 4 * vi;
+        if (vt >= NDV) continue;
         unsigned char *sl = rec + L.region1 + vt * L.slice;
         OH *wU = reinterpret_cast<OH *>(sl + L.ut);
         OH *wO = reinterpret_cast<OH *>(sl + L.oit);
