@@ -224,6 +224,7 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: branches on it stay scalar
+    __builtin_assume(wave >= 0 && wave < 4);                    // 256 threads
     const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const size_t head = (size_t)b * H + h;
     size_t tok0, recno;
@@ -484,6 +485,7 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     }
     {
         constexpr int LPR = DK / 4, RPP = 256 / LPR;
+#pragma unroll
         for (int r0 = 0; r0 < C; r0 += RPP) {
             const int s = r0 + tid / LPR, c = (tid % LPR) * 4;
             if (s < C) {
@@ -503,7 +505,10 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
         constexpr int RB = DV * Cfg::ES, NPR = (RB + 255) / 256;
         const unsigned char *vg = reinterpret_cast<const unsigned char *>(v + tok0 * DV);
         lds_u8 *sVb = lds_base(smem) + C * PA * 4;  // sV, LDS-typed
-        for (int x = wave; x < C * NPR; x += 4) {
+#pragma unroll
+        for (int xi = 0; xi < (C * NPR + 3) / 4; ++xi) {
+            const int x = wave + 4 * xi;
+            if (x >= C * NPR) continue;
             const int r = x / NPR, part = x % NPR, off = part * 256 + lane * 4;
             // rows past a short chunk's tokens repeat its last row (finite; beta = 0 there)
             const int rs = (!VL || r < nrow) ? r : nrow - 1;
