@@ -127,6 +127,7 @@ __global__ __launch_bounds__(320) void kda_bwd_dstate_kernel(
 
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    __builtin_assume(wave >= 0 && wave < 5);  // 320 threads: the range readfirstlane hides
     const int bh = blockIdx.x / NS, slice = blockIdx.x % NS, j0 = 16 * slice;
     const int NC = T / 16;
     const unsigned char *rec0 = ws + (size_t)bh * NC * L.stride;
@@ -270,6 +271,7 @@ __global__ __launch_bounds__(512, 1) void kda_bwd_chunk_kernel(
 
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    __builtin_assume(wave >= 0 && wave < 8);  // 512 threads: the range readfirstlane hides
     const int n = blockIdx.x, bh = blockIdx.y, NC = T / C;
     const size_t t0 = (size_t)bh * T + (size_t)n * C;  // first token row of the chunk
     const float *Sg = states + ((size_t)bh * NC + n) * DV * DK;

@@ -77,6 +77,7 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(
     constexpr int NB = DV / RB;    // row blocks per head
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    __builtin_assume(wave >= 0 && wave < 4);  // 256 threads: the range readfirstlane hides
     const size_t head = blockIdx.x / NB;
     const int c0 = 4 * (lane % LPR);                               // this lane's 4 key channels
     const int rw = (blockIdx.x % NB) * RB + RPW * wave + lane / LPR;  // its row in access 0
