@@ -249,6 +249,27 @@ def test_power_of_two_scaling_of_v_is_exact(io, chunk):
         assert torch.equal(f2, fs * 2.0 ** e), e
 
 
+def test_value_scale_jumping_between_chunks():
+    # v's magnitude jumps by up to 2^8 from one chunk to the next, so the state's largest
+    # magnitude leaves the window its scale is kept in, upwards and downwards, many times: the
+    # state stage then forms the wave-wide maximum and rescales, where at other chunks it only
+    # checks the window with lane masks.  Chunk by chunk against the oracle, each chunk held to
+    # the bound relative to its own RMS.
+    w = KI.Workload("jump", 1, 3, 64 * 12, 128, 128, 64, "bf16", 1.0, False, 913)
+    _say("value scale jumping between chunks")
+    inp = _to_dev(KI.make_inputs(w))
+    e = torch.tensor([0, 8, -8, 4, -4, 8, 8, -8, -8, 0, 6, -6], dtype=torch.float32, device="cuda")
+    scale = torch.exp2(e).repeat_interleave(64)  # per token; powers of two are exact in bf16
+    inp["v"] = (inp["v"].float() * scale[None, None, :, None]).to(inp["v"].dtype)
+    out, fs = _gpu_run(inp, 64)
+    torch.cuda.synchronize()
+    ro, rf = _oracle(KI.to_f64(inp))
+    got = out.double().cpu().numpy()
+    for n in range(12):
+        _tol_check(got[:, :, 64 * n:64 * n + 64], ro[:, :, 64 * n:64 * n + 64], "bf16", "chunk %d" % n)
+    _tol_check(fs.double().cpu().numpy(), rf, "bf16", "final_state")
+
+
 @pytest.mark.parametrize("io,chunk", [("bf16", 64), ("bf16", 16), ("fp32", 64)])
 def test_every_gate_saturated_at_the_bound(io, chunk):
     # a = +12 everywhere: every g sits at g_min = -5, the most negative value accepted, so the
