@@ -338,8 +338,9 @@ def backward_bench(args):
 
 
 def cpu_baseline(inputs, w, seconds):
-    """The float64 oracle on whole heads of the same workload until `seconds`
-    have passed; returns whole-job tokens/s extrapolated from the sampled heads."""
+    """The float64 oracle on whole heads of the same workload, all host threads, until `seconds`
+    have passed: whole-job tokens/s extrapolated from the sampled heads.  Beside it, the same
+    oracle on one thread over the first 16,384 tokens of head (0, 0)."""
     import kda_inputs as KI
     from oracle import native
     done, t_used = 0, 0.0
@@ -354,9 +355,59 @@ def cpu_baseline(inputs, w, seconds):
             break
     per_head = t_used / done
     job_time = per_head * len(heads)
-    return {"value": w.B * w.T / job_time, "unit": "tokens/s", "cores": native.threads(), "kind": "oracle",
-            "sample": "%d of %d heads (%d tokens each), float64 token recurrence, %.1f s; "
-                      "whole job extrapolated per head" % (done, len(heads), w.T, t_used)}
+    threads = native.threads()
+    t1n = min(w.T, 16384)
+    hs = KI.head_slice(inputs, 0, 0, t1n)
+    old = native.set_threads(1)
+    try:
+        t0 = time.perf_counter()
+        native.recurrent(hs["q"], hs["k"], hs["v"], hs["a"], hs["beta"], w.g_min)
+        one = time.perf_counter() - t0
+    finally:
+        native.set_threads(old)
+    return {"value": w.B * w.T / job_time, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "%d of %d heads (%d tokens each), float64 token recurrence, %.1f s on %d threads; "
+                      "whole job extrapolated per head" % (done, len(heads), w.T, t_used, threads),
+            "cpu_model": native.cpu_model(),
+            "one_core": {"value": t1n / one / (w.B * w.H), "unit": "tokens/s",
+                         "sample": "%d tokens of one head on 1 thread, %.2f s; whole job extrapolated" % (t1n, one),
+                         "token_heads_per_s": t1n / one}}
+
+
+def ablation_bench(args):
+    """The 1m workload (B=1, H=8, T=1,048,576, d=128, bf16) with the bounded gate and with the
+    unbounded log-sigmoid gate it replaces, one forward each: the device counters of non-finite
+    Gamma-scaled bf16 key operands of the diagonal 16-token tiles and of non-finite outputs."""
+    import torch
+    import chunked_gated_linear_bounded_amd as kda
+    import kda_inputs as KI
+    w = KI.BY_NAME["1m"]
+    dev = torch.device("cuda:0")
+    print("bench: generating %s inputs" % w.name, file=sys.stderr, flush=True)
+    inp = KI.make_inputs(w, device=dev)
+    out = torch.empty((w.B, w.H, w.T, w.dv), dtype=w.torch_dtype, device=dev)
+    ws = torch.empty(kda.workspace_bytes(w.B, w.H, w.T, w.dk, w.dv, w.chunk, w.torch_dtype), dtype=torch.uint8,
+                     device=dev)
+    res = {}
+    for gate in ("bounded", "logsigmoid"):
+        cnt = torch.zeros(2, dtype=torch.int64, device=dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        stream = torch.cuda.current_stream(dev)
+        e0.record(stream)
+        kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["a"], inp["beta"], w.g_min, w.chunk, out=out, workspace=ws,
+                      stream=stream, gate=gate, counts=cnt)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        c = cnt.tolist()
+        res[gate] = {"nonfinite_operands": c[0], "nonfinite_outputs": c[1], "ms": e0.elapsed_time(e1)}
+    th = w.B * w.H * w.T
+    print(json.dumps({
+        "metric": "bf16 overflow count, bounded vs unbounded gate (1m workload)", "unit": "count",
+        "dtype": w.io, "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "dk": w.dk, "dv": w.dv, "chunk": w.chunk,
+                   "a": "0.9 N(0,1) + 0.1 (+-12)"},
+        "operands_checked": th * w.dk, "outputs": th * w.dv, "bounded": res["bounded"],
+        "logsigmoid": res["logsigmoid"]}), flush=True)
 
 
 def main():
@@ -380,6 +431,9 @@ def main():
                     help="instead of reading a, form the gate pre-activation from a rank-R factor (64k workload)")
     ap.add_argument("--backward", action="store_true",
                     help="instead of the forward, time the backward pass (kda_chunk_bwd) on the 64k workload")
+    ap.add_argument("--ablation", action="store_true",
+                    help="instead of timing, count non-finite operands and outputs of the 1m workload with the "
+                         "bounded and the unbounded gate")
     args = ap.parse_args()
     if args.decode_batch > 0:
         decode_bench(args)
@@ -392,6 +446,9 @@ def main():
         return
     if args.backward:
         backward_bench(args)
+        return
+    if args.ablation:
+        ablation_bench(args)
         return
     if args.traffic_from:
         if args.copy_calibration <= 0:
@@ -456,7 +513,8 @@ def main():
     flops = flops_per_token_head(w.dk, w.dv, w.chunk) * th
     peak = PEAK_BF16_FLOPS if w.io == "bf16" else PEAK_FP32_FLOPS
     tokens_per_s = w.B * w.T / (ms_step * 1e-3)
-    rec_bytes = ws.numel()  # every record written once by the intra stage, read once by the state stage
+    alg_bytes = path_bytes_per_token_head(w.dk, w.dv, es) * th  # each input read once, out written once
+    rec_bytes = ws.numel()  # every record written once by the chunk stage, read once by the state stage
     in_bytes = th * ((3 * w.dk + w.dv) * es + es)
     out_bytes = th * w.dv * es
     kern = {
@@ -464,8 +522,13 @@ def main():
         "kda_state_kernel": {"ms": state_ms, "bytes": rec_bytes + out_bytes},
     }
     dom = max(kern, key=lambda k: kern[k]["ms"])
-    ach = kern[dom]["bytes"] / (kern[dom]["ms"] * 1e-3)
+    # the roofline of the dominant kernel on the path's algorithmic bytes (inputs read once, out
+    # written once): what the whole path has to move, over the time this one kernel takes
+    ach = alg_bytes / (kern[dom]["ms"] * 1e-3)
     traffic = _traffic(dom, w.name)
+    step_traffic = [_traffic(k, w.name) for k in kern]
+    step_traffic = None if None in step_traffic else sum(step_traffic)
+    t_floor = max(flops / peak, alg_bytes / PEAK_HBM)
     res = {
         "metric": METRIC,
         "value": tokens_per_s,
@@ -483,14 +546,18 @@ def main():
                    "io": w.io, "g_min": w.g_min},
         "mfma_peak_frac": flops / (ms_step * 1e-3) / peak,
         "path": {"tflops_algorithmic": flops / (ms_step * 1e-3) / 1e12,
-                 "gbps_algorithmic": path_bytes_per_token_head(w.dk, w.dv, es) * th / (ms_step * 1e-3) / 1e9,
-                 "hbm_peak_frac": path_bytes_per_token_head(w.dk, w.dv, es) * th / (ms_step * 1e-3) / PEAK_HBM,
+                 "gbps_algorithmic": alg_bytes / (ms_step * 1e-3) / 1e9,
+                 "hbm_peak_frac": alg_bytes / (ms_step * 1e-3) / PEAK_HBM,
+                 "attainable_frac": t_floor / (ms_step * 1e-3),
                  "flop_per_token_head": flops_per_token_head(w.dk, w.dv, w.chunk),
-                 "bytes_per_token_head": path_bytes_per_token_head(w.dk, w.dv, es)},
+                 "bytes_per_token_head": path_bytes_per_token_head(w.dk, w.dv, es),
+                 "traffic_counters": step_traffic,
+                 "traffic_over_algorithmic": None if step_traffic is None else step_traffic / alg_bytes},
         "kernels_ms": {k: v["ms"] for k, v in kern.items()},
+        "kernels_design_bytes": {k: v["bytes"] for k, v in kern.items()},
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": ach / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
-                     "frac": ach / PEAK_HBM,
-                     "traffic": traffic},
+                     "frac": ach / PEAK_HBM, "algorithmic_bytes": alg_bytes, "traffic": traffic,
+                     "traffic_over_algorithmic": None if traffic is None else traffic / alg_bytes},
     }
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle", file=sys.stderr, flush=True)

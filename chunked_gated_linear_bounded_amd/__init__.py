@@ -101,6 +101,17 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _empty(shape, dtype, device, stream):
+    """A new tensor for the library to write on `stream` (None: the current stream).  The caching
+    allocator ties a block to the stream it was allocated on and hands it out again, once freed,
+    only to work on that stream; allocating on the launch stream keeps a block that the caller
+    drops before the kernels finish (the workspace, always) from going to other work meanwhile."""
+    if stream is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    with torch.cuda.stream(stream):
+        return torch.empty(shape, dtype=dtype, device=device)
+
+
 def _check(t, name, dtype=None, device=None):
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a torch.Tensor" % name)
@@ -119,7 +130,7 @@ def gate_cumsum(a, g_min=-5.0, chunk=64, gate="bounded", out=None, stream=None):
     _check(a, "a")
     B, H, T, dk = a.shape
     if out is None:
-        out = torch.empty((B, H, T, dk), dtype=torch.float32, device=a.device)
+        out = _empty((B, H, T, dk), torch.float32, a.device, stream)
     _check(out, "out", torch.float32, a.device)
     st = lib().kda_gate_cumsum(_ptr(a), float(g_min), int(chunk), B, H, T, dk, _DTYPES[a.dtype],
                                GATE_MODES[gate], _ptr(out), _stream(stream))
@@ -148,15 +159,15 @@ def chunk_fwd(q, k, v, a, beta, g_min=-5.0, chunk=64, out=None, final_state=None
     if k.shape != q.shape or a.shape != q.shape or v.shape != (B, H, T, dv) or beta.shape != (B, H, T):
         raise ValueError("shape mismatch")
     if out is None:
-        out = torch.empty((B, H, T, dv), dtype=dtype, device=dev)
+        out = _empty((B, H, T, dv), dtype, dev, stream)
     _check(out, "out", dtype, dev)
     if final_state is None and return_final_state:
-        final_state = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+        final_state = _empty((B, H, dv, dk), torch.float32, dev, stream)
     if final_state is not None:
         _check(final_state, "final_state", torch.float32, dev)
     need = workspace_bytes(B, H, T, dk, dv, chunk, dtype)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        workspace = _empty(max(need, 1), torch.uint8, dev, stream)
     _check(workspace, "workspace", torch.uint8, dev)
     if counts is not None:
         _check(counts, "counts", torch.int64, dev)
@@ -231,10 +242,10 @@ def chunk_fwd_lowrank(q, k, v, h, z, A_log, beta, g_min=-5.0, chunk=64, out=None
             z.shape != (H, dk, R) or A_log.shape != (H, dk):
         raise ValueError("shape mismatch")
     if out is None:
-        out = torch.empty((B, H, T, dv), dtype=dtype, device=dev)
+        out = _empty((B, H, T, dv), dtype, dev, stream)
     _check(out, "out", dtype, dev)
     if final_state is None and return_final_state:
-        final_state = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+        final_state = _empty((B, H, dv, dk), torch.float32, dev, stream)
     for t, n in ((final_state, "final_state"), (initial_state, "initial_state")):
         if t is not None:
             _check(t, n, torch.float32, dev)
@@ -242,7 +253,7 @@ def chunk_fwd_lowrank(q, k, v, h, z, A_log, beta, g_min=-5.0, chunk=64, out=None
                 raise ValueError("%s must be [B,H,dv,dk]" % n)
     need = workspace_bytes(B, H, T, dk, dv, chunk, dtype)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        workspace = _empty(max(need, 1), torch.uint8, dev, stream)
     _check(workspace, "workspace", torch.uint8, dev)
     if counts is not None:
         _check(counts, "counts", torch.int64, dev)
@@ -283,10 +294,10 @@ def chunk_fwd_varlen(q, k, v, a, beta, cu_seqlens, g_min=-5.0, chunk=64, out=Non
         raise ValueError("shape mismatch")
     N = cu_seqlens.numel() - 1
     if out is None:
-        out = torch.empty((H, T, dv), dtype=dtype, device=dev)
+        out = _empty((H, T, dv), dtype, dev, stream)
     _check(out, "out", dtype, dev)
     if final_state is None and return_final_state:
-        final_state = torch.empty((N, H, dv, dk), dtype=torch.float32, device=dev)
+        final_state = _empty((N, H, dv, dk), torch.float32, dev, stream)
     for t, n in ((final_state, "final_state"), (initial_state, "initial_state")):
         if t is not None:
             _check(t, n, torch.float32, dev)
@@ -294,7 +305,7 @@ def chunk_fwd_varlen(q, k, v, a, beta, cu_seqlens, g_min=-5.0, chunk=64, out=Non
                 raise ValueError("%s must be [N,H,dv,dk]" % n)
     need = varlen_workspace_bytes(N, H, T, dk, dv, chunk, dtype)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        workspace = _empty(max(need, 1), torch.uint8, dev, stream)
     _check(workspace, "workspace", torch.uint8, dev)
     if counts is not None:
         _check(counts, "counts", torch.int64, dev)
@@ -336,14 +347,14 @@ def chunk_bwd(q, k, v, a, beta, dout, g_min=-5.0, initial_state=None, dfinal_sta
             _check(t, n, torch.float32, dev)
             if tuple(t.shape) != (B, H, dv, dk):
                 raise ValueError("%s must be [B,H,dv,dk]" % n)
-    f32 = dict(dtype=torch.float32, device=dev)
-    g = {"dq": torch.empty((B, H, T, dk), **f32), "dk": torch.empty((B, H, T, dk), **f32),
-         "dv": torch.empty((B, H, T, dv), **f32), "da": torch.empty((B, H, T, dk), **f32),
-         "dbeta": torch.empty((B, H, T), **f32),
-         "dinitial_state": torch.empty((B, H, dv, dk), **f32) if want_dinitial else None}
+    def f32(*shape):
+        return _empty(shape, torch.float32, dev, stream)
+
+    g = {"dq": f32(B, H, T, dk), "dk": f32(B, H, T, dk), "dv": f32(B, H, T, dv), "da": f32(B, H, T, dk),
+         "dbeta": f32(B, H, T), "dinitial_state": f32(B, H, dv, dk) if want_dinitial else None}
     need = bwd_workspace_bytes(B, H, T, dk, dv, dtype)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        workspace = _empty(max(need, 1), torch.uint8, dev, stream)
     _check(workspace, "workspace", torch.uint8, dev)
     st = lib().kda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(beta), float(g_min), B, H, T, dk, dv,
                              _DTYPES[dtype], GATE_MODES[gate], _ptr(initial_state), _ptr(dout), _ptr(dfinal_state),
@@ -394,7 +405,7 @@ def decode_step(q, k, v, a, beta, state, g_min=-5.0, gate="bounded", out=None, s
             tuple(state.shape) != (B, H, dv, dk):
         raise ValueError("shape mismatch")
     if out is None:
-        out = torch.empty((B, H, dv), dtype=dtype, device=dev)
+        out = _empty((B, H, dv), dtype, dev, stream)
     _check(out, "out", dtype, dev)
     st = lib().kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(beta), float(g_min), B, H, dk, dv,
                                _DTYPES[dtype], GATE_MODES[gate], _ptr(state), _ptr(out), _stream(stream))

@@ -23,9 +23,11 @@
 // Precision: the Gamma-scaled operands of the diagonal sub-tiles of M and A
 // (factors up to e^75, outside the fp16 range) enter their products as bf16
 // hi + lo pairs (three MFMAs per K-block); M, W and U~ enter M W and M U~ as
-// fp16 (|M| <= 1); T diag(beta), K e^G and V are bf16 operands; W, Qbar, K^,
-// U~ and Oi are stored as fp16, each block scaled by a power of two from its
-// largest magnitude (the sequential stage undoes the scale on its fp32 results).
+// fp16; T diag(beta), K e^G and V are bf16 operands; W, Qbar, K^, U~ and Oi are
+// stored as fp16.  Every fp16 operand and stored block is scaled by a power of
+// two from its block's largest magnitude, and the scale is undone exactly on the
+// fp32 results (here, or in the sequential stage for the stored blocks), so no
+// fp16 value depends on the magnitudes of q, k or v.
 //
 // UT solve: each 16x16 diagonal block of T from the finite product series of
 // its strictly lower triangular A block (one wave per block), then the
@@ -420,6 +422,7 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
             }
         }
     }
+    float mmax = 0.f;  // largest |M| of row tile I
     if (I < NT) {
         // element (row r = 16I + 4g + i, col s = 16J + l16): M keeps s <= r, A keeps s < r (times beta_r)
 #pragma unroll
@@ -429,9 +432,11 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
                 const int rr = 4 * g + i;
                 if (I == J && l16 > rr) accMs[J][i] = 0.f;
                 accAs[J][i] = (I > J || l16 < rr) ? accAs[J][i] * sB[16 * I + rr] : 0.f;
+                if (J <= I) mmax = fmaxf(mmax, fabsf(accMs[J][i]));
             }
         }
     }
+    mmax = wave_max(mmax);
 
     // K^ tiles (st, ct) wait in registers for the chunk's scale; gamma goes to the workspace.
     constexpr int MAXKH = (NT * NDK + 3) / 4;
@@ -452,7 +457,10 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
         }
     }
     khmax = wave_max(khmax);
-    if (lane == 0) sScr[wave] = khmax;
+    if (lane == 0) {
+        sScr[wave] = khmax;
+        sScr[12 + wave] = mmax;
+    }
     if (tid < DK) wGam[tid] = ex2(sG[(C - 1) * PG + tid]);
     __syncthreads();  // raw k and the shared key operands are no longer read
 
@@ -580,13 +588,15 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
         }
         barrier_lds();
     }
-    // A is dead: M takes its place
+    // A is dead: M takes its place, scaled by 2^sM (the fp16 operand of M W and M U~, whatever the
+    // magnitudes of q and k)
+    const int sM_ = F32 ? 0 : pow2_scale(fmaxf(fmaxf(sScr[12], sScr[13]), fmaxf(sScr[14], sScr[15])));
     if (I < NT) {
 #pragma unroll
         for (int J = 0; J < NT; ++J) {
             if (J > I) continue;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sA[(16 * I + 4 * g + i) * PA + 16 * J + l16] = accMs[J][i];
+            for (int i = 0; i < 4; ++i) sA[(16 * I + 4 * g + i) * PA + 16 * J + l16] = ldexp2(accMs[J][i], sM_);
         }
     }
     wait_vmcnt<0>();  // V has landed in LDS
@@ -595,11 +605,10 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 
     // ------------------------------------------------ phase 3
     // Fragments indexed by (row tile rt, token K-block kb): lane l holds row r = 16 rt + l16,
-    // slots = columns 32 kb + kslot.  tf: T diag(beta); mf: M.  The products with M (M W and
+    // slots = columns 32 kb + kslot.  tf: T diag(beta); mf: M 2^sM.  The products with M (M W and
     // M U~) take fp16 operands, so one fp16 MFMA (11 significand bits) replaces the two or three
-    // bf16 hi + lo products: |M| <= 1 (unit q, k and factors e^{G_r - G_s} <= 1) and W is far
-    // inside the fp16 range (unit keys); U~ follows the scale of v, so it enters scaled by the
-    // power of two of its block's maximum.
+    // bf16 hi + lo products; M, W and U~ each enter scaled by the power of two of their block's
+    // maximum, so their fp16 range holds whatever the magnitudes of q, k and v.
     // Only the causal K-blocks kb <= rt / 2 are used.  T and M are stored for blocks on and
     // below the diagonal only; the one block above the diagonal that such a K-block spans
     // (column tile 2 kb + 1 = rt + 1) is zero and is never read.
@@ -644,6 +653,7 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
             kf[kb] = F::make(x);
         }
         f32x4 wrow[NT];  // W tiles (st, ct): rows s, cols dk
+        float wtile = 0.f;  // largest |W| of this dk tile
 #pragma unroll
         for (int rt = 0; rt < NT; ++rt) {
             f32x4 accT = {0.f, 0.f, 0.f, 0.f}, accW = {0.f, 0.f, 0.f, 0.f};
@@ -654,20 +664,24 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
             }
             wtr[ci][rt] = accT;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) wmax = fmaxf(wmax, fabsf(accT[i]));
+            for (int i = 0; i < 4; ++i) wtile = fmaxf(wtile, fabsf(accT[i]));
             wrow[rt] = accW;
         }
-        FM wa[NTKB];  // W as the A operand of W^T (m = dk, k = token)
+        wmax = fmaxf(wmax, wtile);
+        // W 2^sWa as the A operand of W^T (m = dk, k = token); M W comes out scaled by 2^(sWa + sM)
+        const int sWa = F32 ? 0 : pow2_scale(wave_max(wtile));
+        FM wa[NTKB];
 #pragma unroll
         for (int kb = 0; kb < NTKB; ++kb) {
             float x[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int t = 2 * kb + j / 4;
-                x[j] = (t < NT) ? wrow[t < NT ? t : 0][j % 4] : 0.f;
+                x[j] = (t < NT) ? ldexp2(wrow[t < NT ? t : 0][j % 4], sWa) : 0.f;
             }
             wa[kb] = FM::make(x);
         }
+        const int unMW = -(sWa + sM_);
 #pragma unroll
         for (int rt = 0; rt < NT; ++rt) {
             f32x4 mw = {0.f, 0.f, 0.f, 0.f};
@@ -675,7 +689,7 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
             for (int kb = 0; kb <= rt / 2; ++kb) mw = mma(wa[kb], mf[rt][kb], mw);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                qtr[ci][rt][i] -= mw[i];
+                qtr[ci][rt][i] -= ldexp2(mw[i], unMW);
                 qbmax = fmaxf(qbmax, fabsf(qtr[ci][rt][i]));
             }
         }
@@ -731,7 +745,7 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
             }
             ua[kb] = FM::make(x);
         }
-        f32x4 orow[NT];  // Oi 2^sU
+        f32x4 orow[NT];  // Oi 2^(sU + sM)
         float om = 0.f;
 #pragma unroll
         for (int rt = 0; rt < NT; ++rt) {
@@ -742,7 +756,7 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 #pragma unroll
             for (int i = 0; i < 4; ++i) om = fmaxf(om, fabsf(acc[i]));
         }
-        const int sO_ = F32 ? 0 : pow2_scale(wave_max(om));  // Oi is stored scaled by 2^(sU + sO)
+        const int sO_ = F32 ? 0 : pow2_scale(wave_max(om));  // Oi is stored scaled by 2^(sU + sM + sO)
 #pragma unroll
         for (int rt = 0; rt < NT; ++rt) {
             f32x4 u, o;
@@ -756,7 +770,7 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
         }
         if (lane == 0) {
             wS[0] = sU_;
-            wS[1] = sU_ + sO_;
+            wS[1] = sU_ + sM_ + sO_;
             wS[2] = 0;
             wS[3] = 0;
         }

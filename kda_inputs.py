@@ -210,10 +210,10 @@ def make_grads(w: Workload, device="cpu"):
     return dout, dfin
 
 
-def head_slice(inputs, b, h, t_end=None):
-    """float64 NumPy copies of one (b, h) head's inputs (first t_end tokens), with
-    leading singleton B and H axes, for the oracle."""
-    sl = slice(None, t_end)
+def head_slice(inputs, b, h, t_end=None, t_start=None):
+    """float64 NumPy copies of one (b, h) head's inputs (tokens t_start .. t_end - 1, default
+    all), with leading singleton B and H axes, for the oracle."""
+    sl = slice(t_start, t_end)
     res = {}
     for n in ("q", "k", "v", "a"):
         res[n] = inputs[n][b:b + 1, h:h + 1, sl].detach().to("cpu", torch.float64).numpy()

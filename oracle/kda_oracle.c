@@ -62,6 +62,17 @@ int kda_oracle_threads(void)
 #endif
 }
 
+/* Threads of the calls that follow (n >= 1; for timing the oracle on one core).  Returns the
+ * previous count. */
+int kda_oracle_set_threads(int n)
+{
+    const int old = kda_oracle_threads();
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#endif
+    return old;
+}
+
 /* Returns 0 on success, -1 on bad arguments, -2 on allocation failure. */
 int kda_oracle_recurrent(const double *q, const double *k, const double *v,
                          const double *a, const double *beta,

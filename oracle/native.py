@@ -45,6 +45,8 @@ def _load():
             ctypes.c_double, ctypes.c_int, ctypes.c_int, dp, dp, dp]
         lib.kda_oracle_recurrent.restype = ctypes.c_int
         lib.kda_oracle_threads.restype = ctypes.c_int
+        lib.kda_oracle_set_threads.argtypes = [ctypes.c_int]
+        lib.kda_oracle_set_threads.restype = ctypes.c_int
         lib.kda_oracle_backward.argtypes = [dp, dp, dp, dp, dp] + [ctypes.c_long] * 5 + [
             ctypes.c_double, ctypes.c_int, dp, dp, dp, dp, dp, dp, dp, dp, dp]
         lib.kda_oracle_backward.restype = ctypes.c_int
@@ -55,6 +57,23 @@ def _load():
 def threads() -> int:
     """OpenMP threads the oracle uses."""
     return int(_load().kda_oracle_threads())
+
+
+def set_threads(n: int) -> int:
+    """Threads of the calls that follow; returns the previous count."""
+    return int(_load().kda_oracle_set_threads(int(n)))
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (Linux), for reporting the oracle's timings."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def _f64(x):

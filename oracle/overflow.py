@@ -36,6 +36,9 @@ FP32_OVERFLOW_LOG2 = 128.0 + math.log2(1.0 - 2.0 ** -25)
 def _chunk_cumsum(g, chunk):
     """Inclusive cumulative sum of g along time, restarted every `chunk` tokens."""
     T = g.shape[-2]
+    if T % chunk == 0:  # every chunk at once (the same sequential sums as one chunk at a time)
+        s = g.shape
+        return np.cumsum(g.reshape(s[:-2] + (T // chunk, chunk, s[-1])), axis=-2).reshape(s)
     G = np.empty_like(g)
     for n0 in range(0, T, chunk):
         G[..., n0:n0 + chunk, :] = np.cumsum(g[..., n0:n0 + chunk, :], axis=-2)
@@ -66,6 +69,14 @@ def subtile_operand_overflow(a, k, g_min=-5.0, chunk=64, gate_mode="bounded",
     border = 0
     with np.errstate(divide="ignore"):
         lk = np.log2(np.abs(k))
+    if T % SUBTILE == 0:  # every sub-tile at once, the same element-wise arithmetic as the loop below
+        shp = G.shape[:-2] + (T // SUBTILE, SUBTILE, G.shape[-1])
+        G4 = G.reshape(shp)
+        x = G4[..., 0:1, :] - G4
+        y = x + lk.reshape(shp)
+        bad = (x >= 128.0) | (y >= thr)
+        near = (np.abs(x - 128.0) < band) | (np.abs(y - thr) < band)
+        return int(np.count_nonzero(bad)), int(np.count_nonzero(near))
     for s0 in range(0, T, SUBTILE):
         x = G[..., s0:s0 + 1, :] - G[..., s0:s0 + SUBTILE, :]      # log2 of the factor
         y = x + lk[..., s0:s0 + SUBTILE, :]                         # log2 |operand|

@@ -55,3 +55,47 @@ def _grad_check(got, ref, io, what):
     bad = d > allow
     assert not np.any(bad), "%s: %d elements over the bound, worst excess %.4e" % (
         what, int(bad.sum()), float((d - allow).max()))
+
+
+class StreamCheck:
+    """_tol_check over an output compared block by block (a long head whose oracle runs in pieces,
+    each continued from the previous piece's final state).  The element-wise rule
+    |d| <= 2e-2 RMS(ref) + u |ref| (bf16) is max(|d| - u |ref|) <= 2e-2 RMS(ref), so the largest
+    excess, the sums for the RMS values and the largest |d| and |ref| are all it needs to keep."""
+
+    def __init__(self, io, what):
+        self.io, self.what = io, what
+        self.n = 0
+        self.ss_ref = self.ss_d = 0.0
+        self.max_d = self.max_ref = self.max_excess = 0.0
+
+    def add(self, got, ref):
+        got = np.asarray(got, dtype=np.float64)
+        ref = np.asarray(ref, dtype=np.float64)
+        assert got.shape == ref.shape
+        assert np.all(np.isfinite(got)), "non-finite %s" % self.what
+        if ref.size == 0:
+            return
+        d = np.abs(got - ref)
+        self.n += d.size
+        self.ss_ref += float(np.sum(ref ** 2))
+        self.ss_d += float(np.sum(d ** 2))
+        self.max_d = max(self.max_d, float(d.max()))
+        self.max_ref = max(self.max_ref, float(np.abs(ref).max()))
+        if self.io == "bf16":
+            self.max_excess = max(self.max_excess, float((d - BF16_U * np.abs(ref)).max()))
+
+    def finish(self):
+        """Asserts the bar; returns the figures printed (literal max|d|/RMS, excess/RMS, RMS(d)/RMS)."""
+        rms = math.sqrt(self.ss_ref / max(self.n, 1))
+        r = max(rms, 1e-30)
+        stats = {"literal": self.max_d / r, "excess": (self.max_excess if self.io == "bf16" else self.max_d) / r,
+                 "rel_rms": math.sqrt(self.ss_d / max(self.n, 1)) / r, "rms": rms, "max_ref_over_rms": self.max_ref / r}
+        _say("  %s: max|d|/rms=%.3e (literal) max(|d|-u|ref|)/rms=%.3e rel_rms=%.3e rms=%.3e max|ref|/rms=%.1f" % (
+            self.what, stats["literal"], stats["excess"], stats["rel_rms"], rms, stats["max_ref_over_rms"]))
+        if self.io == "bf16":
+            assert self.max_excess <= 2e-2 * rms, "%s: excess over the rounding allowance %.4e > 2e-2 RMS = %.4e" % (
+                self.what, self.max_excess, 2e-2 * rms)
+        else:
+            assert self.max_d <= 1e-4, "%s: max|d| %.4e > 1e-4" % (self.what, self.max_d)
+        return stats

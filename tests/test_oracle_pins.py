@@ -244,6 +244,20 @@ def test_overflow_predictor_exact_counts():
     assert overflow.subtile_operand_overflow(a, k, -6.0, 64, "bounded") == (T // 16, 0)
 
 
+def test_overflow_predictor_counts_per_head_and_ragged_tail():
+    # the same closed form with a different constant gate per (b, h) slab, so the counts add up
+    # over the batch and head axes: |g| = 30, 20, 10 per step overflow from offset 3, 5, 9 on
+    # (13, 11, 7 of 16 per tile); the bounded gate never.  T = 264 ends in a partial tile of 8
+    # tokens (and a partial chunk), where offsets 5..7 of the |g| = 20 slab overflow.
+    k = np.ones((2, 3, 256, 1))
+    a = np.empty_like(k)
+    for (b, h), x in zip(np.ndindex(2, 3), (-30.0, -20.0, -10.0, -20.0, -30.0, -10.0)):
+        a[b, h] = x
+    assert overflow.subtile_operand_overflow(a, k, -5.0, 64, "logsigmoid") == (16 * 2 * (13 + 11 + 7), 0)
+    a = np.full((1, 1, 264, 1), -20.0)
+    assert overflow.subtile_operand_overflow(a, np.ones_like(a), -5.0, 64, "logsigmoid") == (16 * 11 + 3, 0)
+
+
 # ---------------------------------------------------------------- the initial state
 @pytest.mark.parametrize("gate", ["bounded", "logsigmoid"])
 def test_beta_zero_state_only_decays(gate):
