@@ -74,6 +74,8 @@ def lib():
         L.kda_chunk_bwd.restype = i
         L.kda_decode_step.argtypes = [vp] * 5 + [f] + [i] * 6 + [vp, vp, vp]
         L.kda_decode_step.restype = i
+        L.kda_chunk_fwd_noalloc.argtypes = [vp] * 5 + [f] + [i] * 7 + [vp, vp, vp, i, vp, vp]
+        L.kda_chunk_fwd_noalloc.restype = i
         _lib = L
     return _lib
 
@@ -188,6 +190,40 @@ def chunk_fwd(q, k, v, a, beta, g_min=-5.0, chunk=64, out=None, final_state=None
         raise KdaError(fn, st)
     if return_final_state:
         return out, final_state
+    return out
+
+
+def chunk_fwd_noalloc(q, k, v, a, beta, out, g_min=-5.0, chunk=64, final_state=None, stream=None,
+                      gate="bounded", counts=None, initial_state=None):
+    """chunk_fwd through kda_chunk_fwd_noalloc, which allocates no device memory (its chunk records
+    live in a static device array of the library): for callers that cannot allocate, such as code
+    under graph capture.  out [B,H,T,dv] (and final_state [B,H,dv,dk] float32, if wanted) must be
+    given; nothing is allocated here either.  Calls on one GPU share that array, so they must not
+    overlap in time."""
+    dtype = q.dtype
+    if dtype not in _DTYPES:
+        raise ValueError("unsupported dtype %s" % dtype)
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (a, "a"), (beta, "beta")):
+        _check(t, n, dtype, dev)
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or a.shape != q.shape or v.shape != (B, H, T, dv) or beta.shape != (B, H, T) or \
+            tuple(out.shape) != (B, H, T, dv):
+        raise ValueError("shape mismatch")
+    _check(out, "out", dtype, dev)
+    for t, n in ((final_state, "final_state"), (initial_state, "initial_state")):
+        if t is not None:
+            _check(t, n, torch.float32, dev)
+            if tuple(t.shape) != (B, H, dv, dk):
+                raise ValueError("%s must be [B,H,dv,dk]" % n)
+    if counts is not None:
+        _check(counts, "counts", torch.int64, dev)
+    st = lib().kda_chunk_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(beta), float(g_min), int(chunk), B, H,
+                                     T, dk, dv, _DTYPES[dtype], _ptr(out), _ptr(final_state), _stream(stream),
+                                     GATE_MODES[gate], _ptr(counts), _ptr(initial_state))
+    if st != KDA_OK:
+        raise KdaError("kda_chunk_fwd_noalloc", st)
     return out
 
 

@@ -135,6 +135,55 @@ int fwd_impl(const void *q, const void *k, const void *v, const void *a, const v
                       counts, init_state, true);
 }
 
+// The allocation-free forward: windows of chunks whose records fit the static scratch, each a
+// chunk stage and a state stage launch; the state goes from window to window through final_state
+// (else the scratch's first bytes).  All checks run before the first HIP call.
+int noalloc_impl(const void *q, const void *k, const void *v, const void *a, const void *beta, float g_min,
+                 int chunk, int B, int H, int T, int dk, int dv, int io, void *out, float *final_state,
+                 hipStream_t stream, int gate_mode, unsigned long long *counts, const float *init_state) {
+    int st = check_shape(B, H, T, dk, dv, chunk, io);
+    if (st != KDA_OK) return st;
+    st = check_gate(g_min, gate_mode);
+    if (st != KDA_OK) return st;
+    if (T > 0 && (!q || !k || !v || !a || !beta || !out)) return KDA_ERR_NULL;  // empty arrays may be NULL
+    const size_t esz = io == KDA_FP32 ? 4 : 2;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(a, 16) || !aligned(beta, esz) ||
+        !aligned(out, 16) || (final_state && !aligned(final_state, 16)) || (init_state && !aligned(init_state, 16)) ||
+        (counts && !aligned(counts, 8)))
+        return KDA_ERR_ALIGN;
+    const KdaLayout L = kda_layout(chunk, dk, dv, (int)esz);
+    const size_t nstate = (size_t)B * H * dv * dk;
+    const size_t state_bytes = final_state ? 0 : (nstate * sizeof(float) + 255) / 256 * 256;
+    const size_t per_chunk = (size_t)B * H * L.stride;  // one chunk of every head
+    if (state_bytes + per_chunk > (size_t)KDA_NOALLOC_SCRATCH_BYTES) return KDA_ERR_SCRATCH;
+    void *scr = nullptr;
+    if (kda::noalloc_scratch(&scr) != hipSuccess) return KDA_ERR_HIP;
+    float *carrier = final_state ? final_state : reinterpret_cast<float *>(scr);
+    if (T == 0)  // the state of an empty sequence is the initial one
+        return kda::launch_state_fill(carrier, init_state, final_state ? nstate : 0, stream) == hipSuccess
+                   ? KDA_OK : KDA_ERR_HIP;
+    const int NC = T / chunk;
+    const size_t fit = ((size_t)KDA_NOALLOC_SCRATCH_BYTES - state_bytes) / per_chunk;
+    const int ncw = fit < (size_t)NC ? (int)fit : NC;
+    kda::LaunchArgs p{};
+    p.q = q; p.k = k; p.v = v; p.a = a; p.beta = beta;
+    p.g_min = g_min;
+    p.logsig = gate_mode == KDA_GATE_LOGSIGMOID;
+    p.chunk = chunk; p.B = B; p.H = H; p.T = T; p.dk = dk; p.dv = dv;
+    p.fp32 = io == KDA_FP32;
+    p.out = out; p.final_state = carrier;
+    p.workspace = static_cast<unsigned char *>(scr) + state_bytes;
+    p.counts = counts; p.stream = stream;
+    for (int c0 = 0; c0 < NC; c0 += ncw) {
+        p.c0 = c0;
+        p.ncw = NC - c0 < ncw ? NC - c0 : ncw;
+        p.init_state = c0 == 0 ? init_state : carrier;
+        if (kda::launch_intra(p) != hipSuccess) return KDA_ERR_HIP;
+        if (kda::launch_state(p) != hipSuccess) return KDA_ERR_HIP;
+    }
+    return KDA_OK;
+}
+
 // Packed documents: chunk records per head (an upper bound on the chunks the documents
 // can need, whatever cu_seqlens holds), and where the plan tables start.
 struct VarlenSizes {
@@ -232,6 +281,7 @@ const char *kda_status_string(int status) {
     case KDA_ERR_HIP: return "a HIP call or kernel launch failed";
     case KDA_ERR_ALIGN: return "a pointer is not aligned as required (16 bytes; beta: element size)";
     case KDA_ERR_MODE: return "unknown gate_mode";
+    case KDA_ERR_SCRATCH: return "problem needs more device scratch than KDA_NOALLOC_SCRATCH_BYTES (kda_chunk_fwd_noalloc)";
     default: return "unknown status";
     }
 }
@@ -296,6 +346,14 @@ int kda_chunk_fwd_lowrank(const void *q, const void *k, const void *v, const voi
     return fwd_impl(q, k, v, nullptr, beta, g_min, chunk, B, H, T, dk, dv, io_dtype, out, final_state, workspace,
                     workspace_bytes_given, stream, gate_mode, nonfinite_counts, initial_state,
                     LowRank{true, h, z, A_log, rank});
+}
+
+int kda_chunk_fwd_noalloc(const void *q, const void *k, const void *v, const void *a, const void *beta,
+                          float g_min, int chunk, int B, int H, int T, int dk, int dv, int io_dtype, void *out,
+                          float *final_state, hipStream_t stream, int gate_mode, unsigned long long *nonfinite_counts,
+                          const float *initial_state) {
+    return noalloc_impl(q, k, v, a, beta, g_min, chunk, B, H, T, dk, dv, io_dtype, out, final_state, stream,
+                        gate_mode, nonfinite_counts, initial_state);
 }
 
 size_t kda_chunk_fwd_varlen_workspace_bytes(int N, int H, int T, int dk, int dv, int chunk, int io_dtype) {

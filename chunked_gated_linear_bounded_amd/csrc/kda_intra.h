@@ -181,6 +181,8 @@ struct LowRankGate {
     }
 };
 
+// Fixed-length batches: work-group (x, h, b) takes chunk c0 + x of head (b, h) and writes its
+// record at (b H + h) NCw + x, so a launch can cover a window of NCw chunks of every head.
 // VL: packed documents (kda_varlen.h).  Work-group x then takes chunk x of the chunk
 // table ctab (records at head * NCmax + x); a chunk with fewer than C rows is padded with
 // zero q, k, beta and a zero gate, and a table entry with no rows ends the work-group.
@@ -194,7 +196,7 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     const typename IntraCfg<C, DK, DV, F32>::E *__restrict__ a,
     const typename IntraCfg<C, DK, DV, F32>::E *__restrict__ beta,
     float gmin2, int logsig, int H, int T, unsigned char *__restrict__ ws,
-    unsigned long long *__restrict__ counts, const int4 *__restrict__ ctab, int NCmax,
+    unsigned long long *__restrict__ counts, const int4 *__restrict__ ctab, int NCmax, int c0, int NCw,
     const typename IntraCfg<C, DK, DV, F32>::E *__restrict__ lrh,
     const typename IntraCfg<C, DK, DV, F32>::E *__restrict__ lrz, const float *__restrict__ lrA)
 {
@@ -237,9 +239,9 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
         nrow = ce.y < C ? ce.y : C;
         tok0 = head * (size_t)T + (size_t)ce.x;
         recno = head * (size_t)NCmax + n;
-    } else {
-        tok0 = head * (size_t)T + (size_t)n * C;
-        recno = head * (size_t)(T / C) + n;
+    } else {  // chunk c0 + n of the sequence; the window's records are [head][NCw]
+        tok0 = head * (size_t)T + (size_t)(c0 + n) * C;
+        recno = head * (size_t)NCw + n;
     }
     unsigned char *rec = ws + recno * L.stride;
     OH *wWT = reinterpret_cast<OH *>(rec + L.wt);
@@ -258,7 +260,7 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
         GateScan<C, DK, E> gate;
         LowRankGate<C, DK, E, LR ? LRK : 16> lrt;  // its loads go first: its MFMAs need nothing else
         if constexpr (LR) {
-            lrt.load(lrh + ((size_t)b * T + (size_t)n * C) * LRK, lrz + (size_t)h * DK * LRK, wave, lane);
+            lrt.load(lrh + ((size_t)b * T + (size_t)(c0 + n) * C) * LRK, lrz + (size_t)h * DK * LRK, wave, lane);
         } else {
             gate.load(a + tok0 * DK, tid, nrow);
         }

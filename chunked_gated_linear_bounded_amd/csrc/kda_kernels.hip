@@ -1,5 +1,8 @@
-// Kernel instantiations and launchers for the C ABI in include/kda.h.
+// Kernel instantiations and launchers for the C ABI in include/kda.h, and the device scratch of
+// the allocation-free forward.
 #include <hip/hip_runtime.h>
+
+#include <mutex>
 
 #include "kda_decode.h"
 #include "kda_device.h"
@@ -7,8 +10,51 @@
 #include "kda_launch.h"
 #include "kda_state.h"
 #include "kda_varlen.h"
+#include "kda.h"
 
 namespace kda {
+
+// Scratch of kda_chunk_fwd_noalloc: the chunk records of one window of the sequence and, when the
+// caller passes no final_state, the state carried from window to window.  Every GPU the library
+// runs on holds its own copy for the life of the process.  Host code never uses the array's name
+// as an address (on the host it stands for no device memory): noalloc_scratch() hands out the
+// device address hipGetSymbolAddress gives for the current device, looked up once per device.
+static __device__ __align__(256) unsigned char scratch[KDA_NOALLOC_SCRATCH_BYTES];
+
+hipError_t noalloc_scratch(void **ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void *dev_ptr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (dev_ptr[dev] == nullptr) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        dev_ptr[dev] = p;
+    }
+    *ptr = dev_ptr[dev];
+    return hipSuccess;
+}
+
+// dst[i] = src[i] (src not NULL) or 0, i < n: the state of an empty sequence, written by a kernel
+// rather than a memset or copy node so that it can sit in a captured graph.
+__global__ __launch_bounds__(256) void kda_state_fill_kernel(float *__restrict__ dst, const float *__restrict__ src,
+                                                            size_t n)
+{
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) dst[i] = src != nullptr ? src[i] : 0.f;
+}
+
+hipError_t launch_state_fill(float *dst, const float *src, size_t n, hipStream_t stream) {
+    if (n == 0 || dst == src) return hipSuccess;
+    hipLaunchKernelGGL(kda_state_fill_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, dst, src, n);
+    return hipGetLastError();
+}
 
 // Standalone gate + per-chunk prefix sum: G_out[t][c] = sum over the chunk of
 // g (natural log units).  One work-group per (chunk, head, batch).
@@ -79,18 +125,19 @@ static hipError_t launch_intra_t(const LaunchArgs &p) {
                            p.stream, reinterpret_cast<const E *>(p.q), reinterpret_cast<const E *>(p.k),
                            reinterpret_cast<const E *>(p.v), reinterpret_cast<const E *>(p.a),
                            reinterpret_cast<const E *>(p.beta), p.g_min * kLog2e, p.logsig, p.H, p.T,
-                           reinterpret_cast<unsigned char *>(p.workspace), p.counts, pl.ctab, p.ncmax, nullptr,
-                           nullptr, nullptr);
+                           reinterpret_cast<unsigned char *>(p.workspace), p.counts, pl.ctab, p.ncmax, 0, 0,
+                           nullptr, nullptr, nullptr);
         return hipGetLastError();
     }
     if (p.lr_h != nullptr) return launch_intra_lowrank(p);
-    dim3 grid(p.T / C, p.H, p.B);
+    const int ncw = p.ncw > 0 ? p.ncw : p.T / C;
+    dim3 grid(ncw, p.H, p.B);
     hipLaunchKernelGGL((kda_intra_kernel<C, DK, DV, F32, false, 0>), grid, dim3(256), 0, p.stream,
                        reinterpret_cast<const E *>(p.q), reinterpret_cast<const E *>(p.k),
                        reinterpret_cast<const E *>(p.v), reinterpret_cast<const E *>(p.a),
                        reinterpret_cast<const E *>(p.beta), p.g_min * kLog2e, p.logsig, p.H, p.T,
-                       reinterpret_cast<unsigned char *>(p.workspace), p.counts, nullptr, 0, nullptr, nullptr,
-                       nullptr);
+                       reinterpret_cast<unsigned char *>(p.workspace), p.counts, nullptr, 0, p.c0, ncw, nullptr,
+                       nullptr, nullptr);
     return hipGetLastError();
 }
 
@@ -106,12 +153,12 @@ static hipError_t launch_state_t(const LaunchArgs &p) {
         hipLaunchKernelGGL((kda_state_kernel<C, DK, DV, F32, true>), grid, dim3(192), 0, p.stream,
                            reinterpret_cast<const unsigned char *>(p.workspace), reinterpret_cast<E *>(p.out),
                            p.final_state, p.init_state, BH, p.T, p.counts, pl.ctab, pl.seg, pl.coff, p.H, p.ncmax,
-                           nullptr);
+                           nullptr, 0, 0);
     else
         hipLaunchKernelGGL((kda_state_kernel<C, DK, DV, F32, false>), grid, dim3(192), 0, p.stream,
                            reinterpret_cast<const unsigned char *>(p.workspace), reinterpret_cast<E *>(p.out),
                            p.final_state, p.init_state, BH, p.T, p.counts, nullptr, nullptr, nullptr, p.H, 0,
-                           p.states);
+                           p.states, p.c0, p.ncw > 0 ? p.ncw : p.T / C);
     return hipGetLastError();
 }
 

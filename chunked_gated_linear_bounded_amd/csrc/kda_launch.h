@@ -18,6 +18,9 @@ struct LaunchArgs {
     float *G_out;
     unsigned long long *counts;
     hipStream_t stream;
+    // a window of the sequence (fixed-length batches): chunks c0 .. c0 + ncw - 1 of every head, whose
+    // records sit in the workspace as [B*H][ncw]; ncw = 0 means the whole sequence (c0 = 0)
+    int c0, ncw;
     // packed documents (NULL cu: fixed-length batch)
     const int *cu;              // device cu_seqlens[nseq + 1]
     int nseq;                   // documents
@@ -42,5 +45,7 @@ hipError_t launch_state(const LaunchArgs &p);  // sequential stage: workspace ->
 hipError_t launch_gate_cumsum(const LaunchArgs &p);
 hipError_t launch_decode(const LaunchArgs &p);  // one token per head, state in place
 hipError_t launch_bwd(const LaunchArgs &p);     // gradients (recompute, reverse state pass, chunk stage)
+hipError_t noalloc_scratch(void **ptr);         // this device's scratch of kda_chunk_fwd_noalloc
+hipError_t launch_state_fill(float *dst, const float *src, size_t n, hipStream_t stream);  // dst = src or 0
 
 }  // namespace kda

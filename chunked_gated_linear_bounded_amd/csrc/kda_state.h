@@ -112,10 +112,12 @@ __global__ __launch_bounds__(192, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     const unsigned char *__restrict__ ws, typename StateCfg<C, DK, DV, F32, VL>::E *__restrict__ out,
     float *final_state, const float *init_state, int BH, int T, unsigned long long *__restrict__ counts,
     const int4 *__restrict__ ctab, const int *__restrict__ seg, const int *__restrict__ coff, int H, int NCmax,
-    float *__restrict__ states)
+    float *__restrict__ states, int c0, int NCw)
 {
     // states (nullable, fixed-length only): the state each chunk starts from, [BH][NC][DV][DK] float32 in
-    // final_state's orientation, for the backward pass; out may then be NULL (no outputs stored)
+    // final_state's orientation, for the backward pass; out may then be NULL (no outputs stored).
+    // Fixed-length batches: the unit walks chunks c0 .. c0 + NCw - 1 (a window of the sequence)
+    // from init_state, whose records the workspace holds as [unit][NCw].
     using Cfg = StateCfg<C, DK, DV, F32, VL>;
     using E = typename Cfg::E;
     using OH = typename std::conditional<F32, float, _Float16>::type;
@@ -149,9 +151,9 @@ __global__ __launch_bounds__(192, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         cbase = c0;
         row0 = (size_t)head * T;
         rec0 = ws + ((size_t)head * NCmax + c0) * L.stride;
-    } else {
-        NC = T / C;
-        row0 = (size_t)hb * T;
+    } else {  // chunks c0 .. c0 + NCw - 1 of the sequence, records [unit][NCw]
+        NC = NCw;
+        row0 = (size_t)hb * T + (size_t)c0 * C;
         rec0 = ws + (size_t)hb * NC * L.stride;
     }
     const int4 *ent0 = VL ? ctab + cbase : nullptr;  // VL: the run's chunk-table entries, in chunk order

@@ -44,7 +44,9 @@
  *    a launch error (hipGetLastError) after enqueueing.
  *  - Outputs are fully overwritten, never accumulated.  out must not alias any
  *    input.  Results are bitwise reproducible run to run (no float atomics).
- *  - No global mutable state: calls from several host threads are safe.
+ *  - No global mutable state: calls from several host threads are safe.  The one
+ *    exception is kda_chunk_fwd_noalloc, whose calls on one GPU share a static
+ *    device array.
  */
 #ifndef KDA_H
 #define KDA_H
@@ -56,7 +58,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 6
+#define KDA_ABI_VERSION 7
 /* The most negative g_min accepted: the constant the method fixes.  Inside a
  * 16-token tile the key operands of the diagonal sub-tile grow by up to
  * e^(15 |g_min|) and the row operands shrink by as much; at g_min = -5 both stay
@@ -77,8 +79,14 @@ typedef enum {
     KDA_ERR_WORKSPACE = -6, /* workspace NULL or smaller than required          */
     KDA_ERR_HIP = -7,       /* a HIP call or kernel launch failed               */
     KDA_ERR_ALIGN = -8,     /* a pointer is not aligned as required             */
-    KDA_ERR_MODE = -9       /* gate_mode unknown                                */
+    KDA_ERR_MODE = -9,      /* gate_mode unknown                                */
+    KDA_ERR_SCRATCH = -10   /* kda_chunk_fwd_noalloc: the problem needs more than
+                               KDA_NOALLOC_SCRATCH_BYTES of device scratch      */
 } kda_status;
+
+/* Bytes of device scratch that kda_chunk_fwd_noalloc works in: a static device array of the
+ * library, one per GPU it runs on, held until the process ends. */
+#define KDA_NOALLOC_SCRATCH_BYTES (128u << 20)
 
 typedef enum { KDA_BF16 = 0, KDA_FP32 = 1 } kda_dtype;
 
@@ -108,12 +116,12 @@ int kda_gate_cumsum(const void *a, float g_min, int chunk, int B, int H, int T, 
                     int io_dtype, int gate_mode, float *G_out, hipStream_t stream);
 
 /* Chunked forward: out[b][h][t] = o_t for every token; if final_state is not
- * NULL it receives S_T.  q and k are expected L2-normalised per token and head
- * (the delta rule's convention, under which I - beta k k^T is a contraction):
- * the fp16 operands formed from them inside the chunk stage (M, W) rely on it.
- * v may have any magnitude in the range of the I/O type: every operand that
- * follows its scale is block-scaled by a power of two, so scaling v by 2^e
- * scales out and the final state by exactly 2^e.  workspace: device buffer of at least
+ * NULL it receives S_T.  q, k and v may have any magnitude in the range of the
+ * I/O type: every 16-bit operand inside the kernels is block-scaled by a power of
+ * two taken from its own block, so scaling v (or q) by 2^e scales out by exactly
+ * 2^e.  The delta rule's usual convention, L2-normalised q and k, is not needed;
+ * the recurrence itself stays bounded only while beta |k|^2 <= 2 (each step
+ * I - beta k k^T is then a contraction).  workspace: device buffer of at least
  * kda_chunk_fwd_workspace_bytes(...) bytes, contents undefined on entry and on
  * return; it must not overlap any other argument. */
 int kda_chunk_fwd(const void *q, const void *k, const void *v, const void *a, const void *beta,
@@ -213,6 +221,24 @@ int kda_chunk_fwd_varlen(const void *q, const void *k, const void *v, const void
                          int dv, int io_dtype, void *out, float *final_state, void *workspace,
                          size_t workspace_bytes, hipStream_t stream, int gate_mode,
                          unsigned long long *nonfinite_counts, const float *initial_state);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): kda_chunk_fwd_ex without a workspace argument.  It
+ * allocates nothing (no hipMalloc, hipFree, memset or copy node): its chunk records go to a
+ * static device array of KDA_NOALLOC_SCRATCH_BYTES, one per GPU, and the sequence is processed
+ * in windows of whole chunks whose records fit there, the state carried from window to window
+ * (in final_state when given, else in the same array).  Results match kda_chunk_fwd_ex within
+ * the parity tolerance (the state is re-scaled at window boundaries, so not bit for bit).
+ * Arguments, layouts, validation and asynchrony as kda_chunk_fwd_ex.  Returns KDA_ERR_SCRATCH,
+ * before anything is launched, when one chunk of every head, plus the state if final_state is
+ * NULL, does not fit: B*H*(record bytes of one chunk) + (final_state ? 0 : B*H*dv*dk*4) >
+ * KDA_NOALLOC_SCRATCH_BYTES (about 1,600 heads at dk = dv = 128, chunk 64, bf16).  Every call on
+ * one GPU uses that GPU's one array: calls that overlap in time on the same GPU (other streams,
+ * other host threads) race and must be ordered by the caller. */
+int kda_chunk_fwd_noalloc(const void *q, const void *k, const void *v, const void *a, const void *beta,
+                          float g_min, int chunk, int B, int H, int T, int dk, int dv, int io_dtype,
+                          void *out, float *final_state, hipStream_t stream, int gate_mode,
+                          unsigned long long *nonfinite_counts, const float *initial_state);
 
 /* Backward pass: the gradients of L = sum_t dout_t . o_t + <dfinal_state, S_T>
  * with respect to q, k, v, a, beta and the initial state, for training (the

@@ -14,6 +14,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kda.h")
 
 OK, E_NULL, E_SHAPE, E_DTYPE, E_CHUNK, E_GMIN, E_WS, E_HIP, E_ALIGN, E_MODE = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
+E_SCRATCH = -10
 
 
 def _declared_functions():
@@ -28,14 +29,15 @@ def test_header_symbols_exported():
     assert {"kda_abi_version", "kda_status_string", "kda_chunk_fwd_workspace_bytes",
             "kda_gate_cumsum", "kda_chunk_fwd", "kda_chunk_fwd_ex", "kda_chunk_intra", "kda_chunk_state",
             "kda_decode_step", "kda_chunk_fwd_varlen", "kda_chunk_fwd_varlen_workspace_bytes",
-            "kda_chunk_fwd_lowrank", "kda_chunk_bwd", "kda_chunk_bwd_workspace_bytes"} <= set(names)
+            "kda_chunk_fwd_lowrank", "kda_chunk_bwd", "kda_chunk_bwd_workspace_bytes",
+            "kda_chunk_fwd_noalloc"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
 
 def test_version_and_strings():
-    assert kda.abi_version() == 6
-    for st in (OK, E_NULL, E_SHAPE, E_DTYPE, E_CHUNK, E_GMIN, E_WS, E_HIP, E_ALIGN, E_MODE):
+    assert kda.abi_version() == 7
+    for st in (OK, E_NULL, E_SHAPE, E_DTYPE, E_CHUNK, E_GMIN, E_WS, E_HIP, E_ALIGN, E_MODE, E_SCRATCH):
         s = kda.status_string(st)
         assert s and s != "unknown status"
     assert kda.status_string(12345) == "unknown status"
@@ -230,3 +232,33 @@ def test_lowest_g_min_is_the_pages_constant(golden_dir):
     assert _fwd(g_min=lowest, wsb=1000) == E_WS
     assert _fwd(g_min=lowest - 0.001, wsb=1000) == E_GMIN
 
+
+
+def _noalloc(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, a=FAKE, beta=FAKE, g_min=-5.0, chunk=64, B=1, H=2, T=256, dk=128, dv=128,
+             io=0, out=FAKE, fs=None, stream=None, mode=0, counts=None, init=None)
+    a.update(kw)
+    return kda.lib().kda_chunk_fwd_noalloc(a["q"], a["k"], a["v"], a["a"], a["beta"], a["g_min"], a["chunk"], a["B"],
+                                           a["H"], a["T"], a["dk"], a["dv"], a["io"], a["out"], a["fs"], a["stream"],
+                                           a["mode"], a["counts"], a["init"])
+
+
+def test_noalloc_validation():
+    # the same checks as kda_chunk_fwd_ex, and the size limit of the static scratch, all before any HIP call
+    assert _noalloc(q=None) == E_NULL
+    assert _noalloc(out=None) == E_NULL
+    assert _noalloc(T=100) == E_SHAPE
+    assert _noalloc(chunk=48) == E_CHUNK
+    assert _noalloc(io=5) == E_DTYPE
+    assert _noalloc(g_min=-6.0) == E_GMIN
+    assert _noalloc(mode=3) == E_MODE
+    assert _noalloc(out=FAKE + 8) == E_ALIGN
+    # one 64-token chunk record of every head must fit in 128 MiB: 1,600 heads do, 1,700 do not;
+    # without a final_state the 64 KiB state of every head has to fit beside them
+    rec = kda.workspace_bytes(1, 1, 64, 128, 128, 64, torch.bfloat16)
+    limit = 128 << 20
+    fits = limit // rec
+    assert _noalloc(H=fits + 1, fs=FAKE) == E_SCRATCH
+    with_state = limit // (rec + 128 * 128 * 4)
+    assert _noalloc(H=with_state + 1) == E_SCRATCH
+    assert with_state < fits
