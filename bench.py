@@ -42,8 +42,53 @@ def path_bytes_per_token_head(dk, dv, es):
 
 # the sources the forward's chunk and state kernels are compiled from (the translation unit and
 # every header it includes): counters taken on other sources are not reported
-FWD_SOURCES = ("kda_kernels.hip", "kda_device.h", "kda_intra.h", "kda_state.h", "kda_layout.h", "kda_launch.h",
-               "kda_varlen.h", "kda_decode.h")
+FWD_SOURCES = ("kda_kernels.hip", "kda_device.h", "kda_intra.h", "kda_state.h", "kda_state_seg.h", "kda_layout.h",
+               "kda_launch.h", "kda_varlen.h", "kda_decode.h")
+
+# the forward's two stages and the kernels each dispatches once per step
+STAGES = {"kda_intra_kernel": ("kda_intra_kernel",),
+          "state_stage": ("kda_seg_state_kernel", "kda_seg_scan_kernel", "kda_state_kernel")}
+
+
+def record_layout(dk, dv, C, es):
+    """Byte sizes of one chunk record (kda_layout.h): region 1 (W^T, Qbar^T, K^, gamma, exponents),
+    one value slice (exponents, U~, Oi^T), and the record stride."""
+    nt, ndk, ndv = C // 16, dk // 16, dv // 16
+    tile = 256 * es
+    wt = ndk * nt * tile
+    kh = 2 * ((nt + 1) // 2) * ndk * tile
+    region1 = 2 * wt + kh + dk * 4 + 16
+    slice_ = 16 + 2 * nt * tile
+    stride = (region1 + ndv * slice_ + 255) // 256 * 256
+    return {"wt": wt, "kh": kh, "region1": region1, "slice": slice_, "ut_part": 16 + nt * tile, "stride": stride}
+
+
+def seg_count(units, nc):
+    """Segments per head of the state stage (kda_seg_count in kda_layout.h): enough (head, segment)
+    work-groups for 256 compute units, at least 8 chunks each, none empty."""
+    if units <= 0 or units >= 256 or nc < 16:
+        return 1
+    s = max(1, min(256 // units, nc // 8))
+    ln = -(-nc // s)
+    return -(-nc // ln)
+
+
+def state_stage_bytes(B, H, T, dk, dv, C, es):
+    """Design bytes of the state stage per step: pass 0 reads W^T, K^, gamma, the exponents and every
+    slice's U~ of the chunks in all segments but the last and writes two float32 maps per segment;
+    the scan reads and writes them; pass 1 reads region 1 and every slice of every chunk and writes
+    out (one segment: pass 1 alone)."""
+    L = record_layout(dk, dv, C, es)
+    units, nc = B * H, T // C
+    nseg = seg_count(units, nc)
+    seglen = -(-nc // nseg) if nc else 0
+    p1 = units * nc * (L["region1"] + (dv // 16) * L["slice"]) + units * T * dv * es
+    if nseg == 1:
+        return p1
+    nc0 = units * min(nc, (nseg - 1) * seglen)
+    p0 = nc0 * (L["wt"] + L["kh"] + dk * 4 + 16 + (dv // 16) * L["ut_part"])
+    maps = units * (nseg - 1) * (dv * dk + dk * dk) * 4
+    return p0 + maps + 3 * units * (nseg - 1) * dv * dk * 4 + p1
 
 
 def _src_sha():
@@ -100,15 +145,20 @@ def record_traffic(fetch_dir, write_dir, workload, copy_bytes):
         if not cal:
             raise SystemExit("no calibration copy dispatch under %s" % d)
         factor = copy_bytes / (sum(cal) / len(cal) * 1024.0)
-        for kern in ("kda_intra_kernel", "kda_state_kernel"):
-            vals = [v for (k, _, v) in rows if kern in k]
-            if not vals:
-                raise SystemExit("no %s dispatches under %s" % (kern, d))
-            rec = out.setdefault(kern + "@" + workload, {"src_sha": _src_sha()})
-            rec[counter.lower() + "_kib_raw"] = sum(vals) / len(vals)
+        for stage, pats in STAGES.items():
+            # per step: the mean over its dispatches of every kernel the stage launches, summed
+            names = sorted({k for (k, _, _) in rows if any(p in k for p in pats)})
+            if not names:
+                raise SystemExit("no %s dispatches under %s" % (stage, d))
+            kib = 0.0
+            for n in names:
+                vals = [v for (k, _, v) in rows if k == n]
+                kib += sum(vals) / len(vals)
+            rec = out.setdefault(stage + "@" + workload, {"src_sha": _src_sha()})
+            rec[counter.lower() + "_kib_raw"] = kib
             rec[counter.lower() + "_factor"] = factor
-            rec[counter.lower() + "_bytes"] = sum(vals) / len(vals) * 1024.0 * factor
-            rec["dispatches"] = len(vals)
+            rec[counter.lower() + "_bytes"] = kib * 1024.0 * factor
+            rec["kernels"] = len(names)
     for rec in out.values():
         rec["bytes_per_launch"] = rec["fetch_size_bytes"] + rec["write_size_bytes"]
     p = os.path.join(ROOT, "profiles", "traffic.json")
@@ -514,12 +564,11 @@ def main():
     peak = PEAK_BF16_FLOPS if w.io == "bf16" else PEAK_FP32_FLOPS
     tokens_per_s = w.B * w.T / (ms_step * 1e-3)
     alg_bytes = path_bytes_per_token_head(w.dk, w.dv, es) * th  # each input read once, out written once
-    rec_bytes = ws.numel()  # every record written once by the chunk stage, read once by the state stage
+    rec_bytes = w.B * w.H * (w.T // w.chunk) * record_layout(w.dk, w.dv, w.chunk, es)["stride"]
     in_bytes = th * ((3 * w.dk + w.dv) * es + es)
-    out_bytes = th * w.dv * es
-    kern = {
+    kern = {  # the chunk stage writes every record once; the state stage's passes read them
         "kda_intra_kernel": {"ms": intra_ms, "bytes": in_bytes + rec_bytes},
-        "kda_state_kernel": {"ms": state_ms, "bytes": rec_bytes + out_bytes},
+        "state_stage": {"ms": state_ms, "bytes": state_stage_bytes(w.B, w.H, w.T, w.dk, w.dv, w.chunk, es)},
     }
     dom = max(kern, key=lambda k: kern[k]["ms"])
     # the roofline of the dominant kernel on the path's algorithmic bytes (inputs read once, out

@@ -32,9 +32,9 @@ int check_gate(float g_min, int gate_mode) {
     return KDA_OK;
 }
 
+// the chunk records and, when the state stage runs in segments, the segments' states and maps
 size_t workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, int io) {
-    const KdaLayout L = kda_layout(chunk, dk, dv, io == KDA_FP32 ? 4 : 2);
-    return (size_t)B * (size_t)H * (size_t)(T / chunk) * L.stride;
+    return kda_fwd_plan(B, H, T, chunk, dk, dv, io == KDA_FP32 ? 4 : 2).total;
 }
 
 int check_ptrs_ws(int B, int H, int T, int dk, int dv, int chunk, int io, const void *workspace,

@@ -9,6 +9,7 @@
 #include "kda_intra.h"
 #include "kda_launch.h"
 #include "kda_state.h"
+#include "kda_state_seg.h"
 #include "kda_varlen.h"
 #include "kda.h"
 
@@ -141,10 +142,45 @@ static hipError_t launch_intra_t(const LaunchArgs &p) {
     return hipGetLastError();
 }
 
+// The segmented state stage (kda_state_seg.h) for a whole fixed-length sequence: pass 0 and the
+// scan when there are several segments, then pass 1.  The workspace is laid out by kda_fwd_plan.
+template <int C, int DK, int DV, bool F32>
+static hipError_t launch_state_seg(const LaunchArgs &p, const KdaFwdPlan &plan) {
+    using E = typename std::conditional<F32, float, __bf16>::type;
+    const int U = p.B * p.H, NC = p.T / C;
+    unsigned char *ws = reinterpret_cast<unsigned char *>(p.workspace);
+    float *segbuf = reinterpret_cast<float *>(ws + plan.seg_off);
+    float *phibuf = reinterpret_cast<float *>(ws + plan.phi_off);
+    if (plan.nseg > 1) {
+        hipLaunchKernelGGL((kda_seg_state_kernel<C, DK, DV, F32, 0>), dim3(U * (plan.nseg - 1)),
+                           dim3(SegCfg<C, DK, DV, F32, 0>::THREADS), 0,
+                           p.stream, ws, nullptr, nullptr, p.init_state, segbuf, phibuf, U, NC, plan.nseg,
+                           plan.seglen, p.T, nullptr);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        if (plan.nseg > 2) {
+            hipLaunchKernelGGL((kda_seg_scan_kernel<DK, DV>), dim3(U * (DV / 16)), dim3(256), 0, p.stream, segbuf,
+                               phibuf, plan.nseg);
+            e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+    }
+    hipLaunchKernelGGL((kda_seg_state_kernel<C, DK, DV, F32, 1>), dim3(U * plan.nseg),
+                       dim3(SegCfg<C, DK, DV, F32, 1>::THREADS), 0, p.stream, ws,
+                       reinterpret_cast<E *>(p.out), p.final_state, p.init_state, segbuf, phibuf, U, NC, plan.nseg,
+                       plan.seglen, p.T, p.counts);
+    return hipGetLastError();
+}
+
 template <int C, int DK, int DV, bool F32>
 static hipError_t launch_state_t(const LaunchArgs &p) {
     using E = typename std::conditional<F32, float, __bf16>::type;
     const bool vl = p.cu != nullptr;
+    if constexpr (kda_seg_supported(kda_layout(C, DK, DV, F32 ? 4 : 2))) {
+        // whole fixed-length sequences with outputs: the segmented stage
+        if (!vl && p.states == nullptr && p.ncw == 0 && p.c0 == 0 && p.out != nullptr)
+            return launch_state_seg<C, DK, DV, F32>(p, kda_fwd_plan(p.B, p.H, p.T, C, DK, DV, F32 ? 4 : 2));
+    }
     const int BH = vl ? p.nrun * p.H : p.B * p.H;  // units: (run of documents, head) or (batch, head)
     const int groups = (BH + 7) / 8;
     dim3 grid(groups * 8 * (DV / 16));

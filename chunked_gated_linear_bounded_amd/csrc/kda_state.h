@@ -341,8 +341,12 @@ __global__ __launch_bounds__(192, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             f32x4 gm[NDK];
 #pragma unroll
             for (int mt = 0; mt < NDK; ++mt) gm[mt] = *reinterpret_cast<const f32x4 *>(bG + 16 * mt + 4 * g);
-            // U = U~ - W S^T (both scalings are exact, the difference rounds once)
-            const float fW = ldexp2(1.f, -(sS + eW)), fU = ldexp2(1.f, -eU);
+            // U = U~ - W S^T (both scalings are exact, the difference rounds once), formed at the
+            // working scale 2^sW: the state's own scale unless U~ is far larger than the state (one
+            // that has decayed to almost nothing), when the state is taken down to U~'s.  Every
+            // factor is then a moderate power of two, whatever the state has decayed by.
+            const int sW = min(sS, eU + 16);
+            const float fW = ldexp2(1.f, sW - sS - eW), fU = ldexp2(1.f, sW - eU);
             f32x4 U[NT];
             float um = 0.f;
 #pragma unroll
@@ -373,7 +377,14 @@ __global__ __launch_bounds__(192, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             for (int kb = 0; kb < NTKB; ++kb)
 #pragma unroll
                 for (int mt = 0; mt < NDK; ++mt) A[mt] = mma(kh[kb][mt], Uh[kb], A[mt]);
-            const float unS = ldexp2(1.f, sS - (sU + eK));
+            if (sW != sS) {  // rare
+#pragma unroll
+                for (int mt = 0; mt < NDK; ++mt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) S[mt][i] = ldexp2(S[mt][i], sW - sS);
+                sS = sW;
+            }
+            const float unS = ldexp2(1.f, -(sU + eK));
 #pragma unroll
             for (int mt = 0; mt < NDK; ++mt)
 #pragma unroll

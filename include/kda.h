@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 7
+#define KDA_ABI_VERSION 8
 /* The most negative g_min accepted: the constant the method fixes.  Inside a
  * 16-token tile the key operands of the diagonal sub-tile grow by up to
  * e^(15 |g_min|) and the row operands shrink by as much; at g_min = -5 both stay
@@ -103,7 +103,11 @@ const char *kda_status_string(int status);
 
 /* Bytes of device workspace kda_chunk_fwd needs for this problem (0 for an
  * invalid problem).  The workspace holds the per-chunk operands the chunk-
- * parallel stage hands to the sequential state stage. */
+ * parallel stage hands to the sequential state stage and, when that stage cuts
+ * each sequence into segments walked side by side (fewer than 256 heads; the
+ * segments' affine state maps composed as in context-parallel prefill, third
+ * page sec. 3), each segment's float32 end state and transition: 2 x 64 KiB
+ * per segment and head at dk = dv = 128. */
 size_t kda_chunk_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, int io_dtype);
 
 /* Gate and per-chunk prefix sum (first page sec. 3.2 / third page sec. 2.1 for

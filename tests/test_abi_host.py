@@ -36,7 +36,7 @@ def test_header_symbols_exported():
 
 
 def test_version_and_strings():
-    assert kda.abi_version() == 7
+    assert kda.abi_version() == 8
     for st in (OK, E_NULL, E_SHAPE, E_DTYPE, E_CHUNK, E_GMIN, E_WS, E_HIP, E_ALIGN, E_MODE, E_SCRATCH):
         s = kda.status_string(st)
         assert s and s != "unknown status"
@@ -49,7 +49,16 @@ def test_workspace_bytes():
     # each of the 8 value slices 4 int exponents and U~, Oi^T as 4 fp16 tiles each
     rec = 3 * 32 * 512 + 128 * 4 + 16 + 8 * (16 + 2 * 4 * 512)
     rec = (rec + 255) // 256 * 256
-    assert kda.workspace_bytes(1, 32, 65536, 128, 128, 64, torch.bfloat16) == 32 * 1024 * rec
+    # the state stage walks each head's 1024 chunks as 8 segments (32 heads x 8 = 256 work-groups):
+    # per head 8 state slots and 7 transition slots, 128 x 128 float32 each
+    seg = 32 * (8 + 7) * 128 * 128 * 4
+    assert kda.workspace_bytes(1, 32, 65536, 128, 128, 64, torch.bfloat16) == 32 * 1024 * rec + seg
+    # 256 or more heads: one segment, the records alone
+    assert kda.workspace_bytes(4, 64, 8192, 128, 128, 64, torch.bfloat16) == 4 * 64 * 128 * rec
+    # fp32 records of 64-token chunks at d = 128 do not fit the segmented stage's ring twice
+    L = 3 * 32 * 1024 + 128 * 4 + 16 + 8 * (16 + 2 * 4 * 1024)
+    L = (L + 255) // 256 * 256
+    assert kda.workspace_bytes(1, 32, 65536, 128, 128, 64, torch.float32) == 32 * 1024 * L
     assert kda.workspace_bytes(1, 2, 256, 64, 64, 16, torch.float32) > 0
     assert kda.workspace_bytes(1, 2, 0, 64, 64, 16, torch.float32) == 0
     assert kda.workspace_bytes(1, 2, 100, 64, 64, 16, torch.float32) == 0   # T % chunk != 0

@@ -64,32 +64,37 @@ def test_record_traffic_calibrates_each_counter_by_the_copy(tmp_path, monkeypatc
     fetch, write = str(tmp_path / "fetch"), str(tmp_path / "write")
     neg = "void at::native::vectorized_elementwise_kernel<4, at::native::neg_kernel_cuda(...)>"
     intra = "void kda::kda_intra_kernel<64, 128, 128, false, false, 0>(...)"
-    state = "void kda::kda_state_kernel<64, 128, 128, false, false>(...)"
-    # the copy's FETCH_SIZE reads half its true bytes (factor 2), its WRITE_SIZE all of them
+    pass0 = "void kda::kda_seg_state_kernel<64, 128, 128, false, 0>(...)"
+    pass1 = "void kda::kda_seg_state_kernel<64, 128, 128, false, 1>(...)"
+    scan = "void kda::kda_seg_scan_kernel<128, 128>(...)"
+    # the copy's FETCH_SIZE reads half its true bytes (factor 2), its WRITE_SIZE all of them; the
+    # state stage is three kernels per step, each averaged over its own dispatches
     _write_counters(fetch, [(neg, "FETCH_SIZE", copy / 2048.0), (intra, "FETCH_SIZE", 1000.0),
-                            (intra, "FETCH_SIZE", 1100.0), (state, "FETCH_SIZE", 500.0)])
+                            (intra, "FETCH_SIZE", 1100.0), (pass0, "FETCH_SIZE", 200.0), (pass0, "FETCH_SIZE", 220.0),
+                            (scan, "FETCH_SIZE", 10.0), (pass1, "FETCH_SIZE", 500.0)])
     _write_counters(write, [(neg, "WRITE_SIZE", copy / 1024.0), (intra, "WRITE_SIZE", 2000.0),
-                            (intra, "WRITE_SIZE", 2000.0), (state, "WRITE_SIZE", 300.0)])
+                            (intra, "WRITE_SIZE", 2000.0), (pass0, "WRITE_SIZE", 5.0), (scan, "WRITE_SIZE", 4.0),
+                            (pass1, "WRITE_SIZE", 300.0)])
     os.makedirs(tmp_path / "profiles")
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     monkeypatch.setattr(bench, "_src_sha", lambda: "feedface")
     bench.record_traffic(fetch, write, "64k", copy)
     rec = json.load(open(tmp_path / "profiles" / "traffic.json"))
-    i, s = rec["kda_intra_kernel@64k"], rec["kda_state_kernel@64k"]
+    i, s = rec["kda_intra_kernel@64k"], rec["state_stage@64k"]
     assert i["fetch_size_factor"] == pytest.approx(2.0) and i["write_size_factor"] == pytest.approx(1.0)
     assert i["bytes_per_launch"] == pytest.approx(1050.0 * 1024 * 2 + 2000.0 * 1024)
-    assert s["bytes_per_launch"] == pytest.approx(500.0 * 1024 * 2 + 300.0 * 1024)
-    assert i["dispatches"] == 2 and i["src_sha"] == "feedface"
+    assert s["bytes_per_launch"] == pytest.approx((210.0 + 10.0 + 500.0) * 1024 * 2 + (5.0 + 4.0 + 300.0) * 1024)
+    assert i["kernels"] == 1 and s["kernels"] == 3 and i["src_sha"] == "feedface"
     # the stored figure is reported only for the sources it was taken on
-    assert bench._traffic("kda_state_kernel", "64k") == pytest.approx(s["bytes_per_launch"])
+    assert bench._traffic("state_stage", "64k") == pytest.approx(s["bytes_per_launch"])
     monkeypatch.setattr(bench, "_src_sha", lambda: "0ddba11")
-    assert bench._traffic("kda_state_kernel", "64k") is None
+    assert bench._traffic("state_stage", "64k") is None
 
 
 def test_record_traffic_needs_the_calibration_copy(tmp_path, monkeypatch):
     fetch, write = str(tmp_path / "fetch"), str(tmp_path / "write")
-    _write_counters(fetch, [("kda_intra_kernel", "FETCH_SIZE", 1.0), ("kda_state_kernel", "FETCH_SIZE", 1.0)])
-    _write_counters(write, [("kda_intra_kernel", "WRITE_SIZE", 1.0), ("kda_state_kernel", "WRITE_SIZE", 1.0)])
+    _write_counters(fetch, [("kda_intra_kernel", "FETCH_SIZE", 1.0), ("kda_seg_state_kernel", "FETCH_SIZE", 1.0)])
+    _write_counters(write, [("kda_intra_kernel", "WRITE_SIZE", 1.0), ("kda_seg_state_kernel", "WRITE_SIZE", 1.0)])
     os.makedirs(tmp_path / "profiles")
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     with pytest.raises(SystemExit):
@@ -101,3 +106,26 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+@pytest.mark.parametrize("B,H,T,d,C,es", [(1, 32, 65536, 128, 64, 2), (1, 8, 1048576, 128, 64, 2),
+                                          (4, 16, 8192, 128, 64, 2), (1, 2, 256, 64, 16, 4),
+                                          (1, 3, 512, 64, 32, 2), (4, 64, 8192, 128, 64, 2)])
+def test_record_layout_and_segments_match_the_library(B, H, T, d, C, es):
+    # the workspace is the records plus, with several segments, two float32 maps per segment and head
+    import torch
+    import chunked_gated_linear_bounded_amd as kda
+    L = bench.record_layout(d, d, C, es)
+    units, nc = B * H, T // C
+    nseg = bench.seg_count(units, nc)
+    extra = 0 if nseg == 1 else units * (nseg + nseg - 1) * d * d * 4
+    want = units * nc * L["stride"] + extra
+    assert kda.workspace_bytes(B, H, T, d, d, C, torch.float32 if es == 4 else torch.bfloat16) == want
+    assert nseg * units <= max(256, units) and (nseg == 1 or -(-nc // nseg) >= 8)
+
+
+def test_segment_counts_of_the_workloads():
+    # 256 (head, segment) work-groups for the large workloads, one segment at 256 heads or more
+    assert [bench.seg_count(u, nc) for (u, nc) in ((32, 1024), (16, 4096), (8, 16384), (64, 128), (256, 128))] == \
+        [8, 16, 32, 4, 1]
+    assert bench.seg_count(2, 16) == 2 and bench.seg_count(2, 15) == 1 and bench.seg_count(3, 100) == 12

@@ -216,6 +216,47 @@ def test_value_scale_jumping_between_chunks():
     _tol_check(fs.double().cpu().numpy(), rf, "bf16", "final_state")
 
 
+@pytest.mark.parametrize("path", ["segmented", "noalloc", "packed"])
+def test_state_that_decays_to_nothing_then_takes_new_values(path):
+    # From a random initial state, eight chunks with v = 0 under saturated gates (g = g_min, a decay
+    # of e^-320 per channel and chunk) take the state far below the float32 range, then ordinary
+    # chunks follow.  The state stage keeps the state as a scaled mantissa and an integer exponent,
+    # so its exponent grows by hundreds; the products of the next chunk must stay finite and exact
+    # (the oracle's state is exactly zero by then in float64 too).  24 chunks: the segmented stage
+    # walks three segments of 8 (the quiet stretch covers a whole segment); the allocation-free and
+    # packed forwards use the per-slice stage.
+    w = KI.Workload("decay", 1, 2, 64 * 24, 128, 128, 64, "bf16", 2.0, False, 515)
+    _say("decayed state then new values", path)
+    inp = _to_dev(KI.make_inputs(w))
+    quiet = slice(64 * 4, 64 * 12)
+    inp["v"][:, :, quiet] = 0
+    inp["a"][:, :, quiet] = 12.0
+    g = torch.Generator(device="cpu").manual_seed(5151)
+    s0 = torch.randn((1, 2, 128, 128), generator=g, dtype=torch.float64).float().cuda()
+    if path == "segmented":
+        out, fs = kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["a"], inp["beta"], chunk=64,
+                                return_final_state=True, initial_state=s0)
+    elif path == "noalloc":
+        out = torch.empty_like(inp["v"])
+        fs = torch.empty_like(s0)
+        kda.chunk_fwd_noalloc(inp["q"], inp["k"], inp["v"], inp["a"], inp["beta"], out, chunk=64, final_state=fs,
+                              initial_state=s0)
+    else:
+        cu = torch.tensor([0, w.T], dtype=torch.int32, device="cuda")
+        o, f = kda.chunk_fwd_varlen(inp["q"][0], inp["k"][0], inp["v"][0], inp["a"][0], inp["beta"][0], cu, chunk=64,
+                                    return_final_state=True, initial_state=s0.reshape(1, 2, 128, 128))
+        out, fs = o[None], f.reshape(1, 2, 128, 128)
+    torch.cuda.synchronize()
+    i64 = KI.to_f64(inp)
+    ro, rf = native.recurrent(i64["q"], i64["k"], i64["v"], i64["a"], i64["beta"], -5.0, S0=s0.double().cpu().numpy())
+    got = out.double().cpu().numpy()
+    assert np.all(np.isfinite(got))
+    _tol_check(got, ro, "bf16", "whole sequence")
+    for n in range(12, 24):  # the chunks after the quiet stretch, each against its own RMS
+        _tol_check(got[:, :, 64 * n:64 * n + 64], ro[:, :, 64 * n:64 * n + 64], "bf16", "chunk %d" % n)
+    _tol_check(fs.double().cpu().numpy(), rf, "bf16", "final_state")
+
+
 @pytest.mark.parametrize("io,chunk", [("bf16", 64), ("bf16", 16), ("fp32", 64)])
 def test_every_gate_saturated_at_the_bound(io, chunk):
     # a = +12 everywhere: every g sits at g_min = -5, the most negative value accepted, so the
