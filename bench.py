@@ -73,6 +73,24 @@ def seg_count(units, nc):
     return -(-nc // ln)
 
 
+def use_segmented(units, dv, dk, C, es):
+    """Whether the state stage runs segmented (kda_use_segmented in kda_layout.h): where the
+    per-slice stage's (head, value slice) work-groups do not fill 256 compute units, or with 256
+    heads or more -- and only where the segmented stage's LDS ring holds two chunks."""
+    L = record_layout(dk, dv, C, es)
+    # the two passes' ring parts: pass 0 W^T, then K^, gamma and the exponents; pass 1 region 1
+    rings = ((L["wt"], L["region1"] - 2 * L["wt"]), (L["region1"], 0))
+    lds = 160 * 1024
+
+    def ok(p1, p2):
+        slot = (p1 + p2 + 15) // 16 * 16
+        depth = 4 if 4 * slot <= lds else 3 if 3 * slot <= lds else 2 if 2 * slot <= lds else 0
+        ndma = -(-p1 // 1024) + -(-p2 // 1024)
+        return depth >= 2 and ((ndma + 3) // 4) * (depth - 2) <= 63
+
+    return all(ok(*r) for r in rings) and (units * (dv // 16) < 256 or units >= 256)
+
+
 def state_stage_bytes(B, H, T, dk, dv, C, es):
     """Design bytes of the state stage per step: pass 0 reads W^T, K^, gamma, the exponents and every
     slice's U~ of the chunks in all segments but the last and writes two float32 maps per segment;
@@ -80,7 +98,7 @@ def state_stage_bytes(B, H, T, dk, dv, C, es):
     out (one segment: pass 1 alone)."""
     L = record_layout(dk, dv, C, es)
     units, nc = B * H, T // C
-    nseg = seg_count(units, nc)
+    nseg = seg_count(units, nc) if use_segmented(units, dv, dk, C, es) else 1
     seglen = -(-nc // nseg) if nc else 0
     p1 = units * nc * (L["region1"] + (dv // 16) * L["slice"]) + units * T * dv * es
     if nseg == 1:

@@ -177,9 +177,11 @@ static hipError_t launch_state_t(const LaunchArgs &p) {
     using E = typename std::conditional<F32, float, __bf16>::type;
     const bool vl = p.cu != nullptr;
     if constexpr (kda_seg_supported(kda_layout(C, DK, DV, F32 ? 4 : 2))) {
-        // whole fixed-length sequences with outputs: the segmented stage
-        if (!vl && p.states == nullptr && p.ncw == 0 && p.c0 == 0 && p.out != nullptr)
-            return launch_state_seg<C, DK, DV, F32>(p, kda_fwd_plan(p.B, p.H, p.T, C, DK, DV, F32 ? 4 : 2));
+        // whole fixed-length sequences with outputs: the segmented stage where kda_fwd_plan picks it
+        if (!vl && p.states == nullptr && p.ncw == 0 && p.c0 == 0 && p.out != nullptr) {
+            const KdaFwdPlan plan = kda_fwd_plan(p.B, p.H, p.T, C, DK, DV, F32 ? 4 : 2);
+            if (plan.segmented) return launch_state_seg<C, DK, DV, F32>(p, plan);
+        }
     }
     const int BH = vl ? p.nrun * p.H : p.B * p.H;  // units: (run of documents, head) or (batch, head)
     const int groups = (BH + 7) / 8;

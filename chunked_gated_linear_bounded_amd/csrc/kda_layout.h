@@ -123,12 +123,24 @@ static inline constexpr int kda_seg_count(long long units, int nc)
     return (int)((nc + len - 1) / len);
 }
 
+// Which state stage a fixed-length forward runs.  The per-slice stage (kda_state.h) gives each
+// (head, 16-wide value slice) one work-group walking the whole sequence: where those work-groups
+// fill the 256 compute units it is the faster of the two (it moves each record once and its chain
+// is short).  Where they do not -- fewer than 256 / (dv / 16) heads -- the segmented stage cuts the
+// sequence so that 256 work-groups run; with 256 heads or more it runs one segment (pass 1 alone,
+// one work-group per head instead of dv / 16 rounds of per-slice work-groups).
+static inline constexpr bool kda_use_segmented(const KdaLayout &L, long long units)
+{
+    return kda_seg_supported(L) && (units * L.NDV < 256 || units >= 256);
+}
+
 // The whole forward workspace: the records [unit][chunk], then (segments > 1) the segment states
 // [unit][nseg][dv][dk] fp32 (slot j < nseg - 1: segment j's end state from pass 0, after the scan
 // segment j + 1's incoming state; slot nseg - 1: a copy of the initial state) and the segment
 // transitions [unit][nseg - 1][dk][dk] fp32 (slot j = Phi of segment j, stored transposed; slot 0
 // unused).
 struct KdaFwdPlan {
+    bool segmented;  // the state stage runs kda_state_seg.h (else the per-slice stage)
     int nseg, seglen;
     size_t rec_bytes, seg_off, phi_off, total;
 };
@@ -140,7 +152,8 @@ static inline constexpr KdaFwdPlan kda_fwd_plan(int B, int H, int T, int C, int 
     const long long units = (long long)B * H;
     const int nc = T / C;
     p.rec_bytes = (size_t)units * (size_t)nc * L.stride;
-    p.nseg = kda_seg_supported(L) ? kda_seg_count(units, nc) : 1;
+    p.segmented = kda_use_segmented(L, units);
+    p.nseg = p.segmented ? kda_seg_count(units, nc) : 1;
     p.seglen = p.nseg > 0 && nc > 0 ? (nc + p.nseg - 1) / p.nseg : nc;
     p.seg_off = p.rec_bytes;
     p.phi_off = p.seg_off;

@@ -128,10 +128,10 @@ __global__ __launch_bounds__((SegCfg<C, DK, DV, F32, PASS>::THREADS), 1) void kd
 
     // chain c of this wave: index gi = wave + NW c; gi < NDV: state slice gi (columns 16 gi of
     // S^T), else (pass 0) Phi slice gi - NDV (columns 16 (gi - NDV) of Phi)
-    auto is_phi = [&](int c) { return wave + NW * c >= NDV; };
+    // (a compile-time property of c when NDV is a multiple of NW).  The first segment's Phi is
+    // not needed; its chains run anyway, so that no product sits behind a branch.
+    auto is_phi = [&](int c) { return NDV % NW == 0 ? NW * c >= NDV : wave + NW * c >= NDV; };
     auto col0 = [&](int c) { return 16 * (is_phi(c) ? wave + NW * c - NDV : wave + NW * c); };
-    // pass 0, first segment: the Phi chains have nothing to do
-    auto idle = [&](int c) { return PASS == 0 && seg == 0 && is_phi(c); };
 
     auto load_slice = [&](SR &r, int c, int m) {
         if (is_phi(c)) return;
@@ -278,8 +278,7 @@ __global__ __launch_bounds__((SegCfg<C, DK, DV, F32, PASS>::THREADS), 1) void kd
             for (int tt = 0; tt < NT; ++tt) {
                 const FH wf = FH::load_pair(bWT + (kb * NT + tt) * PE, lane);
 #pragma unroll
-                for (int c = 0; c < NCH; ++c)
-                    if (!idle(c)) P[c][tt] = mma(wf, Sh[c][kb], P[c][tt]);
+                for (int c = 0; c < NCH; ++c) P[c][tt] = mma(wf, Sh[c][kb], P[c][tt]);
             }
         // U = U~ - W S^T (U~ = 0 for Phi) at the chain's working scale 2^sW, then scaled to fp16 by
         // its wave-wide maximum.  sW is the state's own scale unless U~ is far larger than the state
@@ -327,8 +326,7 @@ __global__ __launch_bounds__((SegCfg<C, DK, DV, F32, PASS>::THREADS), 1) void kd
             for (int mt = 0; mt < NDK; ++mt) {
                 const FH kf = FH::load_pair(bKH + (kb * NDK + mt) * PE, lane);
 #pragma unroll
-                for (int c = 0; c < NCH; ++c)
-                    if (!idle(c)) A[c][mt] = mma(kf, Uh[c][kb], A[c][mt]);
+                for (int c = 0; c < NCH; ++c) A[c][mt] = mma(kf, Uh[c][kb], A[c][mt]);
             }
 #pragma unroll
         for (int c = 0; c < NCH; ++c)
@@ -388,33 +386,40 @@ __global__ __launch_bounds__((SegCfg<C, DK, DV, F32, PASS>::THREADS), 1) void kd
                     for (int c = 0; c < NCH; ++c) O[c][tt] = mma(Sh[c][kb], qf, O[c][tt]);
                 }
             const size_t row0 = (size_t)unit * T + (size_t)(cb + n) * C;
+            // the stores, with (COUNT) or without the non-finite count, so that no branch splits them
+            auto store = [&](auto count) {
 #pragma unroll
-            for (int c = 0; c < NCH; ++c) {
-                const int j0 = col0(c);
-                const float fO = ldexp2(1.f, -(sS0[c] + eQ)), fI = ldexp2(1.f, -cur[c].eo);
+                for (int c = 0; c < NCH; ++c) {
+                    const int j0 = col0(c);
+                    const float fO = ldexp2(1.f, -(sS0[c] + eQ)), fI = ldexp2(1.f, -cur[c].eo);
 #pragma unroll
-                for (int tt = 0; tt < NT; ++tt) {
-                    f32x4 o;
+                    for (int tt = 0; tt < NT; ++tt) {
+                        f32x4 o;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) o[i] = fmaf(O[c][tt][i], fO, (float)cur[c].o[tt][i] * fI);
-                    // lane holds out[token 16 tt + l16][value j0 + 4g + i]
-                    E *op = out + (row0 + 16 * tt + l16) * DV + j0 + 4 * g;
-                    if constexpr (F32) {
-                        *reinterpret_cast<f32x4 *>(op) = o;
-                    } else {
-                        bf16x4 bo;
+                        for (int i = 0; i < 4; ++i) o[i] = fmaf(O[c][tt][i], fO, (float)cur[c].o[tt][i] * fI);
+                        // lane holds out[token 16 tt + l16][value j0 + 4g + i]
+                        E *op = out + (row0 + 16 * tt + l16) * DV + j0 + 4 * g;
+                        if constexpr (F32) {
+                            *reinterpret_cast<f32x4 *>(op) = o;
+                        } else {
+                            bf16x4 bo;
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) bo[i] = (__bf16)o[i];
-                        *reinterpret_cast<bf16x4 *>(op) = bo;
+                            for (int i = 0; i < 4; ++i) bo[i] = (__bf16)o[i];
+                            *reinterpret_cast<bf16x4 *>(op) = bo;
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) o[i] = (float)bo[i];  // what was stored
-                    }
-                    if (counts != nullptr) {
+                            for (int i = 0; i < 4; ++i) o[i] = (float)bo[i];  // what was stored
+                        }
+                        if constexpr (decltype(count)::value) {
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) nonfinite += !__builtin_isfinite(o[i]);
+                            for (int i = 0; i < 4; ++i) nonfinite += !__builtin_isfinite(o[i]);
+                        }
                     }
                 }
-            }
+            };
+            if (counts != nullptr)
+                store(std::true_type{});
+            else
+                store(std::false_type{});
         }
 #pragma unroll
         for (int c = 0; c < NCH; ++c) cur[c] = nxt[c];

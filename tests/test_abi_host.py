@@ -49,11 +49,13 @@ def test_workspace_bytes():
     # each of the 8 value slices 4 int exponents and U~, Oi^T as 4 fp16 tiles each
     rec = 3 * 32 * 512 + 128 * 4 + 16 + 8 * (16 + 2 * 4 * 512)
     rec = (rec + 255) // 256 * 256
-    # the state stage walks each head's 1024 chunks as 8 segments (32 heads x 8 = 256 work-groups):
-    # per head 8 state slots and 7 transition slots, 128 x 128 float32 each
-    seg = 32 * (8 + 7) * 128 * 128 * 4
-    assert kda.workspace_bytes(1, 32, 65536, 128, 128, 64, torch.bfloat16) == 32 * 1024 * rec + seg
-    # 256 or more heads: one segment, the records alone
+    # 32 heads x 8 value slices fill the 256 compute units: the per-slice state stage, records alone
+    assert kda.workspace_bytes(1, 32, 65536, 128, 128, 64, torch.bfloat16) == 32 * 1024 * rec
+    # 16 heads: the segmented stage walks each head's 4096 chunks as 16 segments (256 work-groups),
+    # per head 16 state slots and 15 transition slots, 128 x 128 float32 each
+    seg = 16 * (16 + 15) * 128 * 128 * 4
+    assert kda.workspace_bytes(1, 16, 262144, 128, 128, 64, torch.bfloat16) == 16 * 4096 * rec + seg
+    # 256 or more heads: the segmented stage with one segment, the records alone
     assert kda.workspace_bytes(4, 64, 8192, 128, 128, 64, torch.bfloat16) == 4 * 64 * 128 * rec
     # fp32 records of 64-token chunks at d = 128 do not fit the segmented stage's ring twice
     L = 3 * 32 * 1024 + 128 * 4 + 16 + 8 * (16 + 2 * 4 * 1024)

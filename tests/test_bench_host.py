@@ -109,15 +109,16 @@ def test_more_than_one_gpu_is_refused():
 
 
 @pytest.mark.parametrize("B,H,T,d,C,es", [(1, 32, 65536, 128, 64, 2), (1, 8, 1048576, 128, 64, 2),
-                                          (4, 16, 8192, 128, 64, 2), (1, 2, 256, 64, 16, 4),
-                                          (1, 3, 512, 64, 32, 2), (4, 64, 8192, 128, 64, 2)])
+                                          (1, 16, 262144, 128, 64, 2), (4, 16, 8192, 128, 64, 2),
+                                          (1, 2, 256, 64, 16, 4), (1, 3, 512, 64, 32, 2), (4, 64, 8192, 128, 64, 2),
+                                          (1, 16, 65536, 128, 64, 4), (1, 31, 2048, 128, 64, 2)])
 def test_record_layout_and_segments_match_the_library(B, H, T, d, C, es):
     # the workspace is the records plus, with several segments, two float32 maps per segment and head
     import torch
     import chunked_gated_linear_bounded_amd as kda
     L = bench.record_layout(d, d, C, es)
     units, nc = B * H, T // C
-    nseg = bench.seg_count(units, nc)
+    nseg = bench.seg_count(units, nc) if bench.use_segmented(units, d, d, C, es) else 1
     extra = 0 if nseg == 1 else units * (nseg + nseg - 1) * d * d * 4
     want = units * nc * L["stride"] + extra
     assert kda.workspace_bytes(B, H, T, d, d, C, torch.float32 if es == 4 else torch.bfloat16) == want
@@ -129,3 +130,13 @@ def test_segment_counts_of_the_workloads():
     assert [bench.seg_count(u, nc) for (u, nc) in ((32, 1024), (16, 4096), (8, 16384), (64, 128), (256, 128))] == \
         [8, 16, 32, 4, 1]
     assert bench.seg_count(2, 16) == 2 and bench.seg_count(2, 15) == 1 and bench.seg_count(3, 100) == 12
+
+
+def test_state_stage_choice():
+    # per-slice where its (head, value slice) work-groups fill 256 compute units (64k: 32 x 8; 8k:
+    # 64 x 8), segmented below that (256k: 16 heads, 1m: 8) and from 256 heads on; fp32 records of
+    # 64-token chunks at d = 128 do not fit the segmented stage's ring twice
+    assert [bench.use_segmented(u, 128, 128, 64, 2) for u in (32, 64, 16, 8, 31, 255, 256)] == \
+        [False, False, True, True, True, False, True]
+    assert not bench.use_segmented(16, 128, 128, 64, 4)
+    assert bench.use_segmented(2, 64, 64, 16, 4) and bench.use_segmented(16, 128, 128, 32, 4)

@@ -216,6 +216,22 @@ def test_value_scale_jumping_between_chunks():
     _tol_check(fs.double().cpu().numpy(), rf, "bf16", "final_state")
 
 
+@pytest.mark.parametrize("B,H,T,d,chunk,nseg", [(2, 128, 256, 64, 16, 1), (1, 5, 64 * 40, 128, 64, 40 // 8),
+                                               (1, 3, 32 * 85, 128, 32, 10)])
+def test_state_stage_segment_layouts(B, H, T, d, chunk, nseg):
+    # 256 heads: the segmented stage with one segment (pass 1 alone, one work-group per head);
+    # 5 heads x 40 chunks: 5 segments of 8 chunks; 3 heads x 85 chunks: 10 segments of 9, the last
+    # one of 4 (segments are never empty) -- every output and final state against the oracle
+    w = KI.Workload("seg", B, H, T, d, d, chunk, "bf16", 4.0, False, 600 + H)
+    _say("segment layout", B, H, T, d, chunk, nseg)
+    inp = _to_dev(KI.make_inputs(w))
+    out, fs = _gpu_run(inp, chunk)
+    torch.cuda.synchronize()
+    ro, rf = _oracle(KI.to_f64(inp))
+    _tol_check(out.double().cpu().numpy(), ro, "bf16")
+    _tol_check(fs.double().cpu().numpy(), rf, "bf16", "final_state")
+
+
 @pytest.mark.parametrize("path", ["segmented", "noalloc", "packed"])
 def test_state_that_decays_to_nothing_then_takes_new_values(path):
     # From a random initial state, eight chunks with v = 0 under saturated gates (g = g_min, a decay
