@@ -1,4 +1,4 @@
-// Chunk-parallel stage: one work-group (4 waves) per (chunk, head, batch).
+// Chunk-parallel stage: one work-group (8 waves) per (chunk, head, batch).
 //
 // For one chunk of C tokens (r, s = 0..C-1 local positions, G = inclusive
 // log-cumsum of the gate inside the chunk) it computes, fp32 accumulation:
@@ -47,6 +47,10 @@ struct IntraCfg {
     static constexpr int NKB = DK / 32;          // channel K-blocks
     static constexpr int NTKB = (NT + 1) / 2;    // token K-blocks
     static constexpr int NJOB = NT * (NT + 1) / 2;
+    // 8 waves, two per SIMD and work-group; with the LDS allowing two work-groups per CU that is
+    // four waves per SIMD to hide each other's latencies (with 4-wave work-groups, two per SIMD)
+    static constexpr int NW = 8, THREADS = NW * 64;
+    static constexpr int NKBH = NKB / 2;         // channel K-blocks per wave of a row tile's pair
     static constexpr int PG = DK + 4;            // sG pitch (floats)
     static constexpr int PQ = DK + (F32 ? 4 : 8);  // q/k pitch (elements)
     static constexpr int PV = DV + (F32 ? 4 : 8);
@@ -60,14 +64,19 @@ struct IntraCfg {
     // fragment per lane and K-block) and the steps e^{rho_{J+1} - rho_J}
     static constexpr int SZ_X = (NT - 1) * NKB * 512 * 4;
     static constexpr int SZ_XD = SZ_X + (NT - 1) * DK * 4;
-    static constexpr int R1 = SZ_Q > SZ_A ? (SZ_Q > SZ_XD ? SZ_Q : SZ_XD) : (SZ_A > SZ_XD ? SZ_A : SZ_XD);
+    // after the products of phase 1: the second wave of each row tile's pair hands its partial M
+    // and A sub-tiles to the first through R1
+    static constexpr int SZ_P = NJOB * 2 * 256 * 4;
+    static constexpr int R1A = SZ_Q > SZ_A ? (SZ_Q > SZ_XD ? SZ_Q : SZ_XD) : (SZ_A > SZ_XD ? SZ_A : SZ_XD);
+    static constexpr int R1 = R1A > SZ_P ? R1A : SZ_P;
     static constexpr int R2 = C * PQ * ES;
     static constexpr int OFF_R1 = R0, OFF_R2 = R0 + R1, OFF_B = R0 + R1 + R2;
 
     static constexpr int OFF_SCR = OFF_B + C * 4;
     static constexpr int SMEM = OFF_SCR + 256 * 4;
     static constexpr int VEC = 16 / ES;          // elements per 16-byte access
-    static constexpr int MAXCT = (NDK + 3) / 4;  // dk tiles per wave
+    static constexpr int MAXCT = (NDK + NW - 1) / NW;  // dk tiles per wave
+    static constexpr int MAXVT = (NDV + NW - 1) / NW;  // dv slices per wave
 };
 
 // Gate pre-activation and its prefix sum from a rank-R factor, on MFMA:
@@ -189,7 +198,7 @@ struct LowRankGate {
 // LRK > 0: the gate pre-activation is formed from lrh [B][T][LRK] (shared by the heads), lrz
 // [H][DK][LRK] and lrA [H][DK] (LowRankGate) instead of being read from a.
 template <int C, int DK, int DV, bool F32, bool VL, int LRK>
-__global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void kda_intra_kernel(
+__global__ __launch_bounds__(512, 4) __attribute__((amdgpu_waves_per_eu(4, 4))) void kda_intra_kernel(
     const typename IntraCfg<C, DK, DV, F32>::E *__restrict__ q,
     const typename IntraCfg<C, DK, DV, F32>::E *__restrict__ k,
     const typename IntraCfg<C, DK, DV, F32>::E *__restrict__ v,
@@ -210,7 +219,8 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     using SP = Split<OW>;
     constexpr int NT = Cfg::NT, NDK = Cfg::NDK, NDV = Cfg::NDV, NKB = Cfg::NKB, NTKB = Cfg::NTKB;
     constexpr int PG = Cfg::PG, PQ = Cfg::PQ, PV = Cfg::PV, PA = Cfg::PA, VEC = Cfg::VEC;
-    constexpr int MAXCT = Cfg::MAXCT;
+    constexpr int MAXCT = Cfg::MAXCT, MAXVT = Cfg::MAXVT, NW = Cfg::NW, THREADS = Cfg::THREADS, NKBH = Cfg::NKBH;
+    static_assert(NKB % 2 == 0, "the two waves of a row tile take half the channel K-blocks each");
     constexpr KdaLayout L = kda_layout(C, DK, DV, Cfg::ES);
     constexpr int TE = 256;  // elements per tile
 
@@ -225,10 +235,19 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     E *sK = reinterpret_cast<E *>(smem + Cfg::OFF_R2);             // R2: k, then K e^G
     float *sB = reinterpret_cast<float *>(smem + Cfg::OFF_B);      // beta
     float *sScr = reinterpret_cast<float *>(smem + Cfg::OFF_SCR);
+    float *sP = reinterpret_cast<float *>(smem + Cfg::OFF_R1);     // R1 after phase 1's products: partials
+    // block maxima, one per wave: K^ [0, NW), Qbar [NW, 2NW), W [2NW, 3NW), M [3NW, 4NW)
+    float *sMaxK = sScr, *sMaxQ = sScr + NW, *sMaxW = sScr + 2 * NW, *sMaxM = sScr + 3 * NW;
+    auto max_of = [](const float *m) {
+        float x = m[0];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) x = fmaxf(x, m[w]);
+        return x;
+    };
 
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: branches on it stay scalar
-    __builtin_assume(wave >= 0 && wave < 4);                    // 256 threads
+    __builtin_assume(wave >= 0 && wave < NW);                   // 512 threads
     const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const size_t head = (size_t)b * H + h;
     size_t tok0, recno;
@@ -255,14 +274,16 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     // any of them is consumed, so the chunk pays one memory round trip.  The gate and its
     // prefix sum run in registers and write G once.
     {
-        constexpr int LPR = DK / VEC, RPP = 256 / LPR, NP = (C + RPP - 1) / RPP;
+        constexpr int LPR = DK / VEC, RPP = THREADS / LPR, NP = (C + RPP - 1) / RPP;
         const E *qg = q + tok0 * DK, *kg = k + tok0 * DK;
         GateScan<C, DK, E> gate;
         LowRankGate<C, DK, E, LR ? LRK : 16> lrt;  // its loads go first: its MFMAs need nothing else
+        // the gate and its prefix sum take the first four waves (256 threads)
         if constexpr (LR) {
-            lrt.load(lrh + ((size_t)b * T + (size_t)(c0 + n) * C) * LRK, lrz + (size_t)h * DK * LRK, wave, lane);
+            if (wave < 4)
+                lrt.load(lrh + ((size_t)b * T + (size_t)(c0 + n) * C) * LRK, lrz + (size_t)h * DK * LRK, wave, lane);
         } else {
-            gate.load(a + tok0 * DK, tid, nrow);
+            if (wave < 4) gate.load(a + tok0 * DK, tid, nrow);
         }
         // loads are unconditional (row indices clamped into the chunk's tokens); only the
         // stores are guarded, and rows past the tokens of a short chunk are stored as zeros
@@ -276,7 +297,9 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
             xk[p] = *reinterpret_cast<const uint4 *>(kg + off);
         }
         // the low-rank gate's MFMAs and prefix sum run while q, k and beta are still in flight
-        if constexpr (LR) lrt.finish(lrA + (size_t)h * DK, gmin2, logsig, sG, PG, lane);
+        if constexpr (LR) {
+            if (wave < 4) lrt.finish(lrA + (size_t)h * DK, gmin2, logsig, sG, PG, lane);
+        }
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
             const int r = p * RPP + tid / LPR, c = (tid % LPR) * VEC;
@@ -292,7 +315,9 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
             }
         }
         if (tid < C) sB[tid] = (!VL || tid < nrow) ? to_f(bv) : 0.f;
-        if constexpr (!LR) gate.finish(gmin2, logsig, sG, PG, tid, nrow);
+        if constexpr (!LR) {
+            if (wave < 4) gate.finish(gmin2, logsig, sG, PG, tid, nrow);
+        }
         __syncthreads();
     }
 
@@ -305,6 +330,8 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     // K'_J = k e^{rho_J - G} goes to LDS in fp32, and a later wave I forms its key operand as
     // K'_J e^{rho_I - rho_J}, the per-channel factor built from the steps between tile starts
     // e^{rho_{J+1} - rho_J}.  Each pair's key operand is still rounded once, from fp32.
+    // Row tile I is carried by the pair of waves I and I + 4, each over half the channel
+    // K-blocks; the second hands its partial sub-tiles to the first through LDS.
     f32x4 accMs[NT], accAs[NT];  // indexed by J
 #pragma unroll
     for (int J = 0; J < NT; ++J) {
@@ -312,14 +339,16 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
         accAs[J] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     unsigned int nonfinite = 0;
-    const int I = wave;
-    F fqh[NKB], fkh[NKB];  // row operands of tile I (single bf16) for the earlier key tiles
-    float kown[NKB][8];    // K'_I in fp32, for the later row tiles
+    const int I = wave & 3, hs = wave >> 2;  // row tile; which half of the channel K-blocks
+    const int kb0 = hs * NKBH;
+    F fqh[NKBH], fkh[NKBH];  // row operands of tile I (single bf16) for the earlier key tiles
+    float kown[NKBH][8];     // K'_I in fp32, for the later row tiles
     if (I < NT) {
         const int r = 16 * I + l16;  // this lane's row (A operand) and key (B operand)
         const float *rho = sG + (16 * I) * PG;
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
+        for (int kbi = 0; kbi < NKBH; ++kbi) {
+            const int kb = kb0 + kbi;
             float qv[8], kv[8];
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
@@ -334,16 +363,16 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
                     const float e = ex2(gr[i] - rr[i]);  // <= 1
                     qv[4 * hh + i] = qr[i] * e;
                     kv[4 * hh + i] = kr[i] * e;
-                    kown[kb][4 * hh + i] = kr[i] * ex2(rr[i] - gr[i]);  // in [|k|, e^{15 |g_min|} |k|]
+                    kown[kbi][4 * hh + i] = kr[i] * ex2(rr[i] - gr[i]);  // in [|k|, e^{15 |g_min|} |k|]
                 }
             }
-            const SP fq = SP::make(qv), fk = SP::make(kv), fc = SP::make(kown[kb]);
+            const SP fq = SP::make(qv), fk = SP::make(kv), fc = SP::make(kown[kbi]);
             if (counts != nullptr) {
 #pragma unroll
                 for (int j = 0; j < 8; ++j) nonfinite += !__builtin_isfinite(fc.hi.get(j));
             }
-            fqh[kb] = fq.hi;
-            fkh[kb] = fk.hi;
+            fqh[kbi] = fq.hi;
+            fkh[kbi] = fk.hi;
 #pragma unroll
             for (int J = 0; J < NT; ++J) {
                 if (J != I) continue;
@@ -353,11 +382,11 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
         }
     }
     // steps between tile starts, e^{rho_{J+1} - rho_J} (<= 1, J < NT - 1)
-    constexpr int ND = (NT - 1) * DK, NDR = (ND + 255) / 256;
+    constexpr int ND = (NT - 1) * DK, NDR = (ND + THREADS - 1) / THREADS;
     float dtab[NDR > 0 ? NDR : 1];
 #pragma unroll
     for (int x = 0; x < NDR; ++x) {
-        const int e = tid + 256 * x;
+        const int e = tid + THREADS * x;
         if (e < ND) {
             const int J = e / DK, c = e % DK;
             dtab[x] = ex2(sG[(16 * J + 16) * PG + c] - sG[(16 * J) * PG + c]);
@@ -368,7 +397,7 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     f32x4 qtr[MAXCT][NT];
 #pragma unroll
     for (int ci = 0; ci < MAXCT; ++ci) {
-        const int ct = wave + 4 * ci;
+        const int ct = wave + NW * ci;
         if (ct >= NDK) continue;
 #pragma unroll
         for (int rt = 0; rt < NT; ++rt) {
@@ -384,21 +413,22 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
         __syncthreads();  // q is no longer read: its region takes the shared key operands and steps
         if (I < NT - 1) {
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
-                float *xp = sXk + ((I * NKB + kb) * 64 + lane) * 8;
-                *reinterpret_cast<f32x4 *>(xp) = f32x4{kown[kb][0], kown[kb][1], kown[kb][2], kown[kb][3]};
-                *reinterpret_cast<f32x4 *>(xp + 4) = f32x4{kown[kb][4], kown[kb][5], kown[kb][6], kown[kb][7]};
+            for (int kbi = 0; kbi < NKBH; ++kbi) {
+                float *xp = sXk + ((I * NKB + kb0 + kbi) * 64 + lane) * 8;
+                *reinterpret_cast<f32x4 *>(xp) = f32x4{kown[kbi][0], kown[kbi][1], kown[kbi][2], kown[kbi][3]};
+                *reinterpret_cast<f32x4 *>(xp + 4) = f32x4{kown[kbi][4], kown[kbi][5], kown[kbi][6], kown[kbi][7]};
             }
         }
 #pragma unroll
         for (int x = 0; x < NDR; ++x) {
-            const int e = tid + 256 * x;
+            const int e = tid + THREADS * x;
             if (e < ND) sDt[e] = dtab[x];
         }
         __syncthreads();
         if (I < NT) {
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
+            for (int kbi = 0; kbi < NKBH; ++kbi) {
+                const int kb = kb0 + kbi;
                 float f[8];  // e^{rho_I - rho_J} for this lane's channels, J descending
 #pragma unroll
                 for (int j = 0; j < 8; ++j) f[j] = 1.f;
@@ -418,14 +448,35 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
                         cv[j] = (j < 4 ? x0[j] : x1[j - 4]) * f[j];  // k_s e^{rho_I - G_s} <= |k_s|
                     }
                     const F fc = F::make(cv);
-                    accMs[J] = mma(fqh[kb], fc, accMs[J]);
-                    accAs[J] = mma(fkh[kb], fc, accAs[J]);
+                    accMs[J] = mma(fqh[kbi], fc, accMs[J]);
+                    accAs[J] = mma(fkh[kbi], fc, accAs[J]);
                 }
             }
         }
     }
+    // the pair's partial sub-tiles summed in its first wave: slot I (I + 1) / 2 + J holds M, A
+    __syncthreads();  // q and the shared key operands are no longer read: R1 takes the partials
+    if (hs == 1 && I < NT) {
+#pragma unroll
+        for (int J = 0; J < NT; ++J) {
+            if (J > I) continue;
+            float *pp = sP + (size_t)(I * (I + 1) / 2 + J) * 512 + 4 * lane;
+            *reinterpret_cast<f32x4 *>(pp) = accMs[J];
+            *reinterpret_cast<f32x4 *>(pp + 256) = accAs[J];
+        }
+    }
+    __syncthreads();
+    if (hs == 0 && I < NT) {
+#pragma unroll
+        for (int J = 0; J < NT; ++J) {
+            if (J > I) continue;
+            const float *pp = sP + (size_t)(I * (I + 1) / 2 + J) * 512 + 4 * lane;
+            accMs[J] += *reinterpret_cast<const f32x4 *>(pp);
+            accAs[J] += *reinterpret_cast<const f32x4 *>(pp + 256);
+        }
+    }
     float mmax = 0.f;  // largest |M| of row tile I
-    if (I < NT) {
+    if (hs == 0 && I < NT) {
         // element (row r = 16I + 4g + i, col s = 16J + l16): M keeps s <= r, A keeps s < r (times beta_r)
 #pragma unroll
         for (int J = 0; J < NT; ++J) {
@@ -441,12 +492,12 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     mmax = wave_max(mmax);
 
     // K^ tiles (st, ct) wait in registers for the chunk's scale; gamma goes to the workspace.
-    constexpr int MAXKH = (NT * NDK + 3) / 4;
+    constexpr int MAXKH = (NT * NDK + NW - 1) / NW;
     f32x4 khr[MAXKH];
     float khmax = 0.f;
 #pragma unroll
     for (int xi = 0; xi < MAXKH; ++xi) {
-        const int tix = wave + 4 * xi;
+        const int tix = wave + NW * xi;
         if (tix >= NT * NDK) continue;
         const int st = tix / NDK, ct = tix % NDK;
         const int c = 16 * ct + l16;
@@ -460,19 +511,19 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     }
     khmax = wave_max(khmax);
     if (lane == 0) {
-        sScr[wave] = khmax;
-        sScr[12 + wave] = mmax;
+        sMaxK[wave] = khmax;
+        sMaxM[wave] = mmax;
     }
     if (tid < DK) wGam[tid] = ex2(sG[(C - 1) * PG + tid]);
     __syncthreads();  // raw k and the shared key operands are no longer read
 
     // ------------------------------------------------ K^ scaled to fp16 range
     {
-        const int sK_ = F32 ? 0 : pow2_scale(fmaxf(fmaxf(sScr[0], sScr[1]), fmaxf(sScr[2], sScr[3])));
+        const int sK_ = F32 ? 0 : pow2_scale(max_of(sMaxK));
         if (tid == 0) wScl[2] = sK_;
 #pragma unroll
         for (int xi = 0; xi < MAXKH; ++xi) {
-            const int tix = wave + 4 * xi;
+            const int tix = wave + NW * xi;
             if (tix >= NT * NDK) continue;
             const int st = tix / NDK, ct = tix % NDK;
             f32x4 o;
@@ -485,7 +536,7 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     }
 
     // ------------------------------------------------ phase 1c: A -> LDS, K -> K e^G in place
-    if (I < NT) {
+    if (hs == 0 && I < NT) {
 #pragma unroll
         for (int J = 0; J < NT; ++J) {
             if (J > I) continue;
@@ -494,7 +545,7 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
         }
     }
     {
-        constexpr int LPR = DK / 4, RPP = 256 / LPR;
+        constexpr int LPR = DK / 4, RPP = THREADS / LPR;
 #pragma unroll
         for (int r0 = 0; r0 < C; r0 += RPP) {
             const int s = r0 + tid / LPR, c = (tid % LPR) * 4;
@@ -516,8 +567,8 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
         const unsigned char *vg = reinterpret_cast<const unsigned char *>(v + tok0 * DV);
         lds_u8 *sVb = lds_base(smem) + C * PA * 4;  // sV, LDS-typed
 #pragma unroll
-        for (int xi = 0; xi < (C * NPR + 3) / 4; ++xi) {
-            const int x = wave + 4 * xi;
+        for (int xi = 0; xi < (C * NPR + NW - 1) / NW; ++xi) {
+            const int x = wave + NW * xi;
             if (x >= C * NPR) continue;
             const int r = x / NPR, part = x % NPR, off = part * 256 + lane * 4;
             // rows past a short chunk's tokens repeat its last row (finite; beta = 0 there)
@@ -592,8 +643,8 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     }
     // A is dead: M takes its place, scaled by 2^sM (the fp16 operand of M W and M U~, whatever the
     // magnitudes of q and k)
-    const int sM_ = F32 ? 0 : pow2_scale(fmaxf(fmaxf(sScr[12], sScr[13]), fmaxf(sScr[14], sScr[15])));
-    if (I < NT) {
+    const int sM_ = F32 ? 0 : pow2_scale(max_of(sMaxM));
+    if (hs == 0 && I < NT) {
 #pragma unroll
         for (int J = 0; J < NT; ++J) {
             if (J > I) continue;
@@ -615,177 +666,208 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     // below the diagonal only; the one block above the diagonal that such a K-block spans
     // (column tile 2 kb + 1 = rt + 1) is zero and is never read.
     using FM = Frag<OH>;  // fp16 (fp32 with fp32 I/O)
-    F tf[NT][NTKB];
-    FM mf[NT][NTKB];
-#pragma unroll
-    for (int rt = 0; rt < NT; ++rt)
-#pragma unroll
-        for (int kb = 0; kb < NTKB; ++kb) {
-            if (kb > rt / 2) continue;
-            float x[8], y[8];
-            const int r = 16 * rt + l16;
-            const bool hi = 2 * kb + 1 <= rt;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int s0 = 32 * kb + 4 * g + i, s1 = s0 + 16;
-                x[i] = sT[r * PA + s0] * sB[s0];
-                x[4 + i] = hi ? sT[r * PA + s1] * sB[s1] : 0.f;
-                y[i] = sM[r * PA + s0];
-                y[4 + i] = hi ? sM[r * PA + s1] : 0.f;
-            }
-            tf[rt][kb] = F::make(x);
-            mf[rt][kb] = FM::make(y);
-        }
-    // dk tiles: W^T, W and Qbar^T = (Q e^G)^T - W^T M^T, kept in registers for the chunk's scale
+    // Two passes, so that the T and M fragments are never held together: the first forms W^T and
+    // W of this wave's dk tile and U~ of its dv slice from T diag(beta), the second the products
+    // with M.
     float qbmax = 0.f, wmax = 0.f;
-    f32x4 wtr[MAXCT][NT];
+    f32x4 wtr[MAXCT][NT], wrow[MAXCT][NT];  // W^T tiles (ct, rt) and W tiles (rt, ct)
+    float wtile[MAXCT];                      // largest |W| of each dk tile
+    f32x4 urow[MAXVT][NT];                   // U~ tiles (rt, vt)
+    float um[MAXVT];
+    {
+        F tf[NT][NTKB];
 #pragma unroll
-    for (int ci = 0; ci < MAXCT; ++ci) {
-        const int ct = wave + 4 * ci;
-        if (ct >= NDK) continue;
-        F kf[NTKB];  // (K e^G): lane l holds column c = 16 ct + l16 at token slots
+        for (int rt = 0; rt < NT; ++rt)
 #pragma unroll
-        for (int kb = 0; kb < NTKB; ++kb) {
-            float x[8];
+            for (int kb = 0; kb < NTKB; ++kb) {
+                if (kb > rt / 2) continue;
+                float x[8];
+                const int r = 16 * rt + l16;
+                const bool hi = 2 * kb + 1 <= rt;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int s = 32 * kb + (j < 4 ? 4 * g + j : 16 + 4 * g + j - 4);
-                x[j] = (s < C) ? to_f(sK[s * PQ + 16 * ct + l16]) : 0.f;
+                for (int i = 0; i < 4; ++i) {
+                    const int s0 = 32 * kb + 4 * g + i, s1 = s0 + 16;
+                    x[i] = sT[r * PA + s0] * sB[s0];
+                    x[4 + i] = hi ? sT[r * PA + s1] * sB[s1] : 0.f;
+                }
+                tf[rt][kb] = F::make(x);
             }
-            kf[kb] = F::make(x);
-        }
-        f32x4 wrow[NT];  // W tiles (st, ct): rows s, cols dk
-        float wtile = 0.f;  // largest |W| of this dk tile
 #pragma unroll
-        for (int rt = 0; rt < NT; ++rt) {
-            f32x4 accT = {0.f, 0.f, 0.f, 0.f}, accW = {0.f, 0.f, 0.f, 0.f};
+        for (int ci = 0; ci < MAXCT; ++ci) {
+            const int ct = wave + NW * ci;
+            wtile[ci] = 0.f;
+            if (ct >= NDK) continue;
+            F kf[NTKB];  // (K e^G): lane l holds column c = 16 ct + l16 at token slots
 #pragma unroll
-            for (int kb = 0; kb <= rt / 2; ++kb) {
-                accT = mma(kf[kb], tf[rt][kb], accT);  // W^T (ct, rt)
-                accW = mma(tf[rt][kb], kf[kb], accW);  // W (rt, ct)
+            for (int kb = 0; kb < NTKB; ++kb) {
+                float x[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int s = 32 * kb + (j < 4 ? 4 * g + j : 16 + 4 * g + j - 4);
+                    x[j] = (s < C) ? to_f(sK[s * PQ + 16 * ct + l16]) : 0.f;
+                }
+                kf[kb] = F::make(x);
             }
-            wtr[ci][rt] = accT;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) wtile = fmaxf(wtile, fabsf(accT[i]));
-            wrow[rt] = accW;
-        }
-        wmax = fmaxf(wmax, wtile);
-        // W 2^sWa as the A operand of W^T (m = dk, k = token); M W comes out scaled by 2^(sWa + sM)
-        const int sWa = F32 ? 0 : pow2_scale(wave_max(wtile));
-        FM wa[NTKB];
+            for (int rt = 0; rt < NT; ++rt) {
+                f32x4 accT = {0.f, 0.f, 0.f, 0.f}, accW = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < NTKB; ++kb) {
-            float x[8];
+                for (int kb = 0; kb <= rt / 2; ++kb) {
+                    accT = mma(kf[kb], tf[rt][kb], accT);  // W^T (ct, rt)
+                    accW = mma(tf[rt][kb], kf[kb], accW);  // W (rt, ct)
+                }
+                wtr[ci][rt] = accT;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int t = 2 * kb + j / 4;
-                x[j] = (t < NT) ? ldexp2(wrow[t < NT ? t : 0][j % 4], sWa) : 0.f;
+                for (int i = 0; i < 4; ++i) wtile[ci] = fmaxf(wtile[ci], fabsf(accT[i]));
+                wrow[ci][rt] = accW;
             }
-            wa[kb] = FM::make(x);
         }
-        const int unMW = -(sWa + sM_);
 #pragma unroll
-        for (int rt = 0; rt < NT; ++rt) {
-            f32x4 mw = {0.f, 0.f, 0.f, 0.f};
+        for (int vi = 0; vi < MAXVT; ++vi) {
+            const int vt = wave + NW * vi;
+            um[vi] = 0.f;
+            if (vt >= NDV) continue;
+            F vf[NTKB];  // V: lane l holds column 16 vt + l16 at token slots
 #pragma unroll
-            for (int kb = 0; kb <= rt / 2; ++kb) mw = mma(wa[kb], mf[rt][kb], mw);
+            for (int kb = 0; kb < NTKB; ++kb) {
+                float x[8];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                qtr[ci][rt][i] -= ldexp2(mw[i], unMW);
-                qbmax = fmaxf(qbmax, fabsf(qtr[ci][rt][i]));
+                for (int j = 0; j < 8; ++j) {
+                    const int s = 32 * kb + (j < 4 ? 4 * g + j : 16 + 4 * g + j - 4);
+                    x[j] = (s < C) ? to_f(sV[s * PV + 16 * vt + l16]) : 0.f;
+                }
+                vf[kb] = F::make(x);
+            }
+#pragma unroll
+            for (int rt = 0; rt < NT; ++rt) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb <= rt / 2; ++kb) acc = mma(tf[rt][kb], vf[kb], acc);
+                urow[vi][rt] = acc;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) um[vi] = fmaxf(um[vi], fabsf(acc[i]));
+            }
+        }
+    }
+    {
+        FM mf[NT][NTKB];  // M 2^sM
+#pragma unroll
+        for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+            for (int kb = 0; kb < NTKB; ++kb) {
+                if (kb > rt / 2) continue;
+                float y[8];
+                const int r = 16 * rt + l16;
+                const bool hi = 2 * kb + 1 <= rt;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int s0 = 32 * kb + 4 * g + i, s1 = s0 + 16;
+                    y[i] = sM[r * PA + s0];
+                    y[4 + i] = hi ? sM[r * PA + s1] : 0.f;
+                }
+                mf[rt][kb] = FM::make(y);
+            }
+        // dk tiles: Qbar^T = (Q e^G)^T - W^T M^T, kept in registers for the chunk's scale
+#pragma unroll
+        for (int ci = 0; ci < MAXCT; ++ci) {
+            const int ct = wave + NW * ci;
+            if (ct >= NDK) continue;
+            wmax = fmaxf(wmax, wtile[ci]);
+            // W 2^sWa as the A operand of W^T (m = dk, k = token); M W comes out scaled by 2^(sWa + sM)
+            const int sWa = F32 ? 0 : pow2_scale(wave_max(wtile[ci]));
+            FM wa[NTKB];
+#pragma unroll
+            for (int kb = 0; kb < NTKB; ++kb) {
+                float x[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int t = 2 * kb + j / 4;
+                    x[j] = (t < NT) ? ldexp2(wrow[ci][t < NT ? t : 0][j % 4], sWa) : 0.f;
+                }
+                wa[kb] = FM::make(x);
+            }
+            const int unMW = -(sWa + sM_);
+#pragma unroll
+            for (int rt = 0; rt < NT; ++rt) {
+                f32x4 mw = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb <= rt / 2; ++kb) mw = mma(wa[kb], mf[rt][kb], mw);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    qtr[ci][rt][i] -= ldexp2(mw[i], unMW);
+                    qbmax = fmaxf(qbmax, fabsf(qtr[ci][rt][i]));
+                }
+            }
+        }
+        // dv slices: U~ and Oi^T = U~^T M^T, scaled per slice to fp16 range
+#pragma unroll
+        for (int vi = 0; vi < MAXVT; ++vi) {
+            const int vt = wave + NW * vi;
+            if (vt >= NDV) continue;
+            unsigned char *sl = rec + L.region1 + vt * L.slice;
+            OH *wU = reinterpret_cast<OH *>(sl + L.ut);
+            OH *wO = reinterpret_cast<OH *>(sl + L.oit);
+            int *wS = reinterpret_cast<int *>(sl + L.ssc);
+            // U~ 2^sU as the A operand of U~^T (m = dv, k = token): the block scale keeps the fp16
+            // operand in range whatever the magnitude of v; Oi comes out scaled by 2^sU as well
+            const int sU_ = F32 ? 0 : pow2_scale(wave_max(um[vi]));
+            FM ua[NTKB];
+#pragma unroll
+            for (int kb = 0; kb < NTKB; ++kb) {
+                float x[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int t = 2 * kb + j / 4;
+                    x[j] = (t < NT) ? ldexp2(urow[vi][t < NT ? t : 0][j % 4], sU_) : 0.f;
+                }
+                ua[kb] = FM::make(x);
+            }
+            f32x4 orow[NT];  // Oi 2^(sU + sM)
+            float om = 0.f;
+#pragma unroll
+            for (int rt = 0; rt < NT; ++rt) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb <= rt / 2; ++kb) acc = mma(ua[kb], mf[rt][kb], acc);
+                orow[rt] = acc;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) om = fmaxf(om, fabsf(acc[i]));
+            }
+            const int sO_ = F32 ? 0 : pow2_scale(wave_max(om));  // Oi is stored scaled by 2^(sU + sM + sO)
+#pragma unroll
+            for (int rt = 0; rt < NT; ++rt) {
+                f32x4 u, o;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    u[i] = ldexp2(urow[vi][rt][i], sU_);
+                    o[i] = ldexp2(orow[rt][i], sO_);
+                }
+                st_tile(wU + rt * TE, lane, u);
+                st_tile(wO + rt * TE, lane, o);
+            }
+            if (lane == 0) {
+                wS[0] = sU_;
+                wS[1] = sU_ + sM_ + sO_;
+                wS[2] = 0;
+                wS[3] = 0;
             }
         }
     }
     qbmax = wave_max(qbmax);
     wmax = wave_max(wmax);
     if (lane == 0) {
-        sScr[4 + wave] = qbmax;
-        sScr[8 + wave] = wmax;
-    }
-    // dv slices (one wave each): U~ and Oi^T = U~^T M^T, scaled per slice to fp16 range
-#pragma unroll
-    for (int vi = 0; vi < (NDV + 3) / 4; ++vi) {  // unrolled: the slices' chains interleave
-        const int vt = wave + 4 * vi;
-        if (vt >= NDV) continue;
-        unsigned char *sl = rec + L.region1 + vt * L.slice;
-        OH *wU = reinterpret_cast<OH *>(sl + L.ut);
-        OH *wO = reinterpret_cast<OH *>(sl + L.oit);
-        int *wS = reinterpret_cast<int *>(sl + L.ssc);
-        F vf[NTKB];  // V: lane l holds column 16 vt + l16 at token slots
-#pragma unroll
-        for (int kb = 0; kb < NTKB; ++kb) {
-            float x[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int s = 32 * kb + (j < 4 ? 4 * g + j : 16 + 4 * g + j - 4);
-                x[j] = (s < C) ? to_f(sV[s * PV + 16 * vt + l16]) : 0.f;
-            }
-            vf[kb] = F::make(x);
-        }
-        f32x4 urow[NT];
-        float um = 0.f;
-#pragma unroll
-        for (int rt = 0; rt < NT; ++rt) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb <= rt / 2; ++kb) acc = mma(tf[rt][kb], vf[kb], acc);
-            urow[rt] = acc;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) um = fmaxf(um, fabsf(acc[i]));
-        }
-        // U~ 2^sU as the A operand of U~^T (m = dv, k = token): the block scale keeps the fp16
-        // operand in range whatever the magnitude of v; Oi comes out scaled by 2^sU as well
-        const int sU_ = F32 ? 0 : pow2_scale(wave_max(um));
-        FM ua[NTKB];
-#pragma unroll
-        for (int kb = 0; kb < NTKB; ++kb) {
-            float x[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int t = 2 * kb + j / 4;
-                x[j] = (t < NT) ? ldexp2(urow[t < NT ? t : 0][j % 4], sU_) : 0.f;
-            }
-            ua[kb] = FM::make(x);
-        }
-        f32x4 orow[NT];  // Oi 2^(sU + sM)
-        float om = 0.f;
-#pragma unroll
-        for (int rt = 0; rt < NT; ++rt) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb <= rt / 2; ++kb) acc = mma(ua[kb], mf[rt][kb], acc);
-            orow[rt] = acc;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) om = fmaxf(om, fabsf(acc[i]));
-        }
-        const int sO_ = F32 ? 0 : pow2_scale(wave_max(om));  // Oi is stored scaled by 2^(sU + sM + sO)
-#pragma unroll
-        for (int rt = 0; rt < NT; ++rt) {
-            f32x4 u, o;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                u[i] = ldexp2(urow[rt][i], sU_);
-                o[i] = ldexp2(orow[rt][i], sO_);
-            }
-            st_tile(wU + rt * TE, lane, u);
-            st_tile(wO + rt * TE, lane, o);
-        }
-        if (lane == 0) {
-            wS[0] = sU_;
-            wS[1] = sU_ + sM_ + sO_;
-            wS[2] = 0;
-            wS[3] = 0;
-        }
+        sMaxQ[wave] = qbmax;
+        sMaxW[wave] = wmax;
     }
     __syncthreads();
     // W^T and Qbar^T scaled to fp16 range, stored as tile pairs along dk
     {
-        const int sQ_ = F32 ? 0 : pow2_scale(fmaxf(fmaxf(sScr[4], sScr[5]), fmaxf(sScr[6], sScr[7])));
-        const int sW_ = F32 ? 0 : pow2_scale(fmaxf(fmaxf(sScr[8], sScr[9]), fmaxf(sScr[10], sScr[11])));
+        const int sQ_ = F32 ? 0 : pow2_scale(max_of(sMaxQ));
+        const int sW_ = F32 ? 0 : pow2_scale(max_of(sMaxW));
         if (tid == 0) { wScl[0] = sW_; wScl[1] = sQ_; wScl[3] = 0; }
 #pragma unroll
         for (int ci = 0; ci < MAXCT; ++ci) {
-            const int ct = wave + 4 * ci;
+            const int ct = wave + NW * ci;
             if (ct >= NDK) continue;
 #pragma unroll
             for (int rt = 0; rt < NT; ++rt) {
