@@ -47,10 +47,14 @@ struct IntraCfg {
     static constexpr int NKB = DK / 32;          // channel K-blocks
     static constexpr int NTKB = (NT + 1) / 2;    // token K-blocks
     static constexpr int NJOB = NT * (NT + 1) / 2;
-    // 8 waves, two per SIMD and work-group; with the LDS allowing two work-groups per CU that is
-    // four waves per SIMD to hide each other's latencies (with 4-wave work-groups, two per SIMD)
-    static constexpr int NW = 8, THREADS = NW * 64;
-    static constexpr int NKBH = NKB / 2;         // channel K-blocks per wave of a row tile's pair
+    // 64-token chunks: 8 waves, two per SIMD and work-group; with the LDS allowing two work-groups
+    // per CU that is four waves per SIMD to hide each other's latencies (with 4-wave work-groups,
+    // two per SIMD).  Each row tile is then carried by a pair of waves (HS = 2 halves of the
+    // channel K-blocks).  Shorter chunks (one or two row tiles) keep 4 waves: there most waves of
+    // an 8-wave group would idle through phases 1 and 2 while still paying their setup.
+    static constexpr int NW = NT >= 4 ? 8 : 4, THREADS = NW * 64;
+    static constexpr int HS = NW / 4;
+    static constexpr int NKBH = NKB / HS;        // channel K-blocks per wave of a row tile
     static constexpr int PG = DK + 4;            // sG pitch (floats)
     static constexpr int PQ = DK + (F32 ? 4 : 8);  // q/k pitch (elements)
     static constexpr int PV = DV + (F32 ? 4 : 8);
@@ -66,7 +70,7 @@ struct IntraCfg {
     static constexpr int SZ_XD = SZ_X + (NT - 1) * DK * 4;
     // after the products of phase 1: the second wave of each row tile's pair hands its partial M
     // and A sub-tiles to the first through R1
-    static constexpr int SZ_P = NJOB * 2 * 256 * 4;
+    static constexpr int SZ_P = HS == 2 ? NJOB * 2 * 256 * 4 : 0;
     static constexpr int R1A = SZ_Q > SZ_A ? (SZ_Q > SZ_XD ? SZ_Q : SZ_XD) : (SZ_A > SZ_XD ? SZ_A : SZ_XD);
     static constexpr int R1 = R1A > SZ_P ? R1A : SZ_P;
     static constexpr int R2 = C * PQ * ES;
@@ -198,7 +202,7 @@ struct LowRankGate {
 // LRK > 0: the gate pre-activation is formed from lrh [B][T][LRK] (shared by the heads), lrz
 // [H][DK][LRK] and lrA [H][DK] (LowRankGate) instead of being read from a.
 template <int C, int DK, int DV, bool F32, bool VL, int LRK>
-__global__ __launch_bounds__(512, 4) __attribute__((amdgpu_waves_per_eu(4, 4))) void kda_intra_kernel(
+__global__ __launch_bounds__((IntraCfg<C, DK, DV, F32>::THREADS), 4) __attribute__((amdgpu_waves_per_eu(4, 4))) void kda_intra_kernel(
     const typename IntraCfg<C, DK, DV, F32>::E *__restrict__ q,
     const typename IntraCfg<C, DK, DV, F32>::E *__restrict__ k,
     const typename IntraCfg<C, DK, DV, F32>::E *__restrict__ v,
@@ -220,7 +224,8 @@ __global__ __launch_bounds__(512, 4) __attribute__((amdgpu_waves_per_eu(4, 4))) 
     constexpr int NT = Cfg::NT, NDK = Cfg::NDK, NDV = Cfg::NDV, NKB = Cfg::NKB, NTKB = Cfg::NTKB;
     constexpr int PG = Cfg::PG, PQ = Cfg::PQ, PV = Cfg::PV, PA = Cfg::PA, VEC = Cfg::VEC;
     constexpr int MAXCT = Cfg::MAXCT, MAXVT = Cfg::MAXVT, NW = Cfg::NW, THREADS = Cfg::THREADS, NKBH = Cfg::NKBH;
-    static_assert(NKB % 2 == 0, "the two waves of a row tile take half the channel K-blocks each");
+    constexpr int HS = Cfg::HS;
+    static_assert(NKB % HS == 0, "the waves of a row tile take equal shares of the channel K-blocks");
     constexpr KdaLayout L = kda_layout(C, DK, DV, Cfg::ES);
     constexpr int TE = 256;  // elements per tile
 
@@ -247,7 +252,7 @@ __global__ __launch_bounds__(512, 4) __attribute__((amdgpu_waves_per_eu(4, 4))) 
 
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: branches on it stay scalar
-    __builtin_assume(wave >= 0 && wave < NW);                   // 512 threads
+    __builtin_assume(wave >= 0 && wave < NW);                   // THREADS threads
     const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const size_t head = (size_t)b * H + h;
     size_t tok0, recno;
@@ -455,6 +460,7 @@ __global__ __launch_bounds__(512, 4) __attribute__((amdgpu_waves_per_eu(4, 4))) 
         }
     }
     // the pair's partial sub-tiles summed in its first wave: slot I (I + 1) / 2 + J holds M, A
+    if constexpr (HS == 2) {
     __syncthreads();  // q and the shared key operands are no longer read: R1 takes the partials
     if (hs == 1 && I < NT) {
 #pragma unroll
@@ -474,6 +480,7 @@ __global__ __launch_bounds__(512, 4) __attribute__((amdgpu_waves_per_eu(4, 4))) 
             accMs[J] += *reinterpret_cast<const f32x4 *>(pp);
             accAs[J] += *reinterpret_cast<const f32x4 *>(pp + 256);
         }
+    }
     }
     float mmax = 0.f;  // largest |M| of row tile I
     if (hs == 0 && I < NT) {

@@ -122,7 +122,8 @@ static hipError_t launch_intra_t(const LaunchArgs &p) {
                            p.H * p.dv * p.dk);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((kda_intra_kernel<C, DK, DV, F32, true, 0>), dim3(p.ncmax, p.H, 1), dim3(512), 0,
+        hipLaunchKernelGGL((kda_intra_kernel<C, DK, DV, F32, true, 0>), dim3(p.ncmax, p.H, 1),
+                           dim3(IntraCfg<C, DK, DV, F32>::THREADS), 0,
                            p.stream, reinterpret_cast<const E *>(p.q), reinterpret_cast<const E *>(p.k),
                            reinterpret_cast<const E *>(p.v), reinterpret_cast<const E *>(p.a),
                            reinterpret_cast<const E *>(p.beta), p.g_min * kLog2e, p.logsig, p.H, p.T,
@@ -133,7 +134,7 @@ static hipError_t launch_intra_t(const LaunchArgs &p) {
     if (p.lr_h != nullptr) return launch_intra_lowrank(p);
     const int ncw = p.ncw > 0 ? p.ncw : p.T / C;
     dim3 grid(ncw, p.H, p.B);
-    hipLaunchKernelGGL((kda_intra_kernel<C, DK, DV, F32, false, 0>), grid, dim3(512), 0, p.stream,
+    hipLaunchKernelGGL((kda_intra_kernel<C, DK, DV, F32, false, 0>), grid, dim3(IntraCfg<C, DK, DV, F32>::THREADS), 0, p.stream,
                        reinterpret_cast<const E *>(p.q), reinterpret_cast<const E *>(p.k),
                        reinterpret_cast<const E *>(p.v), reinterpret_cast<const E *>(p.a),
                        reinterpret_cast<const E *>(p.beta), p.g_min * kLog2e, p.logsig, p.H, p.T,

@@ -12,7 +12,8 @@ template <int C, int DK, int DV, bool F32, int R>
 static hipError_t launch_lr_t(const LaunchArgs &p) {
     using E = typename std::conditional<F32, float, __bf16>::type;
     const int ncw = p.ncw > 0 ? p.ncw : p.T / C;
-    hipLaunchKernelGGL((kda_intra_kernel<C, DK, DV, F32, false, R>), dim3(ncw, p.H, p.B), dim3(512), 0,
+    hipLaunchKernelGGL((kda_intra_kernel<C, DK, DV, F32, false, R>), dim3(ncw, p.H, p.B),
+                       dim3(IntraCfg<C, DK, DV, F32>::THREADS), 0,
                        p.stream, reinterpret_cast<const E *>(p.q), reinterpret_cast<const E *>(p.k),
                        reinterpret_cast<const E *>(p.v), nullptr, reinterpret_cast<const E *>(p.beta),
                        p.g_min * kLog2e, p.logsig, p.H, p.T, reinterpret_cast<unsigned char *>(p.workspace), p.counts,
