@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include "kda_bwd.h"
+#include "kda_bwd_chunk.h"
 #include "kda_launch.h"
 
 namespace kda {
@@ -17,11 +18,18 @@ static hipError_t launch_bwd_t(const LaunchArgs &p) {
                        p.dfinal, p.T, p.dstates, p.dinit);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((kda_bwd_chunk_kernel<DK, DV, F32>), dim3(NC, BH), dim3(512), 0, p.stream,
-                       reinterpret_cast<const E *>(p.q), reinterpret_cast<const E *>(p.k),
-                       reinterpret_cast<const E *>(p.v), reinterpret_cast<const E *>(p.a),
-                       reinterpret_cast<const E *>(p.beta), reinterpret_cast<const E *>(p.dout), p.g_min * kLog2e,
-                       p.g_min, p.logsig, p.T, p.states, p.dstates, p.dq, p.dk_, p.dv_, p.da, p.dbeta);
+    if constexpr (F32)  // fp32 inputs: every product in fp32 (their 1e-4 bar)
+        hipLaunchKernelGGL((kda_bwd_chunk_kernel<DK, DV, F32>), dim3(NC, BH), dim3(512), 0, p.stream,
+                           reinterpret_cast<const E *>(p.q), reinterpret_cast<const E *>(p.k),
+                           reinterpret_cast<const E *>(p.v), reinterpret_cast<const E *>(p.a),
+                           reinterpret_cast<const E *>(p.beta), reinterpret_cast<const E *>(p.dout), p.g_min * kLog2e,
+                           p.g_min, p.logsig, p.T, p.states, p.dstates, p.dq, p.dk_, p.dv_, p.da, p.dbeta);
+    else  // bf16 inputs: state operands in registers, shared operands split once in LDS
+        hipLaunchKernelGGL((kda_bwd_chunk16_kernel<DK, DV>), dim3(NC, BH), dim3(256), 0, p.stream,
+                           reinterpret_cast<const E *>(p.q), reinterpret_cast<const E *>(p.k),
+                           reinterpret_cast<const E *>(p.v), reinterpret_cast<const E *>(p.a),
+                           reinterpret_cast<const E *>(p.beta), reinterpret_cast<const E *>(p.dout), p.g_min * kLog2e,
+                           p.g_min, p.logsig, p.T, p.states, p.dstates, p.dq, p.dk_, p.dv_, p.da, p.dbeta);
     return hipGetLastError();
 }
 
