@@ -107,7 +107,7 @@ struct BwdCfg {
 template <int DK, int DV, bool F32>
 __global__ __launch_bounds__(320) void kda_bwd_dstate_kernel(
     const unsigned char *__restrict__ ws, const typename BwdCfg<DK, DV, F32>::E *__restrict__ dout,
-    const float *__restrict__ dfinal, int T, float *__restrict__ dstates, float *__restrict__ dinit)
+    const float *__restrict__ dfinal, int T, int BH, float *__restrict__ dstates, float *__restrict__ dinit)
 {
     using Cfg = BwdCfg<DK, DV, F32>;
     using E = typename Cfg::E;
@@ -128,7 +128,11 @@ __global__ __launch_bounds__(320) void kda_bwd_dstate_kernel(
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     __builtin_assume(wave >= 0 && wave < 5);  // 320 threads: the range readfirstlane hides
-    const int bh = blockIdx.x / NS, slice = blockIdx.x % NS, j0 = 16 * slice;
+    // all slices of a head on one XCD (work-group ids are dealt round-robin to the 8 XCDs), so
+    // that the slices' reads of the same chunk record meet in that XCD's L2
+    const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
+    const int bh = (local / NS) * 8 + xcd, slice = local % NS, j0 = 16 * slice;
+    if (bh >= BH) return;
     const int NC = T / 16;
     const unsigned char *rec0 = ws + (size_t)bh * NC * L.stride;
 

@@ -19,7 +19,7 @@
 //     as its B operand (lane group g supplies k = 4 g + i in step i, which is where the
 //     accumulator holds row 4 g + i);
 //   - T = (I + A)^-1 is the exact finite series (I - N)(I + N^2)(I + N^4)(I + N^8), N = A strictly
-//     lower, on one wave while the others form dQ~ and K^ dS'.
+//     lower, on one wave while the others form dQ~.
 #pragma once
 #include "kda_device.h"
 
@@ -182,7 +182,9 @@ __global__ __launch_bounds__(256, 2) void kda_bwd_chunk16_kernel(
 
     // ---------------------------------------------------------------- loads
     // Inputs first (one 16-byte unit of q, k, a, v, dout per thread), then this wave's state
-    // columns (for dQ~ and dW) and dS' rows (for K^ dS'); nothing waits until it is used.
+    // columns (for dQ~ and dW) and rows (for U); nothing waits until it is used.  The two reads
+    // of the state (and later the two of dS') are issued together, so that the second finds the
+    // lines the first brought into L2.
     const int rk = tid / (DK / 8), ck = 8 * (tid % (DK / 8));
     const int rv = tid / (DV / 8), cv = 8 * (tid % (DV / 8));
     const bool hk = UK == NTH || tid < UK, hv = UV == NTH || tid < UV;
@@ -197,11 +199,11 @@ __global__ __launch_bounds__(256, 2) void kda_bwd_chunk16_kernel(
         xo = reinterpret_cast<const uint4 *>(dout + t0 * DV)[tid];
     }
     const float bv = tid < C ? (float)beta[t0 + tid] : 0.f;
-    float scol[TK][NBV][8], drow[TV][NBK][8];
+    float scol[TK][NBV][8], srow[TV][NBK][8];
 #pragma unroll
     for (int t = 0; t < TK; ++t) load_cols<DK, DV>(Sg, 16 * (wave + NW * t), lane, scol[t]);
 #pragma unroll
-    for (int t = 0; t < TV; ++t) load_rows<DK>(Dg, 16 * (wave + NW * t), lane, drow[t]);
+    for (int t = 0; t < TV; ++t) load_rows<DK>(Sg, 16 * (wave + NW * t), lane, srow[t]);
 
     if (hk) {
         *reinterpret_cast<uint4 *>(sQ + rk * LK + ck) = xq;
@@ -294,16 +296,9 @@ __global__ __launch_bounds__(256, 2) void kda_bwd_chunk16_kernel(
         for (int i = 0; i < 4; ++i) sM[(4 * g + i) * P16 + l16] = l16 <= 4 * g + i ? m[i] : 0.f;
     }
 
-    // ---------------------------------------------------------------- K^ dS', dQ~ = dO S^T
+    // ---------------------------------------------------------------- dQ~ = dO S^T
     f32x4 dQa[TK], dKa[TK], dGa[TK], dUa[TV];  // this wave's key tiles of dq, dk, dG; value tiles of dU
     HL8 scs[TK][NBV];                            // state columns, split, kept for dW
-#pragma unroll
-    for (int t = 0; t < TV; ++t) {
-        HL8 drs[NBK];
-#pragma unroll
-        for (int b = 0; b < NBK; ++b) drs[b] = split8(drow[t][b]);
-        dUa[t] = mm_hl_reg<NBK, LK>(zero, bH, drs, lane);
-    }
 #pragma unroll
     for (int t = 0; t < TK; ++t) {
         const int c = 16 * (wave + NW * t) + l16;
@@ -319,12 +314,6 @@ __global__ __launch_bounds__(256, 2) void kda_bwd_chunk16_kernel(
         }
         asm volatile("" : "+v"(dQa[t]), "+v"(dGa[t]));  // formed here, not where they are next used
     }
-    // The next two state blocks are issued where the registers of the previous ones are free;
-    // the scheduling barrier keeps the compiler from hoisting them above that point.
-    __builtin_amdgcn_sched_barrier(0);
-    float srow[TV][NBK][8];  // state rows of this wave's value tiles, for U
-#pragma unroll
-    for (int t = 0; t < TV; ++t) load_rows<DK>(Sg, 16 * (wave + NW * t), lane, srow[t]);
     __syncthreads();  // T and M are in; the P, M operand blocks are free
 
     // ---------------------------------------------------------------- W = T diag(b) K e^G, U~ = T diag(b) V
@@ -357,6 +346,20 @@ __global__ __launch_bounds__(256, 2) void kda_bwd_chunk16_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) Ua[t][i] -= ws[i];
         st_acc_hl<LM>(bB, Ua[t], j0, lane);
+    }
+    // dS' rows (for K^ dS') and then its columns (for dK^, dgamma), each where the registers of
+    // the previous block are free; the scheduling barriers keep the compiler from hoisting them.
+    __builtin_amdgcn_sched_barrier(0);
+    float drow[TV][NBK][8];
+#pragma unroll
+    for (int t = 0; t < TV; ++t) load_rows<DK>(Dg, 16 * (wave + NW * t), lane, drow[t]);
+#pragma unroll
+    for (int t = 0; t < TV; ++t) {
+        const int j0 = 16 * (wave + NW * t);
+        HL8 drs[NBK];
+#pragma unroll
+        for (int b = 0; b < NBK; ++b) drs[b] = split8(drow[t][b]);
+        dUa[t] = mm_hl_reg<NBK, LK>(zero, bH, drs, lane);
         dUa[t] = mm16(dUa[t], [&](int i) { return sM[(4 * g + i) * P16 + l16]; },
                       [&](int i) { return (float)sO[(4 * g + i) * LV + j0 + l16]; });
         st_acc_hl<LM>(bC, dUa[t], j0, lane);

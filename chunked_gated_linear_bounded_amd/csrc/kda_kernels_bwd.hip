@@ -5,6 +5,7 @@
 
 #include "kda_bwd.h"
 #include "kda_bwd_chunk.h"
+#include "kda_bwd_rev.h"
 #include "kda_launch.h"
 
 namespace kda {
@@ -13,9 +14,15 @@ template <int DK, int DV, bool F32>
 static hipError_t launch_bwd_t(const LaunchArgs &p) {
     using E = typename std::conditional<F32, float, __bf16>::type;
     const int BH = p.B * p.H, NC = p.T / 16;
-    hipLaunchKernelGGL((kda_bwd_dstate_kernel<DK, DV, F32>), dim3(BH * (DV / 16)), dim3(320), 0, p.stream,
-                       reinterpret_cast<const unsigned char *>(p.workspace), reinterpret_cast<const E *>(p.dout),
-                       p.dfinal, p.T, p.dstates, p.dinit);
+    const dim3 rgrid((BH + 7) / 8 * 8 * (DV / 16));  // whole groups of 8 heads (XCD dealing)
+    if constexpr (F32)
+        hipLaunchKernelGGL((kda_bwd_dstate_kernel<DK, DV, F32>), rgrid, dim3(320), 0, p.stream,
+                           reinterpret_cast<const unsigned char *>(p.workspace),
+                           reinterpret_cast<const E *>(p.dout), p.dfinal, p.T, BH, p.dstates, p.dinit);
+    else
+        hipLaunchKernelGGL((kda_bwd_rev_kernel<DK, DV>), rgrid, dim3(320), 0, p.stream,
+                           reinterpret_cast<const unsigned char *>(p.workspace),
+                           reinterpret_cast<const E *>(p.dout), p.dfinal, p.T, BH, p.dstates, p.dinit);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if constexpr (F32)  // fp32 inputs: every product in fp32 (their 1e-4 bar)
