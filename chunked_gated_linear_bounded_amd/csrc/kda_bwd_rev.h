@@ -11,11 +11,11 @@
 //   - dS' and P, fp32, are split into bf16 hi + lo (about 16 significand bits, the full range);
 //     the record's fp16 blocks are exact as hi + lo, and their power-of-two scales are applied to
 //     the products;
-//   - four waves each own two 16-row key tiles of the slice; each forms its part of K^ dS' over
-//     its own tiles, and one barrier per chunk hands the four parts to everyone;
+//   - one wave per 16-row key tile of the slice (eight at dk = 128, two per SIMD) forms its part of
+//     K^ dS' over its tile, and one barrier per chunk hands the parts to everyone;
 //   - each chunk's operands are read from the ring and split during the previous chunk's update,
 //     and Qbar^T dO, which does not depend on dS', before the barrier.
-// A fifth wave streams each chunk's record and dout block into a ring of LDS slots (five where they
+// One more wave streams each chunk's record and dout block into a ring of LDS slots (five where they
 // fit) with direct global->LDS loads, as many chunks ahead as the ring holds, touches the lines
 // of a chunk eight ahead into L2 (each slice a share of them) so that the ring's loads hit there,
 // and alone waits on its memory counter.
@@ -47,13 +47,13 @@ __device__ __forceinline__ void split4(const V &x, bf16x4 &h, bf16x4 &l) {
 }
 
 template <int DK, int DV>
-__global__ __launch_bounds__(320) void kda_bwd_rev_kernel(
+__global__ __launch_bounds__((DK / 16 + 1) * 64) void kda_bwd_rev_kernel(
     const unsigned char *__restrict__ ws, const __bf16 *__restrict__ dout, const float *__restrict__ dfinal, int T,
     int BH, float *__restrict__ dstates, float *__restrict__ dinit)
 {
     constexpr KdaLayout L = kda_layout(16, DK, DV, 2);
-    constexpr int NS = DV / 16, NDK = DK / 16, NTW = NDK / 4;  // key tiles per compute wave
-    static_assert(NDK % 4 == 0, "dk of 64 or 128");
+    constexpr int NS = DV / 16, NDK = DK / 16, NCW = NDK, NTW = 1;  // one compute wave per key tile
+    static_assert(NDK == 4 || NDK == 8, "dk of 64 or 128");
     constexpr int R1 = (int)L.region1, NU = (R1 + 15) / 16;  // 16-byte units of region 1
     constexpr int NBLK = (NU + 63) / 64;                     // 1 KiB direct-load blocks
     constexpr int RB = NBLK * 1024, SLOT = RB + 1024;        // record + dout block
@@ -73,11 +73,11 @@ __global__ __launch_bounds__(320) void kda_bwd_rev_kernel(
 
     __shared__ __attribute__((aligned(1024))) unsigned char sRing[NSLOT * SLOT];
     __shared__ __attribute__((aligned(16))) unsigned char sSink[256];
-    __shared__ f32x4 sPp[2][4][64];  // each compute wave's part of K^ dS', as its lanes hold it; two sets
+    __shared__ f32x4 sPp[2][NCW][64];  // each compute wave's part of K^ dS', as its lanes hold it; two sets
 
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    __builtin_assume(wave >= 0 && wave < 5);  // 320 threads: the range readfirstlane hides
+    __builtin_assume(wave >= 0 && wave <= NCW);  // the range readfirstlane hides
     // all slices of a head on one XCD (work-group ids are dealt round-robin to the 8 XCDs), so
     // that the slices' reads of the same chunk record meet in that XCD's L2
     const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
@@ -119,16 +119,16 @@ __global__ __launch_bounds__(320) void kda_bwd_rev_kernel(
         else wait_vmcnt<0>();
     };
 
-    // dS' of the last chunk: dfinal (or zero); tile x of wave w is key rows 16 (w + 4 x) .. + 15,
+    // dS' of the last chunk: dfinal (or zero); wave w's tile is key rows 16 w .. 16 w + 15,
     // held as an accumulator (lane (g, j) holds rows 4 g + i of value column j)
     f32x4 D[NTW];
 #pragma unroll
     for (int x = 0; x < NTW; ++x) {
-        const int mt = wave + 4 * x;
+        const int mt = wave + NCW * x;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int c = 16 * mt + 4 * g + i;
-            D[x][i] = (wave < 4 && dfinal != nullptr) ? dfinal[((size_t)bh * DV + j0 + l16) * DK + c] : 0.f;
+            D[x][i] = (wave < NCW && dfinal != nullptr) ? dfinal[((size_t)bh * DV + j0 + l16) * DK + c] : 0.f;
         }
     }
     // A chunk's operands, read from its ring slot and split one chunk ahead, off the chain:
@@ -154,7 +154,7 @@ __global__ __launch_bounds__(320) void kda_bwd_rev_kernel(
         o.fK = ldexp2(1.f, -rS[2]);
 #pragma unroll
         for (int x = 0; x < NTW; ++x) {
-            const int mt = wave + 4 * x;
+            const int mt = wave + NCW * x;
             float ka[4], wa[4], qa[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -172,7 +172,7 @@ __global__ __launch_bounds__(320) void kda_bwd_rev_kernel(
         return o;
     };
 
-    if (wave == 4) {  // chunks NC-1 .. NC-NSLOT+1 into the ring, the chunks after them touched
+    if (wave == NCW) {  // chunks NC-1 .. NC-NSLOT+1 into the ring, the chunks after them touched
 #pragma unroll
         for (int s = 0; s < NSLOT - 1; ++s)
             if (NC - 1 - s >= 0) issue(NC - 1 - s, s);
@@ -181,15 +181,15 @@ __global__ __launch_bounds__(320) void kda_bwd_rev_kernel(
     }
     barrier_lds();  // chunk NC-1 has landed
     Ops op;
-    if (wave < 4 && NC > 0) op = prefetch(0);
+    if (wave < NCW && NC > 0) op = prefetch(0);
 
-    // One barrier per chunk: it publishes the four parts of P (two alternating sets, so a wave
+    // One barrier per chunk: it publishes the parts of P (two alternating sets, so a wave
     // that runs ahead never overwrites a set another wave still reads) and chunk n - 1's slot;
     // the loader refills the slot of chunk n + 1, whose operands were read two barriers before.
     for (int it = 0; it < NC; ++it) {
         const int n = NC - 1 - it, ps = it & 1;
         f32x4 qdo[NTW];
-        if (wave == 4) {
+        if (wave == NCW) {
             if (n - (NSLOT - 1) >= 0) issue(n - (NSLOT - 1), (it + NSLOT - 1) % NSLOT);
             if (n - PF >= 0) touch(n - PF);
             wait_next(n);  // chunk n - 1 has landed (the ones after it may be in flight)
@@ -212,7 +212,7 @@ __global__ __launch_bounds__(320) void kda_bwd_rev_kernel(
             // dS' of this chunk's end, for the chunk-parallel stage: dstates[bh][n][value][key]
 #pragma unroll
             for (int x = 0; x < NTW; ++x) {
-                const int mt = wave + 4 * x;
+                const int mt = wave + NCW * x;
                 *reinterpret_cast<f32x4 *>(dstates + (((size_t)bh * NC + n) * DV + j0 + l16) * DK + 16 * mt + 4 * g) = D[x];
             }
             // diag(gamma) dS' + Qbar^T dO: the part of the update that does not wait for P
@@ -226,13 +226,19 @@ __global__ __launch_bounds__(320) void kda_bwd_rev_kernel(
             }
         }
         barrier_lds();  // the four parts of P are in; chunk n - 1 has landed
-        if (wave < 4) {
-            const f32x4 p0 = sPp[ps][0][lane], p1 = sPp[ps][1][lane], p2 = sPp[ps][2][lane], p3 = sPp[ps][3][lane];
+        if (wave < NCW) {
+            f32x4 pw[NCW];
+#pragma unroll
+            for (int w = 0; w < NCW; ++w) pw[w] = sPp[ps][w][lane];
             const Ops cur = op;
             if (n >= 1) op = prefetch((it + 1) % NSLOT);  // chunk n - 1's operands, read during the update
+#pragma unroll
+            for (int h = NCW / 2; h >= 1; h /= 2)
+#pragma unroll
+                for (int w = 0; w < h; ++w) pw[w] += pw[w + h];
             float pv[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) pv[i] = (p0[i] + p1[i]) + (p2[i] + p3[i]);
+            for (int i = 0; i < 4; ++i) pv[i] = pw[0][i];
             bf16x4 ph, pl;
             split4(pv, ph, pl);
             // dS = diag(gamma) dS' + Qbar^T dO - W^T P  (rows of this wave's key tiles)
@@ -247,10 +253,10 @@ __global__ __launch_bounds__(320) void kda_bwd_rev_kernel(
             }
         }
     }
-    if (dinit != nullptr && wave < 4) {
+    if (dinit != nullptr && wave < NCW) {
 #pragma unroll
         for (int x = 0; x < NTW; ++x) {
-            const int mt = wave + 4 * x;
+            const int mt = wave + NCW * x;
             *reinterpret_cast<f32x4 *>(dinit + ((size_t)bh * DV + j0 + l16) * DK + 16 * mt + 4 * g) = D[x];
         }
     }

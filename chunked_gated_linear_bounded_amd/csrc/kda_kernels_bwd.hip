@@ -20,7 +20,7 @@ static hipError_t launch_bwd_t(const LaunchArgs &p) {
                            reinterpret_cast<const unsigned char *>(p.workspace),
                            reinterpret_cast<const E *>(p.dout), p.dfinal, p.T, BH, p.dstates, p.dinit);
     else
-        hipLaunchKernelGGL((kda_bwd_rev_kernel<DK, DV>), rgrid, dim3(320), 0, p.stream,
+        hipLaunchKernelGGL((kda_bwd_rev_kernel<DK, DV>), rgrid, dim3((DK / 16 + 1) * 64), 0, p.stream,
                            reinterpret_cast<const unsigned char *>(p.workspace),
                            reinterpret_cast<const E *>(p.dout), p.dfinal, p.T, BH, p.dstates, p.dinit);
     hipError_t e = hipGetLastError();
