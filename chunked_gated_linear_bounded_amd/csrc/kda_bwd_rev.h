@@ -15,7 +15,7 @@
 //     K^ dS' over its tile, and one barrier per chunk hands the parts to everyone;
 //   - each chunk's operands are read from the ring and split during the previous chunk's update,
 //     and Qbar^T dO, which does not depend on dS', before the barrier.
-// One more wave streams each chunk's record and dout block into a ring of LDS slots (five where they
+// One more wave streams each chunk's record and dout block into a ring of LDS slots (four where they
 // fit) with direct global->LDS loads, as many chunks ahead as the ring holds, touches the lines
 // of a chunk eight ahead into L2 (each slice a share of them) so that the ring's loads hit there,
 // and alone waits on its memory counter.
@@ -58,10 +58,10 @@ __global__ __launch_bounds__((DK / 16 + 1) * 64) void kda_bwd_rev_kernel(
     constexpr int NBLK = (NU + 63) / 64;                     // 1 KiB direct-load blocks
     constexpr int RB = NBLK * 1024, SLOT = RB + 1024;        // record + dout block
     constexpr int NDMA = NBLK + 1;                           // loader instructions per chunk
-    // ring depth: as many slots as the LDS and the 6-bit memory counter allow (the loader keeps
-    // NSLOT - 2 chunks in flight beyond the one it waits for), at most 5
-    constexpr int NSLOT = (5 * SLOT <= 150 * 1024 && 1 + 3 * (NDMA + 1) <= 63) ? 5
-                        : (4 * SLOT <= 150 * 1024 && 1 + 2 * (NDMA + 1) <= 63) ? 4 : 3;
+    // ring depth: four slots where they fit in 80 KB (the loader keeps NSLOT - 2 chunks in flight
+    // beyond the one it waits for); the work-group then leaves room in LDS for one of the state
+    // recompute (about 62 KB), which runs at the same time on another stream
+    constexpr int NSLOT = (4 * SLOT <= 80 * 1024 && 1 + 2 * (NDMA + 1) <= 63) ? 4 : 3;
     // vmem instructions the loader issues after a chunk's ring loads before it waits for that
     // chunk: its L2 touch in the same iteration, then a ring chunk and a touch per iteration
     constexpr int AFTER = 1 + (NSLOT - 2) * (NDMA + 1);
