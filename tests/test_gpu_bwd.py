@@ -108,6 +108,19 @@ def test_bwd_single_chunk_odd_batch_and_heads(io):
     _run_and_check(w, inp, dout, S0, dF)
 
 
+@pytest.mark.parametrize("T", [32, 48, 144])
+def test_bwd_short_sequences_and_a_partial_head_group(T):
+    """2, 3 and 9 16-token chunks (fewer than the reverse pass's ring holds and than its L2 look-ahead,
+    then just past it) over 9 heads (one group of eight heads on an XCD and one partial group), bf16,
+    d=128, with an initial state and a final-state gradient: every head against the oracle."""
+    w = KI.Workload("bwt%d" % T, 1, 9, T, 128, 128, 16, "bf16", 2.0, False, 140 + T)
+    inp = {n: t.cuda() for n, t in KI.make_inputs(w).items()}
+    dout, dF = (t.cuda() for t in KI.make_grads(w))
+    S0 = torch.randn(1, 9, 128, 128, device="cuda") * 0.5
+    _say("backward short sequence", T)
+    _run_and_check(w, inp, dout, S0, dF)
+
+
 def test_bwd_empty_sequence():
     """No tokens: the only gradient is the initial state's, and it is the final state's."""
     w = KI.Workload("bw0", 1, 2, 0, 64, 64, 16, "bf16", 1.0, False, 132)
