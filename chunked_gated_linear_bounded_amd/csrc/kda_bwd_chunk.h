@@ -29,12 +29,21 @@ struct HL8 {  // one 32-deep block of an MFMA operand, split: x = hi + lo
     bf16x8 h, l;
 };
 
+typedef __attribute__((ext_vector_type(2))) float f32x2_;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_;
+
+// Two values per packed conversion: hi = bf16(x), lo = bf16(x - hi).
 __device__ __forceinline__ HL8 split8(const float (&x)[8]) {
     HL8 s;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        s.h[j] = (__bf16)x[j];
-        s.l[j] = (__bf16)(x[j] - (float)s.h[j]);
+    for (int p = 0; p < 4; ++p) {
+        const f32x2_ v = {x[2 * p], x[2 * p + 1]};
+        const bf16x2_ hp = __builtin_convertvector(v, bf16x2_);
+        const bf16x2_ lp = __builtin_convertvector(v - __builtin_convertvector(hp, f32x2_), bf16x2_);
+        s.h[2 * p] = hp[0];
+        s.h[2 * p + 1] = hp[1];
+        s.l[2 * p] = lp[0];
+        s.l[2 * p + 1] = lp[1];
     }
     return s;
 }
