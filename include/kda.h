@@ -262,7 +262,10 @@ int kda_chunk_fwd_noalloc(const void *q, const void *k, const void *v, const voi
  * recomputed chunk records and two float32 states per 16-token chunk and head,
  * B*H*T/16 * (record + 2*dk*dv*4) bytes; 0 for an invalid problem).  No output
  * may alias an input.  Validation, alignment (16 bytes; beta: element size,
- * dbeta: 4) and asynchrony as above. */
+ * dbeta: 4) and asynchrony as above.  Part of the work (the reverse pass over the chunks)
+ * runs on a second stream the library makes once per GPU (default priority), forked from
+ * stream and joined back to it with events inside the call: work enqueued on stream after
+ * the call still starts only once all of it is done. */
 size_t kda_chunk_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int io_dtype);
 int kda_chunk_bwd(const void *q, const void *k, const void *v, const void *a, const void *beta,
                   float g_min, int B, int H, int T, int dk, int dv, int io_dtype, int gate_mode,
