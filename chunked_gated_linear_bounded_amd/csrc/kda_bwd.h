@@ -25,6 +25,31 @@
 
 namespace kda {
 
+// 16x16x16 bf16 MFMA: lane (g, m) supplies A[m][4 g .. 4 g + 3] and lane (g, n) B[4 g .. 4 g + 3][n],
+// which is where an accumulator tile holds rows 4 g .. 4 g + 3 of column n.
+__device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+
+// x = hi + lo in bf16 (about 16 significand bits, the full fp32 range), two values per packed
+// conversion.  V: float[4] or f32x4.
+template <typename V>
+__device__ __forceinline__ void split4(const V &x, bf16x4 &h, bf16x4 &l) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const f32x2 v = {x[2 * p], x[2 * p + 1]};
+        const bf16x2 hp = __builtin_convertvector(v, bf16x2);
+        const bf16x2 lp = __builtin_convertvector(v - __builtin_convertvector(hp, f32x2), bf16x2);
+        h[2 * p] = hp[0];
+        h[2 * p + 1] = hp[1];
+        l[2 * p] = lp[0];
+        l[2 * p + 1] = lp[1];
+    }
+}
+
 // acc += A (16 x K) B (K x 16) on fp32 MFMA: A(m, k) and B(k, n) return A[m][k] and B[k][n]
 // (m, n in 0..15).  In v_mfma_f32_16x16x4f32 lane l supplies A[l%16][k0 + l/16] and
 // B[k0 + l/16][l%16]; acc[i] is D[4 (l/16) + i][l%16].

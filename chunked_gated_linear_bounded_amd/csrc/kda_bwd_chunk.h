@@ -14,14 +14,18 @@
 //   - every operand that all waves share (K e^{G-G0}, K e^{G0-G}, Q e^{G-G0}, K e^G, K^, W, U, dU,
 //     dW) is formed once, split once and kept in LDS as hi and lo rows, which an MFMA operand reads
 //     as one 16-byte row piece per lane;
-//   - the 16-deep products (W, U~, dU, dX, dY, the solve, dA, the pairwise terms) run on fp32
-//     16x16x4 MFMAs, taking an accumulator tile straight from registers where the product needs it
-//     as its B operand (lane group g supplies k = 4 g + i in step i, which is where the
-//     accumulator holds row 4 g + i);
+//   - the 16-deep products of the pairwise terms (dM, dP against the scaled q and k) run on
+//     16x16x16 bf16 MFMAs with both fp32 operands split into hi + lo (three MFMAs; one fp32
+//     16x16x4 MFMA takes four times the cycles of a bf16 16x16x16 one for a quarter of the depth).
+//     The others (the solve, W, U~, M^T dO, dX, dY, dA) stay on fp32 16x16x4 MFMAs: dv = diag(b)
+//     T^T dU is small beside the terms of dU, and T = (I + A)^-1 and M can hold entries far above 1,
+//     so a 16-bit operand anywhere in dU or a product with T costs dv, dk, da and dbeta their
+//     precision.  Either way an accumulator tile is a B operand as it stands (lane group g holds
+//     rows 4 g .. 4 g + 3 of its column, the B layout of both MFMAs);
 //   - T = (I + A)^-1 is the exact finite series (I - N)(I + N^2)(I + N^4)(I + N^8), N = A strictly
 //     lower, on one wave while the others form dQ~.
 #pragma once
-#include "kda_device.h"
+#include "kda_bwd.h"
 
 namespace kda {
 
@@ -29,17 +33,14 @@ struct HL8 {  // one 32-deep block of an MFMA operand, split: x = hi + lo
     bf16x8 h, l;
 };
 
-typedef __attribute__((ext_vector_type(2))) float f32x2_;
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_;
-
 // Two values per packed conversion: hi = bf16(x), lo = bf16(x - hi).
 __device__ __forceinline__ HL8 split8(const float (&x)[8]) {
     HL8 s;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-        const f32x2_ v = {x[2 * p], x[2 * p + 1]};
-        const bf16x2_ hp = __builtin_convertvector(v, bf16x2_);
-        const bf16x2_ lp = __builtin_convertvector(v - __builtin_convertvector(hp, f32x2_), bf16x2_);
+        const f32x2 v = {x[2 * p], x[2 * p + 1]};
+        const bf16x2 hp = __builtin_convertvector(v, bf16x2);
+        const bf16x2 lp = __builtin_convertvector(v - __builtin_convertvector(hp, f32x2), bf16x2);
         s.h[2 * p] = hp[0];
         s.h[2 * p + 1] = hp[1];
         s.l[2 * p] = lp[0];
@@ -123,6 +124,26 @@ __device__ __forceinline__ f32x4 mm16(f32x4 acc, const FA &a, const FB &b) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a(i), b(i), acc, 0, 0, 0);
     return acc;
+}
+
+// The same operands for a 16x16x16 bf16 MFMA (f(i), i = 0..3: this lane's k = 4 g + i), split.
+struct HL4 {
+    bf16x4 h, l;
+};
+template <typename F>
+__device__ __forceinline__ HL4 split_at(const F &f) {
+    float x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = f(i);
+    HL4 s;
+    split4(x, s.h, s.l);
+    return s;
+}
+// acc += A B over 16, both operands split (lo x lo dropped).
+__device__ __forceinline__ f32x4 mm16_hl(f32x4 acc, const HL4 &a, const HL4 &b) {
+    acc = mfma16(a.h, b.h, acc);
+    acc = mfma16(a.l, b.h, acc);
+    return mfma16(a.h, b.l, acc);
 }
 
 // Row block of the stored state [DV][DK] for value rows j0 .. j0 + 15 (B operand of a key-deep
@@ -487,6 +508,10 @@ __global__ __launch_bounds__(256, 2) void kda_bwd_chunk16_kernel(
     // ---------------------------------------------------------------- pairwise terms of M and P, outputs
     // The 16-deep B operands are this lane's own rows 4g+i of its column, as are the outputs.
     float *sdg = reinterpret_cast<float *>(bX);  // dG [C][LG], K e^G no longer needed
+    const HL4 dMa = split_at([&](int i) { return sdM[l16 * P16 + 4 * g + i]; });    // dM
+    const HL4 dMb = split_at([&](int i) { return sdM[(4 * g + i) * P16 + l16]; });  // dM^T
+    const HL4 dPa = split_at([&](int i) { return sdT[l16 * P16 + 4 * g + i]; });    // dP
+    const HL4 dPb = split_at([&](int i) { return sdT[(4 * g + i) * P16 + l16]; });  // dP^T
 #pragma unroll
     for (int t = 0; t < TK; ++t) {
         const int c = 16 * (wave + NW * t) + l16;
@@ -501,13 +526,11 @@ __global__ __launch_bounds__(256, 2) void kda_bwd_chunk16_kernel(
             kr[i] = (float)sK[r * LK + c];
             qr[i] = (float)sQ[r * LK + c];
         }
-        auto km = [&](int i) { return kr[i] * em[i]; };
-        const f32x4 x1 = mm16(zero, [&](int i) { return sdM[l16 * P16 + 4 * g + i]; }, km);   // dM Km
-        const f32x4 x2 = mm16(zero, [&](int i) { return sdM[(4 * g + i) * P16 + l16]; },
-                              [&](int i) { return qr[i] * ep[i]; });                          // dM^T Qp
-        const f32x4 x3 = mm16(zero, [&](int i) { return sdT[l16 * P16 + 4 * g + i]; }, km);   // dP Km
-        const f32x4 x4 = mm16(zero, [&](int i) { return sdT[(4 * g + i) * P16 + l16]; },
-                              [&](int i) { return kr[i] * ep[i]; });                          // dP^T Kp
+        const HL4 km = split_at([&](int i) { return kr[i] * em[i]; });
+        const f32x4 x1 = mm16_hl(zero, dMa, km);                                                // dM Km
+        const f32x4 x2 = mm16_hl(zero, dMb, split_at([&](int i) { return qr[i] * ep[i]; }));  // dM^T Qp
+        const f32x4 x3 = mm16_hl(zero, dPa, km);                                                // dP Km
+        const f32x4 x4 = mm16_hl(zero, dPb, split_at([&](int i) { return kr[i] * ep[i]; }));  // dP^T Kp
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = 4 * g + i;

@@ -24,28 +24,6 @@
 
 namespace kda {
 
-__device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-}
-
-typedef __attribute__((ext_vector_type(2))) float f32x2;
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-
-// x = hi + lo in bf16, two values per packed conversion.  V: float[4] or f32x4.
-template <typename V>
-__device__ __forceinline__ void split4(const V &x, bf16x4 &h, bf16x4 &l) {
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-        const f32x2 v = {x[2 * p], x[2 * p + 1]};
-        const bf16x2 hp = __builtin_convertvector(v, bf16x2);
-        const bf16x2 lp = __builtin_convertvector(v - __builtin_convertvector(hp, f32x2), bf16x2);
-        h[2 * p] = hp[0];
-        h[2 * p + 1] = hp[1];
-        l[2 * p] = lp[0];
-        l[2 * p + 1] = lp[1];
-    }
-}
-
 template <int DK, int DV>
 __global__ __launch_bounds__((DK / 16 + 1) * 64) void kda_bwd_rev_kernel(
     const unsigned char *__restrict__ ws, const __bf16 *__restrict__ dout, const float *__restrict__ dfinal, int T,
