@@ -24,6 +24,19 @@
 
 namespace kda {
 
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(4))) _Float16 f16x4_;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// gfx950 LDS transpose read of 16-bit values: within each group of 16 lanes, slot k of lane i is
+// value i % 4 of the 8 bytes that lane 4 k + i / 4 of the group addresses.  The result is taken
+// as a whole vector of the wanted type: bit-casting its 16-bit elements one at a time compiles
+// (with this compiler) to code that converts slot 0 only.
+template <typename V>
+__device__ __forceinline__ V ld_tr16(const lds_u8 *p) {
+    return __builtin_bit_cast(V, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p));
+}
+
 template <int DK, int DV>
 __global__ __launch_bounds__((DK / 16 + 1) * 64) void kda_bwd_rev_kernel(
     const unsigned char *__restrict__ ws, const __bf16 *__restrict__ dout, const float *__restrict__ dfinal, int T,
@@ -113,6 +126,11 @@ __global__ __launch_bounds__((DK / 16 + 1) * 64) void kda_bwd_rev_kernel(
     // K^[r][16 mt + 4 g + i] (A of K^ dS'), W^T and Qbar^T [16 mt + r][4 g + i] (A of the update),
     // as stored (their power-of-two scales fK, -fW, fQ are applied to the products), gamma of the
     // wave's key rows, the dout block as the B operand of Qbar^T dO.
+    // The record keeps four consecutive rows of a column together (the operand order of the
+    // forward's products), and these operands need four consecutive columns of a row, so each is
+    // one transpose read: lane (g, s) addresses the 8 bytes of the stored run that lane
+    // (g, 4 (s & 3) + r) needs in slot s >> 2 (r = 0..3).  Four 2-byte reads per operand instead
+    // met every bank four times over.
     struct Ops {
         bf16x4 kh[NTW], kl[NTW], wh[NTW], wl[NTW], qh[NTW], ql[NTW], ob;
         f32x4 gm[NTW];
@@ -121,32 +139,36 @@ __global__ __launch_bounds__((DK / 16 + 1) * 64) void kda_bwd_rev_kernel(
     auto prefetch = [&](int s) {
         Ops o;
         const unsigned char *cur = sRing + s * SLOT;
-        const _Float16 *rWT = reinterpret_cast<const _Float16 *>(cur + L.wt);
-        const _Float16 *rQB = reinterpret_cast<const _Float16 *>(cur + L.qbt);
-        const _Float16 *rKH = reinterpret_cast<const _Float16 *>(cur + L.kh);
+        const lds_u8 *curl = lds_base(sRing) + s * SLOT;
         const float *rG = reinterpret_cast<const float *>(cur + L.gam);
         const int *rS = reinterpret_cast<const int *>(cur + L.scl);
-        const __bf16 *rdO = reinterpret_cast<const __bf16 *>(cur + RB);  // [row][16]
         o.fW = -ldexp2(1.f, -rS[0]);
         o.fQ = ldexp2(1.f, -rS[1]);
         o.fK = ldexp2(1.f, -rS[2]);
+        const int p = l16 & 3, kk = l16 >> 2;  // this lane addresses run 16 p + 4 g + kk of a tile
 #pragma unroll
         for (int x = 0; x < NTW; ++x) {
             const int mt = wave + NCW * x;
+            // K^ [token][key]: key tile mt, tile rows 0..15 (C = 16: the first tile of its pair);
+            // W^T, Qbar^T [key][token]: key tile mt, half mt & 1 of pair mt / 2
+            const f16x4_ kr = ld_tr16<f16x4_>(curl + L.kh + 16 * (mt * 64 + 16 * p + 4 * g + kk));
+            const int wo = 16 * ((mt >> 1) * 64 + 16 * p + 4 * g + kk) + 8 * (mt & 1);
+            const f16x4_ wr = ld_tr16<f16x4_>(curl + L.wt + wo);
+            const f16x4_ qr = ld_tr16<f16x4_>(curl + L.qbt + wo);
             float ka[4], wa[4], qa[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                ka[i] = (float)rKH[pair_offset(l16, 16 * mt + 4 * g + i, NDK)];
-                wa[i] = (float)rWT[pair_offset(16 * mt + l16, 4 * g + i, 1)];
-                qa[i] = (float)rQB[pair_offset(16 * mt + l16, 4 * g + i, 1)];
+                ka[i] = (float)kr[i];
+                wa[i] = (float)wr[i];
+                qa[i] = (float)qr[i];
             }
             split4(ka, o.kh[x], o.kl[x]);
             split4(wa, o.wh[x], o.wl[x]);
             split4(qa, o.qh[x], o.ql[x]);
             o.gm[x] = *reinterpret_cast<const f32x4 *>(rG + 16 * mt + 4 * g);
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o.ob[i] = rdO[(4 * g + i) * 16 + l16];
+        // dout block [token][16 values]: rows 4 g .. 4 g + 3 of column l16
+        o.ob = ld_tr16<bf16x4>(curl + RB + 2 * (16 * (4 * g + kk) + 4 * p));
         return o;
     };
 
