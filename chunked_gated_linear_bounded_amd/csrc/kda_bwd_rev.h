@@ -24,18 +24,7 @@
 
 namespace kda {
 
-typedef __attribute__((ext_vector_type(4))) short s16x4;
 typedef __attribute__((ext_vector_type(4))) _Float16 f16x4_;
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-// gfx950 LDS transpose read of 16-bit values: within each group of 16 lanes, slot k of lane i is
-// value i % 4 of the 8 bytes that lane 4 k + i / 4 of the group addresses.  The result is taken
-// as a whole vector of the wanted type: bit-casting its 16-bit elements one at a time compiles
-// (with this compiler) to code that converts slot 0 only.
-template <typename V>
-__device__ __forceinline__ V ld_tr16(const lds_u8 *p) {
-    return __builtin_bit_cast(V, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p));
-}
 
 template <int DK, int DV>
 __global__ __launch_bounds__((DK / 16 + 1) * 64) void kda_bwd_rev_kernel(

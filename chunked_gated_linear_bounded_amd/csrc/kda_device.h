@@ -36,6 +36,20 @@ typedef __attribute__((address_space(3))) unsigned char lds_u8;
 template <typename T>
 __device__ __forceinline__ lds_u8 *lds_base(T *shared_object) { return (lds_u8 *)shared_object; }
 
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// gfx950 LDS transpose read of 16-bit values: within each group of 16 lanes, slot k of lane i is
+// value i % 4 of the 8 bytes (8-byte aligned) that lane 4 k + i / 4 of the group addresses.  So
+// four consecutive rows of one column of a row-major 16-bit block reach lane (g, n) when lane
+// (g, s) addresses row r0 + (s >> 2), columns c0 + 4 (s & 3) .. + 3: slot k = X[r0 + k][c0 + n].
+// The result is taken as a whole vector of the wanted type: bit-casting its 16-bit elements one
+// at a time compiles (with this compiler) to code that converts slot 0 only.
+template <typename V>
+__device__ __forceinline__ V ld_tr16(const lds_u8 *p) {
+    return __builtin_bit_cast(V, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p));
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 

@@ -509,10 +509,20 @@ __global__ __launch_bounds__((IntraCfg<C, DK, DV, F32>::THREADS), 4) __attribute
         const int st = tix / NDK, ct = tix % NDK;
         const int c = 16 * ct + l16;
         const float glast = sG[(C - 1) * PG + c];
+        float kv[4];  // k of rows 16 st + 4 g + i, column c
+        if constexpr (!F32) {
+            const bf16x4 t = ld_tr16<bf16x4>(lds_base(smem) + Cfg::OFF_R2 +
+                                             2 * ((16 * st + 4 * g + (l16 >> 2)) * PQ + 16 * ct + 4 * (l16 & 3)));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) kv[i] = (float)t[i];
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) kv[i] = to_f(sK[(16 * st + 4 * g + i) * PQ + c]);
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int s = 16 * st + 4 * g + i;
-            khr[xi][i] = to_f(sK[s * PQ + c]) * ex2(glast - sG[s * PG + c]);
+            khr[xi][i] = kv[i] * ex2(glast - sG[s * PG + c]);
             khmax = fmaxf(khmax, fabsf(khr[xi][i]));
         }
     }
@@ -673,6 +683,30 @@ __global__ __launch_bounds__((IntraCfg<C, DK, DV, F32>::THREADS), 4) __attribute
     // below the diagonal only; the one block above the diagonal that such a K-block spans
     // (column tile 2 kb + 1 = rt + 1) is zero and is never read.
     using FM = Frag<OH>;  // fp16 (fp32 with fp32 I/O)
+    // B operand from column c0 + l16 of a row-major [C][pitch] block of E at byte offset off in
+    // LDS: token slots 32 kb + 4 g + j (j < 4) and 32 kb + 16 + 4 g + j - 4, zero past C.  With
+    // bf16, two transpose reads of four rows each.
+    auto col_frag = [&](int off, int pitch, int kb, int c0) {
+        if constexpr (!F32) {
+            const lds_u8 *base = lds_base(smem) + off;
+            const int r = 32 * kb + 4 * g + (l16 >> 2), c = c0 + 4 * (l16 & 3);
+            const bf16x4 lo = ld_tr16<bf16x4>(base + 2 * (r * pitch + c));
+            bf16x4 hi = {};
+            if (32 * kb + 16 < C) hi = ld_tr16<bf16x4>(base + 2 * ((r + 16) * pitch + c));
+            F f;
+            f.v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            return f;
+        } else {
+            const E *blk = reinterpret_cast<const E *>(smem + off);
+            float x[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int s = 32 * kb + (j < 4 ? 4 * g + j : 16 + 4 * g + j - 4);
+                x[j] = (s < C) ? to_f(blk[s * pitch + c0 + l16]) : 0.f;
+            }
+            return F::make(x);
+        }
+    };
     // Two passes, so that the T and M fragments are never held together: the first forms W^T and
     // W of this wave's dk tile and U~ of its dv slice from T diag(beta), the second the products
     // with M.
@@ -706,15 +740,7 @@ __global__ __launch_bounds__((IntraCfg<C, DK, DV, F32>::THREADS), 4) __attribute
             if (ct >= NDK) continue;
             F kf[NTKB];  // (K e^G): lane l holds column c = 16 ct + l16 at token slots
 #pragma unroll
-            for (int kb = 0; kb < NTKB; ++kb) {
-                float x[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int s = 32 * kb + (j < 4 ? 4 * g + j : 16 + 4 * g + j - 4);
-                    x[j] = (s < C) ? to_f(sK[s * PQ + 16 * ct + l16]) : 0.f;
-                }
-                kf[kb] = F::make(x);
-            }
+            for (int kb = 0; kb < NTKB; ++kb) kf[kb] = col_frag(Cfg::OFF_R2, PQ, kb, 16 * ct);
 #pragma unroll
             for (int rt = 0; rt < NT; ++rt) {
                 f32x4 accT = {0.f, 0.f, 0.f, 0.f}, accW = {0.f, 0.f, 0.f, 0.f};
@@ -736,15 +762,7 @@ __global__ __launch_bounds__((IntraCfg<C, DK, DV, F32>::THREADS), 4) __attribute
             if (vt >= NDV) continue;
             F vf[NTKB];  // V: lane l holds column 16 vt + l16 at token slots
 #pragma unroll
-            for (int kb = 0; kb < NTKB; ++kb) {
-                float x[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int s = 32 * kb + (j < 4 ? 4 * g + j : 16 + 4 * g + j - 4);
-                    x[j] = (s < C) ? to_f(sV[s * PV + 16 * vt + l16]) : 0.f;
-                }
-                vf[kb] = F::make(x);
-            }
+            for (int kb = 0; kb < NTKB; ++kb) vf[kb] = col_frag(C * PA * 4, PV, kb, 16 * vt);
 #pragma unroll
             for (int rt = 0; rt < NT; ++rt) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
