@@ -314,9 +314,18 @@ __device__ __forceinline__ void barrier_lds() {
 // ---------------------------------------------------------------- the gate
 // g in log2 units (g * log2 e).  Bounded: g_min * sigmoid(a).  Log-sigmoid:
 // log sigmoid(a) = -(max(-a, 0) + log(1 + e^-|a|)), never overflows.
+template <bool LOGSIG>
+__device__ __forceinline__ float gate_log2_t(float a, float gmin2) {
+    float g;
+    if constexpr (!LOGSIG) g = gmin2 * rcpf(1.f + ex2(-a * kLog2e));
+    else g = -(fmaxf(-a, 0.f) * kLog2e + lg2(1.f + ex2(-fabsf(a) * kLog2e)));
+    // rounded here: a prefix sum adds it as a value and never fuses its product into an fma, so
+    // every caller (with or without a guard on the row) sums the same values
+    asm volatile("" : "+v"(g));
+    return g;
+}
 __device__ __forceinline__ float gate_log2(float a, float gmin2, int logsig) {
-    if (!logsig) return gmin2 * rcpf(1.f + ex2(-a * kLog2e));
-    return -(fmaxf(-a, 0.f) * kLog2e + lg2(1.f + ex2(-fabsf(a) * kLog2e)));
+    return logsig ? gate_log2_t<true>(a, gmin2) : gate_log2_t<false>(a, gmin2);
 }
 
 // Gate and inclusive prefix sum over the C rows of one chunk, per channel, held in registers:
@@ -350,8 +359,15 @@ struct GateScan {
         }
     }
 
-    // G over the chunk; rows from nrow on get g = 0, so G stays flat past the last token
+    // G over the chunk; rows from nrow on get g = 0, so G stays flat past the last token.  One
+    // branch on the gate form for the whole scan (a per-element choice compiles to a branch pair
+    // per element).
     __device__ __forceinline__ void finish(float gmin2, int logsig, float *sG, int ldG, int tid, int nrow) {
+        if (logsig) finish_t<true>(gmin2, sG, ldG, tid, nrow);
+        else finish_t<false>(gmin2, sG, ldG, tid, nrow);
+    }
+    template <bool LS>
+    __device__ __forceinline__ void finish_t(float gmin2, float *sG, int ldG, int tid, int nrow) {
         const int rg = tid >> 4, m = tid & 15;
 #pragma unroll
         for (int p = 0; p < NPASS; ++p) {
@@ -363,7 +379,7 @@ struct GateScan {
                 const E *e = reinterpret_cast<const E *>(&raw[p][j]);
 #pragma unroll
                 for (int c = 0; c < VEC; ++c)
-                    gv[j][c] = (m * RPL + j < nrow ? gate_log2(to_f(e[c]), gmin2, logsig) : 0.f) + (j ? gv[j - 1][c] : 0.f);
+                    gv[j][c] = (m * RPL + j < nrow ? gate_log2_t<LS>(to_f(e[c]), gmin2) : 0.f) + (j ? gv[j - 1][c] : 0.f);
             }
             scan_store(gv, sG, ldG, gi, m);
         }

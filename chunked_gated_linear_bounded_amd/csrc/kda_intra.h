@@ -167,6 +167,16 @@ struct LowRankGate {
 #pragma unroll
                 for (int ci = 0; ci < NCW; ++ci) acc[rt][ci] = mma(fa[sl][rt], fb[sl][ci], acc[rt][ci]);
         }
+        // one branch on the gate form for the whole scan
+        if (logsig) scan<true>(acc, A, gmin2, sG, ldG, lane);
+        else scan<false>(acc, A, gmin2, sG, ldG, lane);
+    }
+
+    // the gate of each pre-activation and its prefix sum down the chunk, stored as G
+    template <bool LS>
+    __device__ __forceinline__ void scan(const f32x4 (&acc)[NT][NCW], const float *__restrict__ A, float gmin2,
+                                         float *sG, int ldG, int lane) {
+        const int g = lane >> 4, l16 = lane & 15;
 #pragma unroll
         for (int ci = 0; ci < NCW; ++ci) {
             const int ct = wave + 4 * ci;
@@ -178,7 +188,7 @@ struct LowRankGate {
             for (int rt = 0; rt < NT; ++rt) {
                 float x[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) x[i] = gate_log2(acc[rt][ci][i] * eA, gmin2, logsig) + (i ? x[i - 1] : 0.f);
+                for (int i = 0; i < 4; ++i) x[i] = gate_log2_t<LS>(acc[rt][ci][i] * eA, gmin2) + (i ? x[i - 1] : 0.f);
                 const float own = x[3];  // inclusive scan of the lane totals over the lane groups
                 float t = own;
                 const float u1 = __shfl_up(t, 16, 64);
