@@ -329,20 +329,25 @@ __device__ __forceinline__ float gate_log2(float a, float gmin2, int logsig) {
 }
 
 // Gate and inclusive prefix sum over the C rows of one chunk, per channel, held in registers:
-// G[r][c] = sum_{s <= r} g2[s][c] (log2 units).  256 threads; the 16 lanes of each row group
-// rg = tid / 16 take one group of VEC channels (rg + 16 p in pass p) and lane m = tid % 16
-// takes the RPL = C / 16 consecutive rows m RPL ...  Each lane loads its values with 16-byte
-// loads, sums its own rows, and the lane totals are prefix-summed across the row group with
-// four DPP row shifts.  load() only issues the loads, so a caller can put other loads in
-// flight before finish() consumes them.
-template <int C, int DK, typename E>
+// G[r][c] = sum_{s <= r} g2[s][c] (log2 units).  NTH threads (256, or 512 with 16-bit inputs);
+// the 16 lanes of each row group rg = tid / 16 take one group of VEC channels (rg + NTH / 16 p
+// in pass p) and lane m = tid % 16 takes the RPL = C / 16 consecutive rows m RPL ...  Each lane
+// loads its values with 16-byte loads (8-byte ones with 512 threads, so that all of them share
+// the work), sums its own rows, and the lane totals are prefix-summed across the row group with
+// four DPP row shifts.  load() only issues the loads, so a caller can put other loads in flight
+// before finish() consumes them.
+template <int C, int DK, typename E, int NTH = 256>
 struct GateScan {
-    static constexpr int VEC = 16 / (int)sizeof(E);  // channels per 16-byte load
-    static constexpr int NG = DK / VEC;              // channel groups
-    static constexpr int NPASS = (NG + 15) / 16;
-    static constexpr int RPL = C / 16;               // rows per lane
-    static_assert(C % 16 == 0 && DK % VEC == 0, "chunk and channel tiling");
-    uint4 raw[NPASS][RPL];
+    static_assert(NTH == 256 || (NTH == 512 && sizeof(E) == 2), "256 threads, or 512 with 16-bit inputs");
+    static constexpr int LB = NTH == 512 ? 8 : 16;    // bytes per load
+    static constexpr int VEC = LB / (int)sizeof(E);   // channels per load
+    static constexpr int NG = DK / VEC;               // channel groups
+    static constexpr int NRG = NTH / 16;              // row groups
+    static constexpr int NPASS = (NG + NRG - 1) / NRG;
+    static constexpr int RPL = C / 16;
+    using LT = typename std::conditional<LB == 16, uint4, uint2>::type;               // rows per lane
+    static_assert(C % 16 == 0 && DK % VEC == 0 && VEC % 4 == 0, "chunk and channel tiling");
+    LT raw[NPASS][RPL];
 
     // a: this chunk's [C][DK] block, of which the first nrow rows are tokens (the others are
     // never read: their loads repeat the last token row)
@@ -350,11 +355,11 @@ struct GateScan {
         const int rg = tid >> 4, m = tid & 15;
 #pragma unroll
         for (int p = 0; p < NPASS; ++p) {
-            const int gi = rg + 16 * p, gc = gi < NG ? gi : NG - 1;  // clamped: loads stay in bounds
+            const int gi = rg + NRG * p, gc = gi < NG ? gi : NG - 1;  // clamped: loads stay in bounds
 #pragma unroll
             for (int j = 0; j < RPL; ++j) {
                 const int r = m * RPL + j;
-                raw[p][j] = *reinterpret_cast<const uint4 *>(a + (size_t)(r < nrow ? r : nrow - 1) * DK + gc * VEC);
+                raw[p][j] = *reinterpret_cast<const LT *>(a + (size_t)(r < nrow ? r : nrow - 1) * DK + gc * VEC);
             }
         }
     }
@@ -371,7 +376,7 @@ struct GateScan {
         const int rg = tid >> 4, m = tid & 15;
 #pragma unroll
         for (int p = 0; p < NPASS; ++p) {
-            const int gi = rg + 16 * p;
+            const int gi = rg + NRG * p;
             if (gi >= NG) continue;  // uniform over the 16 lanes of a row group
             float gv[RPL][VEC];
 #pragma unroll

@@ -291,14 +291,16 @@ __global__ __launch_bounds__((IntraCfg<C, DK, DV, F32>::THREADS), 4) __attribute
     {
         constexpr int LPR = DK / VEC, RPP = THREADS / LPR, NP = (C + RPP - 1) / RPP;
         const E *qg = q + tok0 * DK, *kg = k + tok0 * DK;
-        GateScan<C, DK, E> gate;
+        // eight-wave groups with 16-bit inputs run the gate on all their threads, others on 256
+        constexpr int GT = (THREADS == 512 && !F32) ? 512 : 256;
+        GateScan<C, DK, E, GT> gate;
         LowRankGate<C, DK, E, LR ? LRK : 16> lrt;  // its loads go first: its MFMAs need nothing else
-        // the gate and its prefix sum take the first four waves (256 threads)
+        // the low-rank gate and its prefix sum take the first four waves (256 threads)
         if constexpr (LR) {
             if (wave < 4)
                 lrt.load(lrh + ((size_t)b * T + (size_t)(c0 + n) * C) * LRK, lrz + (size_t)h * DK * LRK, wave, lane);
         } else {
-            if (wave < 4) gate.load(a + tok0 * DK, tid, nrow);
+            if (GT == THREADS || wave < 4) gate.load(a + tok0 * DK, tid, nrow);
         }
         // loads are unconditional (row indices clamped into the chunk's tokens); only the
         // stores are guarded, and rows past the tokens of a short chunk are stored as zeros
@@ -331,7 +333,7 @@ __global__ __launch_bounds__((IntraCfg<C, DK, DV, F32>::THREADS), 4) __attribute
         }
         if (tid < C) sB[tid] = (!VL || tid < nrow) ? to_f(bv) : 0.f;
         if constexpr (!LR) {
-            if (wave < 4) gate.finish(gmin2, logsig, sG, PG, tid, nrow);
+            if (GT == THREADS || wave < 4) gate.finish(gmin2, logsig, sG, PG, tid, nrow);
         }
         __syncthreads();
     }
