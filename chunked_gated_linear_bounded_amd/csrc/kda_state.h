@@ -194,10 +194,15 @@ __global__ __launch_bounds__(192, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 #pragma unroll
     for (int mt = 0; mt < NDK; ++mt) S[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     int sS = 0;
+    // |S 2^sS| < 2^eS (wave-uniform): 15 while the range holds, 14 just after a rescale, ZERO_S
+    // while the state is all zero (its product with W then bounds nothing)
+    constexpr int ZERO_S = -1000;
+    int eS = ZERO_S;
     unsigned int nonfinite = 0;
     // a fresh state taken to the scale the state is kept at (bf16 I/O)
     auto take_scale = [&]() {
         sS = 0;
+        eS = ZERO_S;
         if constexpr (!F32) {
             float m = 0.f;
 #pragma unroll
@@ -205,7 +210,9 @@ __global__ __launch_bounds__(192, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 #pragma unroll
                 for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(S[mt][i]));
             m = wave_max(m);
+            if (m != 0.f) eS = 15;  // a non-finite state bounds nothing either way
             if (m > 0.f && __builtin_isfinite(m)) {
+                eS = 14;
                 sS = pow2_scale(m);
 #pragma unroll
                 for (int mt = 0; mt < NDK; ++mt)
@@ -348,16 +355,19 @@ __global__ __launch_bounds__(192, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             const int sW = min(sS, eU + 16);
             const float fW = ldexp2(1.f, sW - sS - eW), fU = ldexp2(1.f, sW - eU);
             f32x4 U[NT];
-            float um = 0.f;
 #pragma unroll
-            for (int tt = 0; tt < NT; ++tt) {
+            for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    U[tt][i] = fmaf(ut[tt][i], fU, -(P[tt][i] * fW));
-                    um = fmaxf(um, fabsf(U[tt][i]));
-                }
-            }
-            const int sU = F32 ? 0 : pow2_scale(wave_max(um));
+                for (int i = 0; i < 4; ++i) U[tt][i] = fmaf(ut[tt][i], fU, -(P[tt][i] * fW));
+            // U's fp16 scale from bounds rather than from its wave-wide maximum (a chain of
+            // cross-lane steps on the state's critical path): the stored U~ and W^T blocks are below
+            // 2^14 and the state operand below 2^eS, so
+            //   |U| < 2^(14 + sW - eU) + 2^(14 + eS + log2 DK + sW - sS - eW)
+            // (no second term while the state is zero) and U 2^sU stays below 2^15.  A loose bound only moves U's smallest elements nearer
+            // fp16's subnormals, far below the rounding of its largest ones.
+            constexpr int LOG2DK = DK == 128 ? 7 : 6;
+            static_assert(DK == 64 || DK == 128, "dk of 64 or 128");
+            const int sU = F32 ? 0 : 14 - max(14 + sW - eU, eS == ZERO_S ? ZERO_S : 14 + eS + LOG2DK + sW - sS - eW);
             FH Uh[NTKB];
 #pragma unroll
             for (int kb = 0; kb < NTKB; ++kb) {
@@ -397,6 +407,7 @@ __global__ __launch_bounds__(192, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                     for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(S[mt][i]));
                 if (!wave_max_in(m, 2048.f, 32768.f)) {  // the wave-wide maximum only when it is needed
                     m = wave_max(m);
+                    eS = m == 0.f ? ZERO_S : 15;
                     if (m > 0.f && __builtin_isfinite(m) && (m >= 32768.f || m < 2048.f)) {
                         const int d = pow2_scale(m);
 #pragma unroll
@@ -404,7 +415,10 @@ __global__ __launch_bounds__(192, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 #pragma unroll
                             for (int i = 0; i < 4; ++i) S[mt][i] = ldexp2(S[mt][i], d);
                         sS += d;
+                        eS = 14;
                     }
+                } else {
+                    eS = 15;
                 }
             }
             if constexpr (VL) {
