@@ -228,6 +228,21 @@ def test_bounded_gate_keeps_subtile_exponent_within_bf16():
     assert overflow.whole_chunk_inverse_overflow(a, k, -5.0, 64, "bounded") > 0
 
 
+def test_whole_chunk_inverse_overflow_exact_counts():
+    # k = 1 and a constant gate g: referenced to the chunk start, the inverse decay of row s of a
+    # 64-token chunk is 2^(|g| log2(e) (s + 1)) (inclusive prefix sum), which overflows bf16 from the
+    # first row whose exponent reaches the bf16 threshold (~127.997); |k| = 2^10 lowers that row by
+    # ten exponent units.
+    T = 256
+    k = np.ones((1, 1, T, 1))
+    a = np.full((1, 1, T, 1), 50.0)  # sigmoid(50) is 1 in float64: g = -5, 7.2135 per row -> rows 17..63
+    assert overflow.whole_chunk_inverse_overflow(a, k, -5.0, 64, "bounded") == 47 * (T // 64)
+    a0 = np.zeros((1, 1, T, 1))  # g = -2.5, 3.6067 per row -> rows 35..63
+    assert overflow.whole_chunk_inverse_overflow(a0, k, -5.0, 64, "bounded") == 29 * (T // 64)
+    k10 = np.full((1, 1, T, 1), 1024.0)  # exponent + 10 -> rows 16..63
+    assert overflow.whole_chunk_inverse_overflow(a, k10, -5.0, 64, "bounded") == 48 * (T // 64)
+
+
 def test_overflow_predictor_exact_counts():
     # k = 1, constant gate.  Inside a 16-token tile the operand for offset j is
     # 2^(j*|g|*log2 e); it is non-finite in bf16 exactly when that exponent
