@@ -347,8 +347,11 @@ __global__ __launch_bounds__((IntraCfg<C, DK, DV, F32>::THREADS), 4) __attribute
     // K'_J = k e^{rho_J - G} goes to LDS in fp32, and a later wave I forms its key operand as
     // K'_J e^{rho_I - rho_J}, the per-channel factor built from the steps between tile starts
     // e^{rho_{J+1} - rho_J}.  Each pair's key operand is still rounded once, from fp32.
-    // Row tile I is carried by the pair of waves I and I + 4, each over half the channel
-    // K-blocks; the second hands its partial sub-tiles to the first through LDS.
+    // With eight waves, row tile I is carried by the pair of waves I and 7 - I, each over half
+    // the channel K-blocks; the second hands its partial sub-tiles to the first through LDS.
+    // Row tile I has I off-diagonal pairs, and waves w and w + 4 share a SIMD, so pairing tile I
+    // with tile 3 - I on each SIMD gives every SIMD the same three pairs (pairing waves I and
+    // I + 4 put both halves of tile 3 on one SIMD and both of tile 0 on another).
     f32x4 accMs[NT], accAs[NT];  // indexed by J
 #pragma unroll
     for (int J = 0; J < NT; ++J) {
@@ -356,7 +359,8 @@ __global__ __launch_bounds__((IntraCfg<C, DK, DV, F32>::THREADS), 4) __attribute
         accAs[J] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     unsigned int nonfinite = 0;
-    const int I = wave & 3, hs = wave >> 2;  // row tile; which half of the channel K-blocks
+    static_assert(NW == 4 || NT == 4, "eight waves only for four row tiles");
+    const int hs = wave >> 2, I = hs ? 3 - (wave & 3) : (wave & 3);  // channel half; row tile
     const int kb0 = hs * NKBH;
     F fqh[NKBH], fkh[NKBH];  // row operands of tile I (single bf16) for the earlier key tiles
     float kown[NKBH][8];     // K'_I in fp32, for the later row tiles
