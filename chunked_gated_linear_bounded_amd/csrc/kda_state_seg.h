@@ -152,8 +152,13 @@ __global__ __launch_bounds__((SegCfg<C, DK, DV, F32, PASS>::THREADS), 1) void kd
     // ---- the chains' states, kept scaled by 2^sS with the maximum in [2^11, 2^15) (bf16 I/O)
     f32x4 S[NCH][NDK];
     int sS[NCH];
+    // |S 2^sS| < 2^eS per chain (wave-uniform): 15 while the range holds, 14 just after a
+    // rescale, ZERO_S while the chain's state is all zero
+    constexpr int ZERO_S = -1000;
+    int eS[NCH];
     auto take_scale = [&](int c) {
         sS[c] = 0;
+        eS[c] = ZERO_S;
         if constexpr (!F32) {
             float m = 0.f;
 #pragma unroll
@@ -161,7 +166,9 @@ __global__ __launch_bounds__((SegCfg<C, DK, DV, F32, PASS>::THREADS), 1) void kd
 #pragma unroll
                 for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(S[c][mt][i]));
             m = wave_max(m);
+            if (m != 0.f) eS[c] = 15;  // a non-finite state bounds nothing either way
             if (m > 0.f && __builtin_isfinite(m)) {
+                eS[c] = 14;
                 sS[c] = pow2_scale(m);
 #pragma unroll
                 for (int mt = 0; mt < NDK; ++mt)
@@ -294,15 +301,20 @@ __global__ __launch_bounds__((SegCfg<C, DK, DV, F32, PASS>::THREADS), 1) void kd
             const int sW = is_phi(c) ? sS[c] : min(sS[c], cur[c].eu + 16);
             sWk[c] = sW;
             const float fU = is_phi(c) ? 0.f : ldexp2(1.f, sW - cur[c].eu), fW = ldexp2(1.f, sW - sS[c] - eW);
-            float um = 0.f;
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    P[c][tt][i] = fmaf((float)cur[c].u[tt][i], fU, -(P[c][tt][i] * fW));
-                    um = fmaxf(um, fabsf(P[c][tt][i]));
-                }
-            sU[c] = F32 ? 0 : pow2_scale(wave_max(um));
+                for (int i = 0; i < 4; ++i) P[c][tt][i] = fmaf((float)cur[c].u[tt][i], fU, -(P[c][tt][i] * fW));
+            // U's fp16 scale from bounds, as in the per-slice stage: the stored U~ and W^T blocks
+            // are below 2^14 and the chain's state operand below 2^eS, so
+            //   |U| < 2^(14 + sW - eu) + 2^(14 + eS + log2 DK + sW - sS - eW)
+            // (no U~ term on a transition chain, no W S term while the state is zero)
+            constexpr int LOG2DK = DK == 128 ? 7 : 6;
+            static_assert(DK == 64 || DK == 128, "dk of 64 or 128");
+            const int b1 = is_phi(c) ? ZERO_S : 14 + sW - cur[c].eu;
+            const int b2 = eS[c] == ZERO_S ? ZERO_S : 14 + eS[c] + LOG2DK + sW - sS[c] - eW;
+            const int bnd = max(b1, b2);
+            sU[c] = (F32 || bnd == ZERO_S) ? 0 : 14 - bnd;
 #pragma unroll
             for (int kb = 0; kb < NTKB; ++kb) {
                 float x[8];
@@ -357,6 +369,7 @@ __global__ __launch_bounds__((SegCfg<C, DK, DV, F32, PASS>::THREADS), 1) void kd
                     for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(S[c][mt][i]));
                 if (!wave_max_in(m, 2048.f, 32768.f)) {
                     m = wave_max(m);
+                    eS[c] = m == 0.f ? ZERO_S : 15;
                     if (m > 0.f && __builtin_isfinite(m) && (m >= 32768.f || m < 2048.f)) {
                         const int d = pow2_scale(m);
 #pragma unroll
@@ -364,7 +377,10 @@ __global__ __launch_bounds__((SegCfg<C, DK, DV, F32, PASS>::THREADS), 1) void kd
 #pragma unroll
                             for (int i = 0; i < 4; ++i) S[c][mt][i] = ldexp2(S[c][mt][i], d);
                         sS[c] += d;
+                        eS[c] = 14;
                     }
+                } else {
+                    eS[c] = 15;
                 }
             }
         }
