@@ -24,8 +24,6 @@
 
 namespace kda {
 
-typedef __attribute__((ext_vector_type(4))) _Float16 f16x4_;
-
 template <int DK, int DV>
 __global__ __launch_bounds__((DK / 16 + 1) * 64) void kda_bwd_rev_kernel(
     const unsigned char *__restrict__ ws, const __bf16 *__restrict__ dout, const float *__restrict__ dfinal, int T,
@@ -140,10 +138,10 @@ __global__ __launch_bounds__((DK / 16 + 1) * 64) void kda_bwd_rev_kernel(
             const int mt = wave + NCW * x;
             // K^ [token][key]: key tile mt, tile rows 0..15 (C = 16: the first tile of its pair);
             // W^T, Qbar^T [key][token]: key tile mt, half mt & 1 of pair mt / 2
-            const f16x4_ kr = ld_tr16<f16x4_>(curl + L.kh + 16 * (mt * 64 + 16 * p + 4 * g + kk));
+            const f16x4 kr = ld_tr16<f16x4>(curl + L.kh + 16 * (mt * 64 + 16 * p + 4 * g + kk));
             const int wo = 16 * ((mt >> 1) * 64 + 16 * p + 4 * g + kk) + 8 * (mt & 1);
-            const f16x4_ wr = ld_tr16<f16x4_>(curl + L.wt + wo);
-            const f16x4_ qr = ld_tr16<f16x4_>(curl + L.qbt + wo);
+            const f16x4 wr = ld_tr16<f16x4>(curl + L.wt + wo);
+            const f16x4 qr = ld_tr16<f16x4>(curl + L.qbt + wo);
             float ka[4], wa[4], qa[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
