@@ -251,13 +251,17 @@ __global__ __launch_bounds__(256, 2) void kda_bwd_chunk16_kernel(
     __syncthreads();
 
     // ---------------------------------------------------------------- gate, prefix sum
-    if (tid < DK) {
-        float acc = 0.f;
+    if (tid < DK) {  // one branch on the gate form for the whole scan, not one per row
+        auto scan = [&](auto ls) {
+            float acc = 0.f;
 #pragma unroll
-        for (int r = 0; r < C; ++r) {
-            acc += gate_log2(sG[r * LG + tid], gmin2, logsig);
-            sG[r * LG + tid] = acc;
-        }
+            for (int r = 0; r < C; ++r) {
+                acc += gate_log2_t<decltype(ls)::value>(sG[r * LG + tid], gmin2);
+                sG[r * LG + tid] = acc;
+            }
+        };
+        if (logsig) scan(std::true_type{});
+        else scan(std::false_type{});
     }
     __syncthreads();
 
