@@ -273,6 +273,45 @@ def test_state_that_decays_to_nothing_then_takes_new_values(path):
     _tol_check(fs.double().cpu().numpy(), rf, "bf16", "final_state")
 
 
+@pytest.mark.parametrize("path", ["segmented", "noalloc"])
+def test_state_exactly_zero_for_the_first_chunks(path):
+    # v = 0 for the first five chunks: from a zero initial state the state stays exactly zero
+    # (its range check finds a zero maximum), so the fp16 scale of U comes from the bound on U~
+    # alone until values arrive.  Against the oracle, and scaling v by 2^-20 or 2^20 scales every
+    # output and the final state exactly.  The allocation-free forward uses the per-slice stage,
+    # the plain one at two heads the segmented stage (24 chunks: three segments, each of whose
+    # local chains in pass 0 also starts from a zero state, beside the transition chains).
+    w = KI.Workload("zlead", 1, 2, 64 * 24, 128, 128, 64, "bf16", 2.0, False, 717)
+    _say("state exactly zero for the first chunks", path)
+    inp = _to_dev(KI.make_inputs(w))
+    inp["v"][:, :, :64 * 5] = 0
+
+    def run(x):
+        if path == "segmented":
+            return kda.chunk_fwd(x["q"], x["k"], x["v"], x["a"], x["beta"], chunk=64, return_final_state=True)
+        out = torch.empty_like(x["v"])
+        fs = torch.empty((1, 2, 128, 128), dtype=torch.float32, device="cuda")
+        kda.chunk_fwd_noalloc(x["q"], x["k"], x["v"], x["a"], x["beta"], out, chunk=64, final_state=fs)
+        return out, fs
+
+    out, fs = run(inp)
+    torch.cuda.synchronize()
+    ro, rf = _oracle(KI.to_f64(inp))
+    got = out.double().cpu().numpy()
+    assert np.all(got[:, :, :64 * 5] == 0)
+    _tol_check(got, ro, "bf16", "whole sequence")
+    for n in range(5, 24):
+        _tol_check(got[:, :, 64 * n:64 * n + 64], ro[:, :, 64 * n:64 * n + 64], "bf16", "chunk %d" % n)
+    _tol_check(fs.double().cpu().numpy(), rf, "bf16", "final_state")
+    for e in (-20, 20):
+        x = dict(inp)
+        x["v"] = inp["v"] * 2.0 ** e
+        o2, f2 = run(x)
+        torch.cuda.synchronize()
+        assert torch.equal(o2.float(), out.float() * 2.0 ** e), e
+        assert torch.equal(f2, fs * 2.0 ** e), e
+
+
 @pytest.mark.parametrize("io,chunk", [("bf16", 64), ("bf16", 16), ("fp32", 64)])
 def test_every_gate_saturated_at_the_bound(io, chunk):
     # a = +12 everywhere: every g sits at g_min = -5, the most negative value accepted, so the
