@@ -500,16 +500,29 @@ __global__ __launch_bounds__((IntraCfg<C, DK, DV, F32>::THREADS), 4) __attribute
     }
     float mmax = 0.f;  // largest |M| of row tile I
     if (hs == 0 && I < NT) {
-        // element (row r = 16I + 4g + i, col s = 16J + l16): M keeps s <= r, A keeps s < r (times beta_r)
+        // element (row r = 16I + 4g + i, col s = 16J + l16): M keeps s <= r, A keeps s < r (times
+        // beta_r).  The row tile is made a compile-time value, so only its causal tiles J <= I are
+        // touched (with I known only at run time every tile took a select per element).
+        auto mask = [&](auto ic) {
+            constexpr int IC = decltype(ic)::value;
+            if constexpr (IC < NT) {
 #pragma unroll
-        for (int J = 0; J < NT; ++J) {
+                for (int J = 0; J <= IC; ++J) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int rr = 4 * g + i;
-                if (I == J && l16 > rr) accMs[J][i] = 0.f;
-                accAs[J][i] = (I > J || l16 < rr) ? accAs[J][i] * sB[16 * I + rr] : 0.f;
-                if (J <= I) mmax = fmaxf(mmax, fabsf(accMs[J][i]));
+                    for (int i = 0; i < 4; ++i) {
+                        const int rr = 4 * g + i;
+                        if (J == IC && l16 > rr) accMs[J][i] = 0.f;
+                        accAs[J][i] = (J < IC || l16 < rr) ? accAs[J][i] * sB[16 * IC + rr] : 0.f;
+                        mmax = fmaxf(mmax, fabsf(accMs[J][i]));
+                    }
+                }
             }
+        };
+        switch (I) {
+            case 0: mask(std::integral_constant<int, 0>{}); break;
+            case 1: mask(std::integral_constant<int, 1>{}); break;
+            case 2: mask(std::integral_constant<int, 2>{}); break;
+            default: mask(std::integral_constant<int, 3>{}); break;
         }
     }
     mmax = wave_max(mmax);
