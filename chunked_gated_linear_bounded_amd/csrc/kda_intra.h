@@ -71,11 +71,20 @@ struct IntraCfg {
     // after the products of phase 1: the second wave of each row tile's pair hands its partial M
     // and A sub-tiles to the first through R1
     static constexpr int SZ_P = HS == 2 ? NJOB * 2 * 256 * 4 : 0;
+    // phase 3 with 16-bit operands: M in fp16 (pitch PMH halves) where A was, then the causal
+    // (row tile, token K-block) fragments of T diag(beta), each formed once by one wave and read
+    // by all (16 bytes per lane)
+    static constexpr int PMH = C + 8;
+    static constexpr int NTF = NT + (NT - 1) * (NT - 1) / 4;  // sum over rt of rt / 2 + 1
+    static constexpr int SZ_TF = F32 ? 0 : NTF * 64 * 16;
+    static constexpr int SZ_MT = SZ_A + SZ_TF;
     static constexpr int R1A = SZ_Q > SZ_A ? (SZ_Q > SZ_XD ? SZ_Q : SZ_XD) : (SZ_A > SZ_XD ? SZ_A : SZ_XD);
-    static constexpr int R1 = R1A > SZ_P ? R1A : SZ_P;
+    static constexpr int R1B = R1A > SZ_P ? R1A : SZ_P;
+    static constexpr int R1 = R1B > SZ_MT ? R1B : SZ_MT;
     static constexpr int R2 = C * PQ * ES;
     static constexpr int OFF_R1 = R0, OFF_R2 = R0 + R1, OFF_B = R0 + R1 + R2;
 
+    static constexpr int OFF_TF = OFF_R1 + SZ_A;
     static constexpr int OFF_SCR = OFF_B + C * 4;
     static constexpr int SMEM = OFF_SCR + 256 * 4;
     static constexpr int VEC = 16 / ES;          // elements per 16-byte access
@@ -690,12 +699,55 @@ __global__ __launch_bounds__((IntraCfg<C, DK, DV, F32>::THREADS), 4) __attribute
     // A is dead: M takes its place, scaled by 2^sM (the fp16 operand of M W and M U~, whatever the
     // magnitudes of q and k)
     const int sM_ = F32 ? 0 : pow2_scale(max_of(sMaxM));
+    OH *sMh = reinterpret_cast<OH *>(smem + Cfg::OFF_R1);  // 16-bit operands: M 2^sM in fp16
+    using FV = typename std::conditional<F32, f32x4, bf16x8>::type;  // a bf16 fragment
+    FV *sTF = reinterpret_cast<FV *>(smem + Cfg::OFF_TF);
+    static_assert(Cfg::NTF <= NW, "one T diag(beta) fragment per wave at most");
     if (hs == 0 && I < NT) {
 #pragma unroll
         for (int J = 0; J < NT; ++J) {
             if (J > I) continue;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sA[(16 * I + 4 * g + i) * PA + 16 * J + l16] = ldexp2(accMs[J][i], sM_);
+            for (int i = 0; i < 4; ++i) {
+                const float m = ldexp2(accMs[J][i], sM_);
+                if constexpr (F32) sA[(16 * I + 4 * g + i) * PA + 16 * J + l16] = m;
+                else sMh[(16 * I + 4 * g + i) * Cfg::PMH + 16 * J + l16] = (OH)m;
+            }
+        }
+    }
+    if constexpr (!F32) {
+        // Fragment f of T diag(beta) (the f-th causal (rt, kb) pair, row-major), formed by wave
+        // (f + NW / 2) mod NW: the waves that store no M or the fewest tiles of it
+        const int f = (wave + NW / 2) % NW;
+        int frt = -1, fkb = 0;
+        {
+            int n = 0;
+#pragma unroll
+            for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+                for (int kb = 0; kb <= rt / 2; ++kb) {
+                    if (n == f) { frt = rt; fkb = kb; }
+                    ++n;
+                }
+        }
+        if (frt >= 0) {
+            float x[8];
+            const int r = 16 * frt + l16;
+            const bool hi = 2 * fkb + 1 <= frt;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int s0 = 32 * fkb + 4 * g + i;
+                x[i] = sT[r * PA + s0] * sB[s0];
+                x[4 + i] = 0.f;
+            }
+            if (hi) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int s1 = 32 * fkb + 16 + 4 * g + i;
+                    x[4 + i] = sT[r * PA + s1] * sB[s1];
+                }
+            }
+            sTF[f * 64 + lane] = F::make(x).v;
         }
     }
     wait_vmcnt<0>();  // V has landed in LDS
@@ -746,21 +798,36 @@ __global__ __launch_bounds__((IntraCfg<C, DK, DV, F32>::THREADS), 4) __attribute
     float um[MAXVT];
     {
         F tf[NT][NTKB];
+        // fragment (rt, kb): with 16-bit operands read from LDS at its use (the pairs before row
+        // tile rt number rt + (rt - 1)^2 / 4)
+        auto tfr = [&](int rt, int kb) {
+            if constexpr (!F32) {
+                F f;
+                f.v = sTF[(rt + (rt - 1) * (rt - 1) / 4 + kb) * 64 + lane];
+                return f;
+            } else {
+                return tf[rt][kb];
+            }
+        };
 #pragma unroll
         for (int rt = 0; rt < NT; ++rt)
 #pragma unroll
             for (int kb = 0; kb < NTKB; ++kb) {
                 if (kb > rt / 2) continue;
-                float x[8];
-                const int r = 16 * rt + l16;
-                const bool hi = 2 * kb + 1 <= rt;
+                if constexpr (!F32) {
+                    continue;  // read where used
+                } else {
+                    float x[8];
+                    const int r = 16 * rt + l16;
+                    const bool hi = 2 * kb + 1 <= rt;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int s0 = 32 * kb + 4 * g + i, s1 = s0 + 16;
-                    x[i] = sT[r * PA + s0] * sB[s0];
-                    x[4 + i] = hi ? sT[r * PA + s1] * sB[s1] : 0.f;
+                    for (int i = 0; i < 4; ++i) {
+                        const int s0 = 32 * kb + 4 * g + i, s1 = s0 + 16;
+                        x[i] = sT[r * PA + s0] * sB[s0];
+                        x[4 + i] = hi ? sT[r * PA + s1] * sB[s1] : 0.f;
+                    }
+                    tf[rt][kb] = F::make(x);
                 }
-                tf[rt][kb] = F::make(x);
             }
 #pragma unroll
         for (int ci = 0; ci < MAXCT; ++ci) {
@@ -775,8 +842,9 @@ __global__ __launch_bounds__((IntraCfg<C, DK, DV, F32>::THREADS), 4) __attribute
                 f32x4 accT = {0.f, 0.f, 0.f, 0.f}, accW = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kb = 0; kb <= rt / 2; ++kb) {
-                    accT = mma(kf[kb], tf[rt][kb], accT);  // W^T (ct, rt)
-                    accW = mma(tf[rt][kb], kf[kb], accW);  // W (rt, ct)
+                    const F t = tfr(rt, kb);
+                    accT = mma(kf[kb], t, accT);  // W^T (ct, rt)
+                    accW = mma(t, kf[kb], accW);  // W (rt, ct)
                 }
                 wtr[ci][rt] = accT;
 #pragma unroll
@@ -796,7 +864,7 @@ __global__ __launch_bounds__((IntraCfg<C, DK, DV, F32>::THREADS), 4) __attribute
             for (int rt = 0; rt < NT; ++rt) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kb = 0; kb <= rt / 2; ++kb) acc = mma(tf[rt][kb], vf[kb], acc);
+                for (int kb = 0; kb <= rt / 2; ++kb) acc = mma(tfr(rt, kb), vf[kb], acc);
                 urow[vi][rt] = acc;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) um[vi] = fmaxf(um[vi], fabsf(acc[i]));
@@ -805,21 +873,34 @@ __global__ __launch_bounds__((IntraCfg<C, DK, DV, F32>::THREADS), 4) __attribute
     }
     {
         FM mf[NT][NTKB];  // M 2^sM
+        // fragment (rt, kb): with 16-bit operands two 8-byte reads of the fp16 M at its use
+        auto mfr = [&](int rt, int kb) {
+            if constexpr (!F32) {
+                const OH *p = sMh + (16 * rt + l16) * Cfg::PMH + 32 * kb + 4 * g;
+                return 2 * kb + 1 <= rt ? FM::load2(p, p + 16) : FM::load1(p);
+            } else {
+                return mf[rt][kb];
+            }
+        };
 #pragma unroll
         for (int rt = 0; rt < NT; ++rt)
 #pragma unroll
             for (int kb = 0; kb < NTKB; ++kb) {
                 if (kb > rt / 2) continue;
-                float y[8];
                 const int r = 16 * rt + l16;
                 const bool hi = 2 * kb + 1 <= rt;
+                if constexpr (!F32) {
+                    continue;  // read where used
+                } else {
+                    float y[8];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int s0 = 32 * kb + 4 * g + i, s1 = s0 + 16;
-                    y[i] = sM[r * PA + s0];
-                    y[4 + i] = hi ? sM[r * PA + s1] : 0.f;
+                    for (int i = 0; i < 4; ++i) {
+                        const int s0 = 32 * kb + 4 * g + i, s1 = s0 + 16;
+                        y[i] = sM[r * PA + s0];
+                        y[4 + i] = hi ? sM[r * PA + s1] : 0.f;
+                    }
+                    mf[rt][kb] = FM::make(y);
                 }
-                mf[rt][kb] = FM::make(y);
             }
         // dk tiles: Qbar^T = (Q e^G)^T - W^T M^T, kept in registers for the chunk's scale
 #pragma unroll
@@ -845,7 +926,7 @@ __global__ __launch_bounds__((IntraCfg<C, DK, DV, F32>::THREADS), 4) __attribute
             for (int rt = 0; rt < NT; ++rt) {
                 f32x4 mw = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kb = 0; kb <= rt / 2; ++kb) mw = mma(wa[kb], mf[rt][kb], mw);
+                for (int kb = 0; kb <= rt / 2; ++kb) mw = mma(wa[kb], mfr(rt, kb), mw);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     qtr[ci][rt][i] -= ldexp2(mw[i], unMW);
@@ -882,7 +963,7 @@ __global__ __launch_bounds__((IntraCfg<C, DK, DV, F32>::THREADS), 4) __attribute
             for (int rt = 0; rt < NT; ++rt) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kb = 0; kb <= rt / 2; ++kb) acc = mma(ua[kb], mf[rt][kb], acc);
+                for (int kb = 0; kb <= rt / 2; ++kb) acc = mma(ua[kb], mfr(rt, kb), acc);
                 orow[rt] = acc;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) om = fmaxf(om, fabsf(acc[i]));
