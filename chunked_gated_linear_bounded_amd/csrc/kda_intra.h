@@ -635,10 +635,11 @@ __global__ __launch_bounds__((IntraCfg<C, DK, DV, F32>::THREADS), 4) __attribute
     }
     if (wave < NT) {
         // Diagonal block I = wave.  N = A_II is strictly lower triangular, so N^16 = 0 and
-        // (I + N)^-1 = (I - N)(I + N^2)(I + N^4)(I + N^8) exactly: eight chained 16x16x16
-        // fp32 products.  In the 16x16x4 MFMA layout an accumulator holding Z is Z's B operand
+        // (I + N)^-1 = (I - N)(I + N^2)(I + N^4)(I + N^8) exactly: eight 16x16x16 fp32
+        // products.  In the 16x16x4 MFMA layout an accumulator holding Z is Z's B operand
         // and Z^T's A operand as it stands, so Z and Z^T are carried side by side and no
-        // product needs a shuffle.
+        // product needs a shuffle.  The factors commute, so the running product takes each one
+        // as soon as its power exists: four products deep instead of six.
         const int I = wave;
         const float *Ab = sA + (16 * I) * PA + 16 * I;
         f32x4 R, Rt;  // R: N[4g + i][l16]; Rt: N[l16][4g + i]
@@ -658,17 +659,17 @@ __global__ __launch_bounds__((IntraCfg<C, DK, DV, F32>::THREADS), 4) __attribute
         };
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
         const f32x4 N2 = prod(Rt, R, zero), N2t = prod(R, Rt, zero);
+        f32x4 Y, mRt;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            Y[i] = N2[i] + (4 * g + i == l16 ? 1.f : 0.f);
+            mRt[i] = -Rt[i];
+        }
+        Y = prod(mRt, Y, Y);                                     // (I - N)(I + N^2)
         const f32x4 N4 = prod(N2t, N2, zero), N4t = prod(N2, N2t, zero);
-        const f32x4 N8 = prod(N4t, N4, zero);
-        f32x4 Y;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) Y[i] = N8[i] + (4 * g + i == l16 ? 1.f : 0.f);
-        Y = prod(N4t, Y, Y);  // (I + N^4)(I + N^8)
-        Y = prod(N2t, Y, Y);  // (I + N^2)(...)
-        f32x4 mRt;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mRt[i] = -Rt[i];
-        Y = prod(mRt, Y, Y);  // (I - N)(...)
+        Y = prod(N4t, Y, Y);                                     // (I + N^4)(...)
+        const f32x4 N8t = prod(N4, N4t, zero);                   // (N^8)^T
+        Y = prod(N8t, Y, Y);                                     // (I + N^8)(...)
         float *Tb = sT + (16 * I) * PA + 16 * I;
 #pragma unroll
         for (int i = 0; i < 4; ++i) Tb[(4 * g + i) * PA + l16] = Y[i];
