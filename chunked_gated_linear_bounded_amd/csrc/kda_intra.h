@@ -675,27 +675,58 @@ __global__ __launch_bounds__((IntraCfg<C, DK, DV, F32>::THREADS), 4) __attribute
         for (int i = 0; i < 4; ++i) Tb[(4 * g + i) * PA + l16] = Y[i];
     }
     barrier_lds();  // V loads stay in flight through the solve
+    // X += sum_{K=K0}^{K1-1} A_IK T_KJ and Y += T_IK X (accumulator X as the B operand)
+    auto at_sum = [&](int I, int J, int K0, int K1, f32x4 X) {
+        for (int K = K0; K < K1; ++K) {
+            float av[4];
+            ld4(sA + (16 * I + l16) * PA + 16 * K + 4 * g, av);
 #pragma unroll
-    for (int d = 1; d < NT; ++d) {
-        const int J = wave, I = wave + d;
-        if (I < NT) {
-            f32x4 X = {0.f, 0.f, 0.f, 0.f};  // X = sum_{K=J}^{I-1} A_IK T_KJ
-            for (int K = J; K < I; ++K) {
-                float av[4];
-                ld4(sA + (16 * I + l16) * PA + 16 * K + 4 * g, av);
+            for (int st = 0; st < 4; ++st) X = mma4(av[st], sT[(16 * K + 4 * g + st) * PA + 16 * J + l16], X);
+        }
+        return X;
+    };
+    auto t_times = [&](int I, int K, f32x4 X, f32x4 Y) {
+        float tv[4];
+        ld4(sT + (16 * I + l16) * PA + 16 * K + 4 * g, tv);
 #pragma unroll
-                for (int st = 0; st < 4; ++st)
-                    X = mma4(av[st], sT[(16 * K + 4 * g + st) * PA + 16 * J + l16], X);
-            }
-            float tv[4];  // T_IJ = -T_II X
-            ld4(sT + (16 * I + l16) * PA + 16 * I + 4 * g, tv);
-            f32x4 Y = {0.f, 0.f, 0.f, 0.f};
+        for (int st = 0; st < 4; ++st) Y = mma4(tv[st], X[st], Y);
+        return Y;
+    };
+    auto t_store = [&](int I, int J, f32x4 Y) {
 #pragma unroll
-            for (int st = 0; st < 4; ++st) Y = mma4(tv[st], X[st], Y);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sT[(16 * I + 4 * g + i) * PA + 16 * J + l16] = -Y[i];
+        for (int i = 0; i < 4; ++i) sT[(16 * I + 4 * g + i) * PA + 16 * J + l16] = -Y[i];
+    };
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (NT == 4) {
+        // Two levels, from the 2 x 2 block form of the inverse of a block lower triangular
+        // matrix, [[L1, 0], [B, L2]]^-1 = [[T1, 0], [-T2 B T1, T2]], on 32-row halves: first the
+        // off-diagonal tiles of T1 and T2 (T_10, T_32), then the four tiles of -T2 (B T1) at
+        // once, each wave forming the tiles of B T1 it needs.
+        if (wave < 2) {
+            const int J = 2 * wave, I = J + 1;
+            t_store(I, J, t_times(I, I, at_sum(I, J, J, I, zero4), zero4));
         }
         barrier_lds();
+        if (wave < 4) {
+            const int I = 2 + (wave >> 1), J = wave & 1;
+            const f32x4 X2 = at_sum(2, J, J, 2, zero4);  // (B T1)_{2J}
+            f32x4 Y;
+            if (I == 2) {
+                Y = t_times(2, 2, X2, zero4);
+            } else {
+                const f32x4 X3 = at_sum(3, J, J, 2, zero4);  // (B T1)_{3J}
+                Y = t_times(3, 3, X3, t_times(3, 2, X2, zero4));
+            }
+            t_store(I, J, Y);
+        }
+        barrier_lds();
+    } else {
+#pragma unroll
+        for (int d = 1; d < NT; ++d) {
+            const int J = wave, I = wave + d;
+            if (I < NT) t_store(I, J, t_times(I, I, at_sum(I, J, J, I, zero4), zero4));  // T_IJ = -T_II X
+            barrier_lds();
+        }
     }
     // A is dead: M takes its place, scaled by 2^sM (the fp16 operand of M W and M U~, whatever the
     // magnitudes of q and k)
