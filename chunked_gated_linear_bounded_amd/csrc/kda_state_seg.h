@@ -20,7 +20,7 @@
 // with NCH independent chains (16-column slices of S^T, or of Phi in pass 0) whose products share
 // the operand fragments the wave reads from LDS.  The part of each chunk's record every chain
 // reads (W^T, K^, gamma and the exponents; pass 1 also Qbar^T) streams into a ring of LDS slots
-// with direct global->LDS loads, each wave issuing every fourth 1 KiB load and waiting for its
+// with direct global->LDS loads, each of the NW waves issuing every NW-th 1 KiB load and waiting for its
 // own with a partial vmcnt (vector-memory loads of a wave return in order), so that the ring
 // runs depth - 1 chunks ahead.  The per-slice blocks (U~, Oi^T and their exponents) are read by
 // the chain that owns them straight into registers, a chunk ahead.  Operand formats, scalings
@@ -42,8 +42,10 @@ struct SegCfg {
     static constexpr int NT = C / 16, NDK = DK / 16, NDV = DV / 16, NKB = DK / 32, NTKB = (NT + 1) / 2;
     static constexpr int NCHAIN = PASS ? NDV : NDV + NDK;  // pass 0: state slices, then Phi slices
     // eight waves (two per SIMD, so that one's waits are hidden by the other's work) where the
-    // chains divide evenly, else four
-    static constexpr int NW = NCHAIN % 8 == 0 ? 8 : 4;
+    // chains divide evenly, else four.  Pass 0 with 16-bit records and sixteen chains (dk = dv =
+    // 128) takes sixteen waves, one chain each: four per SIMD within 128 registers, so that the
+    // chains' MFMA and LDS latencies overlap further (each wave then reads its own fragments)
+    static constexpr int NW = (PASS == 0 && !F32 && NCHAIN == 16) ? 16 : (NCHAIN % 8 == 0 ? 8 : 4);
     static constexpr int NCH = NCHAIN / NW;
     static constexpr int THREADS = NW * 64;
     static_assert(NCHAIN % NW == 0, "chains per wave");
